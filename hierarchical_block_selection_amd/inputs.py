@@ -1,0 +1,123 @@
+"""Seeded synthetic inputs for PISA workloads.
+
+This module holds no part of the selection or attention arithmetic; it only
+draws tensors.  Both the HIP path's tests/benchmarks and the CPU oracle take
+their inputs from here.
+
+Shapes follow the library's layout: Q [B, Hq, N, d], K/V [B, Hkv, N, d];
+decode: q [B, Hq, d], caches [B, Hkv, capacity, d], cache_len [B].
+
+Value recipes:
+  * "inv_sqrt_d": i.i.d. N(0, 1/d) entries (random long-context prefill);
+  * "unit":       i.i.d. N(0, 1) entries (larger logit spread, fewer near-ties).
+Planted needles (per KV head): ``n_needles`` distinct leaf blocks b drawn from
+[1, M_1 - 3]; for each a target row r from [(b + 2) C, N); the block's keys are
+replaced by alpha * q_r / |q_r| + fresh noise of the recipe's scale, where q_r
+is the first query head of the group at row r.
+
+Seeds: tensor seeds are seed+0 (Q), seed+1 (K), seed+2 (V), seed+3 (needle
+positions, CPU generator), seed+4 (needle noise).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import torch
+
+
+def _sigma(recipe: str, head_dim: int) -> float:
+    if recipe == "inv_sqrt_d":
+        return 1.0 / math.sqrt(head_dim)
+    if recipe == "unit":
+        return 1.0
+    raise ValueError(f"unknown value recipe {recipe!r}")
+
+
+def seeded_normal(shape, seed: int, sigma: float, dtype: torch.dtype, device) -> torch.Tensor:
+    """N(0, sigma^2) tensor drawn in fp32 from a generator seeded with ``seed``,
+    then cast.  Large tensors are drawn slice by slice along dim 0 from the
+    same generator, so the values do not depend on available memory."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    out = torch.empty(shape, dtype=dtype, device=device)
+    for b in range(shape[0]):
+        x = torch.randn(shape[1:], generator=gen, dtype=torch.float32, device=device)
+        out[b] = (x * sigma).to(dtype)
+    return out
+
+
+@dataclass
+class Needle:
+    batch: int
+    kv_head: int
+    block: int
+    target_row: int
+
+
+@dataclass
+class PrefillInputs:
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    needles: list = field(default_factory=list)
+
+
+def prefill_inputs(batch, heads_q, heads_kv, seq_len, head_dim, dtype=torch.bfloat16,
+                   seed=0, recipe="inv_sqrt_d", n_needles=0, alpha=4.0, block=64,
+                   device="cpu") -> PrefillInputs:
+    sigma = _sigma(recipe, head_dim)
+    q = seeded_normal((batch, heads_q, seq_len, head_dim), seed + 0, sigma, dtype, device)
+    k = seeded_normal((batch, heads_kv, seq_len, head_dim), seed + 1, sigma, dtype, device)
+    v = seeded_normal((batch, heads_kv, seq_len, head_dim), seed + 2, sigma, dtype, device)
+    needles = []
+    if n_needles:
+        n_leaves = -(-seq_len // block)
+        if n_leaves - 3 < n_needles:
+            raise ValueError("sequence too short for the requested needles")
+        pos_gen = torch.Generator().manual_seed(seed + 3)
+        noise_gen = torch.Generator(device=device).manual_seed(seed + 4)
+        group = heads_q // heads_kv
+        for b in range(batch):
+            for h in range(heads_kv):
+                blocks = (torch.randperm(n_leaves - 3, generator=pos_gen)[:n_needles] + 1).tolist()
+                for blk in blocks:
+                    lo = (blk + 2) * block
+                    r = int(torch.randint(lo, seq_len, (1,), generator=pos_gen))
+                    qr = q[b, h * group, r].to(torch.float32)
+                    u = qr / qr.norm()
+                    rows = min(block, seq_len - blk * block)
+                    noise = torch.randn((rows, head_dim), generator=noise_gen,
+                                        dtype=torch.float32, device=device) * sigma
+                    k[b, h, blk * block:blk * block + rows] = (alpha * u + noise).to(dtype)
+                    needles.append(Needle(b, h, blk, r))
+    return PrefillInputs(q, k, v, needles)
+
+
+@dataclass
+class DecodeInputs:
+    q: torch.Tensor
+    k_cache: torch.Tensor
+    v_cache: torch.Tensor
+    cache_len: torch.Tensor
+
+
+def decode_inputs(batch, heads_q, heads_kv, capacity, head_dim, dtype=torch.bfloat16,
+                  seed=0, recipe="inv_sqrt_d", cache_len=None, device="cpu") -> DecodeInputs:
+    """One new query token per sequence plus a filled KV cache.
+
+    ``cache_len``: None (every sequence full), an int, or a list of B ints.
+    """
+    sigma = _sigma(recipe, head_dim)
+    q = seeded_normal((batch, heads_q, head_dim), seed + 0, sigma, dtype, device)
+    kc = seeded_normal((batch, heads_kv, capacity, head_dim), seed + 1, sigma, dtype, device)
+    vc = seeded_normal((batch, heads_kv, capacity, head_dim), seed + 2, sigma, dtype, device)
+    if cache_len is None:
+        lens = [capacity] * batch
+    elif isinstance(cache_len, int):
+        lens = [cache_len] * batch
+    else:
+        lens = list(cache_len)
+    if len(lens) != batch or min(lens) < 1 or max(lens) > capacity:
+        raise ValueError("cache_len must hold B values in [1, capacity]")
+    return DecodeInputs(q, kc, vc, torch.tensor(lens, dtype=torch.int32, device=device))

@@ -1,0 +1,72 @@
+"""Plant plausible mistakes in a copy of the oracle and check that the pins catch
+each one (no GPU).  The real oracle is never modified: each mutant is the oracle's
+source text with one edit, loaded as a separate in-memory module."""
+import os
+import sys
+import types
+
+import pytest
+
+import oracle_pins
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "pisa_oracle.py")
+
+# (name, text to find, replacement) -- each must occur exactly once.
+MUTATIONS = [
+    ("lse_replaced_by_mean", "return logsumexp(z)", "return float(np.mean(z))"),
+    ("scale_dropped", "z = scale * (child_vecs @ q)", "z = (child_vecs @ q)"),
+    ("child_index_shifted", "range(branch * node, branch * node + branch)",
+     "range(branch * node + 1, branch * node + branch + 1)"),
+    ("leaf_span_off_by_one", "keys[i * block:min((i + 1) * block, n)].mean(axis=0)",
+     "keys[i * block:min((i + 1) * block + 1, n)].mean(axis=0)"),
+    ("future_drop_strict", "cands = [i for i in cands if i <= limit]",
+     "cands = [i for i in cands if i < limit]"),
+    ("ranking_sign_flipped", "key=lambda i: (-scores[i], i)", "key=lambda i: (scores[i], i)"),
+    ("tie_break_reversed", "key=lambda i: (-scores[i], i)", "key=lambda i: (-scores[i], -i)"),
+    ("prev_block_wrong", "f.add((c - 1) >> (level - 1))", "f.add((c - 2) >> (level - 1))"),
+    ("first_block_not_forced", "        f.add(0)\n", ""),
+    ("keep_all_strict", "if len(cands) <= topk:", "if len(cands) < topk:"),
+    ("forced_not_charged",
+     "best, margin = top_by_score(rankable, scores, topk - len(forced))\n            kept = sorted(forced) + best",
+     "best, margin = top_by_score(rankable, scores, topk)\n            kept = sorted(forced) + best"),
+    ("bsa_forced_not_charged",
+     "best, margin = top_by_score(rankable, scores, topk - len(forced))\n    return RowSelection(",
+     "best, margin = top_by_score(rankable, scores, topk)\n    return RowSelection("),
+    ("attention_mask_off_by_one", "if (not causal) or j <= t]", "if (not causal) or j < t]"),
+    ("gqa_heads_averaged", "        total += reduce_logits(z, variant)\n    return total",
+     "        total += reduce_logits(z, variant)\n    return total / len(q_heads)"),
+    ("softmax_unnormalised", "outs.append((p @ vv) / p.sum())", "outs.append(p @ vv)"),
+    ("pyramid_parent_uses_sum", ".mean(axis=0)\n                                for i in range(m)]))",
+     ".sum(axis=0)\n                                for i in range(m)]))"),
+    ("pisa2_sample_variance", "np.mean(z) + 0.5 * np.var(z)", "np.mean(z) + 0.5 * np.var(z, ddof=1)"),
+    ("bsa_scale_dropped", "lambda i: float(sum(scale * (leaf_sum[i] @ q) for q in q_heads))",
+     "lambda i: float(sum((leaf_sum[i] @ q) for q in q_heads))"),
+]
+
+
+def load_mutant(name, find, repl):
+    text = open(SRC).read()
+    assert text.count(find) == 1, f"mutation {name}: pattern occurs {text.count(find)} times"
+    mutated = text.replace(find, repl)
+    mod = types.ModuleType(f"oracle_mutant_{name}")
+    mod.__file__ = SRC
+    sys.modules[mod.__name__] = mod  # dataclasses look the module up by name
+    try:
+        exec(compile(mutated, f"<mutant {name}>", "exec"), mod.__dict__)
+    finally:
+        sys.modules.pop(mod.__name__, None)
+    return mod
+
+
+@pytest.mark.parametrize("name,find,repl", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_mutation_is_caught(name, find, repl):
+    mutant = load_mutant(name, find, repl)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(mutant)
+        except Exception as exc:  # AssertionError or a crash both count as caught
+            caught.append(f"{pin.__name__}: {type(exc).__name__}")
+            break
+    assert caught, f"no pin caught the planted mistake {name}"

@@ -1,0 +1,49 @@
+// Host-side launch interface between the C ABI (pisa_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "pisa_common.h"
+
+namespace pisa {
+
+// A validated problem in the form the launchers use.
+struct LaunchShape {
+  int batch, heads_q, heads_kv, seq_len, head_dim, block, topk, group;
+  bool bf16, causal, force;
+  float scale;
+  LevelTable lv;
+};
+
+hipError_t launch_pyramid(const LaunchShape& s, const void* k, float* pyr, hipStream_t st);
+
+// Per-query fused selection (leaf level included).
+hipError_t launch_select_fused(const LaunchShape& s, const void* q, const void* k,
+                               const float* pyr, int32_t* idx, float* score, hipStream_t st);
+
+// Two-stage selection: workspace layout and launch.
+size_t select_two_stage_ws_bytes(const LaunchShape& s);
+bool select_two_stage_supported(const LaunchShape& s);
+hipError_t launch_select_two_stage(const LaunchShape& s, const void* q, const void* k,
+                                   const float* pyr, int32_t* idx, float* score, void* ws,
+                                   hipStream_t st);
+
+// BSA flat selection: scores to workspace, then Top-K.
+size_t bsa_ws_bytes(const LaunchShape& s);
+hipError_t launch_bsa(const LaunchShape& s, const void* q, const float* pyr, int32_t* idx,
+                      float* score, void* ws, hipStream_t st);
+
+// Block-sparse attention.
+size_t attn_ws_bytes(const LaunchShape& s);
+hipError_t launch_attn(const LaunchShape& s, const void* q, const void* k, const void* v,
+                       const int32_t* idx, void* out, float* lse, void* ws, hipStream_t st);
+
+// Decode step.
+size_t decode_ws_bytes(const LaunchShape& s);
+hipError_t launch_decode(const LaunchShape& s, const int32_t* cache_len, const void* q,
+                         const void* kc, const void* vc, const float* pyr, int32_t* idx,
+                         float* score, void* out, float* lse, void* ws, hipStream_t st);
+
+}  // namespace pisa

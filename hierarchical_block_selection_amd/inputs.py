@@ -121,3 +121,41 @@ def decode_inputs(batch, heads_q, heads_kv, capacity, head_dim, dtype=torch.bflo
     if len(lens) != batch or min(lens) < 1 or max(lens) > capacity:
         raise ValueError("cache_len must hold B values in [1, capacity]")
     return DecodeInputs(q, kc, vc, torch.tensor(lens, dtype=torch.int32, device=device))
+
+
+# Workload shapes of the five configurations: prefill c1-c4 (c4 sweeps N) and
+# the decode step c5.  Sizes only; inputs come from prefill_inputs /
+# decode_inputs with the given seed and recipe.
+WORKLOADS = {
+    "c1": dict(kind="prefill", batch=1, heads_q=2, heads_kv=2, seq_len=2048, head_dim=64,
+               block=64, topk=4, dtype=torch.float32, recipe="unit", n_needles=0, seed=1000),
+    "c2": dict(kind="prefill", batch=1, heads_q=16, heads_kv=16, seq_len=16384, head_dim=128,
+               block=64, topk=16, dtype=torch.bfloat16, recipe="inv_sqrt_d", n_needles=8,
+               seed=2000),
+    "c3": dict(kind="prefill", batch=1, heads_q=8, heads_kv=8, seq_len=65536, head_dim=128,
+               block=64, topk=16, dtype=torch.bfloat16, recipe="inv_sqrt_d", n_needles=8,
+               seed=3000),
+    "c4a": dict(kind="prefill", batch=1, heads_q=4, heads_kv=4, seq_len=32768, head_dim=128,
+                block=64, topk=16, dtype=torch.bfloat16, recipe="inv_sqrt_d", n_needles=0,
+                seed=4000),
+    "c4b": dict(kind="prefill", batch=1, heads_q=4, heads_kv=4, seq_len=131072, head_dim=128,
+                block=64, topk=16, dtype=torch.bfloat16, recipe="inv_sqrt_d", n_needles=0,
+                seed=4010),
+    "c4c": dict(kind="prefill", batch=1, heads_q=4, heads_kv=4, seq_len=262144, head_dim=128,
+                block=64, topk=16, dtype=torch.bfloat16, recipe="inv_sqrt_d", n_needles=0,
+                seed=4020),
+    "c5": dict(kind="decode", batch=32, heads_q=32, heads_kv=8, seq_len=131072, head_dim=128,
+               block=64, topk=16, dtype=torch.bfloat16, recipe="inv_sqrt_d", n_needles=0,
+               seed=5000),
+}
+
+
+def sample_rows(seq_len: int, block: int, topk: int, n_random: int, seed: int) -> list[int]:
+    """Query rows for sampled checks: block edges near the start, around the
+    budget boundary K*C, the last rows, plus seeded random rows."""
+    fixed = {0, 1, block - 1, block, 2 * block - 1, 2 * block, 3 * block + 5,
+             topk * block - 1, topk * block, topk * block + 1, 2 * topk * block + 7,
+             seq_len // 2, seq_len - block, seq_len - 2, seq_len - 1}
+    gen = torch.Generator().manual_seed(seed)
+    rand = torch.randint(0, seq_len, (n_random,), generator=gen).tolist()
+    return sorted(r for r in fixed | set(rand) if 0 <= r < seq_len)

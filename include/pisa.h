@@ -1,0 +1,196 @@
+/*
+ * pisa.h - C ABI of the MI355X (gfx950) implementation of PISA's forward path:
+ * the mean-pooled key pyramid, coarse-to-fine pyramid Top-K block selection
+ * with LogSumExp scoring, the flat BSA selector it is compared with,
+ * block-sparse attention over the selected blocks, and a GQA decode step.
+ *
+ * Source of the method: "Block Sparse Attention with Log-Linear Complexity"
+ * (PISA), as laid out by the close-reading page "论文精读 · Block Sparse
+ * Attention with Log-Linear Complexity (PISA)"; sections and equations below
+ * refer to that page.
+ *
+ * Conventions shared by every entry point
+ * ----------------------------------------
+ * - All functions are extern "C", never throw, and return a pisa_status.
+ * - Every tensor argument is a DEVICE pointer to contiguous row-major memory,
+ *   16-byte aligned, owned by the caller.  The library allocates no device or
+ *   host memory and keeps no state between calls; calls are re-entrant.
+ * - Layouts (B batch, Hq query heads, Hkv KV heads, N tokens, d head dim,
+ *   K budget, R pyramid rows):
+ *     Q, O        [B, Hq,  N, d]   dtype = problem.dtype
+ *     K, V        [B, Hkv, N, d]   dtype = problem.dtype
+ *     pyramid     [B, Hkv, R, d]   float32; level l occupies rows
+ *                                  row_offsets[l-1] .. row_offsets[l]-1
+ *     block_idx   [B, Hkv, N, K]   int32, each row ascending, padded with -1
+ *     block_score [B, Hkv, N, K]   float32: the score that ranked the entry;
+ *                                  +inf for entries kept without ranking
+ *                                  (forced, or all candidates kept); -inf for
+ *                                  padding
+ *     row_lse     [B, Hq, N]       float32 natural-log softmax normaliser
+ *   Query head h reads KV head h / (Hq / Hkv).
+ * - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *   asynchronously; outputs are valid once the stream has been synchronised.
+ * - Validation happens before anything is enqueued: on any error the function
+ *   returns < 0 and has written nothing.  A failed launch returns PISA_ERR_HIP;
+ *   pisa_last_error() then describes it (thread-local text).
+ * - Outputs are bitwise reproducible run to run (no floating-point atomics).
+ *
+ * Supported now: d in {64, 128}; C in {16, 32, 64}; g = 2; 1 <= K <= 32;
+ * K >= 3 with PISA_FORCE_FIRST_PREV (K >= 1 otherwise); Hq % Hkv == 0 with
+ * Hq / Hkv <= 16; PISA_FORCE_FIRST_PREV requires PISA_CAUSAL.
+ */
+#ifndef PISA_H_
+#define PISA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PISA_OK = 0,
+  PISA_ERR_INVALID = -1,     /* null pointer, bad shape or flag combination  */
+  PISA_ERR_UNSUPPORTED = -2, /* valid but outside the supported d/C/K/g/G    */
+  PISA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required   */
+  PISA_ERR_HIP = -4          /* a HIP call or kernel launch failed           */
+} pisa_status;
+
+typedef enum { PISA_F32 = 0, PISA_BF16 = 1 } pisa_dtype;
+
+enum {
+  /* Causal prefill/decode (§5.3): nodes entirely after the current leaf are
+     dropped, the node holding the current leaf is kept without being ranked,
+     and attention masks tokens after t inside the current block. */
+  PISA_CAUSAL = 1u,
+  /* Also keep leaf 0 and leaf c-1 (and their ancestors) for query t in leaf c,
+     as the NSA/FLA policy of §5.3; they take slots of the budget K. */
+  PISA_FORCE_FIRST_PREV = 2u
+};
+
+enum { PISA_MAX_LEVELS = 32 };
+
+typedef struct {
+  int32_t batch;     /* B */
+  int32_t heads_q;   /* Hq */
+  int32_t heads_kv;  /* Hkv */
+  int32_t seq_len;   /* N (prefill) or cache capacity (decode) */
+  int32_t head_dim;  /* d */
+  int32_t block;     /* C, leaf block size */
+  int32_t topk;      /* K, blocks kept per query and KV head */
+  int32_t branch;    /* g, must be 2 */
+  uint32_t flags;    /* PISA_CAUSAL | PISA_FORCE_FIRST_PREV */
+  int32_t dtype;     /* pisa_dtype of Q/K/V/O */
+  float scale;       /* logit scale; <= 0 selects 1/sqrt(d) */
+} pisa_problem;
+
+/* Operations for pisa_workspace_bytes. */
+enum {
+  PISA_OP_PYRAMID = 0,
+  PISA_OP_SELECT = 1,
+  PISA_OP_BSA = 2,
+  PISA_OP_ATTN = 3,
+  PISA_OP_DECODE = 4
+};
+
+/* Selection strategies for pisa_select (problem-independent hint). */
+enum {
+  PISA_SELECT_AUTO = 0,      /* library picks (two-stage when it pays) */
+  PISA_SELECT_FUSED = 1,     /* one kernel per query, leaf level included */
+  PISA_SELECT_TWO_STAGE = 2  /* intermediate levels per query, then leaf
+                                blocks scored once per group of queries */
+};
+
+/* Pyramid geometry of eq. (3) (§4.1): M_1 = ceil(N/C), M_{l+1} = ceil(M_l/2)
+ * until one node remains.  Host-only, touches no device.
+ *   levels:      out, number of levels L (may be NULL)
+ *   row_offsets: out, L+1 entries: level l starts at row_offsets[l-1]; the
+ *                last entry is R, the total row count (may be NULL)
+ *   max_offsets: capacity of row_offsets (>= L+1 when row_offsets != NULL)
+ * Errors: PISA_ERR_INVALID for N < 1, C < 1, g != 2 or too small a buffer. */
+int pisa_pyramid_layout(int32_t seq_len, int32_t block, int32_t branch, int32_t* levels,
+                        int64_t* row_offsets, int32_t max_offsets);
+
+/* Device workspace (bytes) that `op` needs for this problem; 0 means none.
+ * Pass a buffer at least this large as `ws` / `ws_bytes`.  Host-only. */
+int pisa_workspace_bytes(const pisa_problem* problem, int32_t op, size_t* bytes);
+
+/* Key pyramid (§4.1 eqs. (3), (4)): level 1 row i is the mean of keys
+ * [iC, min((i+1)C, N)); level l+1 row i is the mean of the existing level-l
+ * rows {2i, 2i+1}.  Reads K once, writes every level of `pyramid`.
+ *   k:        [B, Hkv, N, d] dtype
+ *   pyramid:  [B, Hkv, R, d] float32, out */
+int pisa_build_pyramid(const pisa_problem* problem, const void* k, float* pyramid, void* stream);
+
+/* PISA selection (§4.2 eqs. (5), (6); §4.3 eq. (7); §4.4 eq. (11); §5.3):
+ * per (b, kv head, t), descend from the root; at each level drop future nodes,
+ * keep all candidates if there are at most K, else keep the forced nodes plus
+ * the best K-#F others by sum over the group's heads of
+ * LSE_r(scale * q . kbar_r) over the node's children (raw keys at level 1),
+ * ties to the lower index; expand kept nodes to their children.
+ *   q:           [B, Hq, N, d] dtype
+ *   k:           [B, Hkv, N, d] dtype (leaf level scores raw keys)
+ *   pyramid:     from pisa_build_pyramid
+ *   block_idx:   [B, Hkv, N, K] int32, out
+ *   block_score: [B, Hkv, N, K] float32, out, may be NULL
+ *   strategy:    PISA_SELECT_*
+ *   ws/ws_bytes: workspace of pisa_workspace_bytes(PISA_OP_SELECT) bytes */
+int pisa_select(const pisa_problem* problem, const void* q, const void* k, const float* pyramid,
+                int32_t* block_idx, float* block_score, int32_t strategy, void* ws,
+                size_t ws_bytes, void* stream);
+
+/* BSA flat selection (§02 eq. (1)): s_{t,i} = sum over the group's heads of
+ * scale * q . kbar_i over every eligible leaf summary (level 1 of `pyramid`),
+ * written in full to the workspace, then the forced blocks plus the best
+ * K-#F others (same forcing, causal and tie rules as pisa_select).
+ *   q, pyramid, block_idx, block_score: as pisa_select
+ *   ws/ws_bytes: pisa_workspace_bytes(PISA_OP_BSA) bytes (holds the scores) */
+int pisa_bsa_select(const pisa_problem* problem, const void* q, const float* pyramid,
+                    int32_t* block_idx, float* block_score, void* ws, size_t ws_bytes,
+                    void* stream);
+
+/* Block-sparse attention (§02 eq. (2); mask of §5.3): for each query head h
+ * and position t, softmax(scale * q . k_j) weighted sum of v_j over the
+ * tokens of the blocks in block_idx[b, h / G, t, :] (-1 entries skipped),
+ * restricted to j <= t when PISA_CAUSAL is set.
+ *   q, k, v:   as above
+ *   block_idx: [B, Hkv, N, K] int32 leaf indices; rows need not be sorted;
+ *              entries < 0 or >= ceil(N/C) are skipped; duplicates are
+ *              not allowed (they would be counted twice)
+ *   out:       [B, Hq, N, d] dtype, out
+ *   row_lse:   [B, Hq, N] float32, out, may be NULL
+ *   ws/ws_bytes: pisa_workspace_bytes(PISA_OP_ATTN) bytes */
+int pisa_block_sparse_attn(const pisa_problem* problem, const void* q, const void* k,
+                           const void* v, const int32_t* block_idx, void* out, float* row_lse,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/* One decode step (§5.1: single fused stage for decode; §5.3 pyramid cache):
+ * for each sequence b the new query sits at t = cache_len[b] - 1 and its key
+ * and value are already in the caches and the pyramid.  Selection and
+ * attention are those of pisa_select / pisa_block_sparse_attn at row t.
+ *   problem.seq_len: cache capacity; PISA_CAUSAL must be set
+ *   cache_len: [B] int32 device, 1 <= cache_len[b] <= capacity (values out
+ *              of range produce -1 indices and zero outputs for that row)
+ *   q:         [B, Hq, d] dtype
+ *   k_cache, v_cache: [B, Hkv, capacity, d] dtype
+ *   pyramid:   [B, Hkv, R(capacity), d] float32 built over the cache
+ *   block_idx: [B, Hkv, K] int32, out;  block_score: same, may be NULL
+ *   out:       [B, Hq, d] dtype, out;   row_lse: [B, Hq] float32, may be NULL
+ *   ws/ws_bytes: pisa_workspace_bytes(PISA_OP_DECODE) bytes */
+int pisa_decode_step(const pisa_problem* problem, const int32_t* cache_len, const void* q,
+                     const void* k_cache, const void* v_cache, const float* pyramid,
+                     int32_t* block_idx, float* block_score, void* out, float* row_lse,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Static text for a status code. */
+const char* pisa_status_string(int status);
+
+/* Detail of the last error on the calling thread ("" if none). */
+const char* pisa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PISA_H_ */

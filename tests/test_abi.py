@@ -1,0 +1,150 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol that
+include/pisa.h declares, computes the pyramid layout, sizes workspaces, and
+rejects every invalid argument before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+from hierarchical_block_selection_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pisa.h")
+
+
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("libpisa.so not built (run __graft_entry__.build())")
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(pisa_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ("pisa_build_pyramid", "pisa_select", "pisa_bsa_select",
+                 "pisa_block_sparse_attn", "pisa_decode_step"):
+        assert want in names
+    assert set(names) == set(_lib.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    L = lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+@pytest.mark.parametrize("n,c", [(2048, 64), (16384, 64), (65536, 64), (131072, 64),
+                                  (262144, 64), (1, 64), (63, 64), (65, 16), (5 * 4 + 3, 4)])
+def test_pyramid_layout_matches_eq3(n, c):
+    L = lib()
+    levels = ctypes.c_int32()
+    offs = (ctypes.c_int64 * 33)()
+    assert L.pisa_pyramid_layout(n, c, 2, ctypes.byref(levels), offs, 33) == 0
+    sizes = oracle.pyramid_level_sizes(n, c)
+    assert levels.value == len(sizes)
+    acc = 0
+    for i, m in enumerate(sizes):
+        assert offs[i] == acc
+        acc += m
+    assert offs[len(sizes)] == acc
+
+
+def test_pyramid_layout_errors():
+    L = lib()
+    n = ctypes.c_int32()
+    offs = (ctypes.c_int64 * 4)()
+    assert L.pisa_pyramid_layout(0, 64, 2, ctypes.byref(n), None, 0) == _lib.PISA_ERR_INVALID
+    assert L.pisa_pyramid_layout(100, 64, 3, ctypes.byref(n), None, 0) == _lib.PISA_ERR_INVALID
+    # 2048/64 -> 6 levels needs 7 offsets
+    assert L.pisa_pyramid_layout(2048, 64, 2, ctypes.byref(n), offs, 4) == _lib.PISA_ERR_INVALID
+
+
+def problem(**kw):
+    base = dict(batch=1, heads_q=4, heads_kv=4, seq_len=4096, head_dim=128, block=64, topk=16,
+                branch=2, flags=_lib.PISA_CAUSAL | _lib.PISA_FORCE_FIRST_PREV,
+                dtype=_lib.PISA_BF16, scale=0.0)
+    base.update(kw)
+    return _lib.PisaProblem(**base)
+
+
+BAD = [
+    (dict(batch=0), _lib.PISA_ERR_INVALID),
+    (dict(heads_q=6, heads_kv=4), _lib.PISA_ERR_INVALID),
+    (dict(seq_len=0), _lib.PISA_ERR_INVALID),
+    (dict(topk=0), _lib.PISA_ERR_INVALID),
+    (dict(dtype=7), _lib.PISA_ERR_INVALID),
+    (dict(flags=_lib.PISA_FORCE_FIRST_PREV), _lib.PISA_ERR_INVALID),
+    (dict(flags=8), _lib.PISA_ERR_INVALID),
+    (dict(scale=float("nan")), _lib.PISA_ERR_INVALID),
+    (dict(branch=4), _lib.PISA_ERR_UNSUPPORTED),
+    (dict(head_dim=96), _lib.PISA_ERR_UNSUPPORTED),
+    (dict(block=128), _lib.PISA_ERR_UNSUPPORTED),
+    (dict(topk=33), _lib.PISA_ERR_UNSUPPORTED),
+    (dict(topk=2), _lib.PISA_ERR_UNSUPPORTED),
+    (dict(heads_q=64, heads_kv=2), _lib.PISA_ERR_UNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("kw,code", BAD, ids=[str(b[0]) for b in BAD])
+def test_invalid_problems_rejected_by_every_entry_point(kw, code):
+    L = lib()
+    p = problem(**kw)
+    dummy = ctypes.create_string_buffer(64)
+    ptr = ctypes.cast(dummy, ctypes.c_void_p)
+    pp = ctypes.byref(p)
+    assert L.pisa_build_pyramid(pp, ptr, ptr, None) == code
+    assert L.pisa_select(pp, ptr, ptr, ptr, ptr, ptr, 0, ptr, 1 << 40, None) == code
+    assert L.pisa_bsa_select(pp, ptr, ptr, ptr, ptr, ptr, 1 << 40, None) == code
+    assert L.pisa_block_sparse_attn(pp, ptr, ptr, ptr, ptr, ptr, ptr, ptr, 1 << 40, None) == code
+    assert L.pisa_decode_step(pp, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, 1 << 40,
+                              None) == code
+    sz = ctypes.c_size_t()
+    assert L.pisa_workspace_bytes(pp, 0, ctypes.byref(sz)) == code
+    assert L.pisa_last_error()
+
+
+def test_null_pointers_and_workspace_rejected():
+    L = lib()
+    p = problem()
+    pp = ctypes.byref(p)
+    dummy = ctypes.create_string_buffer(64)
+    ptr = ctypes.cast(dummy, ctypes.c_void_p)
+    assert L.pisa_build_pyramid(None, ptr, ptr, None) == _lib.PISA_ERR_INVALID
+    assert L.pisa_build_pyramid(pp, None, ptr, None) == _lib.PISA_ERR_INVALID
+    assert L.pisa_select(pp, None, ptr, ptr, ptr, None, 0, None, 0, None) == _lib.PISA_ERR_INVALID
+    assert L.pisa_select(pp, ptr, ptr, ptr, ptr, None, 9, None, 0, None) == _lib.PISA_ERR_INVALID
+    assert L.pisa_bsa_select(pp, ptr, ptr, None, None, ptr, 1 << 40, None) == _lib.PISA_ERR_INVALID
+    # BSA always needs its score workspace
+    sz = ctypes.c_size_t()
+    assert L.pisa_workspace_bytes(pp, _lib.PISA_OP_BSA, ctypes.byref(sz)) == 0
+    assert sz.value == 1 * 4 * 4096 * 64 * 4
+    assert L.pisa_bsa_select(pp, ptr, ptr, ptr, None, ptr, sz.value - 1, None) == _lib.PISA_ERR_WORKSPACE
+    assert L.pisa_bsa_select(pp, ptr, ptr, ptr, None, None, sz.value, None) == _lib.PISA_ERR_WORKSPACE
+    assert L.pisa_block_sparse_attn(pp, ptr, ptr, None, ptr, ptr, None, None, 0, None) == _lib.PISA_ERR_INVALID
+    assert L.pisa_decode_step(pp, None, ptr, ptr, ptr, ptr, ptr, None, ptr, None, None, 0,
+                              None) == _lib.PISA_ERR_INVALID
+    nc = problem(flags=0)
+    assert L.pisa_decode_step(ctypes.byref(nc), ptr, ptr, ptr, ptr, ptr, ptr, None, ptr, None,
+                              None, 0, None) == _lib.PISA_ERR_INVALID
+    big = problem(seq_len=64 * 4097)
+    assert L.pisa_bsa_select(ctypes.byref(big), ptr, ptr, ptr, None, ptr, 1 << 60,
+                             None) == _lib.PISA_ERR_UNSUPPORTED
+    assert L.pisa_workspace_bytes(pp, 99, ctypes.byref(sz)) == _lib.PISA_ERR_INVALID
+    assert L.pisa_status_string(_lib.PISA_ERR_WORKSPACE) == b"workspace missing or too small"
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    missing = str(tmp_path / "libpisa.so")
+    saved = _lib._lib
+    _lib._lib = None
+    try:
+        with pytest.raises(RuntimeError, match="missing"):
+            _lib.load(missing)
+    finally:
+        _lib._lib = saved

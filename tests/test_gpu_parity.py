@@ -1,0 +1,293 @@
+"""HIP path vs the CPU oracle on the same seeded inputs (needs an MI355X).
+
+Every call goes through the C ABI (the ctypes binding marshals arguments only).
+Small shapes are compared on every row; the workload shapes (c1-c5) at their
+full sizes, in the launch configuration the benchmark times, on sampled rows
+and heads.  "unit" variants redraw the same shapes with N(0,1) entries so that
+most rows clear the 1e-3 margin filter (at N(0,1/d) almost every row is a
+near-tie and only structure and attention can be compared).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parity
+from hierarchical_block_selection_amd import (Problem, pisa_block_sparse_attn, pisa_bsa_select,
+                                              pisa_build_pyramid, pisa_decode_step,
+                                              pisa_pyramid_layout, pisa_select)
+from hierarchical_block_selection_amd.inputs import (WORKLOADS, decode_inputs, prefill_inputs,
+                                                     sample_rows)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def announce(msg):
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def problem_of(cfg, **over):
+    kw = dict(batch=cfg["batch"], heads_q=cfg["heads_q"], heads_kv=cfg["heads_kv"],
+              seq_len=cfg["seq_len"], head_dim=cfg["head_dim"], block=cfg["block"],
+              topk=cfg["topk"], dtype=cfg["dtype"], causal=True, force_first_prev=True)
+    kw.update(over)
+    return Problem(**kw)
+
+
+def levels_from_gpu_layout(pyr_head, n, c):
+    offs = pisa_pyramid_layout(n, c)
+    return [pyr_head[offs[i]:offs[i + 1]] for i in range(len(offs) - 1)]
+
+
+def check_pyramid(pyr, k, prob, heads):
+    """Every level of the GPU pyramid against the oracle (fp32 sums of <= C terms)."""
+    for b, h in heads:
+        keys = parity.to_np(k[b, h])
+        want = oracle.build_pyramid(keys, prob.block)
+        got = levels_from_gpu_layout(parity.to_np(pyr[b, h]), prob.seq_len, prob.block)
+        assert len(got) == len(want)
+        tol = 4e-6 * max(np.abs(keys).max(), 1e-30)
+        for lg, lw in zip(got, want):
+            assert lg.shape == lw.shape
+            assert np.max(np.abs(lg - lw)) <= tol
+
+
+def run_and_compare(cfg, recipe, heads, n_random, strategy="auto", check_bsa=True,
+                    min_compared=None):
+    prob = problem_of(cfg)
+    announce(f"prefill N={prob.seq_len} H={prob.heads_q}/{prob.heads_kv} d={prob.head_dim} "
+             f"K={prob.topk} {recipe} strategy={strategy}")
+    inp = prefill_inputs(prob.batch, prob.heads_q, prob.heads_kv, prob.seq_len, prob.head_dim,
+                         prob.dtype, seed=cfg["seed"], recipe=recipe,
+                         n_needles=cfg["n_needles"], block=prob.block, device=DEV)
+    pyr = pisa_build_pyramid(prob, inp.k)
+    idx, score = pisa_select(prob, inp.q, inp.k, pyr, strategy=strategy)
+    if check_bsa:
+        bidx, bscore = pisa_bsa_select(prob, inp.q, pyr)
+    out, lse = pisa_block_sparse_attn(prob, inp.q, inp.k, inp.v, idx)
+    torch.cuda.synchronize()
+    check_pyramid(pyr, inp.k, prob, heads[:2])
+    rows = sample_rows(prob.seq_len, prob.block, prob.topk, n_random, cfg["seed"])
+    g = prob.group
+    fp32 = prob.dtype == torch.float32
+    tallies = {"pisa": parity.Tally(), "bsa": parity.Tally()}
+    for b, h in heads:
+        keys = parity.to_np(inp.k[b, h])
+        vals = parity.to_np(inp.v[b, h])
+        qg = parity.to_np(inp.q[b, h * g:(h + 1) * g])
+        levels = oracle.build_pyramid(keys, prob.block)
+        parity.compare_selection("pisa", idx[b, h].cpu().numpy(), score[b, h].cpu().numpy(), qg,
+                                 keys, levels, rows, prob.block, prob.topk, True, True,
+                                 prob.logit_scale, tallies["pisa"])
+        if check_bsa:
+            parity.compare_selection("bsa", bidx[b, h].cpu().numpy(), bscore[b, h].cpu().numpy(),
+                                     qg, keys, levels, rows, prob.block, prob.topk, True, True,
+                                     prob.logit_scale, tallies["bsa"])
+        parity.compare_attention(parity.to_np(out[b, h * g:(h + 1) * g]),
+                                 lse[b, h * g:(h + 1) * g].cpu().numpy(), qg, keys, vals,
+                                 idx[b, h].cpu().numpy(), rows, prob.block, True,
+                                 prob.logit_scale, fp32)
+    for name, tl in tallies.items():
+        print(f"  {name}: compared {tl.compared}/{tl.rows} rows, mismatches {len(tl.mismatches)}",
+              flush=True)
+        assert not tl.mismatches, tl.mismatches[:3]
+        if min_compared is not None and (name == "pisa" or check_bsa):
+            assert tl.frac() >= min_compared, (name, tl.frac())
+    return tallies
+
+
+HEADS = {"c1": [(0, 0), (0, 1)], "c2": [(0, 0), (0, 9), (0, 15)], "c3": [(0, 0), (0, 6)],
+         "c4a": [(0, 0), (0, 3)], "c4b": [(0, 1), (0, 2)], "c4c": [(0, 0), (0, 3)]}
+
+
+def test_c1_all_rows():
+    cfg = WORKLOADS["c1"]
+    prob = problem_of(cfg)
+    announce("c1 all rows")
+    inp = prefill_inputs(1, 2, 2, 2048, 64, torch.float32, seed=cfg["seed"], recipe="unit",
+                         device=DEV)
+    pyr = pisa_build_pyramid(prob, inp.k)
+    idx, score = pisa_select(prob, inp.q, inp.k, pyr)
+    bidx, bscore = pisa_bsa_select(prob, inp.q, pyr)
+    out, lse = pisa_block_sparse_attn(prob, inp.q, inp.k, inp.v, idx)
+    torch.cuda.synchronize()
+    check_pyramid(pyr, inp.k, prob, [(0, 0), (0, 1)])
+    rows = list(range(2048))
+    for h in range(2):
+        keys, vals = parity.to_np(inp.k[0, h]), parity.to_np(inp.v[0, h])
+        qg = parity.to_np(inp.q[0, h:h + 1])
+        levels = oracle.build_pyramid(keys, 64)
+        tp = parity.compare_selection("pisa", idx[0, h].cpu().numpy(), score[0, h].cpu().numpy(),
+                                      qg, keys, levels, rows, 64, 4, True, True, prob.logit_scale,
+                                      parity.Tally())
+        tb = parity.compare_selection("bsa", bidx[0, h].cpu().numpy(), bscore[0, h].cpu().numpy(),
+                                      qg, keys, levels, rows, 64, 4, True, True, prob.logit_scale,
+                                      parity.Tally())
+        assert not tp.mismatches and not tb.mismatches, (tp.mismatches[:2], tb.mismatches[:2])
+        assert tp.frac() > 0.9 and tb.frac() > 0.9
+        parity.compare_attention(parity.to_np(out[0, h:h + 1]), lse[0, h:h + 1].cpu().numpy(), qg,
+                                 keys, vals, idx[0, h].cpu().numpy(), rows, 64, True,
+                                 prob.logit_scale, fp32=True)
+
+
+@pytest.mark.parametrize("name", ["c2", "c3", "c4a", "c4b", "c4c"])
+def test_workload_parity_unit_variant(name):
+    """Workload shape with N(0,1) entries: most rows clear the margin filter."""
+    run_and_compare(WORKLOADS[name], "unit", HEADS[name], n_random=24, min_compared=0.5)
+
+
+@pytest.mark.parametrize("name", ["c2", "c3", "c4a", "c4b", "c4c"])
+def test_workload_parity_as_configured(name):
+    """Workload as configured (N(0,1/d), needles where stated): near-ties dominate,
+    so structure and attention carry the check; exact sets where margins allow."""
+    run_and_compare(WORKLOADS[name], WORKLOADS[name]["recipe"], HEADS[name], n_random=24)
+
+
+EDGE = [
+    # (N, C, d, K, Hq, Hkv, dtype, causal, force)
+    (1, 64, 64, 4, 1, 1, torch.float32, True, True),
+    (63, 64, 128, 4, 2, 2, torch.bfloat16, True, True),
+    (100, 16, 64, 3, 2, 1, torch.float32, True, True),
+    (1000, 32, 64, 5, 4, 2, torch.float32, True, True),
+    (1000, 16, 128, 7, 2, 2, torch.bfloat16, True, False),
+    (777, 16, 64, 4, 3, 3, torch.float32, False, False),
+    (2048 + 17, 64, 128, 16, 16, 1, torch.bfloat16, True, True),
+    (4096, 64, 64, 32, 4, 4, torch.float32, True, True),
+    (3000, 64, 128, 8, 8, 2, torch.float32, False, False),
+    (5000, 16, 128, 32, 2, 2, torch.bfloat16, True, True),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[f"N{c[0]}_C{c[1]}_d{c[2]}_K{c[3]}_G{c[4]//c[5]}_"
+                                            f"{'bf16' if c[6] == torch.bfloat16 else 'f32'}_"
+                                            f"{'causal' if c[7] else 'full'}{'_force' if c[8] else ''}"
+                                            for c in EDGE])
+def test_edge_shapes_every_row(case):
+    n, c, d, k, hq, hkv, dtype, causal, force = case
+    prob = Problem(1, hq, hkv, n, d, block=c, topk=k, dtype=dtype, causal=causal,
+                   force_first_prev=force)
+    announce(f"edge {case}")
+    inp = prefill_inputs(1, hq, hkv, n, d, dtype, seed=77 + n, recipe="unit", device=DEV)
+    pyr = pisa_build_pyramid(prob, inp.k)
+    idx, score = pisa_select(prob, inp.q, inp.k, pyr)
+    bidx, bscore = pisa_bsa_select(prob, inp.q, pyr)
+    out, lse = pisa_block_sparse_attn(prob, inp.q, inp.k, inp.v, idx)
+    torch.cuda.synchronize()
+    check_pyramid(pyr, inp.k, prob, [(0, h) for h in range(hkv)])
+    g = hq // hkv
+    rows = list(range(n)) if n <= 1100 else list(range(0, n, 3)) + [n - 1]
+    for h in range(hkv):
+        keys, vals = parity.to_np(inp.k[0, h]), parity.to_np(inp.v[0, h])
+        qg = parity.to_np(inp.q[0, h * g:(h + 1) * g])
+        levels = oracle.build_pyramid(keys, c)
+        for kind, ii, ss in (("pisa", idx, score), ("bsa", bidx, bscore)):
+            tl = parity.compare_selection(kind, ii[0, h].cpu().numpy(), ss[0, h].cpu().numpy(), qg,
+                                          keys, levels, rows, c, k, causal, force,
+                                          prob.logit_scale, parity.Tally())
+            assert not tl.mismatches, (kind, tl.mismatches[:3])
+            assert tl.frac() > 0.6, (kind, tl.frac())
+        parity.compare_attention(parity.to_np(out[0, h * g:(h + 1) * g]),
+                                 lse[0, h * g:(h + 1) * g].cpu().numpy(), qg, keys, vals,
+                                 idx[0, h].cpu().numpy(), rows, c, causal, prob.logit_scale,
+                                 fp32=dtype == torch.float32)
+
+
+def test_selection_and_attention_deterministic():
+    cfg = WORKLOADS["c4a"]
+    prob = problem_of(cfg)
+    announce("determinism c4a")
+    inp = prefill_inputs(1, 4, 4, cfg["seq_len"], 128, torch.bfloat16, seed=9, device=DEV)
+    pyr1 = pisa_build_pyramid(prob, inp.k)
+    pyr2 = pisa_build_pyramid(prob, inp.k)
+    i1, s1 = pisa_select(prob, inp.q, inp.k, pyr1)
+    i2, s2 = pisa_select(prob, inp.q, inp.k, pyr2)
+    b1, _ = pisa_bsa_select(prob, inp.q, pyr1)
+    b2, _ = pisa_bsa_select(prob, inp.q, pyr2)
+    o1, l1 = pisa_block_sparse_attn(prob, inp.q, inp.k, inp.v, i1)
+    o2, l2 = pisa_block_sparse_attn(prob, inp.q, inp.k, inp.v, i2)
+    torch.cuda.synchronize()
+    assert torch.equal(pyr1, pyr2)
+    assert torch.equal(i1, i2) and torch.equal(s1, s2) and torch.equal(b1, b2)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def decode_compare(prob, inp, pyr, pairs, fp32=False, min_compared=None):
+    idx, score, out, lse = pisa_decode_step(prob, inp.cache_len, inp.q, inp.k_cache, inp.v_cache,
+                                            pyr)
+    torch.cuda.synchronize()
+    g = prob.group
+    tally = parity.Tally()
+    for b, h in pairs:
+        n = int(inp.cache_len[b])
+        keys = parity.to_np(inp.k_cache[b, h, :n])
+        vals = parity.to_np(inp.v_cache[b, h, :n])
+        qg = parity.to_np(inp.q[b, h * g:(h + 1) * g])
+        sel, ref, ref_lse = oracle.decode_row(qg, keys, vals, n, prob.block, prob.topk)
+        got = [int(x) for x in idx[b, h].cpu()]
+        parity.check_structure(got, n - 1, prob.block, prob.topk, -(-n // prob.block), True, True)
+        tally.rows += 1
+        if sel.min_margin > parity.MARGIN:
+            tally.compared += 1
+            assert got == oracle.padded(sel.leaves, prob.topk), (b, h, got, sel.leaves)
+        # attention against the oracle with the GPU's own selection
+        leaves = [x for x in got if x >= 0]
+        ref2, ref2_lse = oracle.attend_row(qg, keys, vals, leaves, n - 1, prob.block, True)
+        o = parity.to_np(out[b, h * g:(h + 1) * g])
+        d = np.abs(o - ref2)
+        if fp32:
+            assert d.max() <= 1e-3 * np.abs(ref2).max()
+        else:
+            assert d.max() <= 2e-2
+            assert np.linalg.norm(o - ref2) <= 1e-2 * np.linalg.norm(ref2)
+        assert np.max(np.abs(lse[b, h * g:(h + 1) * g].cpu().numpy() - ref2_lse)) <= 1e-3
+    print(f"  decode: compared {tally.compared}/{tally.rows}", flush=True)
+    if min_compared is not None:
+        assert tally.frac() >= min_compared
+    return idx, out
+
+
+def test_decode_c5_sampled():
+    cfg = WORKLOADS["c5"]
+    prob = problem_of(cfg)
+    announce("decode c5 B=32 cache=131072 GQA 32/8")
+    inp = decode_inputs(32, 32, 8, cfg["seq_len"], 128, torch.bfloat16, seed=cfg["seed"],
+                        device=DEV)
+    pyr = pisa_build_pyramid(prob, inp.k_cache)
+    decode_compare(prob, inp, pyr, [(0, h) for h in range(8)] + [(17, h) for h in range(8)])
+
+
+def test_decode_unit_variant_ragged_lengths():
+    prob = Problem(4, 8, 2, 8192, 128, block=64, topk=16, dtype=torch.bfloat16)
+    announce("decode ragged lengths unit")
+    inp = decode_inputs(4, 8, 2, 8192, 128, torch.bfloat16, seed=31, recipe="unit",
+                        cache_len=[1, 63, 3001, 8192], device=DEV)
+    pyr = pisa_build_pyramid(prob, inp.k_cache)
+    decode_compare(prob, inp, pyr, [(b, h) for b in range(4) for h in range(2)], min_compared=0.5)
+
+
+def test_decode_equals_prefill_row():
+    """A decode step at cache length n gives the prefill row t = n - 1 bit for bit."""
+    n_cap, lens = 4096, [4096, 2500]
+    prob = Problem(2, 4, 1, n_cap, 64, block=64, topk=8, dtype=torch.float32)
+    announce("decode == prefill row")
+    inp = decode_inputs(2, 4, 1, n_cap, 64, torch.float32, seed=5, recipe="unit", cache_len=lens,
+                        device=DEV)
+    pyr = pisa_build_pyramid(prob, inp.k_cache)
+    didx, dscore, dout, dlse = pisa_decode_step(prob, inp.cache_len, inp.q, inp.k_cache,
+                                                inp.v_cache, pyr)
+    q_full = torch.zeros((2, 4, n_cap, 64), dtype=torch.float32, device=DEV)
+    for b, n in enumerate(lens):
+        q_full[b, :, n - 1] = inp.q[b]
+    idx, score = pisa_select(prob, q_full, inp.k_cache, pyr)
+    out, lse = pisa_block_sparse_attn(prob, q_full, inp.k_cache, inp.v_cache, idx)
+    torch.cuda.synchronize()
+    for b, n in enumerate(lens):
+        assert torch.equal(didx[b], idx[b, :, n - 1])
+        assert torch.equal(dscore[b], score[b, :, n - 1])
+        assert torch.equal(dout[b], out[b, :, n - 1])
+        assert torch.equal(dlse[b], lse[b, :, n - 1])

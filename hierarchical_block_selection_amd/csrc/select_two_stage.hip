@@ -1,13 +1,549 @@
-// Two-stage PISA selection (placeholder until the stage kernels land).
+// Two-stage PISA selection for bf16 inputs (PISA reading page §05, Algorithm
+// 1 and §5.1: the intermediate levels run per query, then key blocks are
+// loaded once and scored for every query that needs them).
+//
+// The split is placed one level higher than the pages' (which score the leaf
+// level in stage 2): here stage 2 works per kept level-3 node n (4 leaves,
+// 4C raw keys).  Its MFMA pass gives q.k for every key under n; the mean of a
+// leaf's logits equals the leaf summary's logit (eq. (4) is a mean and the dot
+// product is linear), so one pass yields both the level-2 scores of n's two
+// children (eq. (7) over child summaries) and the exact leaf LSEs (eq. (7) at
+// level 1).  Each query then needs K (not 2K) key groups and the level-2
+// summary gathers disappear from stage 1.
+//
+//   stage 1   one wavefront per (b, kv head, t): levels L..3 of the descent,
+//             kept level-3 nodes -> s1_nodes[u][K]; counts pairs per node.
+//   scan      one workgroup: bucket offsets and the stage-2 work list.
+//   scatter   pair ids (u*K + slot) into per-node buckets.
+//   stage 2   one workgroup per (node, <= 256 pairs): the node's keys in LDS,
+//             bf16 MFMA 32x32x16 (keys x queries), per-leaf LSE and mean.
+//   final     one wavefront per (b, kv head, t): level-2 and leaf decisions
+//             from the stage-2 scores; ascending leaf list out.
+// Pair order inside a bucket depends on atomics, but every pair's scores are
+// computed by the same instruction sequence whatever its position, so the
+// outputs are bitwise reproducible.
+#include <algorithm>
+
+#include "bucket.h"
+#include "pisa_common.h"
 #include "pisa_launch.h"
+#include "select_core.h"
 
 namespace pisa {
 
-bool select_two_stage_supported(const LaunchShape&) { return false; }
-size_t select_two_stage_ws_bytes(const LaunchShape&) { return 0; }
-hipError_t launch_select_two_stage(const LaunchShape&, const void*, const void*, const float*,
-                                   int32_t*, float*, void*, hipStream_t) {
-  return hipErrorNotSupported;
+namespace {
+
+constexpr int kSplitLevel = 3;   // stage 1 decides levels L..3
+constexpr int kS1Waves = 4;
+constexpr int kS2Threads = 256;
+constexpr int kS2PairsPerItem = 256;
+constexpr int kS2Cols = 32;      // MFMA 32x32x16: 32 (query, head) columns
+constexpr int kScoreStride = 8;  // floats per pair: 4 leaf LSE, 2 level-2, 2 pad
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+
+struct Ws {
+  int* counts;     // [n_buckets]
+  int* offsets;    // [n_buckets + 1]
+  int* cursors;    // [n_buckets]
+  int* items;      // [max_items * 3] (bucket, start, len)
+  int* n_items;    // [1]
+  int* s1_nodes;   // [U * K]
+  int* pairs;      // [U * K]
+  float* scores;   // [U * K * kScoreStride]
+};
+
+struct WsLayout {
+  size_t counts, offsets, cursors, items, n_items, s1_nodes, pairs, scores, total;
+  int n_buckets, max_items;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+WsLayout ws_layout(const LaunchShape& s) {
+  WsLayout w;
+  const size_t units = (size_t)s.batch * s.heads_kv * s.seq_len;
+  const int m3 = s.lv.n >= kSplitLevel ? s.lv.size[kSplitLevel - 1] : 1;
+  w.n_buckets = s.batch * s.heads_kv * m3;
+  w.max_items = (int)((units * s.topk + kS2PairsPerItem - 1) / kS2PairsPerItem) + w.n_buckets;
+  size_t off = 0;
+  w.counts = off; off = align256(off + sizeof(int) * w.n_buckets);
+  w.offsets = off; off = align256(off + sizeof(int) * (w.n_buckets + 1));
+  w.cursors = off; off = align256(off + sizeof(int) * w.n_buckets);
+  w.items = off; off = align256(off + sizeof(int) * 3 * (size_t)w.max_items);
+  w.n_items = off; off = align256(off + sizeof(int));
+  w.s1_nodes = off; off = align256(off + sizeof(int) * units * s.topk);
+  w.pairs = off; off = align256(off + sizeof(int) * units * s.topk);
+  w.scores = off; off = align256(off + sizeof(float) * units * s.topk * kScoreStride);
+  w.total = off;
+  return w;
+}
+
+Ws ws_bind(const WsLayout& l, void* base) {
+  char* b = static_cast<char*>(base);
+  return {reinterpret_cast<int*>(b + l.counts), reinterpret_cast<int*>(b + l.offsets),
+          reinterpret_cast<int*>(b + l.cursors), reinterpret_cast<int*>(b + l.items),
+          reinterpret_cast<int*>(b + l.n_items), reinterpret_cast<int*>(b + l.s1_nodes),
+          reinterpret_cast<int*>(b + l.pairs), reinterpret_cast<float*>(b + l.scores)};
+}
+
+// ---------------------------------------------------------------------------
+// Stage 1
+// ---------------------------------------------------------------------------
+
+// Eq. (7) scores of up to 64 candidates (lane j owns candidate j) at an
+// intermediate level, coalesced: each child summary row (fp32, D floats) is
+// read by 8 lanes holding D/8 columns each; the group's query columns for
+// those lanes sit in registers.  Returns this lane's candidate score (nats).
+template <int D, int GM>
+__device__ __forceinline__ float score_level_coalesced(const float* __restrict__ child_rows,
+                                                       int m_child, int node, bool rankable,
+                                                       const float (&qreg)[GM][D / 8],
+                                                       int group, float scale_log2,
+                                                       float* dots /* LDS [GM][128] */) {
+  constexpr int CPL = D / 8;  // columns per lane
+  const int lane = lane_id();
+  const uint64_t rm = ballot(rankable);
+  // rows: candidate j -> child rows 2j (always exists) and 2j+1 (if < m_child)
+  const int n_cand = 64 - __builtin_clzll(rm | 1ull);  // highest rankable lane + 1
+  const int n_rows = 2 * n_cand;
+  const int sub = lane >> 3, part = lane & 7;
+  for (int r0 = 0; r0 < n_rows; r0 += 8) {
+    const int r = r0 + sub;
+    const int cand = r >> 1;
+    const int cnode = __shfl(node, cand & 63, kWave);
+    const bool live = r < n_rows && ((rm >> (cand & 63)) & 1ull) && (2 * cnode + (r & 1) < m_child);
+    float acc[GM];
+#pragma unroll
+    for (int h = 0; h < GM; ++h) acc[h] = 0.f;
+    if (live) {
+      const float* row = child_rows + (size_t)(2 * cnode + (r & 1)) * D + part * CPL;
+#pragma unroll
+      for (int c = 0; c < CPL; c += 4) {
+        const float4 x = *reinterpret_cast<const float4*>(row + c);
+#pragma unroll
+        for (int h = 0; h < GM; ++h) {
+          if (h < group)
+            acc[h] += qreg[h][c] * x.x + qreg[h][c + 1] * x.y + qreg[h][c + 2] * x.z +
+                      qreg[h][c + 3] * x.w;
+        }
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < GM; ++h) {
+      if (h < group) {
+        float v = acc[h];
+        v += __shfl_xor(v, 1, kWave);
+        v += __shfl_xor(v, 2, kWave);
+        v += __shfl_xor(v, 4, kWave);
+        if (part == 0 && r < 128) dots[h * 128 + r] = v;
+      }
+    }
+  }
+  wave_lds_sync();
+  float total = neg_inf();
+  if (rankable) {
+    const bool has1 = 2 * node + 1 < m_child;
+    total = 0.f;
+    for (int h = 0; h < group; ++h) {
+      const float z0 = dots[h * 128 + 2 * lane] * scale_log2;
+      if (has1) {
+        const float z1 = dots[h * 128 + 2 * lane + 1] * scale_log2;
+        const float m = fmaxf(z0, z1);
+        total += m + log2f(exp2f(z0 - m) + exp2f(z1 - m));
+      } else {
+        total += z0;
+      }
+    }
+    total *= kLn2;
+  }
+  wave_lds_sync();
+  return total;
+}
+
+template <typename T, int D, int GM>
+__global__ __launch_bounds__(kS1Waves * kWave) void stage1_kernel(
+    const T* __restrict__ q, const float* __restrict__ pyr, int* __restrict__ s1_nodes,
+    int* __restrict__ counts, int heads_q, int heads_kv, int n_tok, int block, int topk, int group,
+    int causal, int force, float scale_log2, LevelTable lv) {
+  constexpr int CPL = D / 8;
+  __shared__ int nbuf_all[kS1Waves][kWave];
+  __shared__ float dots_all[kS1Waves][GM * 128];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int t = blockIdx.x * kS1Waves + wave;
+  if (t >= n_tok) return;
+  const int bh = blockIdx.y;
+  const int b = bh / heads_kv, kvh = bh % heads_kv;
+  const int lane = lane_id();
+  int* nbuf = nbuf_all[wave];
+  float* dots = dots_all[wave];
+  // The group's query columns for this lane's 8-lane part.
+  float qreg[GM][CPL];
+  const int part = lane & 7;
+#pragma unroll
+  for (int h = 0; h < GM; ++h) {
+    if (h < group) {
+      const T* qrow = q + (((size_t)b * heads_q + (size_t)kvh * group + h) * n_tok + t) * D +
+                      part * CPL;
+      constexpr int VEC = Vec16<T>::n;
+#pragma unroll
+      for (int c = 0; c < CPL; c += VEC) load16(qrow + c, &qreg[h][c]);
+    } else {
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) qreg[h][c] = 0.f;
+    }
+  }
+  const float* pb = pyr + (size_t)bh * lv.rows * D;
+  const bool cz = causal != 0, fz = force != 0;
+  const int cur = t / block;
+  int node = lane == 0 ? 0 : -1;
+  bool keep = false;
+  for (int l = lv.n; l >= kSplitLevel; --l) {
+    const int sh = l - 1;
+    const int lim = cur >> sh;
+    bool valid = node >= 0 && (!cz || node <= lim);
+    const uint64_t vm = ballot(valid);
+    const int ncand = __popcll(vm);
+    if (valid) nbuf[lanes_below(vm)] = node;
+    wave_lds_sync();
+    node = lane < ncand ? nbuf[lane] : -1;
+    wave_lds_sync();
+    valid = lane < ncand;
+    const bool forced = valid && cz &&
+                        (node == lim || (fz && (node == 0 || (cur >= 1 && node == ((cur - 1) >> sh)))));
+    if (ncand <= topk) {
+      keep = valid;
+    } else {
+      const int keep_n = topk - __popcll(ballot(forced));
+      const bool rankable = valid && !forced;
+      const float s = score_level_coalesced<D, GM>(pb + (size_t)lv.off[l - 2] * D, lv.size[l - 2],
+                                               node, rankable, qreg, group, scale_log2, dots);
+      const uint64_t rm = ballot(rankable);
+      int rank = 0;
+      uint64_t it = rm;
+      while (it) {
+        const int j = __builtin_ctzll(it);
+        it &= it - 1;
+        rank += ranks_before(readlane_f(s, j), readlane_i(node, j), s, node) ? 1 : 0;
+      }
+      keep = forced || (rankable && rank < keep_n);
+    }
+    if (l > kSplitLevel) {
+      const uint64_t km = ballot(keep);
+      const int p = lanes_below(km);
+      const int m_child = lv.size[l - 2];
+      if (keep) {
+        nbuf[2 * p] = 2 * node;
+        nbuf[2 * p + 1] = (2 * node + 1 < m_child) ? 2 * node + 1 : -1;
+      }
+      wave_lds_sync();
+      node = lane < 2 * __popcll(km) ? nbuf[lane] : -1;
+      wave_lds_sync();
+      keep = false;
+    }
+  }
+  // Kept level-3 nodes: compact into s1_nodes[u][0..nk), -1 after; count pairs.
+  const uint64_t km = ballot(keep);
+  const int nk = __popcll(km);
+  const size_t u = (size_t)bh * n_tok + t;
+  int* out = s1_nodes + u * topk;
+  if (keep) {
+    out[lanes_below(km)] = node;
+    atomicAdd(&counts[(size_t)bh * lv.size[kSplitLevel - 1] + node], 1);
+  }
+  if (lane >= nk && lane < topk) out[lane] = -1;
+}
+
+// ---------------------------------------------------------------------------
+// Stage 2
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// One workgroup per work item (level-3 node n of KV head bh, up to 256 pairs).
+template <int D>
+__global__ __launch_bounds__(kS2Threads) void stage2_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const int* __restrict__ items,
+    const int* __restrict__ n_items, const int* __restrict__ pairs, float* __restrict__ scores,
+    int heads_q, int heads_kv, int n_tok, int block, int topk, int group, int m1, int m2, int m3,
+    float scale_log2) {
+  constexpr int KSTEPS = D / 16;
+  constexpr int ROW = D + 8;  // padded LDS row (bf16 elements) against bank conflicts
+  constexpr int NODE_KEYS = 256;
+  __shared__ __attribute__((aligned(16))) bf16_t ks[NODE_KEYS * ROW];
+  const int item = blockIdx.x;
+  if (item >= *n_items) return;
+  const int bucket = items[3 * item], start = items[3 * item + 1], len = items[3 * item + 2];
+  const int bh = bucket / m3, node = bucket % m3;
+  const int b = bh / heads_kv, kvh = bh % heads_kv;
+  const int tok0 = node * 4 * block;
+  const int n_keys = min(4 * block, n_tok - tok0);
+  // Keys of the node -> LDS (rows past the sequence end are zero-filled).
+  const bf16_t* kb = k + ((size_t)bh * n_tok + tok0) * D;
+  constexpr int V16 = D / 8;  // 16-byte chunks per row
+  for (int x = threadIdx.x; x < NODE_KEYS * V16; x += kS2Threads) {
+    const int r = x / V16, c = (x % V16) * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r < n_keys) v = *reinterpret_cast<const uint4*>(kb + (size_t)r * D + c);
+    *reinterpret_cast<uint4*>(&ks[r * ROW + c]) = v;
+  }
+  __syncthreads();
+
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  const int col = lane & 31;        // query column of this lane
+  const int khalf = lane >> 5;      // which 8-element half of a 16-wide k step
+  const int per_chunk = kS2Cols / group;  // pairs per 32-column chunk
+  const int n_chunks = (len + per_chunk - 1) / per_chunk;
+  const int n_leaves = min(4, m1 - 4 * node);
+  for (int ch = wave; ch < n_chunks; ch += kS2Threads / kWave) {
+    const int p = ch * per_chunk + col / group;
+    const int h = col % group;
+    const bool live = p < len;
+    int pair_id = 0;
+    bf16x8_t bq[KSTEPS];
+    if (live) {
+      pair_id = pairs[start + p];
+      const size_t u = (size_t)pair_id / topk;
+      const int t = (int)(u % n_tok);
+      const bf16_t* qrow = q + (((size_t)b * heads_q + (size_t)kvh * group + h) * n_tok + t) * D;
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s)
+        bq[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 16 * s + 8 * khalf));
+    } else {
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) bq[s] = as_bf16x8(make_uint4(0, 0, 0, 0));
+    }
+    float leaf_lse[4], leaf_mean[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      leaf_lse[f] = neg_inf();
+      leaf_mean[f] = neg_inf();
+      if (f >= n_leaves) continue;
+      f32x16_t acc0 = {}, acc1 = {};
+      const int kr0 = f * block;  // first key row of leaf f in LDS
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) {
+        const bf16x8_t a0 = as_bf16x8(
+            *reinterpret_cast<const uint4*>(&ks[(kr0 + (lane & 31)) * ROW + 16 * s + 8 * khalf]));
+        const bf16x8_t a1 = as_bf16x8(*reinterpret_cast<const uint4*>(
+            &ks[(kr0 + 32 + (lane & 31)) * ROW + 16 * s + 8 * khalf]));
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bq[s], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bq[s], acc1, 0, 0, 0);
+      }
+      // Lane holds logits of keys rows (i/4)*8 + khalf*4 + i%4 (+32 for acc1) of the leaf.
+      const int valid_keys = min(block, n_keys - kr0);
+      float m = neg_inf(), sraw = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = (i / 4) * 8 + khalf * 4 + (i % 4);
+        if (r < valid_keys) {
+          m = fmaxf(m, acc0[i]);
+          sraw += acc0[i];
+        }
+        if (r + 32 < valid_keys) {
+          m = fmaxf(m, acc1[i]);
+          sraw += acc1[i];
+        }
+      }
+      m = fmaxf(m, __shfl_xor(m, 32, kWave));
+      const float ms = m * scale_log2;
+      float se = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = (i / 4) * 8 + khalf * 4 + (i % 4);
+        if (r < valid_keys) se += exp2f(acc0[i] * scale_log2 - ms);
+        if (r + 32 < valid_keys) se += exp2f(acc1[i] * scale_log2 - ms);
+      }
+      se += __shfl_xor(se, 32, kWave);
+      sraw += __shfl_xor(sraw, 32, kWave);
+      leaf_lse[f] = ms + log2f(se);
+      leaf_mean[f] = sraw / float(valid_keys) * scale_log2;
+    }
+    // Level-2 scores of children 2n, 2n+1: LSE over their leaves' mean logits.
+    float lvl2[2];
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      const int f0 = 2 * c2, f1 = 2 * c2 + 1;
+      if (f0 >= n_leaves) {
+        lvl2[c2] = neg_inf();
+      } else if (f1 >= n_leaves) {
+        lvl2[c2] = leaf_mean[f0];
+      } else {
+        const float mm = fmaxf(leaf_mean[f0], leaf_mean[f1]);
+        lvl2[c2] = mm + log2f(exp2f(leaf_mean[f0] - mm) + exp2f(leaf_mean[f1] - mm));
+      }
+    }
+    // Sum over the group's heads (adjacent columns), eq. (11).
+    float outv[6] = {leaf_lse[0], leaf_lse[1], leaf_lse[2], leaf_lse[3], lvl2[0], lvl2[1]};
+    for (int o = 1; o < group; o <<= 1) {
+#pragma unroll
+      for (int j = 0; j < 6; ++j) outv[j] += __shfl_xor(outv[j], o, kWave);
+    }
+    if (live && khalf == 0 && h == 0) {
+      float* dst = scores + (size_t)pair_id * kScoreStride;
+      *reinterpret_cast<float4*>(dst) =
+          make_float4(outv[0] * kLn2, outv[1] * kLn2, outv[2] * kLn2, outv[3] * kLn2);
+      *reinterpret_cast<float4*>(dst + 4) = make_float4(outv[4] * kLn2, outv[5] * kLn2, 0.f, 0.f);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Final decisions at levels 2 and 1
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(kS1Waves * kWave) void final_kernel(
+    const int* __restrict__ s1_nodes, const float* __restrict__ scores, int32_t* __restrict__ idx,
+    float* __restrict__ score_out, int n_tok, int block, int topk, int causal, int force, int m1,
+    int m2) {
+  __shared__ int nbuf_all[kS1Waves][kWave];
+  __shared__ int sbuf_all[kS1Waves][kWave];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int t = blockIdx.x * kS1Waves + wave;
+  if (t >= n_tok) return;
+  const int bh = blockIdx.y;
+  const int lane = lane_id();
+  int* nbuf = nbuf_all[wave];
+  int* sbuf = sbuf_all[wave];
+  const size_t u = (size_t)bh * n_tok + t;
+  const bool cz = causal != 0, fz = force != 0;
+  const int cur = t / block;
+  // Level-2 candidates: children of the kept level-3 nodes.  src = slot*8 + j
+  // locates the candidate's score in scores[u][slot][j].
+  int node = -1, src = -1;
+  {
+    const int slot = lane >> 1, c = lane & 1;
+    const int n3 = slot < topk ? s1_nodes[u * topk + slot] : -1;
+    if (n3 >= 0 && 2 * n3 + c < m2) {
+      node = 2 * n3 + c;
+      src = slot * kScoreStride + 4 + c;
+    }
+  }
+  bool keep = false;
+  float score = pos_inf();
+  for (int l = 2; l >= 1; --l) {
+    const int sh = l - 1;
+    const int lim = cur >> sh;
+    bool valid = node >= 0 && (!cz || node <= lim);
+    const uint64_t vm = ballot(valid);
+    const int ncand = __popcll(vm);
+    if (valid) {
+      nbuf[lanes_below(vm)] = node;
+      sbuf[lanes_below(vm)] = src;
+    }
+    wave_lds_sync();
+    node = lane < ncand ? nbuf[lane] : -1;
+    src = lane < ncand ? sbuf[lane] : -1;
+    wave_lds_sync();
+    valid = lane < ncand;
+    const bool forced = valid && cz &&
+                        (node == lim || (fz && (node == 0 || (cur >= 1 && node == ((cur - 1) >> sh)))));
+    if (ncand <= topk) {
+      keep = valid;
+      score = pos_inf();
+    } else {
+      const int keep_n = topk - __popcll(ballot(forced));
+      const bool rankable = valid && !forced;
+      const float s = rankable ? scores[u * topk * kScoreStride + src] : neg_inf();
+      const uint64_t rm = ballot(rankable);
+      int rank = 0;
+      uint64_t it = rm;
+      while (it) {
+        const int j = __builtin_ctzll(it);
+        it &= it - 1;
+        rank += ranks_before(readlane_f(s, j), readlane_i(node, j), s, node) ? 1 : 0;
+      }
+      keep = forced || (rankable && rank < keep_n);
+      score = forced ? pos_inf() : s;
+    }
+    if (l == 2) {
+      // Expand kept level-2 nodes into leaves; leaf score index = slot*8 + 2*c + c'.
+      const uint64_t km = ballot(keep);
+      const int p = lanes_below(km);
+      if (keep) {
+        const int slot = src / kScoreStride, c = src % kScoreStride - 4;
+        nbuf[2 * p] = 2 * node;
+        sbuf[2 * p] = slot * kScoreStride + 2 * c;
+        const bool has1 = 2 * node + 1 < m1;
+        nbuf[2 * p + 1] = has1 ? 2 * node + 1 : -1;
+        sbuf[2 * p + 1] = slot * kScoreStride + 2 * c + 1;
+      }
+      wave_lds_sync();
+      const int n2 = 2 * __popcll(km);
+      node = lane < n2 ? nbuf[lane] : -1;
+      src = lane < n2 ? sbuf[lane] : -1;
+      wave_lds_sync();
+      keep = false;
+    }
+  }
+  SelectResult r{node, score, keep};
+  write_selection(r, topk, idx + u * topk, score_out ? score_out + u * topk : nullptr);
+}
+
+template <typename T, int D, int GM>
+hipError_t stage1_launch(const LaunchShape& s, const void* q, const float* pyr, const Ws& w,
+                         hipStream_t st) {
+  dim3 grid((s.seq_len + kS1Waves - 1) / kS1Waves, s.batch * s.heads_kv);
+  hipLaunchKernelGGL((stage1_kernel<T, D, GM>), grid, dim3(kS1Waves * kWave), 0, st,
+                     static_cast<const T*>(q), pyr, w.s1_nodes, w.counts, s.heads_q, s.heads_kv,
+                     s.seq_len, s.block, s.topk, s.group, s.causal ? 1 : 0, s.force ? 1 : 0,
+                     s.scale * kLog2e, s.lv);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool select_two_stage_supported(const LaunchShape& s) {
+  const bool pow2_group = (s.group & (s.group - 1)) == 0;
+  return s.bf16 && s.block == 64 && (s.head_dim == 64 || s.head_dim == 128) &&
+         s.lv.n >= kSplitLevel + 1 && pow2_group && s.group <= 4 && s.topk <= 32;
+}
+
+size_t select_two_stage_ws_bytes(const LaunchShape& s) {
+  return select_two_stage_supported(s) ? ws_layout(s).total : 0;
+}
+
+hipError_t launch_select_two_stage(const LaunchShape& s, const void* q, const void* k,
+                                   const float* pyr, int32_t* idx, float* score, void* ws,
+                                   hipStream_t st) {
+  const WsLayout lay = ws_layout(s);
+  const Ws w = ws_bind(lay, ws);
+  const int m1 = s.lv.size[0], m2 = s.lv.size[1], m3 = s.lv.size[kSplitLevel - 1];
+  hipLaunchKernelGGL(bucket::fill_zero_kernel, dim3(bucket::grid_for(lay.n_buckets)), dim3(256),
+                     0, st, w.counts, lay.n_buckets);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (s.group == 1)
+    e = s.head_dim == 128 ? stage1_launch<bf16_t, 128, 1>(s, q, pyr, w, st)
+                          : stage1_launch<bf16_t, 64, 1>(s, q, pyr, w, st);
+  else
+    e = s.head_dim == 128 ? stage1_launch<bf16_t, 128, 4>(s, q, pyr, w, st)
+                          : stage1_launch<bf16_t, 64, 4>(s, q, pyr, w, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bucket::scan_kernel, dim3(1), dim3(1024), 0, st, w.counts, w.offsets,
+                     w.cursors, w.items, w.n_items, lay.n_buckets, lay.max_items, kS2PairsPerItem);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const size_t n_slots = (size_t)s.batch * s.heads_kv * s.seq_len * s.topk;
+  hipLaunchKernelGGL(bucket::scatter_kernel, dim3(bucket::grid_for(n_slots)), dim3(256), 0, st,
+                     w.s1_nodes, w.cursors, w.pairs, s.seq_len, s.topk, m3, n_slots);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (s.head_dim == 128)
+    hipLaunchKernelGGL((stage2_kernel<128>), dim3(lay.max_items), dim3(kS2Threads), 0, st,
+                       static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k), w.items,
+                       w.n_items, w.pairs, w.scores, s.heads_q, s.heads_kv, s.seq_len, s.block,
+                       s.topk, s.group, m1, m2, m3, s.scale * kLog2e);
+  else
+    hipLaunchKernelGGL((stage2_kernel<64>), dim3(lay.max_items), dim3(kS2Threads), 0, st,
+                       static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k), w.items,
+                       w.n_items, w.pairs, w.scores, s.heads_q, s.heads_kv, s.seq_len, s.block,
+                       s.topk, s.group, m1, m2, m3, s.scale * kLog2e);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  dim3 grid((s.seq_len + kS1Waves - 1) / kS1Waves, s.batch * s.heads_kv);
+  hipLaunchKernelGGL(final_kernel, grid, dim3(kS1Waves * kWave), 0, st, w.s1_nodes, w.scores, idx,
+                     score, s.seq_len, s.block, s.topk, s.causal ? 1 : 0, s.force ? 1 : 0, m1, m2);
+  return hipGetLastError();
 }
 
 }  // namespace pisa

@@ -72,7 +72,7 @@ typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 struct AttnWs {
-  size_t counts, offsets, cursors, items, n_items, pairs, part_o, part_lse, total;
+  size_t counts, offsets, cursors, item_offsets, pairs, part_o, part_lse, total;
   int n_buckets, max_items;
 };
 
@@ -87,13 +87,12 @@ AttnWs attn_layout(const LaunchShape& s) {
   AttnWs w;
   const size_t slots = (size_t)s.batch * s.heads_kv * s.seq_len * s.topk;
   w.n_buckets = s.batch * s.heads_kv * s.lv.size[0];
-  w.max_items = (int)((slots + kAttnPairsPerItem - 1) / kAttnPairsPerItem) + w.n_buckets;
+  w.max_items = bucket::max_items(slots, w.n_buckets, kAttnPairsPerItem);
   size_t off = 0;
   w.counts = off; off = align256(off + sizeof(int) * w.n_buckets);
   w.offsets = off; off = align256(off + sizeof(int) * (w.n_buckets + 1));
   w.cursors = off; off = align256(off + sizeof(int) * w.n_buckets);
-  w.items = off; off = align256(off + sizeof(int) * 3 * (size_t)w.max_items);
-  w.n_items = off; off = align256(off + sizeof(int));
+  w.item_offsets = off; off = align256(off + sizeof(int) * (w.n_buckets + 1));
   w.pairs = off; off = align256(off + sizeof(int) * slots);
   w.part_o = off; off = align256(off + sizeof(bf16_t) * slots * s.group * s.head_dim);
   w.part_lse = off; off = align256(off + sizeof(float) * slots * s.group);
@@ -104,9 +103,10 @@ AttnWs attn_layout(const LaunchShape& s) {
 template <int D>
 __global__ __launch_bounds__(kAttnThreads) void attn_partial_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
-    const int* __restrict__ items, const int* __restrict__ n_items, const int* __restrict__ pairs,
-    bf16_t* __restrict__ part_o, float* __restrict__ part_lse, int heads_q, int heads_kv,
-    int n_tok, int topk, int group, int m1, int causal, float scale_log2) {
+    const int* __restrict__ item_offsets, const int* __restrict__ offsets,
+    const int* __restrict__ pairs, bf16_t* __restrict__ part_o, float* __restrict__ part_lse,
+    int n_buckets, int heads_q, int heads_kv, int n_tok, int topk, int group, int m1, int causal,
+    float scale_log2) {
   constexpr int C = kAttnBlock;
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;
@@ -117,9 +117,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_partial_kernel(
   __shared__ __attribute__((aligned(16))) bf16_t vt[D * VROW];
   __shared__ float inv_l[NW][kAttnCols];
   __shared__ int pid_s[NW][kAttnCols];
-  const int item = blockIdx.x;
-  if (item >= *n_items) return;
-  const int bucket = items[3 * item], start = items[3 * item + 1], len = items[3 * item + 2];
+  int bucket, start, len;
+  if (!bucket::locate_item(item_offsets, offsets, n_buckets, blockIdx.x, kAttnPairsPerItem,
+                           &bucket, &start, &len))
+    return;
   const int bh = bucket / m1, blk = bucket % m1;
   const int b = bh / heads_kv, kvh = bh % heads_kv;
   const int tok0 = blk * C;
@@ -303,26 +304,20 @@ hipError_t launch_block_path(const LaunchShape& s, const void* q, const void* k,
   int* counts = reinterpret_cast<int*>(base + lay.counts);
   int* offsets = reinterpret_cast<int*>(base + lay.offsets);
   int* cursors = reinterpret_cast<int*>(base + lay.cursors);
-  int* items = reinterpret_cast<int*>(base + lay.items);
-  int* n_items = reinterpret_cast<int*>(base + lay.n_items);
+  int* item_offsets = reinterpret_cast<int*>(base + lay.item_offsets);
   int* pairs = reinterpret_cast<int*>(base + lay.pairs);
   bf16_t* part_o = reinterpret_cast<bf16_t*>(base + lay.part_o);
   float* part_lse = reinterpret_cast<float*>(base + lay.part_lse);
   const int m1 = s.lv.size[0];
-  const size_t slots = (size_t)s.batch * s.heads_kv * s.seq_len * s.topk;
-  hipLaunchKernelGGL(bucket::fill_zero_kernel, dim3(bucket::grid_for(lay.n_buckets)), dim3(256),
-                     0, st, counts, lay.n_buckets);
-  hipLaunchKernelGGL(bucket::count_kernel, dim3(bucket::grid_for(slots)), dim3(256), 0, st, idx,
-                     counts, s.seq_len, s.topk, m1, slots);
-  hipLaunchKernelGGL(bucket::scan_kernel, dim3(1), dim3(1024), 0, st, counts, offsets, cursors,
-                     items, n_items, lay.n_buckets, lay.max_items, kAttnPairsPerItem);
-  hipLaunchKernelGGL(bucket::scatter_kernel, dim3(bucket::grid_for(slots)), dim3(256), 0, st, idx,
-                     cursors, pairs, s.seq_len, s.topk, m1, slots);
+  hipError_t e = bucket::sort_pairs(idx, s.batch * s.heads_kv, s.seq_len, s.topk, m1,
+                                    kAttnPairsPerItem, counts, offsets, cursors, item_offsets,
+                                    pairs, false, st);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_partial_kernel<D>), dim3(lay.max_items), dim3(kAttnThreads), 0, st,
                      static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
-                     static_cast<const bf16_t*>(v), items, n_items, pairs, part_o, part_lse,
-                     s.heads_q, s.heads_kv, s.seq_len, s.topk, s.group, m1, s.causal ? 1 : 0,
-                     s.scale * kLog2e);
+                     static_cast<const bf16_t*>(v), item_offsets, offsets, pairs, part_o,
+                     part_lse, lay.n_buckets, s.heads_q, s.heads_kv, s.seq_len, s.topk, s.group,
+                     m1, s.causal ? 1 : 0, s.scale * kLog2e);
   const size_t rows = (size_t)s.batch * s.heads_kv * s.seq_len * s.group;
   hipLaunchKernelGGL((attn_combine_kernel<D>), dim3((unsigned)((rows * 16 + 255) / 256)),
                      dim3(256), 0, st, idx, part_o, part_lse, static_cast<bf16_t*>(out), lse,

@@ -4,19 +4,22 @@
 // the mean of the existing level-l rows {2i, 2i+1}.  HBM-bound: K is read once
 // (N*d*sizeof(T) bytes per KV head) and R*d*4 bytes of summaries are written.
 //
-// Pass 1 (chunk kernel): one workgroup per (KV head, aligned chunk of 2^j
-// leaves).  Each wave streams whole leaf blocks with 16-byte loads (a row is
-// spread over d*sizeof(T)/16 lanes, several rows per load), reduces the rows
-// across lanes, then the workgroup builds levels 2..j+1 of its chunk in LDS.
-// Pass 2 (top kernel): one workgroup per KV head builds levels j+2..L from
-// level j+1 (M_1/2^j rows, a few hundred KB at most).
+// Pass 1 (chunk kernel): one workgroup of 16 waves per (KV head, aligned
+// chunk of 2^j = 32 leaves).  Each wave streams whole leaf blocks with 16-byte
+// loads (a row is spread over d*sizeof(T)/16 lanes, several rows per load),
+// reduces the rows across lanes, then the workgroup builds levels 2..j+1 of its
+// chunk in LDS.  Pass 2 (top kernel): one workgroup per KV head builds levels
+// j+2..L from level j+1 (M_1/32 rows), keeping every level after the first in
+// LDS when it fits.
 #include "pisa_common.h"
 #include "pisa_launch.h"
 
 namespace pisa {
 
-constexpr int kPyrThreads = 256;
-constexpr int kPyrLeavesLog2 = 3;  // 8 leaf blocks per chunk workgroup
+constexpr int kPyrThreads = 1024;
+constexpr int kPyrLeavesLog2 = 5;  // 32 leaf blocks per chunk workgroup
+constexpr int kTopThreads = 256;
+constexpr size_t kTopLds = 64 * 1024;
 
 template <typename T, int D>
 __global__ __launch_bounds__(kPyrThreads) void pyramid_chunk_kernel(
@@ -88,19 +91,27 @@ __global__ __launch_bounds__(kPyrThreads) void pyramid_chunk_kernel(
   }
 }
 
+// Levels first_level..L.  The first of them is read from global memory; the
+// rest ping-pong in LDS (dynamic, two buffers) when use_lds is set.
 template <int D>
-__global__ __launch_bounds__(kPyrThreads) void pyramid_top_kernel(float* __restrict__ pyr,
-                                                                   LevelTable lv, int first_level) {
+__global__ __launch_bounds__(kTopThreads) void pyramid_top_kernel(float* __restrict__ pyr,
+                                                                   LevelTable lv, int first_level,
+                                                                   int use_lds) {
+  extern __shared__ float top_lds[];
   float* pb = pyr + (size_t)blockIdx.x * lv.rows * D;
+  float* bufs[2] = {top_lds, top_lds + (size_t)lv.size[first_level - 1] * D};
   for (int l = first_level; l <= lv.n; ++l) {
     const int m_prev = lv.size[l - 2], m_cur = lv.size[l - 1];
-    const float* src = pb + (size_t)lv.off[l - 2] * D;
+    const bool from_lds = use_lds && l > first_level;
+    const float* src = from_lds ? bufs[(l - first_level - 1) & 1] : pb + (size_t)lv.off[l - 2] * D;
+    float* ldst = bufs[(l - first_level) & 1];
     float* dst = pb + (size_t)lv.off[l - 1] * D;
-    for (int x = threadIdx.x; x < m_cur * D; x += kPyrThreads) {
+    for (int x = threadIdx.x; x < m_cur * D; x += kTopThreads) {
       const int node = x / D, col = x % D;
       float v = src[(size_t)(2 * node) * D + col];
       if (2 * node + 1 < m_prev) v = 0.5f * (v + src[(size_t)(2 * node + 1) * D + col]);
       dst[(size_t)node * D + col] = v;
+      if (use_lds) ldst[(size_t)node * D + col] = v;
     }
     __syncthreads();
   }
@@ -117,8 +128,11 @@ static hipError_t launch_pyramid_t(const LaunchShape& s, const void* k, float* p
   if (e != hipSuccess) return e;
   const int first = 2 + kPyrLeavesLog2;
   if (s.lv.n >= first) {
-    hipLaunchKernelGGL((pyramid_top_kernel<D>), dim3(s.batch * s.heads_kv), dim3(kPyrThreads),
-                       0, st, pyr, s.lv, first);
+    const size_t lds = (size_t)(s.lv.size[first - 1] + (s.lv.n > first ? s.lv.size[first] : 0)) *
+                       D * sizeof(float);
+    const bool use_lds = lds <= kTopLds;
+    hipLaunchKernelGGL((pyramid_top_kernel<D>), dim3(s.batch * s.heads_kv), dim3(kTopThreads),
+                       use_lds ? lds : 0, st, pyr, s.lv, first, use_lds ? 1 : 0);
     e = hipGetLastError();
   }
   return e;

@@ -44,18 +44,17 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 
 struct Ws {
-  int* counts;     // [n_buckets]
-  int* offsets;    // [n_buckets + 1]
-  int* cursors;    // [n_buckets]
-  int* items;      // [max_items * 3] (bucket, start, len)
-  int* n_items;    // [1]
-  int* s1_nodes;   // [U * K]
-  int* pairs;      // [U * K]
-  float* scores;   // [U * K * kScoreStride]
+  int* counts;        // [n_buckets]
+  int* offsets;       // [n_buckets + 1]
+  int* cursors;       // [n_buckets]
+  int* item_offsets;  // [n_buckets + 1]
+  int* s1_nodes;      // [U * K]
+  int* pairs;         // [U * K]
+  float* scores;      // [U * K * kScoreStride]
 };
 
 struct WsLayout {
-  size_t counts, offsets, cursors, items, n_items, s1_nodes, pairs, scores, total;
+  size_t counts, offsets, cursors, item_offsets, s1_nodes, pairs, scores, total;
   int n_buckets, max_items;
 };
 
@@ -66,13 +65,12 @@ WsLayout ws_layout(const LaunchShape& s) {
   const size_t units = (size_t)s.batch * s.heads_kv * s.seq_len;
   const int m3 = s.lv.n >= kSplitLevel ? s.lv.size[kSplitLevel - 1] : 1;
   w.n_buckets = s.batch * s.heads_kv * m3;
-  w.max_items = (int)((units * s.topk + kS2PairsPerItem - 1) / kS2PairsPerItem) + w.n_buckets;
+  w.max_items = bucket::max_items(units * s.topk, w.n_buckets, kS2PairsPerItem);
   size_t off = 0;
   w.counts = off; off = align256(off + sizeof(int) * w.n_buckets);
   w.offsets = off; off = align256(off + sizeof(int) * (w.n_buckets + 1));
   w.cursors = off; off = align256(off + sizeof(int) * w.n_buckets);
-  w.items = off; off = align256(off + sizeof(int) * 3 * (size_t)w.max_items);
-  w.n_items = off; off = align256(off + sizeof(int));
+  w.item_offsets = off; off = align256(off + sizeof(int) * (w.n_buckets + 1));
   w.s1_nodes = off; off = align256(off + sizeof(int) * units * s.topk);
   w.pairs = off; off = align256(off + sizeof(int) * units * s.topk);
   w.scores = off; off = align256(off + sizeof(float) * units * s.topk * kScoreStride);
@@ -83,9 +81,9 @@ WsLayout ws_layout(const LaunchShape& s) {
 Ws ws_bind(const WsLayout& l, void* base) {
   char* b = static_cast<char*>(base);
   return {reinterpret_cast<int*>(b + l.counts), reinterpret_cast<int*>(b + l.offsets),
-          reinterpret_cast<int*>(b + l.cursors), reinterpret_cast<int*>(b + l.items),
-          reinterpret_cast<int*>(b + l.n_items), reinterpret_cast<int*>(b + l.s1_nodes),
-          reinterpret_cast<int*>(b + l.pairs), reinterpret_cast<float*>(b + l.scores)};
+          reinterpret_cast<int*>(b + l.cursors), reinterpret_cast<int*>(b + l.item_offsets),
+          reinterpret_cast<int*>(b + l.s1_nodes), reinterpret_cast<int*>(b + l.pairs),
+          reinterpret_cast<float*>(b + l.scores)};
 }
 
 // ---------------------------------------------------------------------------
@@ -109,35 +107,42 @@ __device__ __forceinline__ float score_level_coalesced(const float* __restrict__
   const int n_cand = 64 - __builtin_clzll(rm | 1ull);  // highest rankable lane + 1
   const int n_rows = 2 * n_cand;
   const int sub = lane >> 3, part = lane & 7;
-  for (int r0 = 0; r0 < n_rows; r0 += 8) {
-    const int r = r0 + sub;
-    const int cand = r >> 1;
-    const int cnode = __shfl(node, cand & 63, kWave);
-    const bool live = r < n_rows && ((rm >> (cand & 63)) & 1ull) && (2 * cnode + (r & 1) < m_child);
-    float acc[GM];
+  constexpr int BATCH = 4;  // passes of 8 rows whose loads are issued together
+  for (int r0 = 0; r0 < n_rows; r0 += 8 * BATCH) {
+    float4 x[BATCH][CPL / 4];
+    bool live[BATCH];
 #pragma unroll
-    for (int h = 0; h < GM; ++h) acc[h] = 0.f;
-    if (live) {
-      const float* row = child_rows + (size_t)(2 * cnode + (r & 1)) * D + part * CPL;
+    for (int pp = 0; pp < BATCH; ++pp) {
+      const int r = r0 + 8 * pp + sub;
+      const int cand = r >> 1;
+      const int cnode = __shfl(node, cand & 63, kWave);
+      live[pp] = r < n_rows && ((rm >> (cand & 63)) & 1ull) && (2 * cnode + (r & 1) < m_child);
+      const float* row = child_rows + (size_t)(live[pp] ? 2 * cnode + (r & 1) : 0) * D + part * CPL;
 #pragma unroll
-      for (int c = 0; c < CPL; c += 4) {
-        const float4 x = *reinterpret_cast<const float4*>(row + c);
-#pragma unroll
-        for (int h = 0; h < GM; ++h) {
-          if (h < group)
-            acc[h] += qreg[h][c] * x.x + qreg[h][c + 1] * x.y + qreg[h][c + 2] * x.z +
-                      qreg[h][c + 3] * x.w;
-        }
-      }
+      for (int c = 0; c < CPL / 4; ++c)
+        x[pp][c] = live[pp] ? *reinterpret_cast<const float4*>(row + 4 * c) : make_float4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int h = 0; h < GM; ++h) {
-      if (h < group) {
-        float v = acc[h];
-        v += __shfl_xor(v, 1, kWave);
-        v += __shfl_xor(v, 2, kWave);
-        v += __shfl_xor(v, 4, kWave);
-        if (part == 0 && r < 128) dots[h * 128 + r] = v;
+    for (int pp = 0; pp < BATCH; ++pp) {
+      const int r = r0 + 8 * pp + sub;
+      float acc[GM];
+#pragma unroll
+      for (int h = 0; h < GM; ++h) {
+        acc[h] = 0.f;
+#pragma unroll
+        for (int c = 0; c < CPL / 4; ++c)
+          acc[h] += qreg[h][4 * c] * x[pp][c].x + qreg[h][4 * c + 1] * x[pp][c].y +
+                    qreg[h][4 * c + 2] * x[pp][c].z + qreg[h][4 * c + 3] * x[pp][c].w;
+      }
+#pragma unroll
+      for (int h = 0; h < GM; ++h) {
+        if (h < group) {
+          float v = acc[h];
+          v += __shfl_xor(v, 1, kWave);
+          v += __shfl_xor(v, 2, kWave);
+          v += __shfl_xor(v, 4, kWave);
+          if (part == 0 && r < 128) dots[h * 128 + r] = v;
+        }
       }
     }
   }
@@ -165,8 +170,8 @@ __device__ __forceinline__ float score_level_coalesced(const float* __restrict__
 template <typename T, int D, int GM>
 __global__ __launch_bounds__(kS1Waves * kWave) void stage1_kernel(
     const T* __restrict__ q, const float* __restrict__ pyr, int* __restrict__ s1_nodes,
-    int* __restrict__ counts, int heads_q, int heads_kv, int n_tok, int block, int topk, int group,
-    int causal, int force, float scale_log2, LevelTable lv) {
+    int heads_q, int heads_kv, int n_tok, int block, int topk, int group, int causal, int force,
+    float scale_log2, LevelTable lv) {
   constexpr int CPL = D / 8;
   __shared__ int nbuf_all[kS1Waves][kWave];
   __shared__ float dots_all[kS1Waves][GM * 128];
@@ -243,15 +248,12 @@ __global__ __launch_bounds__(kS1Waves * kWave) void stage1_kernel(
       keep = false;
     }
   }
-  // Kept level-3 nodes: compact into s1_nodes[u][0..nk), -1 after; count pairs.
+  // Kept level-3 nodes: compact into s1_nodes[u][0..nk), -1 after.
   const uint64_t km = ballot(keep);
   const int nk = __popcll(km);
   const size_t u = (size_t)bh * n_tok + t;
   int* out = s1_nodes + u * topk;
-  if (keep) {
-    out[lanes_below(km)] = node;
-    atomicAdd(&counts[(size_t)bh * lv.size[kSplitLevel - 1] + node], 1);
-  }
+  if (keep) out[lanes_below(km)] = node;
   if (lane >= nk && lane < topk) out[lane] = -1;
 }
 
@@ -264,17 +266,19 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_ca
 // One workgroup per work item (level-3 node n of KV head bh, up to 256 pairs).
 template <int D>
 __global__ __launch_bounds__(kS2Threads) void stage2_kernel(
-    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const int* __restrict__ items,
-    const int* __restrict__ n_items, const int* __restrict__ pairs, float* __restrict__ scores,
-    int heads_q, int heads_kv, int n_tok, int block, int topk, int group, int m1, int m2, int m3,
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+    const int* __restrict__ item_offsets, const int* __restrict__ offsets,
+    const int* __restrict__ pairs, float* __restrict__ scores, int n_buckets, int heads_q,
+    int heads_kv, int n_tok, int block, int topk, int group, int m1, int m2, int m3,
     float scale_log2) {
   constexpr int KSTEPS = D / 16;
   constexpr int ROW = D + 8;  // padded LDS row (bf16 elements) against bank conflicts
   constexpr int NODE_KEYS = 256;
   __shared__ __attribute__((aligned(16))) bf16_t ks[NODE_KEYS * ROW];
-  const int item = blockIdx.x;
-  if (item >= *n_items) return;
-  const int bucket = items[3 * item], start = items[3 * item + 1], len = items[3 * item + 2];
+  int bucket, start, len;
+  if (!bucket::locate_item(item_offsets, offsets, n_buckets, blockIdx.x, kS2PairsPerItem, &bucket,
+                           &start, &len))
+    return;
   const int bh = bucket / m3, node = bucket % m3;
   const int b = bh / heads_kv, kvh = bh % heads_kv;
   const int tok0 = node * 4 * block;
@@ -487,7 +491,7 @@ hipError_t stage1_launch(const LaunchShape& s, const void* q, const float* pyr, 
                          hipStream_t st) {
   dim3 grid((s.seq_len + kS1Waves - 1) / kS1Waves, s.batch * s.heads_kv);
   hipLaunchKernelGGL((stage1_kernel<T, D, GM>), grid, dim3(kS1Waves * kWave), 0, st,
-                     static_cast<const T*>(q), pyr, w.s1_nodes, w.counts, s.heads_q, s.heads_kv,
+                     static_cast<const T*>(q), pyr, w.s1_nodes, s.heads_q, s.heads_kv,
                      s.seq_len, s.block, s.topk, s.group, s.causal ? 1 : 0, s.force ? 1 : 0,
                      s.scale * kLog2e, s.lv);
   return hipGetLastError();
@@ -511,34 +515,27 @@ hipError_t launch_select_two_stage(const LaunchShape& s, const void* q, const vo
   const WsLayout lay = ws_layout(s);
   const Ws w = ws_bind(lay, ws);
   const int m1 = s.lv.size[0], m2 = s.lv.size[1], m3 = s.lv.size[kSplitLevel - 1];
-  hipLaunchKernelGGL(bucket::fill_zero_kernel, dim3(bucket::grid_for(lay.n_buckets)), dim3(256),
-                     0, st, w.counts, lay.n_buckets);
-  hipError_t e = hipGetLastError();
+  hipError_t e = s.group == 1
+                    ? (s.head_dim == 128 ? stage1_launch<bf16_t, 128, 1>(s, q, pyr, w, st)
+                                         : stage1_launch<bf16_t, 64, 1>(s, q, pyr, w, st))
+                    : (s.head_dim == 128 ? stage1_launch<bf16_t, 128, 4>(s, q, pyr, w, st)
+                                         : stage1_launch<bf16_t, 64, 4>(s, q, pyr, w, st));
   if (e != hipSuccess) return e;
-  if (s.group == 1)
-    e = s.head_dim == 128 ? stage1_launch<bf16_t, 128, 1>(s, q, pyr, w, st)
-                          : stage1_launch<bf16_t, 64, 1>(s, q, pyr, w, st);
-  else
-    e = s.head_dim == 128 ? stage1_launch<bf16_t, 128, 4>(s, q, pyr, w, st)
-                          : stage1_launch<bf16_t, 64, 4>(s, q, pyr, w, st);
+  e = bucket::sort_pairs(w.s1_nodes, s.batch * s.heads_kv, s.seq_len, s.topk, m3, kS2PairsPerItem,
+                         w.counts, w.offsets, w.cursors, w.item_offsets, w.pairs, false, st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bucket::scan_kernel, dim3(1), dim3(1024), 0, st, w.counts, w.offsets,
-                     w.cursors, w.items, w.n_items, lay.n_buckets, lay.max_items, kS2PairsPerItem);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  const size_t n_slots = (size_t)s.batch * s.heads_kv * s.seq_len * s.topk;
-  hipLaunchKernelGGL(bucket::scatter_kernel, dim3(bucket::grid_for(n_slots)), dim3(256), 0, st,
-                     w.s1_nodes, w.cursors, w.pairs, s.seq_len, s.topk, m3, n_slots);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   if (s.head_dim == 128)
     hipLaunchKernelGGL((stage2_kernel<128>), dim3(lay.max_items), dim3(kS2Threads), 0, st,
-                       static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k), w.items,
-                       w.n_items, w.pairs, w.scores, s.heads_q, s.heads_kv, s.seq_len, s.block,
-                       s.topk, s.group, m1, m2, m3, s.scale * kLog2e);
+                       static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
+                       w.item_offsets, w.offsets, w.pairs, w.scores, lay.n_buckets, s.heads_q,
+                       s.heads_kv, s.seq_len, s.block, s.topk, s.group, m1, m2, m3,
+                       s.scale * kLog2e);
   else
     hipLaunchKernelGGL((stage2_kernel<64>), dim3(lay.max_items), dim3(kS2Threads), 0, st,
-                       static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k), w.items,
-                       w.n_items, w.pairs, w.scores, s.heads_q, s.heads_kv, s.seq_len, s.block,
-                       s.topk, s.group, m1, m2, m3, s.scale * kLog2e);
+                       static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
+                       w.item_offsets, w.offsets, w.pairs, w.scores, lay.n_buckets, s.heads_q,
+                       s.heads_kv, s.seq_len, s.block, s.topk, s.group, m1, m2, m3,
+                       s.scale * kLog2e);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   dim3 grid((s.seq_len + kS1Waves - 1) / kS1Waves, s.batch * s.heads_kv);
   hipLaunchKernelGGL(final_kernel, grid, dim3(kS1Waves * kWave), 0, st, w.s1_nodes, w.scores, idx,

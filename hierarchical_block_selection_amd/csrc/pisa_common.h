@@ -98,12 +98,19 @@ __device__ __forceinline__ float wave_sum(float v) {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// Hardware exp2/log2 (v_exp_f32 / v_log_f32, about 1 ulp).  Used where the
+// argument of exp2 is <= 0 (results below 2^-126 flush to 0, which a
+// log-sum-exp does not notice) and the argument of log2 is >= 1.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
 __device__ __forceinline__ float pos_inf() { return __int_as_float(0x7f800000); }
 __device__ __forceinline__ float neg_inf() { return __int_as_float(0xff800000); }
 
 // Ranking order of the selection: higher score first, ties to the lower index.
+// Bitwise (not short-circuit) so that it compiles to compares and selects.
 __device__ __forceinline__ bool ranks_before(float s1, int i1, float s2, int i2) {
-  return s1 > s2 || (s1 == s2 && i1 < i2);
+  return (s1 > s2) | ((s1 == s2) & (i1 < i2));
 }
 
 }  // namespace pisa

@@ -28,6 +28,7 @@
 #include "pisa_common.h"
 #include "pisa_launch.h"
 #include "select_core.h"
+#include "stage1_tile.h"
 
 namespace pisa {
 
@@ -51,10 +52,13 @@ struct Ws {
   int* s1_nodes;      // [U * K]
   int* pairs;         // [U * K]
   float* scores;      // [U * K * kScoreStride]
+  bf16_t* plane_hi;   // [B * Hkv * R * d] bf16 hi part of the pyramid
+  bf16_t* plane_lo;   // [B * Hkv * R * d] bf16 lo part
 };
 
 struct WsLayout {
-  size_t counts, offsets, cursors, item_offsets, s1_nodes, pairs, scores, total;
+  size_t counts, offsets, cursors, item_offsets, s1_nodes, pairs, scores, plane_hi, plane_lo,
+      total;
   int n_buckets, max_items;
 };
 
@@ -74,6 +78,9 @@ WsLayout ws_layout(const LaunchShape& s) {
   w.s1_nodes = off; off = align256(off + sizeof(int) * units * s.topk);
   w.pairs = off; off = align256(off + sizeof(int) * units * s.topk);
   w.scores = off; off = align256(off + sizeof(float) * units * s.topk * kScoreStride);
+  const size_t plane = (size_t)s.batch * s.heads_kv * s.lv.rows * s.head_dim * sizeof(bf16_t);
+  w.plane_hi = off; off = align256(off + plane);
+  w.plane_lo = off; off = align256(off + plane);
   w.total = off;
   return w;
 }
@@ -83,7 +90,8 @@ Ws ws_bind(const WsLayout& l, void* base) {
   return {reinterpret_cast<int*>(b + l.counts), reinterpret_cast<int*>(b + l.offsets),
           reinterpret_cast<int*>(b + l.cursors), reinterpret_cast<int*>(b + l.item_offsets),
           reinterpret_cast<int*>(b + l.s1_nodes), reinterpret_cast<int*>(b + l.pairs),
-          reinterpret_cast<float*>(b + l.scores)};
+          reinterpret_cast<float*>(b + l.scores), reinterpret_cast<bf16_t*>(b + l.plane_hi),
+          reinterpret_cast<bf16_t*>(b + l.plane_lo)};
 }
 
 // ---------------------------------------------------------------------------
@@ -497,6 +505,22 @@ hipError_t stage1_launch(const LaunchShape& s, const void* q, const float* pyr, 
   return hipGetLastError();
 }
 
+template <int D, int G>
+hipError_t stage1_tile_launch(const LaunchShape& s, const void* q, const float* pyr, const Ws& w,
+                              hipStream_t st) {
+  constexpr int T = tile1::kCols / G;
+  dim3 grid((s.seq_len + T - 1) / T, s.batch * s.heads_kv);
+  const size_t n = (size_t)s.batch * s.heads_kv * s.lv.rows * D;
+  hipLaunchKernelGGL(tile1::split_planes_kernel, dim3(bucket::grid_for(n)), dim3(256), 0, st, pyr,
+                     w.plane_hi, w.plane_lo, n);
+  hipLaunchKernelGGL((tile1::stage1_tile_kernel<D, G>), grid, dim3(tile1::kThreads), 0, st,
+                     static_cast<const bf16_t*>(q), pyr, w.plane_hi, w.plane_lo, w.s1_nodes,
+                     s.heads_q, s.heads_kv,
+                     s.seq_len, s.block, s.topk, s.causal ? 1 : 0, s.force ? 1 : 0,
+                     s.scale * kLog2e, s.lv, kSplitLevel);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 bool select_two_stage_supported(const LaunchShape& s) {
@@ -515,11 +539,22 @@ hipError_t launch_select_two_stage(const LaunchShape& s, const void* q, const vo
   const WsLayout lay = ws_layout(s);
   const Ws w = ws_bind(lay, ws);
   const int m1 = s.lv.size[0], m2 = s.lv.size[1], m3 = s.lv.size[kSplitLevel - 1];
-  hipError_t e = s.group == 1
-                    ? (s.head_dim == 128 ? stage1_launch<bf16_t, 128, 1>(s, q, pyr, w, st)
-                                         : stage1_launch<bf16_t, 64, 1>(s, q, pyr, w, st))
-                    : (s.head_dim == 128 ? stage1_launch<bf16_t, 128, 4>(s, q, pyr, w, st)
-                                         : stage1_launch<bf16_t, 64, 4>(s, q, pyr, w, st));
+  hipError_t e;
+  if (s.topk <= 16) {
+    switch (s.group * 1000 + s.head_dim) {
+      case 1128: e = stage1_tile_launch<128, 1>(s, q, pyr, w, st); break;
+      case 1064: e = stage1_tile_launch<64, 1>(s, q, pyr, w, st); break;
+      case 2128: e = stage1_tile_launch<128, 2>(s, q, pyr, w, st); break;
+      case 2064: e = stage1_tile_launch<64, 2>(s, q, pyr, w, st); break;
+      case 4128: e = stage1_tile_launch<128, 4>(s, q, pyr, w, st); break;
+      default: e = stage1_tile_launch<64, 4>(s, q, pyr, w, st); break;
+    }
+  } else {
+    e = s.group == 1 ? (s.head_dim == 128 ? stage1_launch<bf16_t, 128, 1>(s, q, pyr, w, st)
+                                          : stage1_launch<bf16_t, 64, 1>(s, q, pyr, w, st))
+                     : (s.head_dim == 128 ? stage1_launch<bf16_t, 128, 4>(s, q, pyr, w, st)
+                                          : stage1_launch<bf16_t, 64, 4>(s, q, pyr, w, st));
+  }
   if (e != hipSuccess) return e;
   e = bucket::sort_pairs(w.s1_nodes, s.batch * s.heads_kv, s.seq_len, s.topk, m3, kS2PairsPerItem,
                          w.counts, w.offsets, w.cursors, w.item_offsets, w.pairs, false, st);

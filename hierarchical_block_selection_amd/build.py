@@ -25,6 +25,10 @@ CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # packed-fp32 instructions stay off: ordinary float code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # The kernels never rely on signalling-NaN semantics (their sentinels are
+    # +-inf, which stay valid): without IEEE mode fmaxf needs no canonicalising
+    # moves in the reductions.
+    "-fno-honor-nans", "-Xarch_device", "-mno-amdgpu-ieee",
     "-Wno-unused-result", "-I", INCLUDE, "-I", CSRC,
 ]
 

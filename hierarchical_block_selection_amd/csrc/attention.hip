@@ -115,8 +115,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_partial_kernel(
   constexpr int NW = kAttnThreads / kWave;
   __shared__ __attribute__((aligned(16))) bf16_t ks[C * KROW];
   __shared__ __attribute__((aligned(16))) bf16_t vt[D * VROW];
+  constexpr int OROW = D + 8;  // padded output staging row (bf16)
   __shared__ float inv_l[NW][kAttnCols];
   __shared__ int pid_s[NW][kAttnCols];
+  __shared__ __attribute__((aligned(16))) bf16_t obuf[NW][kAttnCols * OROW];
   int bucket, start, len;
   if (!bucket::locate_item(item_offsets, offsets, n_buckets, blockIdx.x, kAttnPairsPerItem,
                            &bucket, &start, &len))
@@ -149,13 +151,12 @@ __global__ __launch_bounds__(kAttnThreads) void attn_partial_kernel(
   const int col = lane & 31, khalf = lane >> 5;
   const int per_chunk = kAttnCols / group;
   const int n_chunks = (len + per_chunk - 1) / per_chunk;
-  for (int ch = wave; ch < n_chunks; ch += NW) {
+  const int h = col % group;
+  auto load_chunk = [&](int ch, bf16x8_t (&bq)[KSTEPS], int& pair_id, int& t) {
     const int p = ch * per_chunk + col / group;
-    const int h = col % group;
-    const bool live = p < len;
-    int pair_id = -1, t = 0;
-    bf16x8_t bq[KSTEPS];
-    if (live) {
+    pair_id = -1;
+    t = 0;
+    if (ch < n_chunks && p < len) {
       pair_id = pairs[start + p];
       t = (int)(((size_t)pair_id / topk) % n_tok);
       const bf16_t* qrow = q + (((size_t)b * heads_q + (size_t)kvh * group + h) * n_tok + t) * D;
@@ -166,6 +167,15 @@ __global__ __launch_bounds__(kAttnThreads) void attn_partial_kernel(
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) bq[s] = as_bf16x8(make_uint4(0, 0, 0, 0));
     }
+  };
+  bf16x8_t bq[KSTEPS];
+  int pair_id, t;
+  load_chunk(wave, bq, pair_id, t);
+  bf16_t* ostage = &obuf[wave][0];
+  for (int ch = wave; ch < n_chunks; ch += NW) {
+    bf16x8_t bn[KSTEPS];
+    int pair_next, t_next;
+    load_chunk(ch + NW, bn, pair_next, t_next);  // prefetch the next chunk
     f32x16_t s0 = {}, s1 = {};
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
@@ -176,24 +186,29 @@ __global__ __launch_bounds__(kAttnThreads) void attn_partial_kernel(
       s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bq[s], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bq[s], s1, 0, 0, 0);
     }
-    // Lane holds logits of key rows (i/4)*8 + khalf*4 + i%4 (+32 in s1) for column col.
+    // Lane holds raw logits of key rows (i/4)*8 + khalf*4 + i%4 (+32 in s1) for column col.
     int lim = n_keys - 1;
     if (causal) lim = min(lim, t - tok0);
+    if (pair_id < 0) lim = -1;
+    const bool any_masked = __ballot(lim < C - 1) != 0;
+    if (any_masked) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = (i / 4) * 8 + khalf * 4 + (i % 4);
+        s0[i] = r <= lim ? s0[i] : neg_inf();
+        s1[i] = r + 32 <= lim ? s1[i] : neg_inf();
+      }
+    }
     float m = neg_inf();
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = (i / 4) * 8 + khalf * 4 + (i % 4);
-      s0[i] = r <= lim ? s0[i] * scale_log2 : neg_inf();
-      s1[i] = r + 32 <= lim ? s1[i] * scale_log2 : neg_inf();
-      m = fmaxf(m, fmaxf(s0[i], s1[i]));
-    }
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, fmaxf(s0[i], s1[i]));
     m = fmaxf(m, __shfl_xor(m, 32, kWave));
-    if (m == neg_inf()) m = 0.f;  // column without keys (dead column)
+    const float ms = m == neg_inf() ? 0.f : m * scale_log2;  // column without keys
     float l = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      s0[i] = exp2f(s0[i] - m);
-      s1[i] = exp2f(s1[i] - m);
+      s0[i] = fast_exp2(fmaf(s0[i], scale_log2, -ms));
+      s1[i] = fast_exp2(fmaf(s1[i], scale_log2, -ms));
       l += s0[i] + s1[i];
     }
     l += __shfl_xor(l, 32, kWave);
@@ -222,21 +237,34 @@ __global__ __launch_bounds__(kAttnThreads) void attn_partial_kernel(
     if (khalf == 0) {
       inv_l[wave][col] = l > 0.f ? 1.f / l : 0.f;
       pid_s[wave][col] = pair_id;
-      if (live) part_lse[(size_t)pair_id * group + h] = m + log2f(l);
+      if (pair_id >= 0) part_lse[(size_t)pair_id * group + h] = ms + fast_log2(l);
     }
     wave_lds_sync();
-    // o[db][i] = O[row (i/4)*8 + khalf*4 + i%4][d = 32*db + col]
+    // o[db][i] = O[row (i/4)*8 + khalf*4 + i%4][d = 32*db + col] -> LDS [row][d] (bf16)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int r = (i / 4) * 8 + khalf * 4 + (i % 4);
-      const int pr = pid_s[wave][r];
-      if (pr < 0) continue;
       const float inv = inv_l[wave][r];
-      bf16_t* dst = part_o + ((size_t)pr * group + (r % group)) * D + col;
 #pragma unroll
-      for (int db = 0; db < DBLK; ++db) dst[32 * db] = f32_to_bf16(o[db][i] * inv);
+      for (int db = 0; db < DBLK; ++db) ostage[r * OROW + 32 * db + col] = f32_to_bf16(o[db][i] * inv);
     }
     wave_lds_sync();
+    // 16-byte stores: each row is D bf16 = D/8 chunks.
+    constexpr int CH_PER_ROW = D / 8;
+#pragma unroll
+    for (int x = lane; x < 32 * CH_PER_ROW; x += kWave) {
+      const int r = x / CH_PER_ROW, c8 = (x % CH_PER_ROW) * 8;
+      const int pr = pid_s[wave][r];
+      if (pr >= 0) {
+        const uint4 v = *reinterpret_cast<const uint4*>(&ostage[r * OROW + c8]);
+        *reinterpret_cast<uint4*>(part_o + ((size_t)pr * group + (r % group)) * D + c8) = v;
+      }
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) bq[s] = bn[s];
+    pair_id = pair_next;
+    t = t_next;
   }
 }
 
@@ -269,7 +297,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
       const int x = ir[j];
       if (x < 0 || x >= m1) continue;
       const size_t pi = (u * topk + j) * group + h;
-      const float w = exp2f(part_lse[pi] - M);
+      const float w = fast_exp2(part_lse[pi] - M);
       W += w;
       const bf16_t* src = part_o + pi * D + sub * EPL;
       float vals[8];
@@ -292,7 +320,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
   for (int e = 0; e < EPL; ++e) dst[e] = f32_to_bf16(acc[e] * inv);
   if (lse_out && sub == 0) {
     lse_out[((size_t)b * heads_q + (size_t)kvh * group + h) * n_tok + t] =
-        W > 0.f ? (M + log2f(W)) * kLn2 : neg_inf();
+        W > 0.f ? (M + fast_log2(W)) * kLn2 : neg_inf();
   }
 }
 

@@ -26,12 +26,12 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
 
-// Round-to-nearest-even float -> bfloat16 bits (NaN stays NaN).
+// Round-to-nearest-even float -> bfloat16 bits (NaN stays NaN), branch-free.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t nan = (u >> 16) | 0x40u;
+  return uint16_t((u & 0x7fffffffu) > 0x7f800000u ? nan : r);
 }
 
 // Elements of T covered by one 16-byte load.

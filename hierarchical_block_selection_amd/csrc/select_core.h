@@ -192,12 +192,12 @@ __device__ SelectResult select_descend(const float* q_s, int group, const T* __r
       const uint64_t km = ballot(keep);
       const int p = lanes_below(km);
       const int m_child = lv.size[l - 2];
-      if (keep) {
+      if (keep && p < topk) {  // p < K unless NaN inputs broke the order
         nbuf[2 * p] = 2 * node;
         nbuf[2 * p + 1] = (2 * node + 1 < m_child) ? 2 * node + 1 : -1;
       }
       wave_lds_sync();
-      node = lane < 2 * __popcll(km) ? nbuf[lane] : -1;
+      node = lane < 2 * min(__popcll(km), topk) ? nbuf[lane] : -1;
       wave_lds_sync();
       keep = false;
     }
@@ -219,7 +219,9 @@ __device__ __forceinline__ void write_selection(const SelectResult& r, int topk,
     it &= it - 1;
     pos += readlane_i(r.node, j) < r.node ? 1 : 0;
   }
-  if (r.keep) {
+  // pos < nk <= topk whenever the scores are totally ordered; the bound keeps
+  // the row in place even if NaN inputs broke that order.
+  if (r.keep && pos < topk) {
     idx_row[pos] = r.node;
     if (score_row) score_row[pos] = r.score;
   }

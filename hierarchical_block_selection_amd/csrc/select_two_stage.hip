@@ -246,12 +246,12 @@ __global__ __launch_bounds__(kS1Waves * kWave) void stage1_kernel(
       const uint64_t km = ballot(keep);
       const int p = lanes_below(km);
       const int m_child = lv.size[l - 2];
-      if (keep) {
+      if (keep && p < topk) {  // p < K unless NaN inputs broke the order
         nbuf[2 * p] = 2 * node;
         nbuf[2 * p + 1] = (2 * node + 1 < m_child) ? 2 * node + 1 : -1;
       }
       wave_lds_sync();
-      node = lane < 2 * __popcll(km) ? nbuf[lane] : -1;
+      node = lane < 2 * min(__popcll(km), topk) ? nbuf[lane] : -1;
       wave_lds_sync();
       keep = false;
     }
@@ -309,16 +309,15 @@ __global__ __launch_bounds__(kS2Threads) void stage2_kernel(
   const int per_chunk = kS2Cols / group;  // pairs per 32-column chunk
   const int n_chunks = (len + per_chunk - 1) / per_chunk;
   const int n_leaves = min(4, m1 - 4 * node);
-  for (int ch = wave; ch < n_chunks; ch += kS2Threads / kWave) {
+  const bool full = n_keys == 4 * block;  // every key of the node exists: no masking
+  const int h = col % group;
+  // Query rows of a chunk -> MFMA B operands (zero for columns past the list).
+  auto load_chunk = [&](int ch, bf16x8_t (&bq)[KSTEPS], int& pair_id) {
     const int p = ch * per_chunk + col / group;
-    const int h = col % group;
-    const bool live = p < len;
-    int pair_id = 0;
-    bf16x8_t bq[KSTEPS];
-    if (live) {
+    pair_id = -1;
+    if (ch < n_chunks && p < len) {
       pair_id = pairs[start + p];
-      const size_t u = (size_t)pair_id / topk;
-      const int t = (int)(u % n_tok);
+      const int t = (int)(((size_t)pair_id / topk) % n_tok);
       const bf16_t* qrow = q + (((size_t)b * heads_q + (size_t)kvh * group + h) * n_tok + t) * D;
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s)
@@ -327,6 +326,14 @@ __global__ __launch_bounds__(kS2Threads) void stage2_kernel(
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) bq[s] = as_bf16x8(make_uint4(0, 0, 0, 0));
     }
+  };
+  bf16x8_t bq[KSTEPS];
+  int pair_id;
+  load_chunk(wave, bq, pair_id);
+  for (int ch = wave; ch < n_chunks; ch += kS2Threads / kWave) {
+    bf16x8_t bn[KSTEPS];
+    int pair_next;
+    load_chunk(ch + kS2Threads / kWave, bn, pair_next);  // prefetch the next chunk
     float leaf_lse[4], leaf_mean[4];
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
@@ -338,54 +345,57 @@ __global__ __launch_bounds__(kS2Threads) void stage2_kernel(
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) {
         const bf16x8_t a0 = as_bf16x8(
-            *reinterpret_cast<const uint4*>(&ks[(kr0 + (lane & 31)) * ROW + 16 * s + 8 * khalf]));
-        const bf16x8_t a1 = as_bf16x8(*reinterpret_cast<const uint4*>(
-            &ks[(kr0 + 32 + (lane & 31)) * ROW + 16 * s + 8 * khalf]));
+            *reinterpret_cast<const uint4*>(&ks[(kr0 + col) * ROW + 16 * s + 8 * khalf]));
+        const bf16x8_t a1 = as_bf16x8(
+            *reinterpret_cast<const uint4*>(&ks[(kr0 + 32 + col) * ROW + 16 * s + 8 * khalf]));
         acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bq[s], acc0, 0, 0, 0);
         acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bq[s], acc1, 0, 0, 0);
       }
-      // Lane holds logits of keys rows (i/4)*8 + khalf*4 + i%4 (+32 for acc1) of the leaf.
-      const int valid_keys = min(block, n_keys - kr0);
-      float m = neg_inf(), sraw = 0.f;
+      // Lane holds raw logits of key rows (i/4)*8 + khalf*4 + i%4 (+32 in acc1).
+      float m = neg_inf(), sraw = 0.f, se = 0.f;
+      int valid_keys = block;
+      if (full) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = (i / 4) * 8 + khalf * 4 + (i % 4);
-        if (r < valid_keys) {
-          m = fmaxf(m, acc0[i]);
-          sraw += acc0[i];
+        for (int i = 0; i < 16; ++i) {
+          m = fmaxf(m, fmaxf(acc0[i], acc1[i]));
+          sraw += acc0[i] + acc1[i];
         }
-        if (r + 32 < valid_keys) {
-          m = fmaxf(m, acc1[i]);
-          sraw += acc1[i];
-        }
-      }
-      m = fmaxf(m, __shfl_xor(m, 32, kWave));
-      const float ms = m * scale_log2;
-      float se = 0.f;
+        m = fmaxf(m, __shfl_xor(m, 32, kWave));
+        const float ms = m * scale_log2;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = (i / 4) * 8 + khalf * 4 + (i % 4);
-        if (r < valid_keys) se += exp2f(acc0[i] * scale_log2 - ms);
-        if (r + 32 < valid_keys) se += exp2f(acc1[i] * scale_log2 - ms);
+        for (int i = 0; i < 16; ++i)
+          se += fast_exp2(fmaf(acc0[i], scale_log2, -ms)) + fast_exp2(fmaf(acc1[i], scale_log2, -ms));
+      } else {
+        valid_keys = min(block, n_keys - kr0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = (i / 4) * 8 + khalf * 4 + (i % 4);
+          const float v0 = r < valid_keys ? acc0[i] : neg_inf();
+          const float v1 = r + 32 < valid_keys ? acc1[i] : neg_inf();
+          m = fmaxf(m, fmaxf(v0, v1));
+          sraw += (r < valid_keys ? acc0[i] : 0.f) + (r + 32 < valid_keys ? acc1[i] : 0.f);
+          acc0[i] = v0;
+          acc1[i] = v1;
+        }
+        m = fmaxf(m, __shfl_xor(m, 32, kWave));
+        const float ms = m * scale_log2;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          se += fast_exp2(fmaf(acc0[i], scale_log2, -ms)) + fast_exp2(fmaf(acc1[i], scale_log2, -ms));
       }
       se += __shfl_xor(se, 32, kWave);
       sraw += __shfl_xor(sraw, 32, kWave);
-      leaf_lse[f] = ms + log2f(se);
+      leaf_lse[f] = m * scale_log2 + fast_log2(se);
       leaf_mean[f] = sraw / float(valid_keys) * scale_log2;
     }
-    // Level-2 scores of children 2n, 2n+1: LSE over their leaves' mean logits.
+    // Level-2 scores of children 2n, 2n+1: LSE over their leaves' mean logits
+    // (a missing leaf has mean -inf and drops out).
     float lvl2[2];
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2) {
-      const int f0 = 2 * c2, f1 = 2 * c2 + 1;
-      if (f0 >= n_leaves) {
-        lvl2[c2] = neg_inf();
-      } else if (f1 >= n_leaves) {
-        lvl2[c2] = leaf_mean[f0];
-      } else {
-        const float mm = fmaxf(leaf_mean[f0], leaf_mean[f1]);
-        lvl2[c2] = mm + log2f(exp2f(leaf_mean[f0] - mm) + exp2f(leaf_mean[f1] - mm));
-      }
+      const float a = leaf_mean[2 * c2], bb = leaf_mean[2 * c2 + 1];
+      const float mm = fmaxf(a, bb);
+      lvl2[c2] = mm == neg_inf() ? neg_inf() : mm + fast_log2(fast_exp2(a - mm) + fast_exp2(bb - mm));
     }
     // Sum over the group's heads (adjacent columns), eq. (11).
     float outv[6] = {leaf_lse[0], leaf_lse[1], leaf_lse[2], leaf_lse[3], lvl2[0], lvl2[1]};
@@ -393,12 +403,15 @@ __global__ __launch_bounds__(kS2Threads) void stage2_kernel(
 #pragma unroll
       for (int j = 0; j < 6; ++j) outv[j] += __shfl_xor(outv[j], o, kWave);
     }
-    if (live && khalf == 0 && h == 0) {
+    if (pair_id >= 0 && khalf == 0 && h == 0) {
       float* dst = scores + (size_t)pair_id * kScoreStride;
       *reinterpret_cast<float4*>(dst) =
           make_float4(outv[0] * kLn2, outv[1] * kLn2, outv[2] * kLn2, outv[3] * kLn2);
       *reinterpret_cast<float4*>(dst + 4) = make_float4(outv[4] * kLn2, outv[5] * kLn2, 0.f, 0.f);
     }
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) bq[s] = bn[s];
+    pair_id = pair_next;
   }
 }
 
@@ -474,7 +487,7 @@ __global__ __launch_bounds__(kS1Waves * kWave) void final_kernel(
       // Expand kept level-2 nodes into leaves; leaf score index = slot*8 + 2*c + c'.
       const uint64_t km = ballot(keep);
       const int p = lanes_below(km);
-      if (keep) {
+      if (keep && p < topk) {  // p < K unless NaN inputs broke the order
         const int slot = src / kScoreStride, c = src % kScoreStride - 4;
         nbuf[2 * p] = 2 * node;
         sbuf[2 * p] = slot * kScoreStride + 2 * c;
@@ -483,7 +496,7 @@ __global__ __launch_bounds__(kS1Waves * kWave) void final_kernel(
         sbuf[2 * p + 1] = slot * kScoreStride + 2 * c + 1;
       }
       wave_lds_sync();
-      const int n2 = 2 * __popcll(km);
+      const int n2 = 2 * min(__popcll(km), topk);
       node = lane < n2 ? nbuf[lane] : -1;
       src = lane < n2 ? sbuf[lane] : -1;
       wave_lds_sync();

@@ -43,41 +43,68 @@ def level_sizes(n, c):
 
 
 def descent_counts(n, c, k, force=True):
-    """For every query row t of a causal prefill: the number of intermediate
-    child summaries and of raw leaf keys the PISA descent scores, per head.
+    """For every query row t of a causal prefill, the dot products the PISA
+    descent performs per head, by level: rankable candidates at level l >= 2
+    score their two child summaries, rankable leaves score their C raw keys.
     Candidate counts are data-independent: every level keeps min(K, #A) nodes,
-    one of which is the current-path node, whose right child may be future."""
+    one of which is the current-path node, whose right child may be future.
+    Returns {level: int64 array over t}."""
     import numpy as np
     sizes = level_sizes(n, c)
     L = len(sizes)
-    inter = np.zeros(n, dtype=np.int64)
-    leaf = np.zeros(n, dtype=np.int64)
+    out = {lvl: np.zeros(n, dtype=np.int64) for lvl in range(1, L + 1)}
     for t in range(n):
         cur = t // c
         cand = 1
         for lvl in range(L, 0, -1):
             sh = lvl - 1
             lim = cur >> sh
-            # candidates after dropping future nodes: bounded by lim+1 nodes
             cand = min(cand, lim + 1)
             forced = {lim}
             if force:
                 forced |= {0}
                 if cur >= 1:
                     forced |= {(cur - 1) >> sh}
-            nf = len(forced)
             if cand > k:
-                ranked = cand - nf
-                if lvl >= 2:
-                    inter[t] += 2 * ranked
-                else:
-                    leaf[t] += c * ranked
+                ranked = cand - len(forced)
+                out[lvl][t] = 2 * ranked if lvl >= 2 else c * ranked
                 kept = k
             else:
                 kept = cand
             if lvl > 1:
                 cand = 2 * kept
-    return inter, leaf
+    return out
+
+
+def source_hash():
+    """Hash of the library's kernel sources (to tie stored counter data to them)."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "hierarchical_block_selection_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.txt")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            key, val = line.split("=", 1)
+            rec[key.strip()] = val.strip()
+    if rec.get("source_hash") != source_hash():
+        return None
+    try:
+        return float(rec["fetch_bytes"]) + float(rec["write_bytes"])
+    except (KeyError, ValueError):
+        return None
 
 
 def attended_keys(n, c, k):
@@ -150,6 +177,8 @@ def run(args):
         step()
     torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    pisa.pisa_profile_report()  # drop anything recorded earlier
+    pisa.pisa_profile_enable(True)
     t0 = time.perf_counter()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
@@ -158,32 +187,43 @@ def run(args):
     stop.record(stream)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    pisa.pisa_profile_enable(False)
+    kernels = {k: tot / cnt for k, (tot, cnt) in pisa.pisa_profile_report().items()}
     ms_per_step = start.elapsed_time(stop) / args.steps
     stage = {name: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in ev]))
              for i, name in enumerate(("pyramid", "select", "attn"))}
 
-    # Algorithmic work of the step.
-    inter, leaf = descent_counts(N, C, K)
+    # Algorithmic work of the step (the method's own dot products and bytes).
+    per_level = descent_counts(N, C, K)
+    L = len(per_level)
+    dots_l3 = sum(float(per_level[lvl].sum()) for lvl in range(3, L + 1))
+    dots_l2 = float(per_level[2].sum()) if L >= 2 else 0.0
+    dots_l1 = float(per_level[1].sum())
     keys = attended_keys(N, C, K)
-    sel_flops = 2.0 * d * float(inter.sum() + leaf.sum()) * H * B
+    sel_flops = 2.0 * d * (dots_l3 + dots_l2 + dots_l1) * H * B
     attn_flops = 4.0 * d * float(keys.sum()) * H * B
     elt = 2 if prob.dtype == torch.bfloat16 else 4
     pyr_bytes = B * H * (N * d * elt + rows * d * 4)
     attn_bytes = B * H * N * d * elt * 4  # Q, K, V read once, O written once
-
-    dominant = max(stage, key=stage.get)
-    if dominant == "pyramid":
-        roof = dict(bound="hbm", achieved=pyr_bytes / (stage["pyramid"] * 1e-3) / 1e9,
-                    peak=HBM_PEAK_GBS, unit="GB/s", kernel="pyramid")
-    elif dominant == "select":
-        roof = dict(bound="alu", achieved=sel_flops / (stage["select"] * 1e-3) / 1e12,
-                    peak=FP32_VALU_PEAK_TFLOPS, unit="TFLOP/s", kernel="select_fused_kernel")
-    else:
-        roof = dict(bound="mfma", achieved=attn_flops / (stage["attn"] * 1e-3) / 1e12,
-                    peak=BF16_MFMA_PEAK_TFLOPS, unit="TFLOP/s", kernel="attention")
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
-    roof["avg_kernel_ms"] = stage[dominant]
+    roof_table = {
+        "pyramid_chunk": ("hbm", pyr_bytes, HBM_PEAK_GBS, "GB/s"),
+        "select_stage1": ("alu", 2.0 * d * dots_l3 * H * B, FP32_VALU_PEAK_TFLOPS, "TFLOP/s"),
+        "select_stage2": ("mfma", 2.0 * d * (dots_l2 + dots_l1) * H * B, BF16_MFMA_PEAK_TFLOPS,
+                          "TFLOP/s"),
+        "select_fused": ("alu", sel_flops, FP32_VALU_PEAK_TFLOPS, "TFLOP/s"),
+        "attn_partial": ("mfma", attn_flops, BF16_MFMA_PEAK_TFLOPS, "TFLOP/s"),
+        "attn_query": ("alu", attn_flops, FP32_VALU_PEAK_TFLOPS, "TFLOP/s"),
+        "attn_combine": ("hbm", B * H * N * d * elt, HBM_PEAK_GBS, "GB/s"),
+    }
+    dominant = max(kernels, key=kernels.get)
+    bound, work, peak, unit = roof_table.get(dominant, ("hbm", 0.0, HBM_PEAK_GBS, "GB/s"))
+    scale = 1e9 if unit == "GB/s" else 1e12
+    achieved = work / (kernels[dominant] * 1e-3) / scale
+    roof = {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+            "frac": achieved / peak, "traffic": stored_traffic(dominant),
+            "kernel": dominant, "avg_kernel_ms": kernels[dominant],
+            "algorithmic_work": work,
+            "work_unit": "bytes" if unit == "GB/s" else "flop"}
 
     result = {
         "metric": METRIC,
@@ -202,9 +242,11 @@ def run(args):
                                "bf16 N(0,1/d), forced first/prev/current blocks",
                    "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)"},
         "stages_ms": stage,
+        "kernels_ms": kernels,
         "wall_ms_per_step": wall_ms,
         "algorithmic": {"select_gflop": sel_flops / 1e9, "attn_gflop": attn_flops / 1e9,
-                        "pyramid_mb": pyr_bytes / 1e6, "attn_compulsory_mb": attn_bytes / 1e6},
+                        "pyramid_mb": pyr_bytes / 1e6, "attn_compulsory_mb": attn_bytes / 1e6,
+                        "source_hash": source_hash()},
         "roofline": roof,
     }
 

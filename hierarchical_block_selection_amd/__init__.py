@@ -23,6 +23,7 @@ from ._lib import PisaError  # noqa: F401
 __all__ = [
     "Problem", "PisaError", "pisa_pyramid_layout", "pisa_workspace_bytes", "pisa_build_pyramid",
     "pisa_select", "pisa_bsa_select", "pisa_block_sparse_attn", "pisa_decode_step",
+    "pisa_profile_enable", "pisa_profile_report",
 ]
 
 _DTYPES = {torch.float32: _lib.PISA_F32, torch.bfloat16: _lib.PISA_BF16}
@@ -235,3 +236,21 @@ def pisa_decode_step(problem: Problem, cache_len, q, k_cache, v_cache, pyramid, 
         _ptr(block_idx), _ptr(block_score), _ptr(out), _ptr(row_lse), _ptr(ws), ws_bytes,
         _stream(stream)))
     return block_idx, block_score, out, row_lse
+
+
+def pisa_profile_enable(enable: bool = True) -> None:
+    """Start (or stop) recording HIP events around every library kernel launch."""
+    _lib.check("pisa_profile_enable", _lib.load().pisa_profile_enable(1 if enable else 0))
+
+
+def pisa_profile_report(max_kernels: int = 64) -> dict:
+    """Wait for the recorded launches and return {kernel: (total_ms, launches)}."""
+    lib = _lib.load()
+    names = ctypes.create_string_buffer(8192)
+    tot = (ctypes.c_float * max_kernels)()
+    cnt = (ctypes.c_int32 * max_kernels)()
+    n = ctypes.c_int32()
+    _lib.check("pisa_profile_report",
+               lib.pisa_profile_report(names, len(names), tot, cnt, max_kernels, ctypes.byref(n)))
+    keys = names.value.decode().split("\n")[:min(n.value, max_kernels)]
+    return {k: (float(tot[i]), int(cnt[i])) for i, k in enumerate(keys)}

@@ -25,7 +25,7 @@ PISA_SELECT_AUTO, PISA_SELECT_FUSED, PISA_SELECT_TWO_STAGE = range(3)
 EXPORTED = (
     "pisa_pyramid_layout", "pisa_workspace_bytes", "pisa_build_pyramid", "pisa_select",
     "pisa_bsa_select", "pisa_block_sparse_attn", "pisa_decode_step", "pisa_status_string",
-    "pisa_last_error",
+    "pisa_last_error", "pisa_profile_enable", "pisa_profile_report",
 )
 
 
@@ -72,6 +72,11 @@ def load(path: str = LIB_PATH):
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = ctypes.c_int
+    lib.pisa_profile_enable.argtypes = [ctypes.c_int]
+    lib.pisa_profile_enable.restype = ctypes.c_int
+    lib.pisa_profile_report.argtypes = [ctypes.c_char_p, sz, ctypes.POINTER(ctypes.c_float),
+                                        ctypes.POINTER(i32), i32, ctypes.POINTER(i32)]
+    lib.pisa_profile_report.restype = ctypes.c_int
     lib.pisa_status_string.argtypes = [ctypes.c_int]
     lib.pisa_status_string.restype = ctypes.c_char_p
     lib.pisa_last_error.argtypes = []

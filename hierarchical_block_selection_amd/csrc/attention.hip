@@ -52,6 +52,7 @@ template <typename T, int D>
 static hipError_t launch_attn_t(const LaunchShape& s, const void* q, const void* k, const void* v,
                                 const int32_t* idx, void* out, float* lse, hipStream_t st) {
   dim3 grid((s.seq_len + kAttnWaves - 1) / kAttnWaves, s.batch * s.heads_q);
+  prof::Scope ps("attn_query", st);
   hipLaunchKernelGGL((attn_query_kernel<T, D>), grid, dim3(kAttnWaves * kWave), 0, st,
                      static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
                      idx, static_cast<T*>(out), lse, s.heads_q, s.heads_kv, s.seq_len, s.block,
@@ -337,15 +338,23 @@ hipError_t launch_block_path(const LaunchShape& s, const void* q, const void* k,
   bf16_t* part_o = reinterpret_cast<bf16_t*>(base + lay.part_o);
   float* part_lse = reinterpret_cast<float*>(base + lay.part_lse);
   const int m1 = s.lv.size[0];
-  hipError_t e = bucket::sort_pairs(idx, s.batch * s.heads_kv, s.seq_len, s.topk, m1,
+  hipError_t e;
+  {
+    prof::Scope ps("attn_sort", st);
+    e = bucket::sort_pairs(idx, s.batch * s.heads_kv, s.seq_len, s.topk, m1,
                                     kAttnPairsPerItem, counts, offsets, cursors, item_offsets,
                                     pairs, false, st);
+  }
   if (e != hipSuccess) return e;
+  {
+  prof::Scope ps("attn_partial", st);
   hipLaunchKernelGGL((attn_partial_kernel<D>), dim3(lay.max_items), dim3(kAttnThreads), 0, st,
                      static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
                      static_cast<const bf16_t*>(v), item_offsets, offsets, pairs, part_o,
                      part_lse, lay.n_buckets, s.heads_q, s.heads_kv, s.seq_len, s.topk, s.group,
                      m1, s.causal ? 1 : 0, s.scale * kLog2e);
+  }
+  prof::Scope ps("attn_combine", st);
   const size_t rows = (size_t)s.batch * s.heads_kv * s.seq_len * s.group;
   hipLaunchKernelGGL((attn_combine_kernel<D>), dim3((unsigned)((rows * 16 + 255) / 256)),
                      dim3(256), 0, st, idx, part_o, part_lse, static_cast<bf16_t*>(out), lse,

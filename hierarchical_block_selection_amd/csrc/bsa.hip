@@ -3,13 +3,18 @@
 // eligible leaf summary, the scores are written in full, then a Top-K pass
 // keeps the forced blocks plus the best K-#F others (ties to the lower index).
 //
-// Scores: s[t, i] = scale * (sum over the group's heads of q_h,t) . kbar_i,
-// which equals eq. (1) summed over the group's heads up to rounding.
-// Kernel 1 tiles 64 queries x 64 leaf summaries per workgroup (LDS-staged,
-// fp32 FMA), skipping tiles entirely above the causal diagonal.  Kernel 2 runs
-// one wavefront per query row: the row (<= 4096 scores) is held in registers,
-// 64 lane-local maxima bound the K-th best from below, the few scores at or
-// above that bound are compacted into LDS and ranked exactly.
+// Scores: s[t, i] = scale * sum over the group's heads of q_h,t . kbar_i
+// (eq. (1) summed over the group's heads).
+// bf16 inputs: the leaf summaries are split once into three bf16 planes
+// (hi + mid + lo carries the fp32 value), and each workgroup computes a tile of
+// 128 queries x 64 leaves as bf16 MFMA 32x32x16 (queries as the A operand, so
+// each output row is a coalesced 128-byte store), skipping tiles entirely
+// above the causal diagonal.  fp32 inputs use the LDS-tiled FMA kernel.
+// Top-K runs one wavefront per query row: the row (<= 4096 scores) is held in
+// registers, 64 lane-local maxima bound the K-th best from below, the few
+// scores at or above that bound are compacted into LDS and ranked exactly.
+#include <algorithm>
+
 #include "pisa_common.h"
 #include "pisa_launch.h"
 
@@ -73,6 +78,80 @@ __global__ __launch_bounds__(256) void bsa_scores_kernel(const T* __restrict__ q
     for (int w = 0; w < 4; ++w) {
       const int i = i0 + tx + 16 * w;
       if (i <= lim && i < m1) S[((size_t)bh * n_tok + t) * m1 + i] = acc[u][w] * scale;
+    }
+  }
+}
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+constexpr int kMfmaQ = 128;  // queries per workgroup tile (32 per wave)
+constexpr int kMfmaL = 64;   // leaves per workgroup tile
+
+// Level-1 summaries of every head -> three bf16 planes x = hi + mid + lo.
+__global__ void bsa_split_kernel(const float* __restrict__ pyr, bf16_t* __restrict__ planes,
+                                 int rows, int m1, int d, size_t n) {
+  // n = heads * m1 * d values; plane p of head bh, leaf i: planes[((p*heads + bh)*m1 + i)*d]
+  for (size_t x = (size_t)blockIdx.x * blockDim.x + threadIdx.x; x < n;
+       x += (size_t)gridDim.x * blockDim.x) {
+    const size_t bh = x / ((size_t)m1 * d), rem = x % ((size_t)m1 * d);
+    const float v = pyr[bh * (size_t)rows * d + rem];
+    const uint16_t h = f32_to_bf16(v);
+    const float r1 = v - bf16_to_f32(h);
+    const uint16_t m = f32_to_bf16(r1);
+    planes[x] = h;
+    planes[n + x] = m;
+    planes[2 * n + x] = f32_to_bf16(r1 - bf16_to_f32(m));
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void bsa_scores_mfma_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ planes, float* __restrict__ S,
+    int heads_q, int heads_kv, int n_tok, int block, int group, int m1, int causal, float scale,
+    size_t plane_stride) {
+  constexpr int KSTEPS = D / 16;
+  const int bh = blockIdx.z;
+  const int t0 = blockIdx.y * kMfmaQ, i0 = blockIdx.x * kMfmaL;
+  const int t_last = min(t0 + kMfmaQ, n_tok) - 1;
+  if (causal && i0 > t_last / block) return;
+  const int b = bh / heads_kv, kvh = bh % heads_kv;
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int col = lane & 31, kh = lane >> 5;
+  const int tq0 = t0 + 32 * wave;  // this wave's 32 queries
+  if (tq0 >= n_tok) return;
+  f32x16_t acc[2] = {};
+  const int tq = min(tq0 + col, n_tok - 1);  // A row (clamped; extra rows are not stored)
+#pragma unroll
+  for (int lb = 0; lb < 2; ++lb) {
+    const int leaf = min(i0 + 32 * lb + col, m1 - 1);  // B column (clamped)
+    const bf16_t* kp = planes + ((size_t)bh * m1 + leaf) * D;
+    for (int h = 0; h < group; ++h) {
+      const bf16_t* qrow = q + (((size_t)b * heads_q + (size_t)kvh * group + h) * n_tok + tq) * D;
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) {
+        const bf16x8_t a = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 16 * s + 8 * kh));
+#pragma unroll
+        for (int p = 2; p >= 0; --p) {
+          const bf16x8_t bb = as_bf16x8(
+              *reinterpret_cast<const uint4*>(kp + p * plane_stride + 16 * s + 8 * kh));
+          acc[lb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bb, acc[lb], 0, 0, 0);
+        }
+      }
+    }
+  }
+  // acc[lb][i] = S[query tq0 + (i/4)*8 + kh*4 + i%4][leaf i0 + 32*lb + col]
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int t = tq0 + (i / 4) * 8 + kh * 4 + (i % 4);
+    if (t >= n_tok) continue;
+    const int lim = causal ? t / block : m1 - 1;
+#pragma unroll
+    for (int lb = 0; lb < 2; ++lb) {
+      const int leaf = i0 + 32 * lb + col;
+      if (leaf <= lim && leaf < m1) S[((size_t)bh * n_tok + t) * m1 + leaf] = acc[lb][i] * scale;
     }
   }
 }
@@ -250,8 +329,16 @@ __global__ __launch_bounds__(256) void bsa_topk_kernel(const float* __restrict__
   }
 }
 
+static size_t scores_bytes(const LaunchShape& s) {
+  return ((size_t)s.batch * s.heads_kv * s.seq_len * s.lv.size[0] * sizeof(float) + 255) &
+         ~size_t(255);
+}
+
 size_t bsa_ws_bytes(const LaunchShape& s) {
-  return (size_t)s.batch * s.heads_kv * s.seq_len * s.lv.size[0] * sizeof(float);
+  const size_t planes = s.bf16 ? 3 * (size_t)s.batch * s.heads_kv * s.lv.size[0] * s.head_dim *
+                                     sizeof(bf16_t)
+                               : 0;
+  return scores_bytes(s) + planes;
 }
 
 template <typename T, int D>
@@ -260,6 +347,7 @@ static hipError_t launch_bsa_scores_t(const LaunchShape& s, const void* q, const
   const int m1 = s.lv.size[0];
   dim3 grid((m1 + kBsaTile - 1) / kBsaTile, (s.seq_len + kBsaTile - 1) / kBsaTile,
             s.batch * s.heads_kv);
+  prof::Scope ps("bsa_scores", st);
   hipLaunchKernelGGL((bsa_scores_kernel<T, D>), grid, dim3(256), 0, st, static_cast<const T*>(q),
                      pyr, S, s.heads_q, s.heads_kv, s.seq_len, s.block, s.group, m1, s.lv.rows,
                      s.causal ? 1 : 0, s.scale);
@@ -270,8 +358,27 @@ template <int VPL>
 static hipError_t launch_bsa_topk_t(const LaunchShape& s, const float* S, int32_t* idx,
                                     float* score, hipStream_t st) {
   dim3 grid((s.seq_len + 3) / 4, s.batch * s.heads_kv);
+  prof::Scope ps("bsa_topk", st);
   hipLaunchKernelGGL((bsa_topk_kernel<VPL>), grid, dim3(256), 0, st, S, idx, score, s.seq_len,
                      s.block, s.lv.size[0], s.topk, s.causal ? 1 : 0, s.force ? 1 : 0);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_bsa_mfma_t(const LaunchShape& s, const void* q, const float* pyr,
+                                    float* S, bf16_t* planes, hipStream_t st) {
+  const int m1 = s.lv.size[0];
+  const size_t n = (size_t)s.batch * s.heads_kv * m1 * D;
+  {
+    prof::Scope ps("bsa_split", st);
+    hipLaunchKernelGGL(bsa_split_kernel, dim3((unsigned)std::min<size_t>(65536, (n + 255) / 256)),
+                       dim3(256), 0, st, pyr, planes, s.lv.rows, m1, D, n);
+  }
+  dim3 grid((m1 + kMfmaL - 1) / kMfmaL, (s.seq_len + kMfmaQ - 1) / kMfmaQ, s.batch * s.heads_kv);
+  prof::Scope ps("bsa_scores", st);
+  hipLaunchKernelGGL((bsa_scores_mfma_kernel<D>), grid, dim3(256), 0, st,
+                     static_cast<const bf16_t*>(q), planes, S, s.heads_q, s.heads_kv, s.seq_len,
+                     s.block, s.group, m1, s.causal ? 1 : 0, s.scale, n);
   return hipGetLastError();
 }
 
@@ -279,10 +386,11 @@ hipError_t launch_bsa(const LaunchShape& s, const void* q, const float* pyr, int
                       float* score, void* ws, hipStream_t st) {
   float* S = static_cast<float*>(ws);
   hipError_t e;
-  if (s.bf16)
-    e = s.head_dim == 128 ? launch_bsa_scores_t<bf16_t, 128>(s, q, pyr, S, st)
-                          : launch_bsa_scores_t<bf16_t, 64>(s, q, pyr, S, st);
-  else
+  if (s.bf16) {
+    bf16_t* planes = reinterpret_cast<bf16_t*>(static_cast<char*>(ws) + scores_bytes(s));
+    e = s.head_dim == 128 ? launch_bsa_mfma_t<128>(s, q, pyr, S, planes, st)
+                          : launch_bsa_mfma_t<64>(s, q, pyr, S, planes, st);
+  } else
     e = s.head_dim == 128 ? launch_bsa_scores_t<float, 128>(s, q, pyr, S, st)
                           : launch_bsa_scores_t<float, 64>(s, q, pyr, S, st);
   if (e != hipSuccess) return e;

@@ -70,6 +70,7 @@ static hipError_t launch_decode_t(const LaunchShape& s, const int32_t* cache_len
                                   const void* kc, const void* vc, const float* pyr, int32_t* idx,
                                   float* score, void* out, float* lse, hipStream_t st) {
   const size_t lds = ((size_t)s.group * D + 3 * kWave) * sizeof(float);
+  prof::Scope ps("decode", st);
   hipLaunchKernelGGL((decode_kernel<T, D>), dim3(s.batch * s.heads_kv), dim3(kWave), lds, st,
                      cache_len, static_cast<const T*>(q), static_cast<const T*>(kc),
                      static_cast<const T*>(vc), pyr, idx, score, static_cast<T*>(out), lse,

@@ -9,6 +9,23 @@
 
 namespace pisa {
 
+namespace prof {
+// Brackets the launches issued while it lives with HIP events on `st` when
+// timing is enabled (pisa_profile_enable); does nothing otherwise.
+class Scope {
+ public:
+  Scope(const char* name, hipStream_t st);
+  ~Scope();
+  Scope(const Scope&) = delete;
+  Scope& operator=(const Scope&) = delete;
+
+ private:
+  const char* name_;
+  hipStream_t st_;
+  hipEvent_t start_;
+};
+}  // namespace prof
+
 // A validated problem in the form the launchers use.
 struct LaunchShape {
   int batch, heads_q, heads_kv, seq_len, head_dim, block, topk, group;

@@ -122,8 +122,11 @@ static hipError_t launch_pyramid_t(const LaunchShape& s, const void* k, float* p
                                    hipStream_t st) {
   const int chunks = (s.lv.size[0] + (1 << kPyrLeavesLog2) - 1) >> kPyrLeavesLog2;
   dim3 grid(chunks, s.batch * s.heads_kv);
-  hipLaunchKernelGGL((pyramid_chunk_kernel<T, D>), grid, dim3(kPyrThreads), 0, st,
-                     static_cast<const T*>(k), pyr, s.seq_len, s.block, s.lv);
+  {
+    prof::Scope ps("pyramid_chunk", st);
+    hipLaunchKernelGGL((pyramid_chunk_kernel<T, D>), grid, dim3(kPyrThreads), 0, st,
+                       static_cast<const T*>(k), pyr, s.seq_len, s.block, s.lv);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int first = 2 + kPyrLeavesLog2;
@@ -131,6 +134,7 @@ static hipError_t launch_pyramid_t(const LaunchShape& s, const void* k, float* p
     const size_t lds = (size_t)(s.lv.size[first - 1] + (s.lv.n > first ? s.lv.size[first] : 0)) *
                        D * sizeof(float);
     const bool use_lds = lds <= kTopLds;
+    prof::Scope ps("pyramid_top", st);
     hipLaunchKernelGGL((pyramid_top_kernel<D>), dim3(s.batch * s.heads_kv), dim3(kTopThreads),
                        use_lds ? lds : 0, st, pyr, s.lv, first, use_lds ? 1 : 0);
     e = hipGetLastError();

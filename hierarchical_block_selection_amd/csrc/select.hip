@@ -38,6 +38,7 @@ static hipError_t launch_fused_t(const LaunchShape& s, const void* q, const void
                                  const float* pyr, int32_t* idx, float* score, hipStream_t st) {
   dim3 grid((s.seq_len + kSelWaves - 1) / kSelWaves, s.batch * s.heads_kv);
   const size_t lds = (size_t)kSelWaves * (s.group * D + kWave) * sizeof(float);
+  prof::Scope ps("select_fused", st);
   hipLaunchKernelGGL((select_fused_kernel<T, D>), grid, dim3(kSelWaves * kWave), lds, st,
                      static_cast<const T*>(q), static_cast<const T*>(k), pyr, idx, score,
                      s.heads_q, s.heads_kv, s.seq_len, s.block, s.topk, s.group, s.causal ? 1 : 0,

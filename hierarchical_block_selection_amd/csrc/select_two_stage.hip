@@ -511,6 +511,7 @@ template <typename T, int D, int GM>
 hipError_t stage1_launch(const LaunchShape& s, const void* q, const float* pyr, const Ws& w,
                          hipStream_t st) {
   dim3 grid((s.seq_len + kS1Waves - 1) / kS1Waves, s.batch * s.heads_kv);
+  prof::Scope ps("select_stage1", st);
   hipLaunchKernelGGL((stage1_kernel<T, D, GM>), grid, dim3(kS1Waves * kWave), 0, st,
                      static_cast<const T*>(q), pyr, w.s1_nodes, s.heads_q, s.heads_kv,
                      s.seq_len, s.block, s.topk, s.group, s.causal ? 1 : 0, s.force ? 1 : 0,
@@ -524,8 +525,12 @@ hipError_t stage1_tile_launch(const LaunchShape& s, const void* q, const float* 
   constexpr int T = tile1::kCols / G;
   dim3 grid((s.seq_len + T - 1) / T, s.batch * s.heads_kv);
   const size_t n = (size_t)s.batch * s.heads_kv * s.lv.rows * D;
-  hipLaunchKernelGGL(tile1::split_planes_kernel, dim3(bucket::grid_for(n)), dim3(256), 0, st, pyr,
-                     w.plane_hi, w.plane_lo, n);
+  {
+    prof::Scope ps("select_split_planes", st);
+    hipLaunchKernelGGL(tile1::split_planes_kernel, dim3(bucket::grid_for(n)), dim3(256), 0, st,
+                       pyr, w.plane_hi, w.plane_lo, n);
+  }
+  prof::Scope ps("select_stage1", st);
   hipLaunchKernelGGL((tile1::stage1_tile_kernel<D, G>), grid, dim3(tile1::kThreads), 0, st,
                      static_cast<const bf16_t*>(q), pyr, w.plane_hi, w.plane_lo, w.s1_nodes,
                      s.heads_q, s.heads_kv,
@@ -569,9 +574,14 @@ hipError_t launch_select_two_stage(const LaunchShape& s, const void* q, const vo
                                           : stage1_launch<bf16_t, 64, 4>(s, q, pyr, w, st));
   }
   if (e != hipSuccess) return e;
-  e = bucket::sort_pairs(w.s1_nodes, s.batch * s.heads_kv, s.seq_len, s.topk, m3, kS2PairsPerItem,
-                         w.counts, w.offsets, w.cursors, w.item_offsets, w.pairs, false, st);
+  {
+    prof::Scope ps("select_sort", st);
+    e = bucket::sort_pairs(w.s1_nodes, s.batch * s.heads_kv, s.seq_len, s.topk, m3, kS2PairsPerItem,
+                           w.counts, w.offsets, w.cursors, w.item_offsets, w.pairs, false, st);
+  }
   if (e != hipSuccess) return e;
+  {
+  prof::Scope ps2("select_stage2", st);
   if (s.head_dim == 128)
     hipLaunchKernelGGL((stage2_kernel<128>), dim3(lay.max_items), dim3(kS2Threads), 0, st,
                        static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
@@ -584,7 +594,9 @@ hipError_t launch_select_two_stage(const LaunchShape& s, const void* q, const vo
                        w.item_offsets, w.offsets, w.pairs, w.scores, lay.n_buckets, s.heads_q,
                        s.heads_kv, s.seq_len, s.block, s.topk, s.group, m1, m2, m3,
                        s.scale * kLog2e);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  prof::Scope ps3("select_final", st);
   dim3 grid((s.seq_len + kS1Waves - 1) / kS1Waves, s.batch * s.heads_kv);
   hipLaunchKernelGGL(final_kernel, grid, dim3(kS1Waves * kWave), 0, st, w.s1_nodes, w.scores, idx,
                      score, s.seq_len, s.block, s.topk, s.causal ? 1 : 0, s.force ? 1 : 0, m1, m2);

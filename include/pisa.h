@@ -183,6 +183,21 @@ int pisa_decode_step(const pisa_problem* problem, const int32_t* cache_len, cons
                      int32_t* block_idx, float* block_score, void* out, float* row_lse,
                      void* ws, size_t ws_bytes, void* stream);
 
+/* Per-kernel timing (diagnostics).  While enabled, every kernel the library
+ * launches is bracketed by two HIP events recorded on its stream (the library
+ * creates and keeps these events; timing is off by default).  Host-only. */
+int pisa_profile_enable(int enable);
+
+/* Waits for the recorded events, aggregates elapsed time by kernel name in
+ * order of first launch, and forgets the records.
+ *   names:     out, '\n'-terminated kernel names (truncated to names_len)
+ *   total_ms:  out [max_kernels], summed milliseconds per kernel
+ *   counts:    out [max_kernels], launches per kernel
+ *   n_kernels: out, number of distinct kernels recorded (may exceed max)
+ * Returns PISA_ERR_HIP if an event could not be read. */
+int pisa_profile_report(char* names, size_t names_len, float* total_ms, int32_t* counts,
+                        int32_t max_kernels, int32_t* n_kernels);
+
 /* Static text for a status code. */
 const char* pisa_status_string(int status);
 

@@ -11,6 +11,7 @@ the roofline of the dominant kernel (HIP events on the launch stream) and the
 CPU oracle timed on a bounded sample of the same workload (cpu_baseline).
 
 Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--no-sweep] [--no-cpu]
+                       [--cpu-seconds 15] [--calibrate-copy-mb 0]
 """
 from __future__ import annotations
 
@@ -173,6 +174,17 @@ def run(args):
         if events:
             events[3].record(stream)
 
+    if args.calibrate_copy_mb:
+        # A plain elementwise pass of known size (reads and writes
+        # calibrate_copy_mb MiB each), launched once so that a counter run
+        # sees it beside the kernels it calibrates.
+        n_el = args.calibrate_copy_mb * (1 << 20) // 4
+        src = torch.ones(n_el, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -349,6 +361,9 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy-mb", type=int, default=0,
+                    help="launch one elementwise copy of this many MiB before the steps "
+                         "(HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "

@@ -11,14 +11,16 @@
 // level 1).  Each query then needs K (not 2K) key groups and the level-2
 // summary gathers disappear from stage 1.
 //
-//   stage 1   one wavefront per (b, kv head, t): levels L..3 of the descent,
-//             kept level-3 nodes -> s1_nodes[u][K]; counts pairs per node.
+//   stage 1   levels L..3 of the descent, kept level-3 nodes -> s1_nodes[u][K]:
+//             K <= 16: one lane per query (select_lpq.h); K <= 32: one
+//             wavefront per (b, kv head, t) (stage1_kernel below).
 //   scan      one workgroup: bucket offsets and the stage-2 work list.
 //   scatter   pair ids (u*K + slot) into per-node buckets.
 //   stage 2   one workgroup per (node, <= 256 pairs): the node's keys in LDS,
 //             bf16 MFMA 32x32x16 (keys x queries), per-leaf LSE and mean.
-//   final     one wavefront per (b, kv head, t): level-2 and leaf decisions
-//             from the stage-2 scores; ascending leaf list out.
+//   final     level-2 and leaf decisions from the stage-2 scores, ascending
+//             leaf list out: one lane per query (K <= 16) or one wavefront
+//             per query (final_kernel below).
 // Pair order inside a bucket depends on atomics, but every pair's scores are
 // computed by the same instruction sequence whatever its position, so the
 // outputs are bitwise reproducible.
@@ -28,7 +30,7 @@
 #include "pisa_common.h"
 #include "pisa_launch.h"
 #include "select_core.h"
-#include "stage1_tile.h"
+#include "select_lpq.h"
 
 namespace pisa {
 
@@ -520,22 +522,21 @@ hipError_t stage1_launch(const LaunchShape& s, const void* q, const float* pyr, 
 }
 
 template <int D, int G>
-hipError_t stage1_tile_launch(const LaunchShape& s, const void* q, const float* pyr, const Ws& w,
-                              hipStream_t st) {
-  constexpr int T = tile1::kCols / G;
-  dim3 grid((s.seq_len + T - 1) / T, s.batch * s.heads_kv);
+hipError_t stage1_lpq_launch(const LaunchShape& s, const void* q, const float* pyr, const Ws& w,
+                             hipStream_t st) {
+  constexpr int T = kWave / G;  // queries per wave
+  dim3 grid((s.seq_len + T * lpq::kWaves - 1) / (T * lpq::kWaves), s.batch * s.heads_kv);
   const size_t n = (size_t)s.batch * s.heads_kv * s.lv.rows * D;
   {
     prof::Scope ps("select_split_planes", st);
-    hipLaunchKernelGGL(tile1::split_planes_kernel, dim3(bucket::grid_for(n)), dim3(256), 0, st,
+    hipLaunchKernelGGL(lpq::split_planes_kernel, dim3(bucket::grid_for(n)), dim3(256), 0, st,
                        pyr, w.plane_hi, w.plane_lo, n);
   }
   prof::Scope ps("select_stage1", st);
-  hipLaunchKernelGGL((tile1::stage1_tile_kernel<D, G>), grid, dim3(tile1::kThreads), 0, st,
+  hipLaunchKernelGGL((lpq::stage1_kernel<D, G>), grid, dim3(lpq::kWaves * kWave), 0, st,
                      static_cast<const bf16_t*>(q), pyr, w.plane_hi, w.plane_lo, w.s1_nodes,
-                     s.heads_q, s.heads_kv,
-                     s.seq_len, s.block, s.topk, s.causal ? 1 : 0, s.force ? 1 : 0,
-                     s.scale * kLog2e, s.lv, kSplitLevel);
+                     s.heads_q, s.heads_kv, s.seq_len, s.block, s.topk, s.causal ? 1 : 0,
+                     s.force ? 1 : 0, s.scale * kLog2e, s.lv, kSplitLevel);
   return hipGetLastError();
 }
 
@@ -560,12 +561,12 @@ hipError_t launch_select_two_stage(const LaunchShape& s, const void* q, const vo
   hipError_t e;
   if (s.topk <= 16) {
     switch (s.group * 1000 + s.head_dim) {
-      case 1128: e = stage1_tile_launch<128, 1>(s, q, pyr, w, st); break;
-      case 1064: e = stage1_tile_launch<64, 1>(s, q, pyr, w, st); break;
-      case 2128: e = stage1_tile_launch<128, 2>(s, q, pyr, w, st); break;
-      case 2064: e = stage1_tile_launch<64, 2>(s, q, pyr, w, st); break;
-      case 4128: e = stage1_tile_launch<128, 4>(s, q, pyr, w, st); break;
-      default: e = stage1_tile_launch<64, 4>(s, q, pyr, w, st); break;
+      case 1128: e = stage1_lpq_launch<128, 1>(s, q, pyr, w, st); break;
+      case 1064: e = stage1_lpq_launch<64, 1>(s, q, pyr, w, st); break;
+      case 2128: e = stage1_lpq_launch<128, 2>(s, q, pyr, w, st); break;
+      case 2064: e = stage1_lpq_launch<64, 2>(s, q, pyr, w, st); break;
+      case 4128: e = stage1_lpq_launch<128, 4>(s, q, pyr, w, st); break;
+      default: e = stage1_lpq_launch<64, 4>(s, q, pyr, w, st); break;
     }
   } else {
     e = s.group == 1 ? (s.head_dim == 128 ? stage1_launch<bf16_t, 128, 1>(s, q, pyr, w, st)
@@ -597,9 +598,18 @@ hipError_t launch_select_two_stage(const LaunchShape& s, const void* q, const vo
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   prof::Scope ps3("select_final", st);
-  dim3 grid((s.seq_len + kS1Waves - 1) / kS1Waves, s.batch * s.heads_kv);
-  hipLaunchKernelGGL(final_kernel, grid, dim3(kS1Waves * kWave), 0, st, w.s1_nodes, w.scores, idx,
-                     score, s.seq_len, s.block, s.topk, s.causal ? 1 : 0, s.force ? 1 : 0, m1, m2);
+  if (s.topk <= lpq::kMaxK) {
+    const int per_group = lpq::kWaves * kWave;
+    dim3 grid((s.seq_len + per_group - 1) / per_group, s.batch * s.heads_kv);
+    hipLaunchKernelGGL((lpq::final_kernel<kScoreStride>), grid, dim3(per_group), 0, st,
+                       w.s1_nodes, w.scores, idx, score, s.seq_len, s.block, s.topk,
+                       s.causal ? 1 : 0, s.force ? 1 : 0, m1, m2);
+  } else {
+    dim3 grid((s.seq_len + kS1Waves - 1) / kS1Waves, s.batch * s.heads_kv);
+    hipLaunchKernelGGL(final_kernel, grid, dim3(kS1Waves * kWave), 0, st, w.s1_nodes, w.scores,
+                       idx, score, s.seq_len, s.block, s.topk, s.causal ? 1 : 0,
+                       s.force ? 1 : 0, m1, m2);
+  }
   return hipGetLastError();
 }
 

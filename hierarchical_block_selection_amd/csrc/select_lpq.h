@@ -13,6 +13,13 @@
 // selection (equal scores -> lower index first).  Scores are fp32 sums of
 // fp32 log-sum-exps, already uncertain at that level.
 //
+// Forced slots.  In causal mode the forced nodes of a level (current path,
+// and with forcing the first and previous leaf's ancestors) are always
+// candidates, because their parents were forced one level up.  The valid
+// candidates are the prefix of the ascending list with nodes <= lim, so the
+// current-path node lim is the last valid slot, the previous leaf's ancestor
+// is lim or lim - 1 (then the slot before), and node 0 is slot 0.
+//
 // Stage 1 (levels L..3).  One wavefront owns 64 (query, head) columns.  For a
 // level whose children fit in kDenseRows rows, the wave computes the logits
 // of every child row needed by any of its columns on the matrix cores
@@ -30,6 +37,8 @@
 // leaves, and writes the ascending leaf list.
 #pragma once
 
+#include <type_traits>
+
 #include "pisa_common.h"
 
 namespace pisa {
@@ -40,8 +49,8 @@ constexpr int kMaxK = 16;
 constexpr int kWaves = 4;        // independent wavefronts per workgroup
 constexpr int kDenseRows = 2048; // child rows scored densely
 constexpr int kMaskWords = kDenseRows / 4 / 32;  // parent bitmask words per query
-constexpr int kScoreRow = 36;    // floats per query of the slot array (16-byte rows)
-constexpr int kListRow = 20;     // ints per query of the kept-list staging (16 + trash)
+// Per-query LDS arrays are stored slot-major ([slot][query]) so that lanes of
+// different queries always touch different banks.
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
@@ -51,7 +60,7 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_ca
 // Order-preserving image of a float (larger float -> larger unsigned).
 __device__ __forceinline__ uint32_t ordered_bits(float s) {
   const uint32_t b = __float_as_uint(s);
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return b ^ (uint32_t(int32_t(b) >> 31) | 0x80000000u);
 }
 
 __device__ __forceinline__ uint32_t rank_key(float s, int slot) {
@@ -89,45 +98,49 @@ __device__ __forceinline__ void sort32_desc(uint32_t (&k)[32]) {
   }
 }
 
-// Forced-node test of §5.3 at a level with shift sh (current-path node always;
-// first and previous leaf's ancestors when forcing is on).
-struct Forced {
-  int lim, prev;  // prev < 0: no previous leaf
-  bool causal, force;
-  __device__ __forceinline__ bool operator()(int node) const {
-    return causal & ((node == lim) | (force & ((node == 0) | (node == prev))));
-  }
-};
+__device__ __forceinline__ uint32_t prefix_mask(int n) {
+  return n >= 32 ? 0xffffffffu : ((1u << n) - 1u);
+}
 
-// One decision over candidate slots 0..n_valid-1 (ascending nodes c(j)).
-// score_of(j) is read only when ranking is needed.  Returns the mask of kept
-// slots.
-template <typename NodeOf, typename ScoreOf>
-__device__ __forceinline__ uint32_t decide(int n_valid, int topk, const Forced& fz,
-                                           NodeOf node_of, ScoreOf score_of) {
-  const uint32_t vm = n_valid >= 32 ? 0xffffffffu : ((1u << n_valid) - 1u);
-  if (n_valid <= topk) return vm;
-  uint32_t fm = 0;
-#pragma unroll
-  for (int j = 0; j < kSlots; ++j) fm |= (fz(node_of(j)) ? (1u << j) : 0u);
-  fm &= vm;
+// Forced slots of a ranked level (n_valid > K >= 1 valid candidates).
+__device__ __forceinline__ uint32_t forced_slots(int n_valid, bool causal, bool force,
+                                                 bool prev_distinct) {
+  uint32_t m = 0;
+  if (causal) {
+    m = 1u << (n_valid - 1);
+    if (force) m |= 1u | (prev_distinct ? (1u << (n_valid - 2)) : 0u);
+  }
+  return m;
+}
+
+// Kept slots of a ranked level: the forced ones plus the best K - #F of the
+// other valid ones by score s[j].
+__device__ __forceinline__ uint32_t top_slots(int n_valid, int topk, uint32_t fm,
+                                              const float (&s)[kSlots]) {
+  const uint32_t rm = prefix_mask(n_valid) & ~fm;
   const int keep_n = topk - __popc(fm);
-  const uint32_t rm = vm & ~fm;
   uint32_t key[kSlots];
 #pragma unroll
-  for (int j = 0; j < kSlots; ++j) key[j] = ((rm >> j) & 1u) ? rank_key(score_of(j), j) : 0u;
+  for (int j = 0; j < kSlots; ++j) key[j] = ((rm >> j) & 1u) ? rank_key(s[j], j) : 0u;
   sort32_desc(key);
   uint32_t km = fm;
 #pragma unroll
-  for (int i = 0; i < kMaxK; ++i)
-    km |= (i < keep_n) ? (1u << (31 - (key[i] & 31u))) : 0u;
+  for (int i = 0; i < kMaxK; ++i) km |= (i < keep_n) ? (1u << (31 - (key[i] & 31u))) : 0u;
   return km;
 }
 
-// Kept slots -> ascending node list through LDS (row of kListRow ints; slot
-// kMaxK of the row takes the stores of slots that are not kept).
+// A query's column of a slot-major LDS array.
+template <typename E>
+struct Column {
+  E* p;
+  int stride;
+  __device__ __forceinline__ E& operator[](int i) const { return p[i * stride]; }
+};
+
+// Kept slots -> ascending node list through LDS (kMaxK + 1 entries; entry
+// kMaxK takes the stores of slots that are not kept).
 template <typename NodeOf>
-__device__ __forceinline__ void compact_kept(uint32_t km, int* row, NodeOf node_of) {
+__device__ __forceinline__ void compact_kept(uint32_t km, Column<int> row, NodeOf node_of) {
 #pragma unroll
   for (int j = 0; j < kSlots; ++j) {
     const bool k = (km >> j) & 1u;
@@ -162,9 +175,9 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void stage1_kernel(
     int split_level) {
   constexpr int T = kWave / G;  // queries per wave
   constexpr int KSTEPS = D / 16;
-  __shared__ __attribute__((aligned(16))) float score_s[kWaves][T][kScoreRow];
-  __shared__ __attribute__((aligned(16))) uint32_t mask_s[kWaves][T][kMaskWords];
-  __shared__ __attribute__((aligned(16))) int list_s[kWaves][T][kListRow];
+  __shared__ float score_s[kWaves][kSlots + 1][T];
+  __shared__ uint32_t mask_s[kWaves][kMaskWords][T];
+  __shared__ int list_s[kWaves][kMaxK + 1][T];
 
   const int wave = threadIdx.x / kWave;
   const int lane = lane_id();
@@ -176,19 +189,18 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void stage1_kernel(
   const size_t head_rows = (size_t)bh * lv.rows;
 
   // MFMA layout: this lane feeds columns col and 32 + col, k half kh.
+  // Columns past the sequence end repeat its last query (never used).
   const int col = lane & 31, kh = lane >> 5;
   bf16x8_t bq[2][KSTEPS];
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
     const int c = 32 * cb + col;
-    const int t = t0 + c / G;
-    const bool ok = t < n_tok;
+    const int tq = min(t0 + c / G, n_tok - 1);
     const bf16_t* qrow =
-        q + (((size_t)b * heads_q + (size_t)kvh * G + c % G) * n_tok + (ok ? t : 0)) * D;
+        q + (((size_t)b * heads_q + (size_t)kvh * G + c % G) * n_tok + tq) * D + 8 * kh;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s)
-      bq[cb][s] = as_bf16x8(ok ? *reinterpret_cast<const uint4*>(qrow + 16 * s + 8 * kh)
-                               : make_uint4(0, 0, 0, 0));
+      bq[cb][s] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 16 * s));
   }
 
   // Decision lane: query t0 + lane (lanes >= T idle in decisions).
@@ -201,27 +213,28 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void stage1_kernel(
   int nk = 1;
 #pragma unroll
   for (int i = 0; i < kMaxK; ++i) kp[i] = 0;
-  float* srow = &score_s[wave][lane < T ? lane : 0][0];
-  int* lrow = &list_s[wave][lane < T ? lane : 0][0];
-  uint32_t* mrow = &mask_s[wave][lane < T ? lane : 0][0];
+  const int ql = lane < T ? lane : 0;
+  const Column<float> srow{&score_s[wave][0][ql], T};
+  const Column<int> lrow{&list_s[wave][0][ql], T};
+  const Column<uint32_t> mrow{&mask_s[wave][0][ql], T};
 
   for (int l = lv.n; l >= split_level; --l) {
     const int sh = l - 1;
     const int size_l = lv.size[l - 1];
     const int lim = cz ? (cur >> sh) : size_l - 1;
     // Candidates: children of the kept nodes, ascending; the valid ones
-    // (existing, not in the future) form a prefix of the list.
+    // (existing, not in the future: node <= x_max) form a prefix.
+    const int x_max = min(size_l - 1, lim);
     int n_valid = 0;
 #pragma unroll
-    for (int j = 0; j < kSlots; ++j) {
-      const int c = 2 * kp[j >> 1] + (j & 1);
-      n_valid += (((j >> 1) < nk) & (c < size_l) & (c <= lim)) ? 1 : 0;
+    for (int i = 0; i < kMaxK; ++i) {
+      const int c = 2 * kp[i];
+      n_valid += (i < nk) ? int(c <= x_max) + int(c + 1 <= x_max) : 0;
     }
     if (!dlane) n_valid = 0;
     const bool need = n_valid > topk;
-    const bool any_need = __ballot(need) != 0;
 
-    if (any_need) {
+    if (__ballot(need) != 0) {
       const int m_child = lv.size[l - 2];
       const size_t child0 = head_rows + lv.off[l - 2];
       if (m_child <= kDenseRows) {
@@ -229,58 +242,76 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void stage1_kernel(
         const int lim_last = cz ? (cur_last >> sh) : size_l - 1;
         const int rows_needed = min(m_child, 2 * lim_last + 2);
         int base[2] = {0, 0};
-        const uint32_t* mcol[2] = {&mask_s[wave][(32 * 0 + col) / G][0],
-                                   &mask_s[wave][(32 * 1 + col) / G][0]};
-        float* scol[2] = {&score_s[wave][(32 * 0 + col) / G][0],
-                          &score_s[wave][(32 * 1 + col) / G][0]};
+        const Column<uint32_t> mcol[2] = {{&mask_s[wave][0][(32 * 0 + col) / G], T},
+                                          {&mask_s[wave][0][(32 * 1 + col) / G], T}};
+        const Column<float> scol[2] = {{&score_s[wave][0][(32 * 0 + col) / G], T},
+                                       {&score_s[wave][0][(32 * 1 + col) / G], T}};
         const bool writer = (col % G) == 0;
         for (int r0 = 0; r0 < rows_needed; r0 += 32) {
-          const int r = r0 + col;
-          const bool ok = r < m_child;
-          const bf16_t* hrow = phi + (child0 + (ok ? r : 0)) * D + 8 * kh;
-          const bf16_t* lrow2 = plo + (child0 + (ok ? r : 0)) * D + 8 * kh;
+          // Rows of this chunk: r0 + 8g + 4kh + i%4 (acc element 4g + i%4);
+          // level-l candidates n = r0/2 + 4g + 2kh + m own rows 2n, 2n+1;
+          // their parents p = r0/4 + 2g + kh (bits p0..p0+7 of the masks).
+          const int p0 = r0 >> 2;  // multiple of 8
+          uint32_t byte[2];
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb) byte[cb] = (mcol[cb][p0 >> 5] >> (p0 & 31)) & 0xffu;
+          if (__ballot((byte[0] | byte[1]) != 0u) == 0) continue;  // no query keeps these parents
+          // Rows past the level end repeat its last row (their logits are
+          // never used: see the ragged-chunk masking below).
+          const int r = min(r0 + col, m_child - 1);
+          const bf16_t* hrow = phi + (child0 + r) * D + 8 * kh;
+          const bf16_t* lrow2 = plo + (child0 + r) * D + 8 * kh;
+          uint4 hv[KSTEPS], lv4[KSTEPS];
+#pragma unroll
+          for (int s = 0; s < KSTEPS; ++s) {
+            hv[s] = *reinterpret_cast<const uint4*>(hrow + 16 * s);
+            lv4[s] = *reinterpret_cast<const uint4*>(lrow2 + 16 * s);
+          }
           f32x16_t acc[2] = {};
 #pragma unroll
           for (int s = 0; s < KSTEPS; ++s) {
-            const uint4 hv = ok ? *reinterpret_cast<const uint4*>(hrow + 16 * s) : make_uint4(0, 0, 0, 0);
-            const uint4 lv4 = ok ? *reinterpret_cast<const uint4*>(lrow2 + 16 * s) : make_uint4(0, 0, 0, 0);
-            const bf16x8_t ah = as_bf16x8(hv), al = as_bf16x8(lv4);
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb) {
-              acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bq[cb][s], acc[cb], 0, 0, 0);
-              acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bq[cb][s], acc[cb], 0, 0, 0);
+              acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lv4[s]), bq[cb][s],
+                                                                acc[cb], 0, 0, 0);
+              acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(hv[s]), bq[cb][s],
+                                                                acc[cb], 0, 0, 0);
             }
           }
-          // Rows of this chunk: r0 + 8g + 4kh + i%4 (acc element 4g + i%4);
-          // level-l candidates n = r0/2 + 4g + 2kh + m own rows 2n, 2n+1;
-          // their parents p = r0/4 + 2g + kh.
-          const int p0 = r0 >> 2;  // multiple of 8
+          auto pickup = [&](auto full_tag) {
+            constexpr bool kFull = decltype(full_tag)::value;  // every row of the chunk exists
 #pragma unroll
-          for (int cb = 0; cb < 2; ++cb) {
-            const uint32_t byte = (mcol[cb][p0 >> 5] >> (p0 & 31)) & 0xffu;
+            for (int cb = 0; cb < 2; ++cb) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const int pb = 2 * g + kh;
-              const bool has = (byte >> pb) & 1u;
-              const int pslot = base[cb] + __popc(byte & ((1u << pb) - 1u));
+              for (int g = 0; g < 4; ++g) {
+                const int pb = 2 * g + kh;
+                const bool has = writer & ((byte[cb] >> pb) & 1u);
+                const int pslot = base[cb] + __popc(byte[cb] & ((1u << pb) - 1u));
 #pragma unroll
-              for (int m = 0; m < 2; ++m) {
-                const int n = (r0 >> 1) + 4 * g + 2 * kh + m;
-                const float z0 = acc[cb][4 * g + 2 * m] * scale_log2;
-                const float z1 = acc[cb][4 * g + 2 * m + 1] * scale_log2;
-                const bool has1 = 2 * n + 1 < m_child;
-                const float mx = has1 ? fmaxf(z0, z1) : z0;
-                const float mn = has1 ? fminf(z0, z1) : neg_inf();
-                float v = mx + fast_log2(1.f + fast_exp2(mn - mx));
-                if (G >= 2) v += __shfl_xor(v, 1, kWave);
-                if (G >= 4) v += __shfl_xor(v, 2, kWave);
-                const int slot = 2 * pslot + m;
-                const bool w = writer & has & (2 * n < m_child) & (slot < kSlots);
-                scol[cb][w ? slot : kSlots] = v;
+                for (int m = 0; m < 2; ++m) {
+                  const int n = (r0 >> 1) + 4 * g + 2 * kh + m;
+                  const float z0 = acc[cb][4 * g + 2 * m];
+                  float z1 = acc[cb][4 * g + 2 * m + 1];
+                  bool w = has;
+                  if (!kFull) {
+                    z1 = 2 * n + 1 < m_child ? z1 : neg_inf();
+                    w &= 2 * n < m_child;
+                  }
+                  const float mx = fmaxf(z0, z1), mn = fminf(z0, z1);
+                  float v =
+                      fmaf(mx, scale_log2, fast_log2(1.f + fast_exp2((mn - mx) * scale_log2)));
+                  if (G >= 2) v += __shfl_xor(v, 1, kWave);
+                  if (G >= 4) v += __shfl_xor(v, 2, kWave);
+                  scol[cb][w ? 2 * pslot + m : kSlots] = v;
+                }
               }
+              base[cb] += __popc(byte[cb]);
             }
-            base[cb] += __popc(byte);
-          }
+          };
+          if (r0 + 32 <= m_child)
+            pickup(std::true_type{});
+          else
+            pickup(std::false_type{});
         }
       } else {
         // Gather: one query at a time; lane L scores child row L of the
@@ -290,7 +321,7 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void stage1_kernel(
           const int j = lane >> 1;
           const int nkq = __builtin_amdgcn_readlane(nk, qi);
           const int nvq = __builtin_amdgcn_readlane(n_valid, qi);
-          const int par = list_s[wave][qi][j >> 1];
+          const int par = list_s[wave][j >> 1][qi];
           const int cnode = 2 * par + (j & 1);
           const int row = 2 * cnode + (lane & 1);
           const bool live = ((j >> 1) < nkq) & (j < nvq) & (row < m_child);
@@ -315,44 +346,53 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void stage1_kernel(
             const float mx = fmaxf(z, zo), mn = fminf(z, zo);
             tot += mx + fast_log2(1.f + fast_exp2(mn - mx));
           }
-          if ((lane & 1) == 0) score_s[wave][qi][live ? j : kSlots] = tot;
+          if ((lane & 1) == 0) score_s[wave][live ? j : kSlots][qi] = tot;
         }
       }
       wave_lds_sync();
     }
 
     // Decision for this lane's query.
-    const Forced fz{lim, (cz && fzon && cur >= 1) ? ((cur - 1) >> sh) : -1, cz, fzon};
-    auto node_of = [&](int j) { return 2 * kp[j >> 1] + (j & 1); };
-    auto score_of = [&](int j) { return srow[j]; };
-    const uint32_t km = dlane ? decide(n_valid, topk, fz, node_of, score_of) : 0u;
-    compact_kept(km, lrow, node_of);
+    uint32_t km = prefix_mask(n_valid);
+    if (need) {
+      float sc[kSlots];
+#pragma unroll
+      for (int j = 0; j < kSlots; ++j) sc[j] = srow[j];
+      const bool prev_distinct = cur >= 1 && ((cur - 1) >> sh) != lim;
+      km = top_slots(n_valid, topk, forced_slots(n_valid, cz, fzon, prev_distinct), sc);
+    }
+    compact_kept(km, lrow, [&](int j) { return 2 * kp[j >> 1] + (j & 1); });
     wave_lds_sync();
     nk = __popc(km);
 #pragma unroll
-    for (int i = 0; i < kMaxK; i += 4) {
-      const int4 v = *reinterpret_cast<const int4*>(lrow + i);
-      kp[i] = v.x; kp[i + 1] = v.y; kp[i + 2] = v.z; kp[i + 3] = v.w;
-    }
+    for (int i = 0; i < kMaxK; ++i) kp[i] = lrow[i];
     if (l == split_level) break;
     // Parent bitmask for the next level's dense pass (kept nodes of level l).
     const int nl = l - 1;
     if (lv.size[nl - 1] > topk && lv.size[nl - 2] <= kDenseRows) {
 #pragma unroll
-      for (int w = 0; w < kMaskWords; w += 4)
-        *reinterpret_cast<uint4*>(mrow + w) = make_uint4(0, 0, 0, 0);
+      for (int w = 0; w < kMaskWords; ++w) mrow[w] = 0u;
       wave_lds_sync();
 #pragma unroll
       for (int i = 0; i < kMaxK; ++i)
-        if (dlane & (i < nk)) atomicOr(mrow + (kp[i] >> 5), 1u << (kp[i] & 31));
+        if (dlane & (i < nk)) atomicOr(&mrow[kp[i] >> 5], 1u << (kp[i] & 31));
     }
     wave_lds_sync();
   }
   if (dlane) {
     int* out = s1_nodes + ((size_t)bh * n_tok + t) * topk;
+    if ((topk & 3) == 0) {
 #pragma unroll
-    for (int i = 0; i < kMaxK; ++i)
-      if (i < topk) out[i] = i < nk ? kp[i] : -1;
+      for (int i = 0; i < kMaxK; i += 4)
+        if (i < topk)
+          *reinterpret_cast<int4*>(out + i) =
+              make_int4(i < nk ? kp[i] : -1, i + 1 < nk ? kp[i + 1] : -1,
+                        i + 2 < nk ? kp[i + 2] : -1, i + 3 < nk ? kp[i + 3] : -1);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kMaxK; ++i)
+        if (i < topk) out[i] = i < nk ? kp[i] : -1;
+    }
   }
 }
 
@@ -360,99 +400,139 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void stage1_kernel(
 // Final decisions at levels 2 and 1
 // ---------------------------------------------------------------------------
 
-// scores[(u*K + slot)*stride + j]: j = 0..3 exact LSE of leaf 4n + j, j = 4, 5
+// scores[(u*K + slot)*STRIDE + j]: j = 0..3 exact LSE of leaf 4n + j, j = 4, 5
 // level-2 score of child 2n + (j - 4), for the slot's level-3 node n (nats).
 template <int STRIDE>
 __global__ __launch_bounds__(kWaves * kWave) void final_kernel(
     const int* __restrict__ s1_nodes, const float* __restrict__ scores, int32_t* __restrict__ idx,
     float* __restrict__ score_out, int n_tok, int block, int topk, int causal, int force, int m1,
-    int m2) {
-  __shared__ __attribute__((aligned(16))) int list_s[kWaves][kWave][kListRow];
-  __shared__ __attribute__((aligned(16))) float out_s[kWaves][kWave][kListRow];
+    int m2, int vec_out) {
+  __shared__ int list_s[kWaves][kMaxK + 1][kWave];
+  __shared__ float out_s[kWaves][kMaxK + 1][kWave];
   const int wave = threadIdx.x / kWave;
   const int lane = lane_id();
   const int t = (blockIdx.x * kWaves + wave) * kWave + lane;
   const bool live = t < n_tok;
   const int bh = blockIdx.y;
-  const size_t u = (size_t)bh * n_tok + (live ? t : 0);
+  const size_t u = (size_t)bh * n_tok + (live ? t : n_tok - 1);
   const bool cz = causal != 0, fzon = force != 0;
   const int cur = live ? t / block : 0;
-  int* lrow = &list_s[wave][lane][0];
-  float* frow = &out_s[wave][lane][0];
+  const Column<int> lrow{&list_s[wave][0][lane], kWave};
+  const Column<float> frow{&out_s[wave][0][lane], kWave};
   const float* sc = scores + u * topk * STRIDE;
 
   int n3[kMaxK];
+  const int* s1 = s1_nodes + u * topk;
+  if ((topk & 3) == 0) {  // 16-byte rows
+#pragma unroll
+    for (int i = 0; i < kMaxK; i += 4) {
+      const int4 v = i < topk ? *reinterpret_cast<const int4*>(s1 + i) : make_int4(-1, -1, -1, -1);
+      n3[i] = v.x; n3[i + 1] = v.y; n3[i + 2] = v.z; n3[i + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kMaxK; ++i) n3[i] = i < topk ? s1[i] : -1;
+  }
   int nk3 = 0;
 #pragma unroll
-  for (int i = 0; i < kMaxK; ++i) {
-    n3[i] = (i < topk && live) ? s1_nodes[u * topk + i] : -1;
-    nk3 += n3[i] >= 0 ? 1 : 0;
-  }
-  // Level 2: candidate j = child (j & 1) of level-3 node n3[j >> 1]; its score
-  // sits in the slot j >> 1 of the stage-2 output.
+  for (int i = 0; i < kMaxK; ++i) nk3 += n3[i] >= 0 ? 1 : 0;
+  // Level-2 scores of both children of every slot (slot indices are clamped
+  // so that unused entries never read past this query's K slots).
+  float2 l2[kMaxK];
+#pragma unroll
+  for (int i = 0; i < kMaxK; ++i)
+    l2[i] = *reinterpret_cast<const float2*>(sc + min(i, topk - 1) * STRIDE + 4);
+
+  // Level 2: candidate j = child (j & 1) of level-3 node n3[j >> 1].
   int lim = cz ? (cur >> 1) : m2 - 1;
+  int x_max = min(m2 - 1, lim);
   int nv = 0;
 #pragma unroll
-  for (int j = 0; j < kSlots; ++j) {
-    const int c = 2 * n3[j >> 1] + (j & 1);
-    nv += (((j >> 1) < nk3) & (c < m2) & (c <= lim)) ? 1 : 0;
+  for (int i = 0; i < kMaxK; ++i) {
+    const int c = 2 * n3[i];
+    nv += (i < nk3) ? int(c <= x_max) + int(c + 1 <= x_max) : 0;
   }
   if (!live) nv = 0;
-  Forced fz{lim, (cz && fzon && cur >= 1) ? ((cur - 1) >> 1) : -1, cz, fzon};
-  auto node2 = [&](int j) { return 2 * n3[j >> 1] + (j & 1); };
-  // (slot indices are clamped so that unused list entries never read past
-  // this query's K slots)
-  auto score2 = [&](int j) { return sc[min(j >> 1, topk - 1) * STRIDE + 4 + (j & 1)]; };
-  const uint32_t km2 = decide(nv, topk, fz, node2, score2);
+  uint32_t km2 = prefix_mask(nv);
+  if (nv > topk) {
+    float s2[kSlots];
+#pragma unroll
+    for (int j = 0; j < kSlots; ++j) s2[j] = (j & 1) ? l2[j >> 1].y : l2[j >> 1].x;
+    const bool prev_distinct = cur >= 1 && ((cur - 1) >> 1) != lim;
+    km2 = top_slots(nv, topk, forced_slots(nv, cz, fzon, prev_distinct), s2);
+  }
   // Kept level-2 candidates, ascending, as (node << 5) | j.
-  compact_kept(km2, lrow, [&](int j) { return (node2(j) << 5) | j; });
+  compact_kept(km2, lrow, [&](int j) { return ((2 * n3[j >> 1] + (j & 1)) << 5) | j; });
   wave_lds_sync();
   const int nk2 = __popc(km2);
   int k2[kMaxK];
 #pragma unroll
-  for (int i = 0; i < kMaxK; i += 4) {
-    const int4 v = *reinterpret_cast<const int4*>(lrow + i);
-    k2[i] = v.x; k2[i + 1] = v.y; k2[i + 2] = v.z; k2[i + 3] = v.w;
-  }
+  for (int i = 0; i < kMaxK; ++i) k2[i] = lrow[i];
   wave_lds_sync();
-  // Level 1: candidate j = leaf (j & 1) of the kept level-2 node k2[j >> 1];
-  // its exact LSE sits in slot (j2 >> 1), entry 2 * (j2 & 1) + (j & 1).
+  // Level 1: candidate j = leaf (j & 1) of the kept level-2 node k2[j >> 1]
+  // (node k2 >> 5); its exact LSE sits in the stage-2 slot (j2 >> 1), entry
+  // 2 * (j2 & 1) + (j & 1), where j2 = k2 & 31.
+  float2 l1[kMaxK];
+#pragma unroll
+  for (int i = 0; i < kMaxK; ++i) {
+    const int j2 = k2[i] & 31;
+    l1[i] = *reinterpret_cast<const float2*>(sc + min(j2 >> 1, topk - 1) * STRIDE + 2 * (j2 & 1));
+  }
   lim = cz ? cur : m1 - 1;
-  auto node1 = [&](int j) { return 2 * (k2[j >> 1] >> 5) + (j & 1); };
-  auto score1 = [&](int j) {
-    const int j2 = k2[j >> 1] & 31;
-    return sc[min(j2 >> 1, topk - 1) * STRIDE + 2 * (j2 & 1) + (j & 1)];
-  };
+  x_max = min(m1 - 1, lim);
   nv = 0;
 #pragma unroll
-  for (int j = 0; j < kSlots; ++j) {
-    const int c = node1(j);
-    nv += (((j >> 1) < nk2) & (c < m1) & (c <= lim)) ? 1 : 0;
+  for (int i = 0; i < kMaxK; ++i) {
+    const int c = 2 * (k2[i] >> 5);
+    nv += (i < nk2) ? int(c <= x_max) + int(c + 1 <= x_max) : 0;
   }
   if (!live) nv = 0;
-  fz = Forced{lim, (cz && fzon && cur >= 1) ? (cur - 1) : -1, cz, fzon};
   const bool ranked = nv > topk;
-  const uint32_t km1 = decide(nv, topk, fz, node1, score1);
+  uint32_t km1 = prefix_mask(nv), fm1 = 0;
+  float s1v[kSlots];
+#pragma unroll
+  for (int j = 0; j < kSlots; ++j) s1v[j] = (j & 1) ? l1[j >> 1].y : l1[j >> 1].x;
+  if (ranked) {
+    fm1 = forced_slots(nv, cz, fzon, cur >= 1);
+    km1 = top_slots(nv, topk, fm1, s1v);
+  }
   const bool want_score = score_out != nullptr;
 #pragma unroll
   for (int j = 0; j < kSlots; ++j) {
     const bool k = (km1 >> j) & 1u;
     const int pos = k ? min(__popc(km1 & ((1u << j) - 1u)), kMaxK) : kMaxK;
-    const int node = node1(j);
-    lrow[pos] = node;
-    if (want_score) frow[pos] = (ranked & !fz(node)) ? score1(j) : pos_inf();
+    lrow[pos] = 2 * (k2[j >> 1] >> 5) + (j & 1);
+    if (want_score) frow[pos] = (ranked & !((fm1 >> j) & 1u)) ? s1v[j] : pos_inf();
   }
   wave_lds_sync();
   if (!live) return;
   const int nk1 = __popc(km1);
   int32_t* orow = idx + u * topk;
   float* srow = want_score ? score_out + u * topk : nullptr;
+  int o[kMaxK];
+  float f[kMaxK];
 #pragma unroll
   for (int i = 0; i < kMaxK; ++i) {
-    if (i < topk) {
-      const bool kept = i < nk1;
-      orow[i] = kept ? lrow[i] : -1;
-      if (want_score) srow[i] = kept ? frow[i] : neg_inf();
+    const bool kept = i < nk1;
+    o[i] = kept ? lrow[i] : -1;
+    f[i] = kept ? frow[i] : neg_inf();
+  }
+  if (vec_out) {  // K % 4 == 0 and 16-byte aligned outputs
+#pragma unroll
+    for (int i = 0; i < kMaxK; i += 4) {
+      if (i < topk) {
+        *reinterpret_cast<int4*>(orow + i) = make_int4(o[i], o[i + 1], o[i + 2], o[i + 3]);
+        if (want_score)
+          *reinterpret_cast<float4*>(srow + i) = make_float4(f[i], f[i + 1], f[i + 2], f[i + 3]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kMaxK; ++i) {
+      if (i < topk) {
+        orow[i] = o[i];
+        if (want_score) srow[i] = f[i];
+      }
     }
   }
 }

@@ -601,9 +601,11 @@ hipError_t launch_select_two_stage(const LaunchShape& s, const void* q, const vo
   if (s.topk <= lpq::kMaxK) {
     const int per_group = lpq::kWaves * kWave;
     dim3 grid((s.seq_len + per_group - 1) / per_group, s.batch * s.heads_kv);
+    const bool vec_out = (s.topk % 4) == 0 && (reinterpret_cast<uintptr_t>(idx) % 16) == 0 &&
+                         (reinterpret_cast<uintptr_t>(score) % 16) == 0;
     hipLaunchKernelGGL((lpq::final_kernel<kScoreStride>), grid, dim3(per_group), 0, st,
                        w.s1_nodes, w.scores, idx, score, s.seq_len, s.block, s.topk,
-                       s.causal ? 1 : 0, s.force ? 1 : 0, m1, m2);
+                       s.causal ? 1 : 0, s.force ? 1 : 0, m1, m2, vec_out ? 1 : 0);
   } else {
     dim3 grid((s.seq_len + kS1Waves - 1) / kS1Waves, s.batch * s.heads_kv);
     hipLaunchKernelGGL(final_kernel, grid, dim3(kS1Waves * kWave), 0, st, w.s1_nodes, w.scores,

@@ -80,8 +80,10 @@ struct AttnWs {
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 bool block_path(const LaunchShape& s) {
+  // (query, slot) pair ids are int32
+  const int64_t slots = (int64_t)s.batch * s.heads_kv * s.seq_len * s.topk;
   return s.bf16 && s.block == kAttnBlock && (s.head_dim == 64 || s.head_dim == 128) &&
-         (s.group & (s.group - 1)) == 0 && s.group <= kMaxGroup;
+         (s.group & (s.group - 1)) == 0 && s.group <= kMaxGroup && slots < INT32_MAX;
 }
 
 AttnWs attn_layout(const LaunchShape& s) {

@@ -39,7 +39,7 @@ namespace {
 constexpr int kSplitLevel = 3;   // stage 1 decides levels L..3
 constexpr int kS1Waves = 4;
 constexpr int kS2Threads = 256;
-constexpr int kS2PairsPerItem = 256;
+constexpr int kS2Rows = 256;    // (pair, head) rows per stage-2 item
 constexpr int kS2Cols = 32;      // MFMA 32x32x16: 32 (query, head) columns
 constexpr int kScoreStride = 8;  // floats per pair: 4 leaf LSE, 2 level-2, 2 pad
 
@@ -71,7 +71,7 @@ WsLayout ws_layout(const LaunchShape& s) {
   const size_t units = (size_t)s.batch * s.heads_kv * s.seq_len;
   const int m3 = s.lv.n >= kSplitLevel ? s.lv.size[kSplitLevel - 1] : 1;
   w.n_buckets = s.batch * s.heads_kv * m3;
-  w.max_items = bucket::max_items(units * s.topk, w.n_buckets, kS2PairsPerItem);
+  w.max_items = bucket::max_items(units * s.topk, w.n_buckets, kS2Rows / s.group);
   size_t off = 0;
   w.counts = off; off = align256(off + sizeof(int) * w.n_buckets);
   w.offsets = off; off = align256(off + sizeof(int) * (w.n_buckets + 1));
@@ -273,147 +273,151 @@ __global__ __launch_bounds__(kS1Waves * kWave) void stage1_kernel(
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-// One workgroup per work item (level-3 node n of KV head bh, up to 256 pairs).
-template <int D>
-__global__ __launch_bounds__(kS2Threads) void stage2_kernel(
+// One workgroup per work item: level-3 node n of KV head bh and up to
+// kS2Rows / G of its (query, slot) pairs; wavefront w owns leaf 4n + w.
+//
+//   1. The item's pair ids, then the query rows of every (pair, head), are
+//      staged in LDS (all loads issued together).
+//   2. Each wave holds its leaf's 64 raw keys as MFMA A operands in registers
+//      and walks the staged rows 32 columns at a time: S = K_leaf . Q^T on bf16
+//      MFMA 32x32x16 (a lane holds 32 keys of one column), then the exact leaf
+//      LSE (eq. (7) at level 1: max, sum of exp2) and the mean logit, which
+//      equals q . kbar_leaf (eq. (4) is a mean), go to LDS per column.
+//   3. After one barrier every thread finishes one pair: the four leaf LSEs
+//      and the two level-2 scores LSE(mean_2c, mean_2c+1), each summed over
+//      the group's heads (eq. (11)), in nats.
+template <int D, int G>
+__global__ __launch_bounds__(kS2Threads, 2) void stage2_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const int* __restrict__ item_offsets, const int* __restrict__ offsets,
     const int* __restrict__ pairs, float* __restrict__ scores, int n_buckets, int heads_q,
-    int heads_kv, int n_tok, int block, int topk, int group, int m1, int m2, int m3,
-    float scale_log2) {
+    int heads_kv, int n_tok, int topk, int m3, float scale_log2) {
   constexpr int KSTEPS = D / 16;
-  constexpr int ROW = D + 8;  // padded LDS row (bf16 elements) against bank conflicts
-  constexpr int NODE_KEYS = 256;
-  __shared__ __attribute__((aligned(16))) bf16_t ks[NODE_KEYS * ROW];
+  constexpr int PAIRS = kS2Rows / G;  // pairs per item
+  constexpr int QROW = D + 8;         // padded LDS row (bf16): 16-byte reads spread over banks
+  constexpr int LEAF = 64;            // keys per leaf (C = 64)
+  __shared__ __attribute__((aligned(16))) bf16_t qs[kS2Rows * QROW];
+  __shared__ float xs[4][2][kS2Rows];  // [leaf][lse, mean][row], log2 units
+  __shared__ int pid_s[PAIRS];
   int bucket, start, len;
-  if (!bucket::locate_item(item_offsets, offsets, n_buckets, blockIdx.x, kS2PairsPerItem, &bucket,
-                           &start, &len))
+  if (!bucket::locate_item(item_offsets, offsets, n_buckets, blockIdx.x, PAIRS, &bucket, &start,
+                           &len))
     return;
   const int bh = bucket / m3, node = bucket % m3;
   const int b = bh / heads_kv, kvh = bh % heads_kv;
-  const int tok0 = node * 4 * block;
-  const int n_keys = min(4 * block, n_tok - tok0);
-  // Keys of the node -> LDS (rows past the sequence end are zero-filled).
-  const bf16_t* kb = k + ((size_t)bh * n_tok + tok0) * D;
-  constexpr int V16 = D / 8;  // 16-byte chunks per row
-  for (int x = threadIdx.x; x < NODE_KEYS * V16; x += kS2Threads) {
-    const int r = x / V16, c = (x % V16) * 8;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (r < n_keys) v = *reinterpret_cast<const uint4*>(kb + (size_t)r * D + c);
-    *reinterpret_cast<uint4*>(&ks[r * ROW + c]) = v;
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid / kWave;
+  const int col = lane & 31, kh = lane >> 5;
+
+  // 1. Pair ids, then query rows (row r = pair r / G, head r % G).
+  if (tid < PAIRS) pid_s[tid] = pairs[start + min(tid, len - 1)];
+  const int leaf_tok0 = (4 * node + wave) * LEAF;
+  const int n_keys = max(0, min(LEAF, n_tok - leaf_tok0));  // keys of this wave's leaf
+  // A operands: key rows leaf_tok0 + 32 rb + col (rows past the sequence end
+  // repeat its last key; they are masked below).
+  const bf16_t* kb = k + (size_t)bh * n_tok * D;
+  bf16x8_t ka[2][KSTEPS];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int row = min(leaf_tok0 + 32 * rb + col, n_tok - 1);
+    const bf16_t* kr = kb + (size_t)row * D + 8 * kh;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) ka[rb][s] = as_bf16x8(*reinterpret_cast<const uint4*>(kr + 16 * s));
+  }
+  __syncthreads();
+  const int n_rows = len * G;
+  constexpr int V16 = D / 8;  // 16-byte pieces per row
+  constexpr int PER_THREAD = kS2Rows * V16 / kS2Threads;
+  uint4 stage[PER_THREAD];
+#pragma unroll
+  for (int i = 0; i < PER_THREAD; ++i) {
+    const int x = tid + i * kS2Threads;
+    const int r = min(x / V16, n_rows - 1), c = x % V16;
+    // pair id = (bh * n_tok + t) * topk + slot
+    const int t = int(uint32_t(pid_s[r / G]) / uint32_t(topk)) - bh * n_tok;
+    stage[i] = *reinterpret_cast<const uint4*>(
+        q + (((size_t)b * heads_q + (size_t)kvh * G + r % G) * n_tok + t) * D + 8 * c);
+  }
+#pragma unroll
+  for (int i = 0; i < PER_THREAD; ++i) {
+    const int x = tid + i * kS2Threads;
+    *reinterpret_cast<uint4*>(&qs[(x / V16) * QROW + 8 * (x % V16)]) = stage[i];
   }
   __syncthreads();
 
-  const int lane = lane_id();
-  const int wave = threadIdx.x / kWave;
-  const int col = lane & 31;        // query column of this lane
-  const int khalf = lane >> 5;      // which 8-element half of a 16-wide k step
-  const int per_chunk = kS2Cols / group;  // pairs per 32-column chunk
-  const int n_chunks = (len + per_chunk - 1) / per_chunk;
-  const int n_leaves = min(4, m1 - 4 * node);
-  const bool full = n_keys == 4 * block;  // every key of the node exists: no masking
-  const int h = col % group;
-  // Query rows of a chunk -> MFMA B operands (zero for columns past the list).
-  auto load_chunk = [&](int ch, bf16x8_t (&bq)[KSTEPS], int& pair_id) {
-    const int p = ch * per_chunk + col / group;
-    pair_id = -1;
-    if (ch < n_chunks && p < len) {
-      pair_id = pairs[start + p];
-      const int t = (int)(((size_t)pair_id / topk) % n_tok);
-      const bf16_t* qrow = q + (((size_t)b * heads_q + (size_t)kvh * group + h) * n_tok + t) * D;
+  // 2. Leaf LSE and mean logit per staged row.
+  const float inv_keys = n_keys > 0 ? 1.f / float(n_keys) : 0.f;
+  const int n_chunks = (n_rows + 31) / 32;
+  for (int ch = 0; ch < n_chunks; ++ch) {
+    const bf16_t* qr = &qs[(32 * ch + col) * QROW + 8 * kh];
+    f32x16_t acc0 = {}, acc1 = {};
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s)
-        bq[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 16 * s + 8 * khalf));
+    for (int s = 0; s < KSTEPS; ++s) {
+      const bf16x8_t bq = as_bf16x8(*reinterpret_cast<const uint4*>(qr + 16 * s));
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0][s], bq, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[1][s], bq, acc1, 0, 0, 0);
+    }
+    // Lane holds the logits of keys (i/4)*8 + 4kh + i%4 (acc0) and 32 + that (acc1).
+    float m, sraw = 0.f, se = 0.f;
+    if (n_keys == LEAF) {
+      m = fmaxf(fmaxf(acc0[0], acc0[1]), fmaxf(acc1[0], acc1[1]));
+#pragma unroll
+      for (int i = 2; i < 16; i += 2)
+        m = fmaxf(m, fmaxf(fmaxf(acc0[i], acc0[i + 1]), fmaxf(acc1[i], acc1[i + 1])));
+      m = fmaxf(m, __shfl_xor(m, 32, kWave));
+      const float ms = m * scale_log2;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        sraw += acc0[i] + acc1[i];
+        se += fast_exp2(fmaf(acc0[i], scale_log2, -ms)) + fast_exp2(fmaf(acc1[i], scale_log2, -ms));
+      }
     } else {
+      m = neg_inf();
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) bq[s] = as_bf16x8(make_uint4(0, 0, 0, 0));
-    }
-  };
-  bf16x8_t bq[KSTEPS];
-  int pair_id;
-  load_chunk(wave, bq, pair_id);
-  for (int ch = wave; ch < n_chunks; ch += kS2Threads / kWave) {
-    bf16x8_t bn[KSTEPS];
-    int pair_next;
-    load_chunk(ch + kS2Threads / kWave, bn, pair_next);  // prefetch the next chunk
-    float leaf_lse[4], leaf_mean[4];
-#pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      leaf_lse[f] = neg_inf();
-      leaf_mean[f] = neg_inf();
-      if (f >= n_leaves) continue;
-      f32x16_t acc0 = {}, acc1 = {};
-      const int kr0 = f * block;  // first key row of leaf f in LDS
-#pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) {
-        const bf16x8_t a0 = as_bf16x8(
-            *reinterpret_cast<const uint4*>(&ks[(kr0 + col) * ROW + 16 * s + 8 * khalf]));
-        const bf16x8_t a1 = as_bf16x8(
-            *reinterpret_cast<const uint4*>(&ks[(kr0 + 32 + col) * ROW + 16 * s + 8 * khalf]));
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bq[s], acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bq[s], acc1, 0, 0, 0);
+      for (int i = 0; i < 16; ++i) {
+        const int r = (i / 4) * 8 + 4 * kh + (i % 4);
+        acc0[i] = r < n_keys ? acc0[i] : neg_inf();
+        acc1[i] = r + 32 < n_keys ? acc1[i] : neg_inf();
+        m = fmaxf(m, fmaxf(acc0[i], acc1[i]));
       }
-      // Lane holds raw logits of key rows (i/4)*8 + khalf*4 + i%4 (+32 in acc1).
-      float m = neg_inf(), sraw = 0.f, se = 0.f;
-      int valid_keys = block;
-      if (full) {
+      m = fmaxf(m, __shfl_xor(m, 32, kWave));
+      const float ms = n_keys > 0 ? m * scale_log2 : 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          m = fmaxf(m, fmaxf(acc0[i], acc1[i]));
-          sraw += acc0[i] + acc1[i];
-        }
-        m = fmaxf(m, __shfl_xor(m, 32, kWave));
-        const float ms = m * scale_log2;
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          se += fast_exp2(fmaf(acc0[i], scale_log2, -ms)) + fast_exp2(fmaf(acc1[i], scale_log2, -ms));
-      } else {
-        valid_keys = min(block, n_keys - kr0);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = (i / 4) * 8 + khalf * 4 + (i % 4);
-          const float v0 = r < valid_keys ? acc0[i] : neg_inf();
-          const float v1 = r + 32 < valid_keys ? acc1[i] : neg_inf();
-          m = fmaxf(m, fmaxf(v0, v1));
-          sraw += (r < valid_keys ? acc0[i] : 0.f) + (r + 32 < valid_keys ? acc1[i] : 0.f);
-          acc0[i] = v0;
-          acc1[i] = v1;
-        }
-        m = fmaxf(m, __shfl_xor(m, 32, kWave));
-        const float ms = m * scale_log2;
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          se += fast_exp2(fmaf(acc0[i], scale_log2, -ms)) + fast_exp2(fmaf(acc1[i], scale_log2, -ms));
+      for (int i = 0; i < 16; ++i) {
+        const int r = (i / 4) * 8 + 4 * kh + (i % 4);
+        sraw += (r < n_keys ? acc0[i] : 0.f) + (r + 32 < n_keys ? acc1[i] : 0.f);
+        se += fast_exp2(fmaf(acc0[i], scale_log2, -ms)) + fast_exp2(fmaf(acc1[i], scale_log2, -ms));
       }
-      se += __shfl_xor(se, 32, kWave);
-      sraw += __shfl_xor(sraw, 32, kWave);
-      leaf_lse[f] = m * scale_log2 + fast_log2(se);
-      leaf_mean[f] = sraw / float(valid_keys) * scale_log2;
     }
-    // Level-2 scores of children 2n, 2n+1: LSE over their leaves' mean logits
-    // (a missing leaf has mean -inf and drops out).
-    float lvl2[2];
+    se += __shfl_xor(se, 32, kWave);
+    sraw += __shfl_xor(sraw, 32, kWave);
+    if (kh == 0) {
+      xs[wave][0][32 * ch + col] = n_keys > 0 ? fmaf(m, scale_log2, fast_log2(se)) : neg_inf();
+      xs[wave][1][32 * ch + col] = n_keys > 0 ? sraw * inv_keys * scale_log2 : neg_inf();
+    }
+  }
+  __syncthreads();
+
+  // 3. One pair per thread.
+  if (tid < len) {
+    float o[6] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2) {
-      const float a = leaf_mean[2 * c2], bb = leaf_mean[2 * c2 + 1];
-      const float mm = fmaxf(a, bb);
-      lvl2[c2] = mm == neg_inf() ? neg_inf() : mm + fast_log2(fast_exp2(a - mm) + fast_exp2(bb - mm));
-    }
-    // Sum over the group's heads (adjacent columns), eq. (11).
-    float outv[6] = {leaf_lse[0], leaf_lse[1], leaf_lse[2], leaf_lse[3], lvl2[0], lvl2[1]};
-    for (int o = 1; o < group; o <<= 1) {
+    for (int hh = 0; hh < G; ++hh) {
+      const int r = tid * G + hh;
 #pragma unroll
-      for (int j = 0; j < 6; ++j) outv[j] += __shfl_xor(outv[j], o, kWave);
-    }
-    if (pair_id >= 0 && khalf == 0 && h == 0) {
-      float* dst = scores + (size_t)pair_id * kScoreStride;
-      *reinterpret_cast<float4*>(dst) =
-          make_float4(outv[0] * kLn2, outv[1] * kLn2, outv[2] * kLn2, outv[3] * kLn2);
-      *reinterpret_cast<float4*>(dst + 4) = make_float4(outv[4] * kLn2, outv[5] * kLn2, 0.f, 0.f);
-    }
+      for (int f = 0; f < 4; ++f) o[f] += xs[f][0][r];
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) bq[s] = bn[s];
-    pair_id = pair_next;
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const float a = xs[2 * c2][1][r], bb = xs[2 * c2 + 1][1][r];
+        const float mx = fmaxf(a, bb), mn = fminf(a, bb);
+        // a missing leaf has mean -inf and drops out
+        o[4 + c2] += mn == neg_inf() ? mx : mx + fast_log2(1.f + fast_exp2(mn - mx));
+      }
+    }
+    float* dst = scores + (size_t)pid_s[tid] * kScoreStride;
+    *reinterpret_cast<float4*>(dst) = make_float4(o[0] * kLn2, o[1] * kLn2, o[2] * kLn2, o[3] * kLn2);
+    *reinterpret_cast<float4*>(dst + 4) = make_float4(o[4] * kLn2, o[5] * kLn2, 0.f, 0.f);
   }
 }
 
@@ -544,8 +548,10 @@ hipError_t stage1_lpq_launch(const LaunchShape& s, const void* q, const float* p
 
 bool select_two_stage_supported(const LaunchShape& s) {
   const bool pow2_group = (s.group & (s.group - 1)) == 0;
+  const int64_t slots = (int64_t)s.batch * s.heads_kv * s.seq_len * s.topk;  // int32 pair ids
   return s.bf16 && s.block == 64 && (s.head_dim == 64 || s.head_dim == 128) &&
-         s.lv.n >= kSplitLevel + 1 && pow2_group && s.group <= 4 && s.topk <= 32;
+         s.lv.n >= kSplitLevel + 1 && pow2_group && s.group <= 4 && s.topk <= 32 &&
+         slots < INT32_MAX;
 }
 
 size_t select_two_stage_ws_bytes(const LaunchShape& s) {
@@ -577,24 +583,28 @@ hipError_t launch_select_two_stage(const LaunchShape& s, const void* q, const vo
   if (e != hipSuccess) return e;
   {
     prof::Scope ps("select_sort", st);
-    e = bucket::sort_pairs(w.s1_nodes, s.batch * s.heads_kv, s.seq_len, s.topk, m3, kS2PairsPerItem,
+    e = bucket::sort_pairs(w.s1_nodes, s.batch * s.heads_kv, s.seq_len, s.topk, m3, kS2Rows / s.group,
                            w.counts, w.offsets, w.cursors, w.item_offsets, w.pairs, false, st);
   }
   if (e != hipSuccess) return e;
   {
-  prof::Scope ps2("select_stage2", st);
-  if (s.head_dim == 128)
-    hipLaunchKernelGGL((stage2_kernel<128>), dim3(lay.max_items), dim3(kS2Threads), 0, st,
-                       static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
-                       w.item_offsets, w.offsets, w.pairs, w.scores, lay.n_buckets, s.heads_q,
-                       s.heads_kv, s.seq_len, s.block, s.topk, s.group, m1, m2, m3,
-                       s.scale * kLog2e);
-  else
-    hipLaunchKernelGGL((stage2_kernel<64>), dim3(lay.max_items), dim3(kS2Threads), 0, st,
-                       static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
-                       w.item_offsets, w.offsets, w.pairs, w.scores, lay.n_buckets, s.heads_q,
-                       s.heads_kv, s.seq_len, s.block, s.topk, s.group, m1, m2, m3,
-                       s.scale * kLog2e);
+    prof::Scope ps2("select_stage2", st);
+    const bf16_t* qb = static_cast<const bf16_t*>(q);
+    const bf16_t* kb = static_cast<const bf16_t*>(k);
+    const float sl = s.scale * kLog2e;
+#define PISA_S2(D, G)                                                                         \
+  hipLaunchKernelGGL((stage2_kernel<D, G>), dim3(lay.max_items), dim3(kS2Threads), 0, st, qb, kb, \
+                     w.item_offsets, w.offsets, w.pairs, w.scores, lay.n_buckets, s.heads_q,   \
+                     s.heads_kv, s.seq_len, s.topk, m3, sl)
+    switch (s.group * 1000 + s.head_dim) {
+      case 1128: PISA_S2(128, 1); break;
+      case 1064: PISA_S2(64, 1); break;
+      case 2128: PISA_S2(128, 2); break;
+      case 2064: PISA_S2(64, 2); break;
+      case 4128: PISA_S2(128, 4); break;
+      default: PISA_S2(64, 4); break;
+    }
+#undef PISA_S2
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   prof::Scope ps3("select_final", st);

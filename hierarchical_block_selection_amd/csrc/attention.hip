@@ -64,7 +64,7 @@ namespace {
 
 constexpr int kAttnBlock = 64;
 constexpr int kAttnThreads = 256;
-constexpr int kAttnPairsPerItem = 256;
+constexpr int kAttnRows = 256;  // (pair, head) rows per work item
 constexpr int kAttnCols = 32;
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
@@ -90,7 +90,7 @@ AttnWs attn_layout(const LaunchShape& s) {
   AttnWs w;
   const size_t slots = (size_t)s.batch * s.heads_kv * s.seq_len * s.topk;
   w.n_buckets = s.batch * s.heads_kv * s.lv.size[0];
-  w.max_items = bucket::max_items(slots, w.n_buckets, kAttnPairsPerItem);
+  w.max_items = bucket::max_items(slots, w.n_buckets, kAttnRows / s.group);
   size_t off = 0;
   w.counts = off; off = align256(off + sizeof(int) * w.n_buckets);
   w.offsets = off; off = align256(off + sizeof(int) * (w.n_buckets + 1));
@@ -103,42 +103,54 @@ AttnWs attn_layout(const LaunchShape& s) {
   return w;
 }
 
-template <int D>
-__global__ __launch_bounds__(kAttnThreads) void attn_partial_kernel(
+// One workgroup per work item: leaf block blk of KV head bh and up to
+// kAttnRows / G of the (query, slot) pairs that selected it.  K_blk (row-major)
+// and V_blk (transposed) sit in LDS; wave w takes the 32-column chunks
+// w, w + 4, ... of the item's (pair, head) rows, all of whose query rows it
+// loads up front.  Per chunk:
+//   S^T = K_blk Q^T   (MFMA A = keys from LDS, B = queries; a lane holds the
+//                      logits of 32 keys for one column)
+//   P   = exp2(S * scale - m) in fp32, row sum l, then bf16
+//   O^T = V_blk^T P^T (MFMA A = V^T from LDS, B = P straight from the S
+//                      accumulators; the key order inside this reduction is
+//                      permuted to match the accumulator layout)
+// Each lane then holds 16 output dims of its own column: it scales them by
+// 1/l and stores them as four 8-byte runs, plus the column's log2-sum-exp.
+template <int D, int G>
+__global__ __launch_bounds__(kAttnThreads, 2) void attn_partial_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const int* __restrict__ item_offsets, const int* __restrict__ offsets,
     const int* __restrict__ pairs, bf16_t* __restrict__ part_o, float* __restrict__ part_lse,
-    int n_buckets, int heads_q, int heads_kv, int n_tok, int topk, int group, int m1, int causal,
+    int n_buckets, int heads_q, int heads_kv, int n_tok, int topk, int m1, int causal,
     float scale_log2) {
   constexpr int C = kAttnBlock;
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;
-  constexpr int KROW = D + 8;  // padded rows against LDS bank conflicts
-  constexpr int VROW = C + 8;
+  constexpr int KROW = D + 8;  // padded rows (bf16) against LDS bank conflicts
+  constexpr int VROW = C + 4;
   constexpr int NW = kAttnThreads / kWave;
+  constexpr int PAIRS = kAttnRows / G;
+  constexpr int NCH = kAttnRows / kAttnCols / NW;  // chunks per wave
   __shared__ __attribute__((aligned(16))) bf16_t ks[C * KROW];
   __shared__ __attribute__((aligned(16))) bf16_t vt[D * VROW];
-  constexpr int OROW = D + 8;  // padded output staging row (bf16)
-  __shared__ float inv_l[NW][kAttnCols];
-  __shared__ int pid_s[NW][kAttnCols];
-  __shared__ __attribute__((aligned(16))) bf16_t obuf[NW][kAttnCols * OROW];
+  __shared__ int pid_s[PAIRS];
   int bucket, start, len;
-  if (!bucket::locate_item(item_offsets, offsets, n_buckets, blockIdx.x, kAttnPairsPerItem,
-                           &bucket, &start, &len))
+  if (!bucket::locate_item(item_offsets, offsets, n_buckets, blockIdx.x, PAIRS, &bucket, &start,
+                           &len))
     return;
   const int bh = bucket / m1, blk = bucket % m1;
   const int b = bh / heads_kv, kvh = bh % heads_kv;
   const int tok0 = blk * C;
   const int n_keys = min(C, n_tok - tok0);
+  const int tid = threadIdx.x;
+  if (tid < PAIRS) pid_s[tid] = pairs[start + min(tid, len - 1)];
   const bf16_t* kb = k + ((size_t)bh * n_tok + tok0) * D;
   const bf16_t* vb = v + ((size_t)bh * n_tok + tok0) * D;
-  for (int x = threadIdx.x; x < C * (D / 8); x += kAttnThreads) {
+  for (int x = tid; x < C * (D / 8); x += kAttnThreads) {
     const int r = x / (D / 8), c = (x % (D / 8)) * 8;
-    uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-    if (r < n_keys) {
-      kv = *reinterpret_cast<const uint4*>(kb + (size_t)r * D + c);
-      vv = *reinterpret_cast<const uint4*>(vb + (size_t)r * D + c);
-    }
+    const int rr = min(r, n_keys - 1);  // rows past the sequence end: masked below
+    const uint4 kv = *reinterpret_cast<const uint4*>(kb + (size_t)rr * D + c);
+    const uint4 vv = *reinterpret_cast<const uint4*>(vb + (size_t)rr * D + c);
     *reinterpret_cast<uint4*>(&ks[r * KROW + c]) = kv;
     const uint32_t w4[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
@@ -150,63 +162,54 @@ __global__ __launch_bounds__(kAttnThreads) void attn_partial_kernel(
   __syncthreads();
 
   const int lane = lane_id();
-  const int wave = threadIdx.x / kWave;
-  const int col = lane & 31, khalf = lane >> 5;
-  const int per_chunk = kAttnCols / group;
-  const int n_chunks = (len + per_chunk - 1) / per_chunk;
-  const int h = col % group;
-  auto load_chunk = [&](int ch, bf16x8_t (&bq)[KSTEPS], int& pair_id, int& t) {
-    const int p = ch * per_chunk + col / group;
-    pair_id = -1;
-    t = 0;
-    if (ch < n_chunks && p < len) {
-      pair_id = pairs[start + p];
-      t = (int)(((size_t)pair_id / topk) % n_tok);
-      const bf16_t* qrow = q + (((size_t)b * heads_q + (size_t)kvh * group + h) * n_tok + t) * D;
+  const int wave = tid / kWave;
+  const int col = lane & 31, kh = lane >> 5;
+  const int h = col % G;
+  const int n_rows = len * G;
+  // Query rows of this wave's chunks (columns past the item repeat its last row).
+  bf16x8_t bq[NCH][KSTEPS];
+  int pid[NCH], tq[NCH];
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s)
-        bq[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 16 * s + 8 * khalf));
-    } else {
+  for (int c = 0; c < NCH; ++c) {
+    const int r = min((wave + NW * c) * kAttnCols + col, n_rows - 1);
+    pid[c] = pid_s[r / G];
+    // pair id = (bh * n_tok + t) * topk + slot
+    tq[c] = int(uint32_t(pid[c]) / uint32_t(topk)) - bh * n_tok;
+    const bf16_t* qrow =
+        q + (((size_t)b * heads_q + (size_t)kvh * G + h) * n_tok + tq[c]) * D + 8 * kh;
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) bq[s] = as_bf16x8(make_uint4(0, 0, 0, 0));
-    }
-  };
-  bf16x8_t bq[KSTEPS];
-  int pair_id, t;
-  load_chunk(wave, bq, pair_id, t);
-  bf16_t* ostage = &obuf[wave][0];
-  for (int ch = wave; ch < n_chunks; ch += NW) {
-    bf16x8_t bn[KSTEPS];
-    int pair_next, t_next;
-    load_chunk(ch + NW, bn, pair_next, t_next);  // prefetch the next chunk
+    for (int s = 0; s < KSTEPS; ++s) bq[c][s] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 16 * s));
+  }
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int r0 = (wave + NW * c) * kAttnCols;
+    if (r0 >= n_rows) break;
+    const bool live = r0 + col < n_rows;
     f32x16_t s0 = {}, s1 = {};
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
-      const bf16x8_t a0 =
-          as_bf16x8(*reinterpret_cast<const uint4*>(&ks[col * KROW + 16 * s + 8 * khalf]));
+      const bf16x8_t a0 = as_bf16x8(*reinterpret_cast<const uint4*>(&ks[col * KROW + 16 * s + 8 * kh]));
       const bf16x8_t a1 =
-          as_bf16x8(*reinterpret_cast<const uint4*>(&ks[(32 + col) * KROW + 16 * s + 8 * khalf]));
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bq[s], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bq[s], s1, 0, 0, 0);
+          as_bf16x8(*reinterpret_cast<const uint4*>(&ks[(32 + col) * KROW + 16 * s + 8 * kh]));
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bq[c][s], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bq[c][s], s1, 0, 0, 0);
     }
-    // Lane holds raw logits of key rows (i/4)*8 + khalf*4 + i%4 (+32 in s1) for column col.
+    // Lane holds logits of keys (i/4)*8 + 4kh + i%4 (s0) and 32 + that (s1).
     int lim = n_keys - 1;
-    if (causal) lim = min(lim, t - tok0);
-    if (pair_id < 0) lim = -1;
-    const bool any_masked = __ballot(lim < C - 1) != 0;
-    if (any_masked) {
+    if (causal) lim = min(lim, tq[c] - tok0);
+    if (__ballot(lim < C - 1) != 0) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int r = (i / 4) * 8 + khalf * 4 + (i % 4);
+        const int r = (i / 4) * 8 + 4 * kh + (i % 4);
         s0[i] = r <= lim ? s0[i] : neg_inf();
         s1[i] = r + 32 <= lim ? s1[i] : neg_inf();
       }
     }
-    float m = neg_inf();
+    float m = fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s1[0], s1[1]));
 #pragma unroll
-    for (int i = 0; i < 16; ++i) m = fmaxf(m, fmaxf(s0[i], s1[i]));
+    for (int i = 2; i < 16; i += 2) m = fmaxf(m, fmaxf(fmaxf(s0[i], s0[i + 1]), fmaxf(s1[i], s1[i + 1])));
     m = fmaxf(m, __shfl_xor(m, 32, kWave));
-    const float ms = m == neg_inf() ? 0.f : m * scale_log2;  // column without keys
+    const float ms = m == neg_inf() ? 0.f : m * scale_log2;  // a column without keys
     float l = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -215,68 +218,56 @@ __global__ __launch_bounds__(kAttnThreads) void attn_partial_kernel(
       l += s0[i] + s1[i];
     }
     l += __shfl_xor(l, 32, kWave);
-    // O = P V: A = P (rows = columns of S), k-step s covers 16 keys.
+    // B operands P^T: step st covers keys 32(st/2) + 16(st%2) + 8(j/4) + 4kh + j%4.
+    bf16x8_t pb[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pb[st][j] = (__bf16)(st < 2 ? s0[8 * st + j] : s1[8 * (st - 2) + j]);
     f32x16_t o[DBLK];
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db) o[db] = f32x16_t{};
+    for (int db = 0; db < DBLK; ++db) {
+      o[db] = f32x16_t{};
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      bf16x8_t pa;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float x = s < 2 ? s0[8 * s + j] : s1[8 * (s - 2) + j];
-        pa[j] = __builtin_bit_cast(__bf16, f32_to_bf16(x));
-      }
-      const int kbase = 32 * (s / 2) + 16 * (s % 2) + 4 * khalf;
-#pragma unroll
-      for (int db = 0; db < DBLK; ++db) {
-        const bf16_t* vrow = &vt[(32 * db + col) * VROW + kbase];
+      for (int st = 0; st < 4; ++st) {
+        const bf16_t* vrow = &vt[(32 * db + col) * VROW + 32 * (st / 2) + 16 * (st % 2) + 4 * kh];
         const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
         const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
-        const bf16x8_t vbop = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, vbop, o[db], 0, 0, 0);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pb[st], o[db], 0, 0, 0);
       }
     }
-    if (khalf == 0) {
-      inv_l[wave][col] = l > 0.f ? 1.f / l : 0.f;
-      pid_s[wave][col] = pair_id;
-      if (pair_id >= 0) part_lse[(size_t)pair_id * group + h] = ms + fast_log2(l);
+    // o[db][i] = O[column][d = 32 db + (i/4)*8 + 4kh + i%4]
+    if (live) {
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      bf16_t* dst = part_o + ((size_t)pid[c] * G + h) * D + 4 * kh;
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+          bf16x4_t w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[db][4 * g4 + e] * inv);
+          *reinterpret_cast<uint2*>(dst + 32 * db + 8 * g4) = __builtin_bit_cast(uint2, w);
+        }
+      if (kh == 0) part_lse[(size_t)pid[c] * G + h] = ms + fast_log2(l);
     }
-    wave_lds_sync();
-    // o[db][i] = O[row (i/4)*8 + khalf*4 + i%4][d = 32*db + col] -> LDS [row][d] (bf16)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = (i / 4) * 8 + khalf * 4 + (i % 4);
-      const float inv = inv_l[wave][r];
-#pragma unroll
-      for (int db = 0; db < DBLK; ++db) ostage[r * OROW + 32 * db + col] = f32_to_bf16(o[db][i] * inv);
-    }
-    wave_lds_sync();
-    // 16-byte stores: each row is D bf16 = D/8 chunks.
-    constexpr int CH_PER_ROW = D / 8;
-#pragma unroll
-    for (int x = lane; x < 32 * CH_PER_ROW; x += kWave) {
-      const int r = x / CH_PER_ROW, c8 = (x % CH_PER_ROW) * 8;
-      const int pr = pid_s[wave][r];
-      if (pr >= 0) {
-        const uint4 v = *reinterpret_cast<const uint4*>(&ostage[r * OROW + c8]);
-        *reinterpret_cast<uint4*>(part_o + ((size_t)pr * group + (r % group)) * D + c8) = v;
-      }
-    }
-    wave_lds_sync();
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) bq[s] = bn[s];
-    pair_id = pair_next;
-    t = t_next;
   }
 }
 
+// Merge the K partials of each (query, head) row: weights exp2(lse_j - M)
+// over the selected blocks, 16 lanes per row.  The row's block ids and LSEs,
+// then up to 16 partials (16-byte loads), are all requested before any is
+// used.  Unused slots (-1) read the row's first partial with weight 0 (slot
+// 0 always holds a selected block).
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(
     const int32_t* __restrict__ idx, const bf16_t* __restrict__ part_o,
     const float* __restrict__ part_lse, bf16_t* __restrict__ out, float* __restrict__ lse_out,
     int heads_q, int heads_kv, int n_tok, int topk, int group, int m1, size_t n_rows) {
   constexpr int EPL = D / 16;  // elements per lane (16 lanes per row)
+  constexpr int B = 16;        // slots per batch
   const size_t row = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) / 16;
   if (row >= n_rows) return;
   const int sub = threadIdx.x & 15;
@@ -286,41 +277,67 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
   const size_t bh = u / n_tok;
   const int b = (int)(bh / heads_kv), kvh = (int)(bh % heads_kv);
   const int32_t* ir = idx + u * topk;
-  float M = neg_inf();
-  for (int j = 0; j < topk; ++j) {
-    const int x = ir[j];
-    if (x >= 0 && x < m1) M = fmaxf(M, part_lse[(u * topk + j) * group + h]);
-  }
   float acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-  float W = 0.f;
-  if (M != neg_inf()) {
-    for (int j = 0; j < topk; ++j) {
-      const int x = ir[j];
-      if (x < 0 || x >= m1) continue;
-      const size_t pi = (u * topk + j) * group + h;
-      const float w = fast_exp2(part_lse[pi] - M);
-      W += w;
-      const bf16_t* src = part_o + pi * D + sub * EPL;
-      float vals[8];
-      if (EPL == 8) {
-        load16(src, vals);
-      } else {
-        const uint2 raw = *reinterpret_cast<const uint2*>(src);
-        vals[0] = __uint_as_float(raw.x << 16);
-        vals[1] = __uint_as_float(raw.x & 0xffff0000u);
-        vals[2] = __uint_as_float(raw.y << 16);
-        vals[3] = __uint_as_float(raw.y & 0xffff0000u);
-      }
+  float M = neg_inf(), W = 0.f;
+  for (int j0 = 0; j0 < topk; j0 += B) {
+    float lj[B];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] += w * vals[e];
+    for (int jj = 0; jj < B; ++jj) {
+      const int j = j0 + jj;
+      const int x = j < topk ? ir[j] : -1;
+      lj[jj] = (x >= 0 && x < m1) ? part_lse[(u * topk + j) * group + h] : neg_inf();
+    }
+    float mb = M;
+#pragma unroll
+    for (int jj = 0; jj < B; ++jj) mb = fmaxf(mb, lj[jj]);
+    if (mb == neg_inf()) continue;
+    // rescale what earlier batches accumulated
+    const float r = M == neg_inf() ? 0.f : fast_exp2(M - mb);
+    W *= r;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] *= r;
+    M = mb;
+    uint32_t raw[B][EPL / 2];  // bf16 pairs, unpacked when used
+#pragma unroll
+    for (int jj = 0; jj < B; ++jj) {
+      const bool ok = lj[jj] != neg_inf();
+      const bf16_t* src = part_o + ((u * topk + (ok ? j0 + jj : 0)) * group + h) * D + sub * EPL;
+      if (EPL == 8) {
+        const uint4 v4 = *reinterpret_cast<const uint4*>(src);
+        raw[jj][0] = v4.x; raw[jj][1] = v4.y; raw[jj][2] = v4.z; raw[jj][3] = v4.w;
+      } else {
+        const uint2 v2 = *reinterpret_cast<const uint2*>(src);
+        raw[jj][0] = v2.x; raw[jj][1] = v2.y;
+      }
+    }
+#pragma unroll
+    for (int jj = 0; jj < B; ++jj) {
+      const float w = lj[jj] != neg_inf() ? fast_exp2(lj[jj] - M) : 0.f;
+      W += w;
+#pragma unroll
+      for (int e = 0; e < EPL / 2; ++e) {
+        acc[2 * e] += w * __uint_as_float(raw[jj][e] << 16);
+        acc[2 * e + 1] += w * __uint_as_float(raw[jj][e] & 0xffff0000u);
+      }
     }
   }
   const float inv = W > 0.f ? 1.f / W : 0.f;
   bf16_t* dst = out + (((size_t)b * heads_q + (size_t)kvh * group + h) * n_tok + t) * D + sub * EPL;
+  if (EPL == 8) {
+    typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8v;
+    bf16x8v o8;
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) dst[e] = f32_to_bf16(acc[e] * inv);
+    for (int e = 0; e < 8; ++e) o8[e] = (__bf16)(acc[e] * inv);
+    *reinterpret_cast<uint4*>(dst) = __builtin_bit_cast(uint4, o8);
+  } else {
+    typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4v;
+    bf16x4v o4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(acc[e] * inv);
+    *reinterpret_cast<uint2*>(dst) = __builtin_bit_cast(uint2, o4);
+  }
   if (lse_out && sub == 0) {
     lse_out[((size_t)b * heads_q + (size_t)kvh * group + h) * n_tok + t] =
         W > 0.f ? (M + fast_log2(W)) * kLn2 : neg_inf();
@@ -343,18 +360,29 @@ hipError_t launch_block_path(const LaunchShape& s, const void* q, const void* k,
   hipError_t e;
   {
     prof::Scope ps("attn_sort", st);
-    e = bucket::sort_pairs(idx, s.batch * s.heads_kv, s.seq_len, s.topk, m1,
-                                    kAttnPairsPerItem, counts, offsets, cursors, item_offsets,
-                                    pairs, false, st);
+    e = bucket::sort_pairs(idx, s.batch * s.heads_kv, s.seq_len, s.topk, m1, kAttnRows / s.group,
+                           counts, offsets, cursors, item_offsets, pairs, false, st);
   }
   if (e != hipSuccess) return e;
   {
-  prof::Scope ps("attn_partial", st);
-  hipLaunchKernelGGL((attn_partial_kernel<D>), dim3(lay.max_items), dim3(kAttnThreads), 0, st,
-                     static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
-                     static_cast<const bf16_t*>(v), item_offsets, offsets, pairs, part_o,
-                     part_lse, lay.n_buckets, s.heads_q, s.heads_kv, s.seq_len, s.topk, s.group,
-                     m1, s.causal ? 1 : 0, s.scale * kLog2e);
+    prof::Scope ps("attn_partial", st);
+    const bf16_t* qb = static_cast<const bf16_t*>(q);
+    const bf16_t* kb = static_cast<const bf16_t*>(k);
+    const bf16_t* vb = static_cast<const bf16_t*>(v);
+    const float sl = s.scale * kLog2e;
+    const int cz = s.causal ? 1 : 0;
+#define PISA_AP(G)                                                                             \
+  hipLaunchKernelGGL((attn_partial_kernel<D, G>), dim3(lay.max_items), dim3(kAttnThreads), 0, st, \
+                     qb, kb, vb, item_offsets, offsets, pairs, part_o, part_lse, lay.n_buckets,  \
+                     s.heads_q, s.heads_kv, s.seq_len, s.topk, m1, cz, sl)
+    switch (s.group) {
+      case 1: PISA_AP(1); break;
+      case 2: PISA_AP(2); break;
+      case 4: PISA_AP(4); break;
+      case 8: PISA_AP(8); break;
+      default: PISA_AP(16); break;
+    }
+#undef PISA_AP
   }
   prof::Scope ps("attn_combine", st);
   const size_t rows = (size_t)s.batch * s.heads_kv * s.seq_len * s.group;

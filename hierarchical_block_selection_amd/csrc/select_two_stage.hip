@@ -39,12 +39,14 @@ namespace {
 constexpr int kSplitLevel = 3;   // stage 1 decides levels L..3
 constexpr int kS1Waves = 4;
 constexpr int kS2Threads = 256;
-constexpr int kS2Rows = 256;    // (pair, head) rows per stage-2 item
+constexpr int kS2Rows = 256;    // (pair, head) rows per stage-2 batch
+constexpr int kS2Batches = 4;   // batches per stage-2 work item
 constexpr int kS2Cols = 32;      // MFMA 32x32x16: 32 (query, head) columns
 constexpr int kScoreStride = 8;  // floats per pair: 4 leaf LSE, 2 level-2, 2 pad
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
 
 struct Ws {
   int* counts;        // [n_buckets]
@@ -71,7 +73,7 @@ WsLayout ws_layout(const LaunchShape& s) {
   const size_t units = (size_t)s.batch * s.heads_kv * s.seq_len;
   const int m3 = s.lv.n >= kSplitLevel ? s.lv.size[kSplitLevel - 1] : 1;
   w.n_buckets = s.batch * s.heads_kv * m3;
-  w.max_items = bucket::max_items(units * s.topk, w.n_buckets, kS2Rows / s.group);
+  w.max_items = bucket::max_items(units * s.topk, w.n_buckets, kS2Rows / s.group * kS2Batches);
   size_t off = 0;
   w.counts = off; off = align256(off + sizeof(int) * w.n_buckets);
   w.offsets = off; off = align256(off + sizeof(int) * (w.n_buckets + 1));
@@ -273,19 +275,44 @@ __global__ __launch_bounds__(kS1Waves * kWave) void stage1_kernel(
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+// Stage 2 batch bt of an item: pair ids (threads < kS2Rows / G) and the query
+// rows of every (pair, head), 16 bytes per load, into registers.  Rows past
+// the item repeat its last pair.
+template <int D, int G, int PER_THREAD>
+__device__ __forceinline__ void stage2_fetch(u32x4_t (&stage)[PER_THREAD], int& pid_reg,
+                                             const int* __restrict__ pairs, int start, int len,
+                                             int bt, const bf16_t* __restrict__ qh, int bh,
+                                             int n_tok, int topk) {
+  constexpr int PAIRS = kS2Rows / G;
+  constexpr int V16 = D / 8;
+  const int tid = threadIdx.x;
+  const int base = bt * PAIRS;
+  const int last = len - 1;
+  if (tid < PAIRS) pid_reg = pairs[start + min(base + tid, last)];
+#pragma unroll
+  for (int i = 0; i < PER_THREAD; ++i) {
+    const int x = tid + i * kS2Threads;
+    const int r = x / V16, c = x % V16;
+    const int pid = pairs[start + min(base + r / G, last)];
+    // pair id = (bh * n_tok + t) * topk + slot
+    const int t = int(uint32_t(pid) / uint32_t(topk)) - bh * n_tok;
+    stage[i] = *reinterpret_cast<const u32x4_t*>(qh + ((size_t)(r % G) * n_tok + t) * D + 8 * c);
+  }
+}
+
 // One workgroup per work item: level-3 node n of KV head bh and up to
-// kS2Rows / G of its (query, slot) pairs; wavefront w owns leaf 4n + w.
-//
-//   1. The item's pair ids, then the query rows of every (pair, head), are
-//      staged in LDS (all loads issued together).
-//   2. Each wave holds its leaf's 64 raw keys as MFMA A operands in registers
-//      and walks the staged rows 32 columns at a time: S = K_leaf . Q^T on bf16
-//      MFMA 32x32x16 (a lane holds 32 keys of one column), then the exact leaf
-//      LSE (eq. (7) at level 1: max, sum of exp2) and the mean logit, which
-//      equals q . kbar_leaf (eq. (4) is a mean), go to LDS per column.
-//   3. After one barrier every thread finishes one pair: the four leaf LSEs
-//      and the two level-2 scores LSE(mean_2c, mean_2c+1), each summed over
-//      the group's heads (eq. (11)), in nats.
+// kS2Batches batches of kS2Rows / G of its (query, slot) pairs; wavefront w
+// owns leaf 4n + w and keeps its 64 raw keys as MFMA A operands in registers
+// for the whole item.  Per batch:
+//   1. the batch's query rows of every (pair, head), loaded into registers
+//      while the previous batch computed, go to LDS;
+//   2. each wave walks the staged rows 32 columns at a time: S = K_leaf . Q^T
+//      on bf16 MFMA 32x32x16 (a lane holds 32 keys of one column), then the
+//      exact leaf LSE (eq. (7) at level 1: max, sum of exp2) and the mean
+//      logit, which equals q . kbar_leaf (eq. (4) is a mean), go to LDS;
+//   3. after a barrier every thread finishes one pair: the four leaf LSEs and
+//      the two level-2 scores LSE(mean_2c, mean_2c+1), each summed over the
+//      group's heads (eq. (11)), in nats.
 template <int D, int G>
 __global__ __launch_bounds__(kS2Threads, 2) void stage2_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
@@ -293,15 +320,17 @@ __global__ __launch_bounds__(kS2Threads, 2) void stage2_kernel(
     const int* __restrict__ pairs, float* __restrict__ scores, int n_buckets, int heads_q,
     int heads_kv, int n_tok, int topk, int m3, float scale_log2) {
   constexpr int KSTEPS = D / 16;
-  constexpr int PAIRS = kS2Rows / G;  // pairs per item
+  constexpr int PAIRS = kS2Rows / G;  // pairs per batch
   constexpr int QROW = D + 8;         // padded LDS row (bf16): 16-byte reads spread over banks
   constexpr int LEAF = 64;            // keys per leaf (C = 64)
+  constexpr int V16 = D / 8;          // 16-byte pieces per row
+  constexpr int PER_THREAD = kS2Rows * V16 / kS2Threads;
   __shared__ __attribute__((aligned(16))) bf16_t qs[kS2Rows * QROW];
   __shared__ float xs[4][2][kS2Rows];  // [leaf][lse, mean][row], log2 units
   __shared__ int pid_s[PAIRS];
   int bucket, start, len;
-  if (!bucket::locate_item(item_offsets, offsets, n_buckets, blockIdx.x, PAIRS, &bucket, &start,
-                           &len))
+  if (!bucket::locate_item(item_offsets, offsets, n_buckets, blockIdx.x, PAIRS * kS2Batches,
+                           &bucket, &start, &len))
     return;
   const int bh = bucket / m3, node = bucket % m3;
   const int b = bh / heads_kv, kvh = bh % heads_kv;
@@ -309,9 +338,13 @@ __global__ __launch_bounds__(kS2Threads, 2) void stage2_kernel(
   const int lane = lane_id();
   const int wave = tid / kWave;
   const int col = lane & 31, kh = lane >> 5;
+  const bf16_t* qh = q + ((size_t)b * heads_q + (size_t)kvh * G) * n_tok * D;
 
-  // 1. Pair ids, then query rows (row r = pair r / G, head r % G).
-  if (tid < PAIRS) pid_s[tid] = pairs[start + min(tid, len - 1)];
+  // Batch bt's pair ids and query rows (row r = pair r / G, head r % G;
+  // rows past the item repeat its last pair) -> registers.
+  u32x4_t stage[PER_THREAD];
+  int pid_reg = 0;
+  stage2_fetch<D, G, PER_THREAD>(stage, pid_reg, pairs, start, len, 0, qh, bh, n_tok, topk);
   const int leaf_tok0 = (4 * node + wave) * LEAF;
   const int n_keys = max(0, min(LEAF, n_tok - leaf_tok0));  // keys of this wave's leaf
   // A operands: key rows leaf_tok0 + 32 rb + col (rows past the sequence end
@@ -325,99 +358,94 @@ __global__ __launch_bounds__(kS2Threads, 2) void stage2_kernel(
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) ka[rb][s] = as_bf16x8(*reinterpret_cast<const uint4*>(kr + 16 * s));
   }
-  __syncthreads();
-  const int n_rows = len * G;
-  constexpr int V16 = D / 8;  // 16-byte pieces per row
-  constexpr int PER_THREAD = kS2Rows * V16 / kS2Threads;
-  uint4 stage[PER_THREAD];
-#pragma unroll
-  for (int i = 0; i < PER_THREAD; ++i) {
-    const int x = tid + i * kS2Threads;
-    const int r = min(x / V16, n_rows - 1), c = x % V16;
-    // pair id = (bh * n_tok + t) * topk + slot
-    const int t = int(uint32_t(pid_s[r / G]) / uint32_t(topk)) - bh * n_tok;
-    stage[i] = *reinterpret_cast<const uint4*>(
-        q + (((size_t)b * heads_q + (size_t)kvh * G + r % G) * n_tok + t) * D + 8 * c);
-  }
-#pragma unroll
-  for (int i = 0; i < PER_THREAD; ++i) {
-    const int x = tid + i * kS2Threads;
-    *reinterpret_cast<uint4*>(&qs[(x / V16) * QROW + 8 * (x % V16)]) = stage[i];
-  }
-  __syncthreads();
-
-  // 2. Leaf LSE and mean logit per staged row.
   const float inv_keys = n_keys > 0 ? 1.f / float(n_keys) : 0.f;
-  const int n_chunks = (n_rows + 31) / 32;
-  for (int ch = 0; ch < n_chunks; ++ch) {
-    const bf16_t* qr = &qs[(32 * ch + col) * QROW + 8 * kh];
-    f32x16_t acc0 = {}, acc1 = {};
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-      const bf16x8_t bq = as_bf16x8(*reinterpret_cast<const uint4*>(qr + 16 * s));
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0][s], bq, acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[1][s], bq, acc1, 0, 0, 0);
-    }
-    // Lane holds the logits of keys (i/4)*8 + 4kh + i%4 (acc0) and 32 + that (acc1).
-    float m, sraw = 0.f, se = 0.f;
-    if (n_keys == LEAF) {
-      m = fmaxf(fmaxf(acc0[0], acc0[1]), fmaxf(acc1[0], acc1[1]));
-#pragma unroll
-      for (int i = 2; i < 16; i += 2)
-        m = fmaxf(m, fmaxf(fmaxf(acc0[i], acc0[i + 1]), fmaxf(acc1[i], acc1[i + 1])));
-      m = fmaxf(m, __shfl_xor(m, 32, kWave));
-      const float ms = m * scale_log2;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        sraw += acc0[i] + acc1[i];
-        se += fast_exp2(fmaf(acc0[i], scale_log2, -ms)) + fast_exp2(fmaf(acc1[i], scale_log2, -ms));
-      }
-    } else {
-      m = neg_inf();
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = (i / 4) * 8 + 4 * kh + (i % 4);
-        acc0[i] = r < n_keys ? acc0[i] : neg_inf();
-        acc1[i] = r + 32 < n_keys ? acc1[i] : neg_inf();
-        m = fmaxf(m, fmaxf(acc0[i], acc1[i]));
-      }
-      m = fmaxf(m, __shfl_xor(m, 32, kWave));
-      const float ms = n_keys > 0 ? m * scale_log2 : 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = (i / 4) * 8 + 4 * kh + (i % 4);
-        sraw += (r < n_keys ? acc0[i] : 0.f) + (r + 32 < n_keys ? acc1[i] : 0.f);
-        se += fast_exp2(fmaf(acc0[i], scale_log2, -ms)) + fast_exp2(fmaf(acc1[i], scale_log2, -ms));
-      }
-    }
-    se += __shfl_xor(se, 32, kWave);
-    sraw += __shfl_xor(sraw, 32, kWave);
-    if (kh == 0) {
-      xs[wave][0][32 * ch + col] = n_keys > 0 ? fmaf(m, scale_log2, fast_log2(se)) : neg_inf();
-      xs[wave][1][32 * ch + col] = n_keys > 0 ? sraw * inv_keys * scale_log2 : neg_inf();
-    }
-  }
-  __syncthreads();
+  const int n_batches = (len + PAIRS - 1) / PAIRS;
 
-  // 3. One pair per thread.
-  if (tid < len) {
-    float o[6] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int bt = 0; bt < n_batches; ++bt) {
+    const int blen = min(PAIRS, len - bt * PAIRS);  // pairs in this batch
+    __syncthreads();  // the previous batch's readers of qs, xs and pid_s are done
+    if (tid < PAIRS) pid_s[tid] = pid_reg;
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      const int r = tid * G + hh;
+    for (int i = 0; i < PER_THREAD; ++i) {
+      const int x = tid + i * kS2Threads;
+      *reinterpret_cast<u32x4_t*>(&qs[(x / V16) * QROW + 8 * (x % V16)]) = stage[i];
+    }
+    __syncthreads();
+    // next batch in flight while this one computes (the last batch fetches itself again)
+    stage2_fetch<D, G, PER_THREAD>(stage, pid_reg, pairs, start, len, min(bt + 1, n_batches - 1),
+                                   qh, bh, n_tok, topk);
+
+    const int n_chunks = (blen * G + 31) / 32;
+    for (int ch = 0; ch < n_chunks; ++ch) {
+      const bf16_t* qr = &qs[(32 * ch + col) * QROW + 8 * kh];
+      f32x16_t acc0 = {}, acc1 = {};
 #pragma unroll
-      for (int f = 0; f < 4; ++f) o[f] += xs[f][0][r];
+      for (int s = 0; s < KSTEPS; ++s) {
+        const bf16x8_t bq = as_bf16x8(*reinterpret_cast<const uint4*>(qr + 16 * s));
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0][s], bq, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[1][s], bq, acc1, 0, 0, 0);
+      }
+      // Lane holds the logits of keys (i/4)*8 + 4kh + i%4 (acc0) and 32 + that (acc1).
+      float m, sraw = 0.f, se = 0.f;
+      if (n_keys == LEAF) {
+        m = fmaxf(fmaxf(acc0[0], acc0[1]), fmaxf(acc1[0], acc1[1]));
 #pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        const float a = xs[2 * c2][1][r], bb = xs[2 * c2 + 1][1][r];
-        const float mx = fmaxf(a, bb), mn = fminf(a, bb);
-        // a missing leaf has mean -inf and drops out
-        o[4 + c2] += mn == neg_inf() ? mx : mx + fast_log2(1.f + fast_exp2(mn - mx));
+        for (int i = 2; i < 16; i += 2)
+          m = fmaxf(m, fmaxf(fmaxf(acc0[i], acc0[i + 1]), fmaxf(acc1[i], acc1[i + 1])));
+        m = fmaxf(m, __shfl_xor(m, 32, kWave));
+        const float ms = m * scale_log2;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          sraw += acc0[i] + acc1[i];
+          se += fast_exp2(fmaf(acc0[i], scale_log2, -ms)) + fast_exp2(fmaf(acc1[i], scale_log2, -ms));
+        }
+      } else {
+        m = neg_inf();
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = (i / 4) * 8 + 4 * kh + (i % 4);
+          acc0[i] = r < n_keys ? acc0[i] : neg_inf();
+          acc1[i] = r + 32 < n_keys ? acc1[i] : neg_inf();
+          m = fmaxf(m, fmaxf(acc0[i], acc1[i]));
+        }
+        m = fmaxf(m, __shfl_xor(m, 32, kWave));
+        const float ms = n_keys > 0 ? m * scale_log2 : 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = (i / 4) * 8 + 4 * kh + (i % 4);
+          sraw += (r < n_keys ? acc0[i] : 0.f) + (r + 32 < n_keys ? acc1[i] : 0.f);
+          se += fast_exp2(fmaf(acc0[i], scale_log2, -ms)) + fast_exp2(fmaf(acc1[i], scale_log2, -ms));
+        }
+      }
+      se += __shfl_xor(se, 32, kWave);
+      sraw += __shfl_xor(sraw, 32, kWave);
+      if (kh == 0) {
+        xs[wave][0][32 * ch + col] = n_keys > 0 ? fmaf(m, scale_log2, fast_log2(se)) : neg_inf();
+        xs[wave][1][32 * ch + col] = n_keys > 0 ? sraw * inv_keys * scale_log2 : neg_inf();
       }
     }
-    float* dst = scores + (size_t)pid_s[tid] * kScoreStride;
-    *reinterpret_cast<float4*>(dst) = make_float4(o[0] * kLn2, o[1] * kLn2, o[2] * kLn2, o[3] * kLn2);
-    *reinterpret_cast<float4*>(dst + 4) = make_float4(o[4] * kLn2, o[5] * kLn2, 0.f, 0.f);
+    __syncthreads();
+
+    // One pair per thread.
+    if (tid < blen) {
+      float o[6] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        const int r = tid * G + hh;
+#pragma unroll
+        for (int f = 0; f < 4; ++f) o[f] += xs[f][0][r];
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+          const float a = xs[2 * c2][1][r], bb = xs[2 * c2 + 1][1][r];
+          const float mx = fmaxf(a, bb), mn = fminf(a, bb);
+          // a missing leaf has mean -inf and drops out
+          o[4 + c2] += mn == neg_inf() ? mx : mx + fast_log2(1.f + fast_exp2(mn - mx));
+        }
+      }
+      float* dst = scores + (size_t)pid_s[tid] * kScoreStride;
+      *reinterpret_cast<float4*>(dst) = make_float4(o[0] * kLn2, o[1] * kLn2, o[2] * kLn2, o[3] * kLn2);
+      *reinterpret_cast<float4*>(dst + 4) = make_float4(o[4] * kLn2, o[5] * kLn2, 0.f, 0.f);
+    }
   }
 }
 
@@ -583,7 +611,8 @@ hipError_t launch_select_two_stage(const LaunchShape& s, const void* q, const vo
   if (e != hipSuccess) return e;
   {
     prof::Scope ps("select_sort", st);
-    e = bucket::sort_pairs(w.s1_nodes, s.batch * s.heads_kv, s.seq_len, s.topk, m3, kS2Rows / s.group,
+    e = bucket::sort_pairs(w.s1_nodes, s.batch * s.heads_kv, s.seq_len, s.topk, m3,
+                           kS2Rows / s.group * kS2Batches,
                            w.counts, w.offsets, w.cursors, w.item_offsets, w.pairs, false, st);
   }
   if (e != hipSuccess) return e;

@@ -64,7 +64,8 @@ namespace {
 
 constexpr int kAttnBlock = 64;
 constexpr int kAttnThreads = 256;
-constexpr int kAttnRows = 256;  // (pair, head) rows per work item
+constexpr int kAttnRows = 256;   // (pair, head) rows per batch
+constexpr int kAttnBatches = 4;  // batches per work item
 constexpr int kAttnCols = 32;
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
@@ -73,7 +74,7 @@ typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 struct AttnWs {
-  size_t counts, offsets, cursors, item_offsets, pairs, part_o, part_lse, total;
+  size_t counts, offsets, cursors, item_offsets, pairs, inv, part_o, part_lse, total;
   int n_buckets, max_items;
 };
 
@@ -90,13 +91,14 @@ AttnWs attn_layout(const LaunchShape& s) {
   AttnWs w;
   const size_t slots = (size_t)s.batch * s.heads_kv * s.seq_len * s.topk;
   w.n_buckets = s.batch * s.heads_kv * s.lv.size[0];
-  w.max_items = bucket::max_items(slots, w.n_buckets, kAttnRows / s.group);
+  w.max_items = bucket::max_items(slots, w.n_buckets, kAttnRows / s.group * kAttnBatches);
   size_t off = 0;
   w.counts = off; off = align256(off + sizeof(int) * w.n_buckets);
   w.offsets = off; off = align256(off + sizeof(int) * (w.n_buckets + 1));
   w.cursors = off; off = align256(off + sizeof(int) * w.n_buckets);
   w.item_offsets = off; off = align256(off + sizeof(int) * (w.n_buckets + 1));
   w.pairs = off; off = align256(off + sizeof(int) * slots);
+  w.inv = off; off = align256(off + sizeof(int) * slots);
   w.part_o = off; off = align256(off + sizeof(bf16_t) * slots * s.group * s.head_dim);
   w.part_lse = off; off = align256(off + sizeof(float) * slots * s.group);
   w.total = off;
@@ -104,10 +106,11 @@ AttnWs attn_layout(const LaunchShape& s) {
 }
 
 // One workgroup per work item: leaf block blk of KV head bh and up to
-// kAttnRows / G of the (query, slot) pairs that selected it.  K_blk (row-major)
-// and V_blk (transposed) sit in LDS; wave w takes the 32-column chunks
-// w, w + 4, ... of the item's (pair, head) rows, all of whose query rows it
-// loads up front.  Per chunk:
+// kAttnBatches batches of kAttnRows / G of the (query, slot) pairs that
+// selected it.  K_blk (row-major) and V_blk (transposed) sit in LDS for the
+// whole item; in every batch wave w takes the 32-column chunks w and w + 4
+// of the batch's (pair, head) rows, whose query rows it loaded while the
+// previous batch computed.  Per chunk:
 //   S^T = K_blk Q^T   (MFMA A = keys from LDS, B = queries; a lane holds the
 //                      logits of 32 keys for one column)
 //   P   = exp2(S * scale - m) in fp32, row sum l, then bf16
@@ -116,6 +119,27 @@ AttnWs attn_layout(const LaunchShape& s) {
 //                      permuted to match the accumulator layout)
 // Each lane then holds 16 output dims of its own column: it scales them by
 // 1/l and stores them as four 8-byte runs, plus the column's log2-sum-exp.
+template <int D, int G, int NCH, int KSTEPS>
+__device__ __forceinline__ void attn_fetch(bf16x8_t (&bq)[NCH][KSTEPS], int (&pid)[NCH],
+                                           int (&tq)[NCH], const int* __restrict__ pairs,
+                                           int start, int len, int bt, int wave, int col, int kh,
+                                           const bf16_t* __restrict__ qh, int bh, int n_tok,
+                                           int topk) {
+  constexpr int NW = kAttnThreads / kWave;
+  const int rows = len * G;
+  const int h = col % G;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int r = min(bt * kAttnRows + (wave + NW * c) * kAttnCols + col, rows - 1);
+    pid[c] = pairs[start + r / G];
+    // pair id = (bh * n_tok + t) * topk + slot
+    tq[c] = int(uint32_t(pid[c]) / uint32_t(topk)) - bh * n_tok;
+    const bf16_t* qrow = qh + ((size_t)h * n_tok + tq[c]) * D + 8 * kh;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) bq[c][s] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 16 * s));
+  }
+}
+
 template <int D, int G>
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_partial_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
@@ -129,21 +153,29 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_partial_kernel(
   constexpr int KROW = D + 8;  // padded rows (bf16) against LDS bank conflicts
   constexpr int VROW = C + 4;
   constexpr int NW = kAttnThreads / kWave;
-  constexpr int PAIRS = kAttnRows / G;
-  constexpr int NCH = kAttnRows / kAttnCols / NW;  // chunks per wave
+  constexpr int PAIRS = kAttnRows / G;             // pairs per batch
+  constexpr int NCH = kAttnRows / kAttnCols / NW;  // chunks per wave and batch
   __shared__ __attribute__((aligned(16))) bf16_t ks[C * KROW];
   __shared__ __attribute__((aligned(16))) bf16_t vt[D * VROW];
-  __shared__ int pid_s[PAIRS];
   int bucket, start, len;
-  if (!bucket::locate_item(item_offsets, offsets, n_buckets, blockIdx.x, PAIRS, &bucket, &start,
-                           &len))
+  if (!bucket::locate_item(item_offsets, offsets, n_buckets, blockIdx.x, PAIRS * kAttnBatches,
+                           &bucket, &start, &len))
     return;
   const int bh = bucket / m1, blk = bucket % m1;
   const int b = bh / heads_kv, kvh = bh % heads_kv;
   const int tok0 = blk * C;
   const int n_keys = min(C, n_tok - tok0);
   const int tid = threadIdx.x;
-  if (tid < PAIRS) pid_s[tid] = pairs[start + min(tid, len - 1)];
+  const int lane = lane_id();
+  const int wave = tid / kWave;
+  const int col = lane & 31, kh = lane >> 5;
+  const int h = col % G;
+  const bf16_t* qh = q + ((size_t)b * heads_q + (size_t)kvh * G) * n_tok * D;
+  // First batch's query rows (in flight while K and V are staged).
+  bf16x8_t bq[NCH][KSTEPS];
+  int pid[NCH], tq[NCH];
+  attn_fetch<D, G, NCH, KSTEPS>(bq, pid, tq, pairs, start, len, 0, wave, col, kh, qh, bh, n_tok,
+                                topk);
   const bf16_t* kb = k + ((size_t)bh * n_tok + tok0) * D;
   const bf16_t* vb = v + ((size_t)bh * n_tok + tok0) * D;
   for (int x = tid; x < C * (D / 8); x += kAttnThreads) {
@@ -161,109 +193,110 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_partial_kernel(
   }
   __syncthreads();
 
-  const int lane = lane_id();
-  const int wave = tid / kWave;
-  const int col = lane & 31, kh = lane >> 5;
-  const int h = col % G;
-  const int n_rows = len * G;
-  // Query rows of this wave's chunks (columns past the item repeat its last row).
-  bf16x8_t bq[NCH][KSTEPS];
-  int pid[NCH], tq[NCH];
+  const int rows = len * G;
+  const int n_batches = (len + PAIRS - 1) / PAIRS;
+  for (int bt = 0; bt < n_batches; ++bt) {
+    bf16x8_t bn[NCH][KSTEPS];
+    int pid_n[NCH], tq_n[NCH];
+    attn_fetch<D, G, NCH, KSTEPS>(bn, pid_n, tq_n, pairs, start, len, min(bt + 1, n_batches - 1),
+                                  wave, col, kh, qh, bh, n_tok, topk);
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    const int r = min((wave + NW * c) * kAttnCols + col, n_rows - 1);
-    pid[c] = pid_s[r / G];
-    // pair id = (bh * n_tok + t) * topk + slot
-    tq[c] = int(uint32_t(pid[c]) / uint32_t(topk)) - bh * n_tok;
-    const bf16_t* qrow =
-        q + (((size_t)b * heads_q + (size_t)kvh * G + h) * n_tok + tq[c]) * D + 8 * kh;
+    for (int c = 0; c < NCH; ++c) {
+      const int r0 = bt * kAttnRows + (wave + NW * c) * kAttnCols;
+      if (r0 >= rows) break;
+      const bool live = r0 + col < rows;
+      f32x16_t s0 = {}, s1 = {};
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) bq[c][s] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 16 * s));
-  }
+      for (int s = 0; s < KSTEPS; ++s) {
+        const bf16x8_t a0 = as_bf16x8(*reinterpret_cast<const uint4*>(&ks[col * KROW + 16 * s + 8 * kh]));
+        const bf16x8_t a1 =
+            as_bf16x8(*reinterpret_cast<const uint4*>(&ks[(32 + col) * KROW + 16 * s + 8 * kh]));
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bq[c][s], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bq[c][s], s1, 0, 0, 0);
+      }
+      // Lane holds logits of keys (i/4)*8 + 4kh + i%4 (s0) and 32 + that (s1).
+      int lim = n_keys - 1;
+      if (causal) lim = min(lim, tq[c] - tok0);
+      if (__ballot(lim < C - 1) != 0) {
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    const int r0 = (wave + NW * c) * kAttnCols;
-    if (r0 >= n_rows) break;
-    const bool live = r0 + col < n_rows;
-    f32x16_t s0 = {}, s1 = {};
+        for (int i = 0; i < 16; ++i) {
+          const int r = (i / 4) * 8 + 4 * kh + (i % 4);
+          s0[i] = r <= lim ? s0[i] : neg_inf();
+          s1[i] = r + 32 <= lim ? s1[i] : neg_inf();
+        }
+      }
+      float m = fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s1[0], s1[1]));
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-      const bf16x8_t a0 = as_bf16x8(*reinterpret_cast<const uint4*>(&ks[col * KROW + 16 * s + 8 * kh]));
-      const bf16x8_t a1 =
-          as_bf16x8(*reinterpret_cast<const uint4*>(&ks[(32 + col) * KROW + 16 * s + 8 * kh]));
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bq[c][s], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bq[c][s], s1, 0, 0, 0);
-    }
-    // Lane holds logits of keys (i/4)*8 + 4kh + i%4 (s0) and 32 + that (s1).
-    int lim = n_keys - 1;
-    if (causal) lim = min(lim, tq[c] - tok0);
-    if (__ballot(lim < C - 1) != 0) {
+      for (int i = 2; i < 16; i += 2)
+        m = fmaxf(m, fmaxf(fmaxf(s0[i], s0[i + 1]), fmaxf(s1[i], s1[i + 1])));
+      m = fmaxf(m, __shfl_xor(m, 32, kWave));
+      const float ms = m == neg_inf() ? 0.f : m * scale_log2;  // a column without keys
+      float l = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int r = (i / 4) * 8 + 4 * kh + (i % 4);
-        s0[i] = r <= lim ? s0[i] : neg_inf();
-        s1[i] = r + 32 <= lim ? s1[i] : neg_inf();
+        s0[i] = fast_exp2(fmaf(s0[i], scale_log2, -ms));
+        s1[i] = fast_exp2(fmaf(s1[i], scale_log2, -ms));
+        l += s0[i] + s1[i];
       }
-    }
-    float m = fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s1[0], s1[1]));
+      l += __shfl_xor(l, 32, kWave);
+      // B operands P^T: step st covers keys 32(st/2) + 16(st%2) + 8(j/4) + 4kh + j%4.
+      bf16x8_t pb[4];
 #pragma unroll
-    for (int i = 2; i < 16; i += 2) m = fmaxf(m, fmaxf(fmaxf(s0[i], s0[i + 1]), fmaxf(s1[i], s1[i + 1])));
-    m = fmaxf(m, __shfl_xor(m, 32, kWave));
-    const float ms = m == neg_inf() ? 0.f : m * scale_log2;  // a column without keys
-    float l = 0.f;
+      for (int st = 0; st < 4; ++st)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      s0[i] = fast_exp2(fmaf(s0[i], scale_log2, -ms));
-      s1[i] = fast_exp2(fmaf(s1[i], scale_log2, -ms));
-      l += s0[i] + s1[i];
-    }
-    l += __shfl_xor(l, 32, kWave);
-    // B operands P^T: step st covers keys 32(st/2) + 16(st%2) + 8(j/4) + 4kh + j%4.
-    bf16x8_t pb[4];
+        for (int j = 0; j < 8; ++j) pb[st][j] = (__bf16)(st < 2 ? s0[8 * st + j] : s1[8 * (st - 2) + j]);
+      f32x16_t o[DBLK];
 #pragma unroll
-    for (int st = 0; st < 4; ++st)
+      for (int db = 0; db < DBLK; ++db) {
+        o[db] = f32x16_t{};
 #pragma unroll
-      for (int j = 0; j < 8; ++j) pb[st][j] = (__bf16)(st < 2 ? s0[8 * st + j] : s1[8 * (st - 2) + j]);
-    f32x16_t o[DBLK];
-#pragma unroll
-    for (int db = 0; db < DBLK; ++db) {
-      o[db] = f32x16_t{};
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const bf16_t* vrow = &vt[(32 * db + col) * VROW + 32 * (st / 2) + 16 * (st % 2) + 4 * kh];
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pb[st], o[db], 0, 0, 0);
-      }
-    }
-    // o[db][i] = O[column][d = 32 db + (i/4)*8 + 4kh + i%4]
-    if (live) {
-      const float inv = l > 0.f ? 1.f / l : 0.f;
-      bf16_t* dst = part_o + ((size_t)pid[c] * G + h) * D + 4 * kh;
-#pragma unroll
-      for (int db = 0; db < DBLK; ++db)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
-          bf16x4_t w;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[db][4 * g4 + e] * inv);
-          *reinterpret_cast<uint2*>(dst + 32 * db + 8 * g4) = __builtin_bit_cast(uint2, w);
+        for (int st = 0; st < 4; ++st) {
+          const bf16_t* vrow = &vt[(32 * db + col) * VROW + 32 * (st / 2) + 16 * (st % 2) + 4 * kh];
+          const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pb[st], o[db], 0, 0, 0);
         }
-      if (kh == 0) part_lse[(size_t)pid[c] * G + h] = ms + fast_log2(l);
+      }
+      // o[db][i] = O[column][d = 32 db + (i/4)*8 + 4kh + i%4]
+      // Partials are stored in bucket order (row start * G + r of the
+      // sorted pairs), so a workgroup writes one contiguous range.
+      const size_t prow = (size_t)start * G + r0 + col;
+      if (live) {
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        bf16_t* dst = part_o + prow * D + 4 * kh;
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+            bf16x4_t w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[db][4 * g4 + e] * inv);
+            *reinterpret_cast<uint2*>(dst + 32 * db + 8 * g4) = __builtin_bit_cast(uint2, w);
+          }
+        if (kh == 0) part_lse[prow] = ms + fast_log2(l);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      pid[c] = pid_n[c];
+      tq[c] = tq_n[c];
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) bq[c][s] = bn[c][s];
     }
   }
 }
 
 // Merge the K partials of each (query, head) row: weights exp2(lse_j - M)
-// over the selected blocks, 16 lanes per row.  The row's block ids and LSEs,
-// then up to 16 partials (16-byte loads), are all requested before any is
-// used.  Unused slots (-1) read the row's first partial with weight 0 (slot
-// 0 always holds a selected block).
+// over the selected blocks, 16 lanes per row.  Slot j of row u sits at
+// position pos_of[u * K + j] of the bucket order.  The row's positions and
+// LSEs, then up to 16 partials (16-byte loads), are all requested before any
+// is used.  Unused slots (-1) read the row's first partial with weight 0
+// (slot 0 always holds a selected block).
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(
-    const int32_t* __restrict__ idx, const bf16_t* __restrict__ part_o,
+    const int32_t* __restrict__ idx, const int* __restrict__ pos_of, const bf16_t* __restrict__ part_o,
     const float* __restrict__ part_lse, bf16_t* __restrict__ out, float* __restrict__ lse_out,
     int heads_q, int heads_kv, int n_tok, int topk, int group, int m1, size_t n_rows) {
   constexpr int EPL = D / 16;  // elements per lane (16 lanes per row)
@@ -283,11 +316,14 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
   float M = neg_inf(), W = 0.f;
   for (int j0 = 0; j0 < topk; j0 += B) {
     float lj[B];
+    int pj[B];
 #pragma unroll
     for (int jj = 0; jj < B; ++jj) {
       const int j = j0 + jj;
       const int x = j < topk ? ir[j] : -1;
-      lj[jj] = (x >= 0 && x < m1) ? part_lse[(u * topk + j) * group + h] : neg_inf();
+      const bool ok = x >= 0 && x < m1;
+      pj[jj] = pos_of[u * topk + (ok ? j : 0)];
+      lj[jj] = ok ? part_lse[(size_t)pj[jj] * group + h] : neg_inf();
     }
     float mb = M;
 #pragma unroll
@@ -302,8 +338,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
     uint32_t raw[B][EPL / 2];  // bf16 pairs, unpacked when used
 #pragma unroll
     for (int jj = 0; jj < B; ++jj) {
-      const bool ok = lj[jj] != neg_inf();
-      const bf16_t* src = part_o + ((u * topk + (ok ? j0 + jj : 0)) * group + h) * D + sub * EPL;
+      const bf16_t* src = part_o + ((size_t)pj[jj] * group + h) * D + sub * EPL;
       if (EPL == 8) {
         const uint4 v4 = *reinterpret_cast<const uint4*>(src);
         raw[jj][0] = v4.x; raw[jj][1] = v4.y; raw[jj][2] = v4.z; raw[jj][3] = v4.w;
@@ -354,14 +389,16 @@ hipError_t launch_block_path(const LaunchShape& s, const void* q, const void* k,
   int* cursors = reinterpret_cast<int*>(base + lay.cursors);
   int* item_offsets = reinterpret_cast<int*>(base + lay.item_offsets);
   int* pairs = reinterpret_cast<int*>(base + lay.pairs);
+  int* inv = reinterpret_cast<int*>(base + lay.inv);
   bf16_t* part_o = reinterpret_cast<bf16_t*>(base + lay.part_o);
   float* part_lse = reinterpret_cast<float*>(base + lay.part_lse);
   const int m1 = s.lv.size[0];
   hipError_t e;
   {
     prof::Scope ps("attn_sort", st);
-    e = bucket::sort_pairs(idx, s.batch * s.heads_kv, s.seq_len, s.topk, m1, kAttnRows / s.group,
-                           counts, offsets, cursors, item_offsets, pairs, false, st);
+    e = bucket::sort_pairs(idx, s.batch * s.heads_kv, s.seq_len, s.topk, m1,
+                           kAttnRows / s.group * kAttnBatches, counts, offsets, cursors,
+                           item_offsets, pairs, inv, false, st);
   }
   if (e != hipSuccess) return e;
   {
@@ -387,7 +424,7 @@ hipError_t launch_block_path(const LaunchShape& s, const void* q, const void* k,
   prof::Scope ps("attn_combine", st);
   const size_t rows = (size_t)s.batch * s.heads_kv * s.seq_len * s.group;
   hipLaunchKernelGGL((attn_combine_kernel<D>), dim3((unsigned)((rows * 16 + 255) / 256)),
-                     dim3(256), 0, st, idx, part_o, part_lse, static_cast<bf16_t*>(out), lse,
+                     dim3(256), 0, st, idx, inv, part_o, part_lse, static_cast<bf16_t*>(out), lse,
                      s.heads_q, s.heads_kv, s.seq_len, s.topk, s.group, m1, rows);
   return hipGetLastError();
 }

@@ -12,7 +12,8 @@
 //            bucket); a consumer finds its item's bucket by binary search;
 //   scatter: per workgroup, reserve a range in each touched bucket with one
 //            global atomic, then place pairs with LDS atomics.  Order inside a
-//            bucket is not fixed; consumers must not depend on it.
+//            bucket is not fixed; consumers must not depend on it.  Optionally
+//            the inverse map (pair id -> position) is written as well.
 #pragma once
 
 #include "pisa_common.h"
@@ -91,8 +92,9 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ coun
 
 __global__ __launch_bounds__(256) void scatter_kernel(const int* __restrict__ node,
                                                       int* __restrict__ cursors,
-                                                      int* __restrict__ pairs, int n_tok,
-                                                      int topk, int m) {
+                                                      int* __restrict__ pairs,
+                                                      int* __restrict__ inv, int n_tok, int topk,
+                                                      int m) {
   extern __shared__ int lds[];  // hist/base [m], local cursor [m]
   int* base = lds;
   int* cur = lds + m;
@@ -115,7 +117,11 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int* __restrict__ no
   __syncthreads();
   for (int i = t0 * topk + threadIdx.x; i < t1 * topk; i += blockDim.x) {
     const int x = src[i];
-    if (x >= 0 && x < m) pairs[base[x] + atomicAdd(&cur[x], 1)] = (int)(row0 * topk + i);
+    if (x >= 0 && x < m) {
+      const int pos = base[x] + atomicAdd(&cur[x], 1);
+      pairs[pos] = (int)(row0 * topk + i);
+      if (inv) inv[row0 * topk + i] = pos;
+    }
   }
 }
 
@@ -131,13 +137,15 @@ __global__ void count_global_kernel(const int* __restrict__ node, int* __restric
 }
 
 __global__ void scatter_global_kernel(const int* __restrict__ node, int* __restrict__ cursors,
-                                      int* __restrict__ pairs, int n_tok, int topk, int m,
-                                      size_t n_slots) {
+                                      int* __restrict__ pairs, int* __restrict__ inv, int n_tok,
+                                      int topk, int m, size_t n_slots) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_slots;
        i += (size_t)gridDim.x * blockDim.x) {
     const int x = node[i];
     if (x < 0 || x >= m) continue;
-    pairs[atomicAdd(&cursors[(i / topk / n_tok) * m + x], 1)] = (int)i;
+    const int pos = atomicAdd(&cursors[(i / topk / n_tok) * m + x], 1);
+    pairs[pos] = (int)i;
+    if (inv) inv[i] = pos;
   }
 }
 
@@ -168,10 +176,11 @@ inline unsigned grid_for(size_t n, unsigned threads = 256, unsigned cap = 65536)
 
 // Zero counters, count, scan and scatter the live slots of node[] (one head =
 // n_tok rows of topk slots).  Work items of per_item pairs are located with
-// locate_item.
+// locate_item.  inv (nullable) receives each live pair's position in pairs[].
 inline hipError_t sort_pairs(const int* node, int batch_heads, int n_tok, int topk, int m,
                              int per_item, int* counts, int* offsets, int* cursors,
-                             int* item_offsets, int* pairs, bool counts_ready, hipStream_t st) {
+                             int* item_offsets, int* pairs, int* inv, bool counts_ready,
+                             hipStream_t st) {
   const int n_buckets = batch_heads * m;
   const size_t n_slots = (size_t)batch_heads * n_tok * topk;
   const dim3 grid((n_tok + kRowsPerGroup - 1) / kRowsPerGroup, batch_heads);
@@ -190,10 +199,10 @@ inline hipError_t sort_pairs(const int* node, int batch_heads, int n_tok, int to
                      item_offsets, n_buckets, per_item);
   if (local)
     hipLaunchKernelGGL(scatter_kernel, grid, dim3(256), 2 * sizeof(int) * m, st, node, cursors,
-                       pairs, n_tok, topk, m);
+                       pairs, inv, n_tok, topk, m);
   else
     hipLaunchKernelGGL(scatter_global_kernel, dim3(grid_for(n_slots)), dim3(256), 0, st, node,
-                       cursors, pairs, n_tok, topk, m, n_slots);
+                       cursors, pairs, inv, n_tok, topk, m, n_slots);
   return hipGetLastError();
 }
 

@@ -613,7 +613,8 @@ hipError_t launch_select_two_stage(const LaunchShape& s, const void* q, const vo
     prof::Scope ps("select_sort", st);
     e = bucket::sort_pairs(w.s1_nodes, s.batch * s.heads_kv, s.seq_len, s.topk, m3,
                            kS2Rows / s.group * kS2Batches,
-                           w.counts, w.offsets, w.cursors, w.item_offsets, w.pairs, false, st);
+                           w.counts, w.offsets, w.cursors, w.item_offsets, w.pairs, nullptr,
+                           false, st);
   }
   if (e != hipSuccess) return e;
   {

@@ -6,13 +6,17 @@
 // Scores: s[t, i] = scale * sum over the group's heads of q_h,t . kbar_i
 // (eq. (1) summed over the group's heads).
 // bf16 inputs: the leaf summaries are split once into three bf16 planes
-// (hi + mid + lo carries the fp32 value), and each workgroup computes a tile of
-// 128 queries x 64 leaves as bf16 MFMA 32x32x16 (queries as the A operand, so
-// each output row is a coalesced 128-byte store), skipping tiles entirely
-// above the causal diagonal.  fp32 inputs use the LDS-tiled FMA kernel.
-// Top-K runs one wavefront per query row: the row (<= 4096 scores) is held in
-// registers, 64 lane-local maxima bound the K-th best from below, the few
-// scores at or above that bound are compacted into LDS and ranked exactly.
+// (hi + mid + lo carries the fp32 value).  A workgroup owns 128 queries (32 per
+// wave, held as MFMA A operands in registers) and walks the leaves 32 at a
+// time up to its causal limit; the three planes of each 32-leaf tile are
+// staged in LDS (double-buffered) and shared by the four waves.  Each output
+// row segment is a coalesced 128-byte store.  fp32 inputs use an LDS-tiled
+// FMA kernel.
+// Top-K runs one wavefront per query row (<= 4096 scores held in registers):
+// the K-#F-th largest of the 64 lane maxima (cross-lane bitonic sort) bounds
+// the answer from below, the scores at or above it are compacted into LDS and
+// ranked exactly on 64-bit (score, index) keys, and the kept leaves are put in
+// ascending order by one more cross-lane sort.
 #include <algorithm>
 
 #include "pisa_common.h"
@@ -84,11 +88,12 @@ __global__ __launch_bounds__(256) void bsa_scores_kernel(const T* __restrict__ q
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
 
-__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-constexpr int kMfmaQ = 128;  // queries per workgroup tile (32 per wave)
-constexpr int kMfmaL = 64;   // leaves per workgroup tile
+constexpr int kMfmaQ = 128;  // queries per workgroup (32 per wave)
+constexpr int kMfmaL = 32;   // leaves per tile
 
 // Level-1 summaries of every head -> three bf16 planes x = hi + mid + lo.
 __global__ void bsa_split_kernel(const float* __restrict__ pyr, bf16_t* __restrict__ planes,
@@ -107,67 +112,132 @@ __global__ void bsa_split_kernel(const float* __restrict__ pyr, bf16_t* __restri
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void bsa_scores_mfma_kernel(
+template <int D, int G>
+__global__ __launch_bounds__(256, 2) void bsa_scores_mfma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ planes, float* __restrict__ S,
-    int heads_q, int heads_kv, int n_tok, int block, int group, int m1, int causal, float scale,
+    int heads_q, int heads_kv, int n_tok, int block, int m1, int causal, float scale,
     size_t plane_stride) {
   constexpr int KSTEPS = D / 16;
-  const int bh = blockIdx.z;
-  const int t0 = blockIdx.y * kMfmaQ, i0 = blockIdx.x * kMfmaL;
-  const int t_last = min(t0 + kMfmaQ, n_tok) - 1;
-  if (causal && i0 > t_last / block) return;
+  constexpr int ROW = D + 8;                 // padded LDS row (bf16)
+  constexpr int V16 = D / 8;                 // 16-byte pieces per row
+  constexpr int PIECES = 3 * kMfmaL * V16;   // per tile
+  constexpr int PER_THREAD = (PIECES + 255) / 256;
+  __shared__ __attribute__((aligned(16))) bf16_t bs[2][3][kMfmaL * ROW];
+  const int bh = blockIdx.y;
   const int b = bh / heads_kv, kvh = bh % heads_kv;
-  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int t0 = blockIdx.x * kMfmaQ;
+  const int t_last = min(t0 + kMfmaQ, n_tok) - 1;
+  const int lim_last = causal ? t_last / block : m1 - 1;
+  const int n_tiles = lim_last / kMfmaL + 1;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
   const int col = lane & 31, kh = lane >> 5;
-  const int tq0 = t0 + 32 * wave;  // this wave's 32 queries
-  if (tq0 >= n_tok) return;
-  f32x16_t acc[2] = {};
-  const int tq = min(tq0 + col, n_tok - 1);  // A row (clamped; extra rows are not stored)
+  const int tq0 = t0 + 32 * wave;
+  // A operands: this lane's query row (clamped), all heads of the group.
+  const int tq = min(tq0 + col, n_tok - 1);
+  bf16x8_t a[G][KSTEPS];
 #pragma unroll
-  for (int lb = 0; lb < 2; ++lb) {
-    const int leaf = min(i0 + 32 * lb + col, m1 - 1);  // B column (clamped)
-    const bf16_t* kp = planes + ((size_t)bh * m1 + leaf) * D;
-    for (int h = 0; h < group; ++h) {
-      const bf16_t* qrow = q + (((size_t)b * heads_q + (size_t)kvh * group + h) * n_tok + tq) * D;
+  for (int h = 0; h < G; ++h) {
+    const bf16_t* qr = q + (((size_t)b * heads_q + (size_t)kvh * G + h) * n_tok + tq) * D + 8 * kh;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) a[h][s] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qr + 16 * s));
+  }
+  const bf16_t* pb = planes + (size_t)bh * m1 * D;
+  u32x4_t stage[PER_THREAD];
+  auto fetch = [&](int lt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < PER_THREAD; ++i) {
+      const int x = tid + 256 * i;
+      const int p = x / (kMfmaL * V16), rem = x % (kMfmaL * V16);
+      const int leaf = min(lt * kMfmaL + rem / V16, m1 - 1);
+      stage[i] = x < PIECES ? *reinterpret_cast<const u32x4_t*>(pb + p * plane_stride +
+                                                                (size_t)leaf * D + 8 * (rem % V16))
+                            : u32x4_t{0, 0, 0, 0};
+    }
+  };
+  auto put = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < PER_THREAD; ++i) {
+      const int x = tid + 256 * i;
+      const int p = x / (kMfmaL * V16), rem = x % (kMfmaL * V16);
+      if (x < PIECES)
+        *reinterpret_cast<u32x4_t*>(&bs[buf][p][(rem / V16) * ROW + 8 * (rem % V16)]) = stage[i];
+    }
+  };
+  fetch(0);
+  put(0);
+  __syncthreads();
+  for (int lt = 0; lt < n_tiles; ++lt) {
+    const int buf = lt & 1;
+    if (lt + 1 < n_tiles) fetch(lt + 1);
+    f32x16_t acc = {};
+#pragma unroll
+    for (int p = 2; p >= 0; --p)
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) {
-        const bf16x8_t a = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 16 * s + 8 * kh));
+        const bf16x8_t bb =
+            as_bf16x8(*reinterpret_cast<const u32x4_t*>(&bs[buf][p][col * ROW + 16 * s + 8 * kh]));
 #pragma unroll
-        for (int p = 2; p >= 0; --p) {
-          const bf16x8_t bb = as_bf16x8(
-              *reinterpret_cast<const uint4*>(kp + p * plane_stride + 16 * s + 8 * kh));
-          acc[lb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bb, acc[lb], 0, 0, 0);
-        }
+        for (int h = 0; h < G; ++h)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[h][s], bb, acc, 0, 0, 0);
       }
+    // acc[i] = S[query tq0 + (i/4)*8 + 4kh + i%4][leaf lt*32 + col]
+    const int leaf = lt * kMfmaL + col;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int t = tq0 + (i / 4) * 8 + 4 * kh + (i % 4);
+      const int lim = causal ? t / block : m1 - 1;
+      if (t < n_tok && leaf <= lim && leaf < m1)
+        S[((size_t)bh * n_tok + t) * m1 + leaf] = acc[i] * scale;
     }
-  }
-  // acc[lb][i] = S[query tq0 + (i/4)*8 + kh*4 + i%4][leaf i0 + 32*lb + col]
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int t = tq0 + (i / 4) * 8 + kh * 4 + (i % 4);
-    if (t >= n_tok) continue;
-    const int lim = causal ? t / block : m1 - 1;
-#pragma unroll
-    for (int lb = 0; lb < 2; ++lb) {
-      const int leaf = i0 + 32 * lb + col;
-      if (leaf <= lim && leaf < m1) S[((size_t)bh * n_tok + t) * m1 + leaf] = acc[lb][i] * scale;
+    if (lt + 1 < n_tiles) {
+      put(buf ^ 1);  // the other buffer was last read one tile ago
+      __syncthreads();
     }
   }
 }
 
-__device__ __forceinline__ bool is_forced_leaf(int i, int cur, bool causal, bool force) {
-  return causal && (i == cur || (force && (i == 0 || i == cur - 1)));
+// 64-bit rank key: higher score first, lower index first on equal scores.
+__device__ __forceinline__ uint32_t ord32(float s) {
+  const uint32_t b = __float_as_uint(s);
+  return b ^ (uint32_t(int32_t(b) >> 31) | 0x80000000u);
 }
 
-template <int VPL>
+// Bitonic sort of one value per lane across the wave, descending.
+__device__ __forceinline__ uint32_t wave_sort_desc(uint32_t x) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int k = 2; k <= kWave; k <<= 1)
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const uint32_t y = __shfl_xor(x, j, kWave);
+      const bool desc = (lane & k) == 0 || k == kWave;
+      const bool lower = (lane & j) == 0;
+      x = (desc == lower) ? max(x, y) : min(x, y);
+    }
+  return x;
+}
+__device__ __forceinline__ uint64_t wave_sort_desc64(uint64_t x) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int k = 2; k <= kWave; k <<= 1)
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const uint64_t y = (uint64_t(uint32_t(__shfl_xor(int(x >> 32), j, kWave))) << 32) |
+                         uint32_t(__shfl_xor(int(uint32_t(x)), j, kWave));
+      const bool desc = (lane & k) == 0 || k == kWave;
+      const bool lower = (lane & j) == 0;
+      x = (desc == lower) ? (x > y ? x : y) : (x < y ? x : y);
+    }
+  return x;
+}
+
+template <int VPL>  // scores per lane (row length <= 64 * VPL), VPL % 4 == 0
 __global__ __launch_bounds__(256) void bsa_topk_kernel(const float* __restrict__ S,
                                                        int32_t* __restrict__ idx,
                                                        float* __restrict__ score, int n_tok,
                                                        int block, int m1, int topk, int causal,
                                                        int force) {
-  __shared__ float cs[4][kWave];
-  __shared__ int ci[4][kWave];
+  __shared__ uint64_t cand[4][kWave + 1];  // entry kWave takes non-candidates
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = lane_id();
   const int t = blockIdx.x * 4 + wave;
@@ -186,151 +256,110 @@ __global__ __launch_bounds__(256) void bsa_topk_kernel(const float* __restrict__
     }
     return;
   }
-  int n_forced = 0;
-  if (cz) n_forced = (fz ? (cur >= 2 ? 3 : 2) : 1);
+  // Forced leaves (§5.3): current, and with forcing the first and previous.
+  const int f1 = (cz && fz) ? 0 : -1;
+  const int f2 = (cz && fz && cur >= 2) ? cur - 1 : -1;
+  const int n_forced = cz ? 1 + (fz ? (cur >= 2 ? 2 : 1) : 0) : 0;
   const int keep_n = topk - n_forced;
-  // Row in registers; forced and out-of-range entries become -inf.
+  // Row in registers: element i = 256 r + 4 lane + e (16-byte loads).
   const float* srow = S + row * m1;
-  float v[VPL];
-  float best = neg_inf();
-  int best_i = 0x7fffffff;
+  uint32_t key[VPL];
+  uint32_t lmax = 0;
 #pragma unroll
-  for (int r = 0; r < VPL; ++r) {
-    const int i = r * kWave + lane;
-    v[r] = (i < n_el && !is_forced_leaf(i, cur, cz, fz)) ? srow[i] : neg_inf();
-    if (i < n_el && !is_forced_leaf(i, cur, cz, fz) && ranks_before(v[r], i, best, best_i)) {
-      best = v[r];
-      best_i = i;
+  for (int r = 0; r < VPL / 4; ++r) {
+    const int i0 = 256 * r + 4 * lane;
+    float4 x4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    // (reads up to 3 floats past the row; the workspace has slack for the last row)
+    if (i0 < n_el) x4 = *reinterpret_cast<const float4*>(srow + i0);
+    const float xs[4] = {x4.x, x4.y, x4.z, x4.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = i0 + e;
+      const bool rankable =
+          (i < n_el) & !(cz & ((i == cur) | (i == f1) | (i == f2)));
+      key[4 * r + e] = rankable ? ord32(xs[e]) | 1u : 0u;  // rankable keys are never 0
+      lmax = max(lmax, key[4 * r + e]);
     }
   }
-  // Threshold: the keep_n-th best lane maximum (in the total order score desc,
-  // index asc) ranks no better than the keep_n-th best element of the row.
-  float thr = neg_inf();
-  int thr_i = 0x7fffffff;
-  if (keep_n > 0) {
-    int rank = 0;
-    for (int j = 0; j < kWave; ++j)
-      rank += ranks_before(readlane_f(best, j), readlane_i(best_i, j), best, best_i) ? 1 : 0;
-    const uint64_t hit = ballot(rank == keep_n - 1 && best_i != 0x7fffffff);
-    if (hit) {
-      const int src = __builtin_ctzll(hit);
-      thr = readlane_f(best, src);
-      thr_i = readlane_i(best_i, src);
-    }
-  }
-  // Candidates: entries ranking at or before the threshold.
-  int mine = 0;
-#pragma unroll
-  for (int r = 0; r < VPL; ++r) {
-    const int i = r * kWave + lane;
-    mine += (i < n_el && v[r] != neg_inf() && !ranks_before(thr, thr_i, v[r], i)) ? 1 : 0;
-  }
-  if (keep_n <= 0) mine = 0;
-  int incl = mine;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int y = __shfl_up(incl, o, kWave);
-    if (lane >= o) incl += y;
-  }
-  const int total = __shfl(incl, kWave - 1, kWave);
-  float cand_s = neg_inf();
-  int cand_i = 0x7fffffff;
   bool chosen = false;
-  if (total <= kWave) {
-    int off = incl - mine;
+  uint64_t mine = 0;
+  if (keep_n > 0) {
+    // Lower bound on the keep_n-th best key: the keep_n-th best lane maximum.
+    // (at least 1: unrankable entries have key 0)
+    const uint32_t sorted = wave_sort_desc(lmax);
+    const uint32_t thr = max(1u, uint32_t(__builtin_amdgcn_readlane(sorted, keep_n - 1)));
+    int cnt = 0;
 #pragma unroll
-    for (int r = 0; r < VPL; ++r) {
-      const int i = r * kWave + lane;
-      if (i < n_el && v[r] != neg_inf() && !ranks_before(thr, thr_i, v[r], i) && keep_n > 0) {
-        cs[wave][off] = v[r];
-        ci[wave][off] = i;
-        ++off;
-      }
+    for (int r = 0; r < VPL; ++r) cnt += key[r] >= thr ? 1 : 0;
+    int incl = cnt;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int y = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += y;
     }
-    wave_lds_sync();
-    if (lane < total) {
-      cand_s = cs[wave][lane];
-      cand_i = ci[wave][lane];
-    }
-    wave_lds_sync();
-    int rank = 0;
-    for (int j = 0; j < total; ++j)
-      rank += ranks_before(readlane_f(cand_s, j), readlane_i(cand_i, j), cand_s, cand_i) ? 1 : 0;
-    chosen = lane < total && rank < keep_n;
-  } else {
-    // Rare: many candidates.  Extract the keep_n best one at a time.
-    for (int k = 0; k < keep_n; ++k) {
-      float bs = neg_inf();
-      int bi = 0x7fffffff;
+    const int total = __shfl(incl, kWave - 1, kWave);
+    if (total <= kWave) {
+      int off = incl - cnt;
 #pragma unroll
       for (int r = 0; r < VPL; ++r) {
-        const int i = r * kWave + lane;
-        if (v[r] != neg_inf() && ranks_before(v[r], i, bs, bi)) {
-          bs = v[r];
-          bi = i;
+        const int i = 256 * (r / 4) + 4 * lane + (r % 4);
+        const bool c = key[r] >= thr;
+        cand[wave][c ? off : kWave] = (uint64_t(key[r]) << 32) | uint32_t(0xffffffffu - uint32_t(i));
+        off += c ? 1 : 0;
+      }
+      wave_lds_sync();
+      const uint64_t ck = lane < total ? cand[wave][lane] : 0ull;
+      wave_lds_sync();
+      const uint64_t srt = wave_sort_desc64(ck);
+      chosen = lane < keep_n;
+      mine = srt;
+    } else {
+      // Rare: many scores at the bound.  Extract the keep_n best one at a time
+      // (largest key, then the lowest index holding it).
+      for (int kk = 0; kk < keep_n; ++kk) {
+        uint32_t best = 0;
+#pragma unroll
+        for (int r = 0; r < VPL; ++r) best = max(best, key[r]);
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) best = max(best, uint32_t(__shfl_xor(int(best), o, kWave)));
+        int bi = 0x7fffffff;
+#pragma unroll
+        for (int r = 0; r < VPL; ++r)
+          bi = key[r] == best ? min(bi, 256 * (r / 4) + 4 * lane + (r % 4)) : bi;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) bi = min(bi, __shfl_xor(bi, o, kWave));
+#pragma unroll
+        for (int r = 0; r < VPL; ++r)
+          key[r] = 256 * (r / 4) + 4 * lane + (r % 4) == bi ? 0u : key[r];
+        if (lane == kk) {
+          chosen = true;
+          mine = (uint64_t(best) << 32) | uint32_t(0xffffffffu - uint32_t(bi));
         }
       }
-      float ws = bs;
-      int wi = bi;
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        const float os = __shfl_xor(ws, o, kWave);
-        const int oi = __shfl_xor(wi, o, kWave);
-        if (ranks_before(os, oi, ws, wi)) {
-          ws = os;
-          wi = oi;
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < VPL; ++r)
-        if (r * kWave + lane == wi) v[r] = neg_inf();
-      if (lane == k) {
-        cand_s = ws;
-        cand_i = wi;
-        chosen = true;
-      }
     }
   }
-  // Final list: chosen candidates compacted first, then the forced leaves
-  // (unranked, +inf); each lane then places its entry in ascending order.
-  const uint64_t chm = ballot(chosen);
-  const int n_ch = __popcll(chm);
-  if (chosen) {
-    cs[wave][lanes_below(chm)] = cand_s;
-    ci[wave][lanes_below(chm)] = cand_i;
+  // Kept leaves: chosen candidates in lanes < keep_n, forced leaves appended,
+  // then ascending order by one more sort (key = ~index puts small first).
+  int node = chosen ? int(0xffffffffu - uint32_t(mine)) : -1;
+  if (cz) {
+    if (lane == keep_n) node = cur;
+    if (fz && lane == keep_n + 1 && cur >= 1) node = 0;
+    if (fz && lane == keep_n + 2 && cur >= 2) node = cur - 1;
   }
-  if (cz && lane == 0) {
-    int f = n_ch;
-    ci[wave][f] = cur;
-    cs[wave][f++] = pos_inf();
-    if (fz && cur >= 1) {
-      ci[wave][f] = 0;
-      cs[wave][f++] = pos_inf();
+  const uint32_t o_sorted = wave_sort_desc(node >= 0 ? 0xffffffffu - uint32_t(node) : 0u);
+  const int out = o_sorted ? int(0xffffffffu - o_sorted) : -1;
+  if (lane < topk) {
+    idx_row[lane] = out;
+    if (score_row) {
+      const bool forced = cz & ((out == cur) | (out == f1) | (out == f2));
+      score_row[lane] = out < 0 ? neg_inf() : (forced ? pos_inf() : srow[out]);
     }
-    if (fz && cur >= 2) {
-      ci[wave][f] = cur - 1;
-      cs[wave][f++] = pos_inf();
-    }
-  }
-  wave_lds_sync();
-  const int nk = n_ch + n_forced;
-  const bool keep = lane < nk;
-  const int node = keep ? ci[wave][lane] : 0x7fffffff;
-  const float sc = keep ? cs[wave][lane] : neg_inf();
-  int pos = 0;
-  for (int j = 0; j < nk; ++j) pos += readlane_i(node, j) < node ? 1 : 0;
-  if (keep) {
-    idx_row[pos] = node;
-    if (score_row) score_row[pos] = sc;
-  }
-  if (lane >= nk && lane < topk) {
-    idx_row[lane] = -1;
-    if (score_row) score_row[lane] = neg_inf();
   }
 }
 
+// Score matrix plus 16 bytes of slack for the Top-K pass's 16-byte row reads.
 static size_t scores_bytes(const LaunchShape& s) {
-  return ((size_t)s.batch * s.heads_kv * s.seq_len * s.lv.size[0] * sizeof(float) + 255) &
+  return ((size_t)s.batch * s.heads_kv * s.seq_len * s.lv.size[0] * sizeof(float) + 16 + 255) &
          ~size_t(255);
 }
 
@@ -364,7 +393,7 @@ static hipError_t launch_bsa_topk_t(const LaunchShape& s, const float* S, int32_
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, int G>
 static hipError_t launch_bsa_mfma_t(const LaunchShape& s, const void* q, const float* pyr,
                                     float* S, bf16_t* planes, hipStream_t st) {
   const int m1 = s.lv.size[0];
@@ -374,30 +403,45 @@ static hipError_t launch_bsa_mfma_t(const LaunchShape& s, const void* q, const f
     hipLaunchKernelGGL(bsa_split_kernel, dim3((unsigned)std::min<size_t>(65536, (n + 255) / 256)),
                        dim3(256), 0, st, pyr, planes, s.lv.rows, m1, D, n);
   }
-  dim3 grid((m1 + kMfmaL - 1) / kMfmaL, (s.seq_len + kMfmaQ - 1) / kMfmaQ, s.batch * s.heads_kv);
+  dim3 grid((s.seq_len + kMfmaQ - 1) / kMfmaQ, s.batch * s.heads_kv);
   prof::Scope ps("bsa_scores", st);
-  hipLaunchKernelGGL((bsa_scores_mfma_kernel<D>), grid, dim3(256), 0, st,
+  hipLaunchKernelGGL((bsa_scores_mfma_kernel<D, G>), grid, dim3(256), 0, st,
                      static_cast<const bf16_t*>(q), planes, S, s.heads_q, s.heads_kv, s.seq_len,
-                     s.block, s.group, m1, s.causal ? 1 : 0, s.scale, n);
+                     s.block, m1, s.causal ? 1 : 0, s.scale, n);
   return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_bsa_mfma_d(const LaunchShape& s, const void* q, const float* pyr,
+                                    float* S, bf16_t* planes, hipStream_t st) {
+  switch (s.group) {
+    case 1: return launch_bsa_mfma_t<D, 1>(s, q, pyr, S, planes, st);
+    case 2: return launch_bsa_mfma_t<D, 2>(s, q, pyr, S, planes, st);
+    default: return launch_bsa_mfma_t<D, 4>(s, q, pyr, S, planes, st);
+  }
 }
 
 hipError_t launch_bsa(const LaunchShape& s, const void* q, const float* pyr, int32_t* idx,
                       float* score, void* ws, hipStream_t st) {
   float* S = static_cast<float*>(ws);
   hipError_t e;
-  if (s.bf16) {
+  // MFMA scores for bf16 with a group of 1, 2 or 4 query heads; else fp32 FMA tiles.
+  if (s.bf16 && (s.group == 1 || s.group == 2 || s.group == 4)) {
     bf16_t* planes = reinterpret_cast<bf16_t*>(static_cast<char*>(ws) + scores_bytes(s));
-    e = s.head_dim == 128 ? launch_bsa_mfma_t<128>(s, q, pyr, S, planes, st)
-                          : launch_bsa_mfma_t<64>(s, q, pyr, S, planes, st);
-  } else
+    e = s.head_dim == 128 ? launch_bsa_mfma_d<128>(s, q, pyr, S, planes, st)
+                          : launch_bsa_mfma_d<64>(s, q, pyr, S, planes, st);
+  } else if (s.bf16) {
+    e = s.head_dim == 128 ? launch_bsa_scores_t<bf16_t, 128>(s, q, pyr, S, st)
+                          : launch_bsa_scores_t<bf16_t, 64>(s, q, pyr, S, st);
+  } else {
     e = s.head_dim == 128 ? launch_bsa_scores_t<float, 128>(s, q, pyr, S, st)
                           : launch_bsa_scores_t<float, 64>(s, q, pyr, S, st);
+  }
   if (e != hipSuccess) return e;
   const int m1 = s.lv.size[0];
-  if (m1 <= 1 * kWave) return launch_bsa_topk_t<1>(s, S, idx, score, st);
   if (m1 <= 4 * kWave) return launch_bsa_topk_t<4>(s, S, idx, score, st);
   if (m1 <= 16 * kWave) return launch_bsa_topk_t<16>(s, S, idx, score, st);
+  if (m1 <= 32 * kWave) return launch_bsa_topk_t<32>(s, S, idx, score, st);
   return launch_bsa_topk_t<kBsaMaxLeaves / kWave>(s, S, idx, score, st);
 }
 

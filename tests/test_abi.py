@@ -123,8 +123,9 @@ def test_null_pointers_and_workspace_rejected():
     # BSA always needs its score workspace
     sz = ctypes.c_size_t()
     assert L.pisa_workspace_bytes(pp, _lib.PISA_OP_BSA, ctypes.byref(sz)) == 0
-    # fp32 scores for every (query, leaf) + three bf16 planes of the leaf summaries
-    assert sz.value == 1 * 4 * 4096 * 64 * 4 + 3 * 1 * 4 * 64 * 128 * 2
+    # fp32 scores for every (query, leaf) (+ slack for 16-byte row reads) + three
+    # bf16 planes of the leaf summaries
+    assert sz.value == 1 * 4 * 4096 * 64 * 4 + 256 + 3 * 1 * 4 * 64 * 128 * 2
     assert L.pisa_bsa_select(pp, ptr, ptr, ptr, None, ptr, sz.value - 1, None) == _lib.PISA_ERR_WORKSPACE
     assert L.pisa_bsa_select(pp, ptr, ptr, ptr, None, None, sz.value, None) == _lib.PISA_ERR_WORKSPACE
     assert L.pisa_block_sparse_attn(pp, ptr, ptr, None, ptr, ptr, None, None, 0, None) == _lib.PISA_ERR_INVALID

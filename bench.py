@@ -10,7 +10,7 @@ selection-latency comparison with the GPU BSA baseline across N (crossover),
 the roofline of the dominant kernel (HIP events on the launch stream) and the
 CPU oracle timed on a bounded sample of the same workload (cpu_baseline).
 
-Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--no-sweep] [--no-cpu]
+Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--no-sweep] [--no-cpu] [--no-decode]
                        [--cpu-seconds 15] [--calibrate-copy-mb 0]
 """
 from __future__ import annotations
@@ -74,6 +74,34 @@ def descent_counts(n, c, k, force=True):
                 kept = cand
             if lvl > 1:
                 cand = 2 * kept
+    return out
+
+
+def descent_row_counts(n, c, k, t, force=True):
+    """descent_counts for the single query row t: {level: dot products}."""
+    sizes = level_sizes(n, c)
+    L = len(sizes)
+    out = {}
+    cur = t // c
+    cand = 1
+    for lvl in range(L, 0, -1):
+        sh = lvl - 1
+        lim = cur >> sh
+        cand = min(cand, lim + 1)
+        forced = {lim}
+        if force:
+            forced |= {0}
+            if cur >= 1:
+                forced |= {(cur - 1) >> sh}
+        if cand > k:
+            ranked = cand - len(forced)
+            out[lvl] = 2 * ranked if lvl >= 2 else c * ranked
+            kept = k
+        else:
+            out[lvl] = 0
+            kept = cand
+        if lvl > 1:
+            cand = 2 * kept
     return out
 
 
@@ -262,11 +290,61 @@ def run(args):
         "roofline": roof,
     }
 
+    if not args.no_decode:
+        result["decode"] = decode_bench(args)
     if not args.no_sweep:
         result["selection_sweep"] = selection_sweep(args)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(args, inp, prob)
     return result
+
+
+def decode_bench(args):
+    """Per-step latency of the GQA decode step: 32 sequences with 131072 cached
+    tokens each, 32 query heads over 8 KV heads, d=128, K=16, bf16, pyramid of
+    the cache prebuilt; one step = selection + attention for every sequence."""
+    import torch
+
+    import hierarchical_block_selection_amd as pisa
+    from hierarchical_block_selection_amd.inputs import WORKLOADS, decode_inputs
+
+    cfg = WORKLOADS["c5"]
+    dev = torch.device("cuda:0")
+    prob = pisa.Problem(cfg["batch"], cfg["heads_q"], cfg["heads_kv"], cfg["seq_len"],
+                        cfg["head_dim"], block=cfg["block"], topk=cfg["topk"], dtype=cfg["dtype"])
+    inp = decode_inputs(prob.batch, prob.heads_q, prob.heads_kv, prob.seq_len, prob.head_dim,
+                        prob.dtype, seed=cfg["seed"], device=dev)
+    pyr = pisa.pisa_build_pyramid(prob, inp.k_cache)
+    idx = torch.empty((prob.batch, prob.heads_kv, prob.topk), dtype=torch.int32, device=dev)
+    out = torch.empty_like(inp.q)
+    ws_n = pisa.pisa_workspace_bytes(prob, "decode")
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
+
+    def step():
+        pisa.pisa_decode_step(prob, inp.cache_len, inp.q, inp.k_cache, inp.v_cache, pyr, idx,
+                              None, out, None, workspace=ws if ws_n else None)
+
+    ms = timed_call(step, 20, 3)
+    # compulsory bytes per step: the level summaries the descent scores, the
+    # raw keys of the scored leaves and the K/V rows of the kept leaves
+    summaries = 0
+    t = prob.seq_len - 1
+    cnt = descent_row_counts(prob.seq_len, prob.block, prob.topk, t)
+    for lvl, dots in cnt.items():
+        if lvl >= 2:
+            summaries += dots  # child summaries read (fp32)
+    leaf_keys = cnt.get(1, 0)  # raw keys scored
+    attn_keys = int(attended_keys(prob.seq_len, prob.block, prob.topk)[t])
+    units = prob.batch * prob.heads_kv
+    bytes_step = units * (summaries * prob.head_dim * 4 + leaf_keys * prob.head_dim * 2 +
+                          2 * attn_keys * prob.head_dim * 2)
+    del inp, pyr
+    torch.cuda.empty_cache()
+    return {"ms_per_step": ms, "tokens_per_s": prob.batch / (ms * 1e-3),
+            "compulsory_mb": bytes_step / 1e6,
+            "achieved_gbs": bytes_step / (ms * 1e-3) / 1e9,
+            "workload": "decode B=32 cache=131072 Hq=32 Hkv=8 d=128 C=64 K=16 bf16, "
+                        "pyramid prebuilt"}
 
 
 def selection_sweep(args):
@@ -360,6 +438,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="launch one elementwise copy of this many MiB before the steps "

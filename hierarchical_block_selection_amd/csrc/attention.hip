@@ -117,8 +117,9 @@ AttnWs attn_layout(const LaunchShape& s) {
 //   O^T = V_blk^T P^T (MFMA A = V^T from LDS, B = P straight from the S
 //                      accumulators; the key order inside this reduction is
 //                      permuted to match the accumulator layout)
-// Each lane then holds 16 output dims of its own column: it scales them by
-// 1/l and stores them as four 8-byte runs, plus the column's log2-sum-exp.
+// Each lane then holds 16 output dims of its own column and scales them by
+// 1/l; the chunk's rows (contiguous in bucket order) pass through an LDS tile
+// and leave as 1 KB store instructions, with each column's log2-sum-exp.
 template <int D, int G, int NCH, int KSTEPS>
 __device__ __forceinline__ void attn_fetch(bf16x8_t (&bq)[NCH][KSTEPS], int (&pid)[NCH],
                                            int (&tq)[NCH], const int* __restrict__ pairs,
@@ -157,6 +158,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_partial_kernel(
   constexpr int NCH = kAttnRows / kAttnCols / NW;  // chunks per wave and batch
   __shared__ __attribute__((aligned(16))) bf16_t ks[C * KROW];
   __shared__ __attribute__((aligned(16))) bf16_t vt[D * VROW];
+  constexpr int OROW = D + 8;  // padded output tile row (bf16)
+  __shared__ __attribute__((aligned(16))) bf16_t os[NW][kAttnCols * OROW];
   int bucket, start, len;
   if (!bucket::locate_item(item_offsets, offsets, n_buckets, blockIdx.x, PAIRS * kAttnBatches,
                            &bucket, &start, &len))
@@ -258,25 +261,36 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_partial_kernel(
               as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pb[st], o[db], 0, 0, 0);
         }
       }
-      // o[db][i] = O[column][d = 32 db + (i/4)*8 + 4kh + i%4]
-      // Partials are stored in bucket order (row start * G + r of the
-      // sorted pairs), so a workgroup writes one contiguous range.
-      const size_t prow = (size_t)start * G + r0 + col;
-      if (live) {
-        const float inv = l > 0.f ? 1.f / l : 0.f;
-        bf16_t* dst = part_o + prow * D + 4 * kh;
+      // o[db][i] = O[column][d = 32 db + (i/4)*8 + 4kh + i%4].  Partials are
+      // stored in bucket order (row start * G + r of the sorted pairs): the
+      // chunk's 32 rows are one contiguous run, written through an LDS tile
+      // as 16-byte pieces, 1 KB per store instruction.
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      bf16_t* tile = &os[wave][0];
 #pragma unroll
-        for (int db = 0; db < DBLK; ++db)
+      for (int db = 0; db < DBLK; ++db)
 #pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
-            bf16x4_t w;
+        for (int g4 = 0; g4 < 4; ++g4) {
+          typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+          bf16x4_t w;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[db][4 * g4 + e] * inv);
-            *reinterpret_cast<uint2*>(dst + 32 * db + 8 * g4) = __builtin_bit_cast(uint2, w);
-          }
-        if (kh == 0) part_lse[prow] = ms + fast_log2(l);
+          for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[db][4 * g4 + e] * inv);
+          *reinterpret_cast<uint2*>(&tile[col * OROW + 32 * db + 8 * g4 + 4 * kh]) =
+              __builtin_bit_cast(uint2, w);
+        }
+      if (live && kh == 0) part_lse[(size_t)start * G + r0 + col] = ms + fast_log2(l);
+      wave_lds_sync();
+      const int n_live = min(kAttnCols, rows - r0);  // rows of this chunk that exist
+      bf16_t* dst = part_o + ((size_t)start * G + r0) * D;
+      constexpr int PIECES = kAttnCols * D / 8;  // 16-byte pieces of the chunk
+#pragma unroll
+      for (int x = lane; x < PIECES; x += kWave) {
+        const int rr = x / (D / 8), c8 = (x % (D / 8)) * 8;
+        if (rr < n_live)
+          *reinterpret_cast<uint4*>(dst + (size_t)rr * D + c8) =
+              *reinterpret_cast<const uint4*>(&tile[rr * OROW + c8]);
       }
+      wave_lds_sync();
     }
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {

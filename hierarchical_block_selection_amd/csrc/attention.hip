@@ -81,10 +81,10 @@ struct AttnWs {
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 bool block_path(const LaunchShape& s) {
-  // (query, slot) pair ids are int32
-  const int64_t slots = (int64_t)s.batch * s.heads_kv * s.seq_len * s.topk;
+  // pairs are stored as (row << 5) | slot in an int32; slot ids index int32 maps
+  const int64_t rows = (int64_t)s.batch * s.heads_kv * s.seq_len;
   return s.bf16 && s.block == kAttnBlock && (s.head_dim == 64 || s.head_dim == 128) &&
-         (s.group & (s.group - 1)) == 0 && s.group <= kMaxGroup && slots < INT32_MAX;
+         (s.group & (s.group - 1)) == 0 && s.group <= kMaxGroup && rows < (int64_t(1) << 26);
 }
 
 AttnWs attn_layout(const LaunchShape& s) {
@@ -133,8 +133,7 @@ __device__ __forceinline__ void attn_fetch(bf16x8_t (&bq)[NCH][KSTEPS], int (&pi
   for (int c = 0; c < NCH; ++c) {
     const int r = min(bt * kAttnRows + (wave + NW * c) * kAttnCols + col, rows - 1);
     pid[c] = pairs[start + r / G];
-    // pair id = (bh * n_tok + t) * topk + slot
-    tq[c] = int(uint32_t(pid[c]) / uint32_t(topk)) - bh * n_tok;
+    tq[c] = (pid[c] >> 5) - bh * n_tok;  // pair = (row << 5) | slot
     const bf16_t* qrow = qh + ((size_t)h * n_tok + tq[c]) * D + 8 * kh;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) bq[c][s] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 16 * s));

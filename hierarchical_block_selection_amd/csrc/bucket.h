@@ -3,7 +3,8 @@
 //
 // Input: node[u * K + slot] in [0, m) for live pairs (anything else is
 // skipped), where row u belongs to head bh = u / n_tok; the pair's bucket is
-// bh * m + node.  A few buckets are very hot (the forced first block is in
+// bh * m + node.  A pair is stored as (u << 5) | slot (K <= 32; callers keep
+// u below 2^26).  A few buckets are very hot (the forced first block is in
 // every row), so counting and scattering aggregate per workgroup in LDS and
 // touch global counters once per (workgroup, bucket):
 //   count:   grid (row chunks, heads); LDS histogram, then global adds;
@@ -119,7 +120,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int* __restrict__ no
     const int x = src[i];
     if (x >= 0 && x < m) {
       const int pos = base[x] + atomicAdd(&cur[x], 1);
-      pairs[pos] = (int)(row0 * topk + i);
+      pairs[pos] = (int)(((row0 + i / topk) << 5) | (i % topk));
       if (inv) inv[row0 * topk + i] = pos;
     }
   }
@@ -144,7 +145,7 @@ __global__ void scatter_global_kernel(const int* __restrict__ node, int* __restr
     const int x = node[i];
     if (x < 0 || x >= m) continue;
     const int pos = atomicAdd(&cursors[(i / topk / n_tok) * m + x], 1);
-    pairs[pos] = (int)i;
+    pairs[pos] = (int)(((i / topk) << 5) | (i % topk));
     if (inv) inv[i] = pos;
   }
 }

@@ -15,7 +15,7 @@
 //             K <= 16: one lane per query (select_lpq.h); K <= 32: one
 //             wavefront per (b, kv head, t) (stage1_kernel below).
 //   scan      one workgroup: bucket offsets and the stage-2 work list.
-//   scatter   pair ids (u*K + slot) into per-node buckets.
+//   scatter   pairs (row << 5 | slot) into per-node buckets.
 //   stage 2   one workgroup per (node, <= 256 pairs): the node's keys in LDS,
 //             bf16 MFMA 32x32x16 (keys x queries), per-leaf LSE and mean.
 //   final     level-2 and leaf decisions from the stage-2 scores, ascending
@@ -25,6 +25,7 @@
 // computed by the same instruction sequence whatever its position, so the
 // outputs are bitwise reproducible.
 #include <algorithm>
+#include <type_traits>
 
 #include "bucket.h"
 #include "pisa_common.h"
@@ -294,8 +295,7 @@ __device__ __forceinline__ void stage2_fetch(u32x4_t (&stage)[PER_THREAD], int& 
     const int x = tid + i * kS2Threads;
     const int r = x / V16, c = x % V16;
     const int pid = pairs[start + min(base + r / G, last)];
-    // pair id = (bh * n_tok + t) * topk + slot
-    const int t = int(uint32_t(pid) / uint32_t(topk)) - bh * n_tok;
+    const int t = (pid >> 5) - bh * n_tok;  // pair = (row << 5) | slot
     stage[i] = *reinterpret_cast<const u32x4_t*>(qh + ((size_t)(r % G) * n_tok + t) * D + 8 * c);
   }
 }
@@ -361,92 +361,96 @@ __global__ __launch_bounds__(kS2Threads, 2) void stage2_kernel(
   const float inv_keys = n_keys > 0 ? 1.f / float(n_keys) : 0.f;
   const int n_batches = (len + PAIRS - 1) / PAIRS;
 
-  for (int bt = 0; bt < n_batches; ++bt) {
-    const int blen = min(PAIRS, len - bt * PAIRS);  // pairs in this batch
-    __syncthreads();  // the previous batch's readers of qs, xs and pid_s are done
-    if (tid < PAIRS) pid_s[tid] = pid_reg;
+  // The batch loop, compiled twice: for a leaf with all C keys (no masking)
+  // and for the sequence's last, partial leaf.  Waves of one workgroup may
+  // run different copies; both pass the same barriers in the same order.
+  auto run = [&](auto full_tag) __attribute__((always_inline)) {
+    constexpr bool kFull = decltype(full_tag)::value;
+    for (int bt = 0; bt < n_batches; ++bt) {
+      const int blen = min(PAIRS, len - bt * PAIRS);  // pairs in this batch
+      __syncthreads();  // the previous batch's readers of qs, xs and pid_s are done
+      if (tid < PAIRS) pid_s[tid] = pid_reg;
 #pragma unroll
-    for (int i = 0; i < PER_THREAD; ++i) {
-      const int x = tid + i * kS2Threads;
-      *reinterpret_cast<u32x4_t*>(&qs[(x / V16) * QROW + 8 * (x % V16)]) = stage[i];
-    }
-    __syncthreads();
-    // next batch in flight while this one computes (the last batch fetches itself again)
-    stage2_fetch<D, G, PER_THREAD>(stage, pid_reg, pairs, start, len, min(bt + 1, n_batches - 1),
-                                   qh, bh, n_tok, topk);
-
-    const int n_chunks = (blen * G + 31) / 32;
-    for (int ch = 0; ch < n_chunks; ++ch) {
-      const bf16_t* qr = &qs[(32 * ch + col) * QROW + 8 * kh];
-      f32x16_t acc0 = {}, acc1 = {};
-#pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) {
-        const bf16x8_t bq = as_bf16x8(*reinterpret_cast<const uint4*>(qr + 16 * s));
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0][s], bq, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[1][s], bq, acc1, 0, 0, 0);
+      for (int i = 0; i < PER_THREAD; ++i) {
+        const int x = tid + i * kS2Threads;
+        *reinterpret_cast<u32x4_t*>(&qs[(x / V16) * QROW + 8 * (x % V16)]) = stage[i];
       }
-      // Lane holds the logits of keys (i/4)*8 + 4kh + i%4 (acc0) and 32 + that (acc1).
-      float m, sraw = 0.f, se = 0.f;
-      if (n_keys == LEAF) {
-        m = fmaxf(fmaxf(acc0[0], acc0[1]), fmaxf(acc1[0], acc1[1]));
+      __syncthreads();
+      // next batch in flight while this one computes (the last batch fetches itself again)
+      stage2_fetch<D, G, PER_THREAD>(stage, pid_reg, pairs, start, len,
+                                     min(bt + 1, n_batches - 1), qh, bh, n_tok, topk);
+
+      const int n_chunks = (blen * G + 31) / 32;
+      for (int ch = 0; ch < n_chunks; ++ch) {
+        const bf16_t* qr = &qs[(32 * ch + col) * QROW + 8 * kh];
+        f32x16_t acc0 = {}, acc1 = {};
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) {
+          const bf16x8_t bq = as_bf16x8(*reinterpret_cast<const uint4*>(qr + 16 * s));
+          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0][s], bq, acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[1][s], bq, acc1, 0, 0, 0);
+        }
+        // Lane holds the logits of keys (i/4)*8 + 4kh + i%4 (acc0) and 32 + that (acc1).
+        float sraw = 0.f, se = 0.f;
+        if constexpr (!kFull) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int r = (i / 4) * 8 + 4 * kh + (i % 4);
+            sraw += (r < n_keys ? acc0[i] : 0.f) + (r + 32 < n_keys ? acc1[i] : 0.f);
+            acc0[i] = r < n_keys ? acc0[i] : neg_inf();
+            acc1[i] = r + 32 < n_keys ? acc1[i] : neg_inf();
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sraw += acc0[i] + acc1[i];
+        }
+        float m = fmaxf(fmaxf(acc0[0], acc0[1]), fmaxf(acc1[0], acc1[1]));
 #pragma unroll
         for (int i = 2; i < 16; i += 2)
           m = fmaxf(m, fmaxf(fmaxf(acc0[i], acc0[i + 1]), fmaxf(acc1[i], acc1[i + 1])));
         m = fmaxf(m, __shfl_xor(m, 32, kWave));
-        const float ms = m * scale_log2;
+        const float ms = (kFull || n_keys > 0) ? m * scale_log2 : 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          sraw += acc0[i] + acc1[i];
+        for (int i = 0; i < 16; ++i)
           se += fast_exp2(fmaf(acc0[i], scale_log2, -ms)) + fast_exp2(fmaf(acc1[i], scale_log2, -ms));
-        }
-      } else {
-        m = neg_inf();
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = (i / 4) * 8 + 4 * kh + (i % 4);
-          acc0[i] = r < n_keys ? acc0[i] : neg_inf();
-          acc1[i] = r + 32 < n_keys ? acc1[i] : neg_inf();
-          m = fmaxf(m, fmaxf(acc0[i], acc1[i]));
-        }
-        m = fmaxf(m, __shfl_xor(m, 32, kWave));
-        const float ms = n_keys > 0 ? m * scale_log2 : 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = (i / 4) * 8 + 4 * kh + (i % 4);
-          sraw += (r < n_keys ? acc0[i] : 0.f) + (r + 32 < n_keys ? acc1[i] : 0.f);
-          se += fast_exp2(fmaf(acc0[i], scale_log2, -ms)) + fast_exp2(fmaf(acc1[i], scale_log2, -ms));
+        se += __shfl_xor(se, 32, kWave);
+        sraw += __shfl_xor(sraw, 32, kWave);
+        if (kh == 0) {
+          const bool has = kFull || n_keys > 0;
+          xs[wave][0][32 * ch + col] = has ? fmaf(m, scale_log2, fast_log2(se)) : neg_inf();
+          xs[wave][1][32 * ch + col] = has ? sraw * inv_keys * scale_log2 : neg_inf();
         }
       }
-      se += __shfl_xor(se, 32, kWave);
-      sraw += __shfl_xor(sraw, 32, kWave);
-      if (kh == 0) {
-        xs[wave][0][32 * ch + col] = n_keys > 0 ? fmaf(m, scale_log2, fast_log2(se)) : neg_inf();
-        xs[wave][1][32 * ch + col] = n_keys > 0 ? sraw * inv_keys * scale_log2 : neg_inf();
-      }
-    }
-    __syncthreads();
+      __syncthreads();
 
-    // One pair per thread.
-    if (tid < blen) {
-      float o[6] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      // One pair per thread.
+      if (tid < blen) {
+        float o[6] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        const int r = tid * G + hh;
+        for (int hh = 0; hh < G; ++hh) {
+          const int r = tid * G + hh;
 #pragma unroll
-        for (int f = 0; f < 4; ++f) o[f] += xs[f][0][r];
+          for (int f = 0; f < 4; ++f) o[f] += xs[f][0][r];
 #pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-          const float a = xs[2 * c2][1][r], bb = xs[2 * c2 + 1][1][r];
-          const float mx = fmaxf(a, bb), mn = fminf(a, bb);
-          // a missing leaf has mean -inf and drops out
-          o[4 + c2] += mn == neg_inf() ? mx : mx + fast_log2(1.f + fast_exp2(mn - mx));
+          for (int c2 = 0; c2 < 2; ++c2) {
+            const float a = xs[2 * c2][1][r], bb = xs[2 * c2 + 1][1][r];
+            const float mx = fmaxf(a, bb), mn = fminf(a, bb);
+            // a missing leaf has mean -inf and drops out
+            o[4 + c2] += mn == neg_inf() ? mx : mx + fast_log2(1.f + fast_exp2(mn - mx));
+          }
         }
+        const int pid = pid_s[tid];  // (row << 5) | slot
+        float* dst = scores + ((size_t)(pid >> 5) * topk + (pid & 31)) * kScoreStride;
+        *reinterpret_cast<float4*>(dst) =
+            make_float4(o[0] * kLn2, o[1] * kLn2, o[2] * kLn2, o[3] * kLn2);
+        *reinterpret_cast<float4*>(dst + 4) = make_float4(o[4] * kLn2, o[5] * kLn2, 0.f, 0.f);
       }
-      float* dst = scores + (size_t)pid_s[tid] * kScoreStride;
-      *reinterpret_cast<float4*>(dst) = make_float4(o[0] * kLn2, o[1] * kLn2, o[2] * kLn2, o[3] * kLn2);
-      *reinterpret_cast<float4*>(dst + 4) = make_float4(o[4] * kLn2, o[5] * kLn2, 0.f, 0.f);
     }
-  }
+  };
+  if (n_keys == LEAF)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
 }
 
 // ---------------------------------------------------------------------------
@@ -576,10 +580,11 @@ hipError_t stage1_lpq_launch(const LaunchShape& s, const void* q, const float* p
 
 bool select_two_stage_supported(const LaunchShape& s) {
   const bool pow2_group = (s.group & (s.group - 1)) == 0;
-  const int64_t slots = (int64_t)s.batch * s.heads_kv * s.seq_len * s.topk;  // int32 pair ids
+  // pairs are stored as (row << 5) | slot in an int32
+  const int64_t rows = (int64_t)s.batch * s.heads_kv * s.seq_len;
   return s.bf16 && s.block == 64 && (s.head_dim == 64 || s.head_dim == 128) &&
          s.lv.n >= kSplitLevel + 1 && pow2_group && s.group <= 4 && s.topk <= 32 &&
-         slots < INT32_MAX;
+         rows < (int64_t(1) << 26);
 }
 
 size_t select_two_stage_ws_bytes(const LaunchShape& s) {

@@ -416,7 +416,7 @@ def cpu_baseline(args, inp, prob):
         budget = args.cpu_seconds
         done = 0
         t_rows = 0.0
-        while t_rows < budget and done < 4096:
+        while t_rows < budget and done < 65536:
             t = int(rng.integers(K * C, N))
             t1 = time.perf_counter()
             sel = oracle.select_pisa_row(qh[:, t], keys, levels, t, C, K, True, True)

@@ -25,6 +25,7 @@
 // computed by the same instruction sequence whatever its position, so the
 // outputs are bitwise reproducible.
 #include <algorithm>
+#include <cfloat>
 #include <type_traits>
 
 #include "bucket.h"
@@ -404,21 +405,34 @@ __global__ __launch_bounds__(kS2Threads, 2) void stage2_kernel(
 #pragma unroll
           for (int i = 0; i < 16; ++i) sraw += acc0[i] + acc1[i];
         }
-        float m = fmaxf(fmaxf(acc0[0], acc0[1]), fmaxf(acc1[0], acc1[1]));
-#pragma unroll
-        for (int i = 2; i < 16; i += 2)
-          m = fmaxf(m, fmaxf(fmaxf(acc0[i], acc0[i + 1]), fmaxf(acc1[i], acc1[i + 1])));
-        m = fmaxf(m, __shfl_xor(m, 32, kWave));
-        const float ms = (kFull || n_keys > 0) ? m * scale_log2 : 0.f;
+        // The exps are taken relative to the mean logit, which the level-2
+        // scores need anyway: the sum is >= 1 (some logit is >= the mean) and
+        // only overflows when a logit exceeds the mean by ~128 (log2 units);
+        // then the wave redoes the column relative to its maximum.
+        sraw += __shfl_xor(sraw, 32, kWave);
+        const float mean = sraw * inv_keys * scale_log2;
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          se += fast_exp2(fmaf(acc0[i], scale_log2, -ms)) + fast_exp2(fmaf(acc1[i], scale_log2, -ms));
+          se += fast_exp2(fmaf(acc0[i], scale_log2, -mean)) + fast_exp2(fmaf(acc1[i], scale_log2, -mean));
         se += __shfl_xor(se, 32, kWave);
-        sraw += __shfl_xor(sraw, 32, kWave);
+        float ref = mean;
+        if (__ballot(!(se <= FLT_MAX)) != 0) {
+          float m = fmaxf(fmaxf(acc0[0], acc0[1]), fmaxf(acc1[0], acc1[1]));
+#pragma unroll
+          for (int i = 2; i < 16; i += 2)
+            m = fmaxf(m, fmaxf(fmaxf(acc0[i], acc0[i + 1]), fmaxf(acc1[i], acc1[i + 1])));
+          m = fmaxf(m, __shfl_xor(m, 32, kWave));
+          ref = (kFull || n_keys > 0) ? m * scale_log2 : 0.f;
+          se = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            se += fast_exp2(fmaf(acc0[i], scale_log2, -ref)) + fast_exp2(fmaf(acc1[i], scale_log2, -ref));
+          se += __shfl_xor(se, 32, kWave);
+        }
         if (kh == 0) {
           const bool has = kFull || n_keys > 0;
-          xs[wave][0][32 * ch + col] = has ? fmaf(m, scale_log2, fast_log2(se)) : neg_inf();
-          xs[wave][1][32 * ch + col] = has ? sraw * inv_keys * scale_log2 : neg_inf();
+          xs[wave][0][32 * ch + col] = has ? ref + fast_log2(se) : neg_inf();
+          xs[wave][1][32 * ch + col] = has ? mean : neg_inf();
         }
       }
       __syncthreads();

@@ -70,6 +70,7 @@ constexpr int kAttnCols = 32;
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
@@ -286,8 +287,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_partial_kernel(
       for (int x = lane; x < PIECES; x += kWave) {
         const int rr = x / (D / 8), c8 = (x % (D / 8)) * 8;
         if (rr < n_live)
-          *reinterpret_cast<uint4*>(dst + (size_t)rr * D + c8) =
-              *reinterpret_cast<const uint4*>(&tile[rr * OROW + c8]);
+          // streamed out: read once, by the combine
+          __builtin_nontemporal_store(*reinterpret_cast<const u32x4_t*>(&tile[rr * OROW + c8]),
+                                      reinterpret_cast<u32x4_t*>(dst + (size_t)rr * D + c8));
       }
       wave_lds_sync();
     }
@@ -305,8 +307,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_partial_kernel(
 // over the selected blocks, 16 lanes per row.  Slot j of row u sits at
 // position pos_of[u * K + j] of the bucket order.  The row's positions and
 // LSEs, then up to 16 partials (16-byte loads), are all requested before any
-// is used.  Unused slots (-1) read the row's first partial with weight 0
-// (slot 0 always holds a selected block).
+// is used.  Slots that are -1 or out of range have no position (rows need
+// not be sorted, so slot 0 may be one of them): they read position 0, which
+// is always inside the partial buffers, with weight 0.
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(
     const int32_t* __restrict__ idx, const int* __restrict__ pos_of, const bf16_t* __restrict__ part_o,
@@ -332,11 +335,14 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
     int pj[B];
 #pragma unroll
     for (int jj = 0; jj < B; ++jj) {
-      const int j = j0 + jj;
-      const int x = j < topk ? ir[j] : -1;
-      const bool ok = x >= 0 && x < m1;
-      pj[jj] = pos_of[u * topk + (ok ? j : 0)];
-      lj[jj] = ok ? part_lse[(size_t)pj[jj] * group + h] : neg_inf();
+      const int j = min(j0 + jj, topk - 1);
+      const int x = ir[j];
+      const bool ok = j0 + jj < topk && x >= 0 && x < m1;
+      // a slot that is not live was never given a position: use position 0
+      const int p = pos_of[u * topk + j];
+      pj[jj] = ok ? p : 0;
+      const float lv = part_lse[(size_t)pj[jj] * group + h];
+      lj[jj] = ok ? lv : neg_inf();
     }
     float mb = M;
 #pragma unroll
@@ -353,7 +359,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
     for (int jj = 0; jj < B; ++jj) {
       const bf16_t* src = part_o + ((size_t)pj[jj] * group + h) * D + sub * EPL;
       if (EPL == 8) {
-        const uint4 v4 = *reinterpret_cast<const uint4*>(src);
+        const u32x4_t v4 = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src));
         raw[jj][0] = v4.x; raw[jj][1] = v4.y; raw[jj][2] = v4.z; raw[jj][3] = v4.w;
       } else {
         const uint2 v2 = *reinterpret_cast<const uint2*>(src);

@@ -181,9 +181,13 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void stage1_kernel(
 
   const int wave = threadIdx.x / kWave;
   const int lane = lane_id();
-  const int bh = blockIdx.y;
+  // A causal query's dense work grows with t: workgroups are dispatched in
+  // linear order, so the latest positions of every head go first.
+  const unsigned lin = blockIdx.x + blockIdx.y * gridDim.x;
+  const int bh = (int)(lin % gridDim.y);
+  const int bx = (int)(gridDim.x - 1 - lin / gridDim.y);
   const int b = bh / heads_kv, kvh = bh % heads_kv;
-  const int t0 = (blockIdx.x * kWaves + wave) * T;
+  const int t0 = (bx * kWaves + wave) * T;
   if (t0 >= n_tok) return;
   const bool cz = causal != 0, fzon = force != 0;
   const size_t head_rows = (size_t)bh * lv.rows;

@@ -157,7 +157,8 @@ int pisa_bsa_select(const pisa_problem* problem, const void* q, const float* pyr
  *   q, k, v:   as above
  *   block_idx: [B, Hkv, N, K] int32 leaf indices; rows need not be sorted;
  *              entries < 0 or >= ceil(N/C) are skipped; duplicates are
- *              not allowed (they would be counted twice)
+ *              not allowed (they would be counted twice); a row whose blocks
+ *              hold no attendable token gets zeros and row_lse = -inf
  *   out:       [B, Hq, N, d] dtype, out
  *   row_lse:   [B, Hq, N] float32, out, may be NULL
  *   ws/ws_bytes: pisa_workspace_bytes(PISA_OP_ATTN) bytes */

@@ -308,3 +308,87 @@ def test_decode_equals_prefill_row():
         assert torch.equal(dscore[b], score[b, :, n - 1])
         assert torch.equal(dout[b], out[b, :, n - 1])
         assert torch.equal(dlse[b], lse[b, :, n - 1])
+
+
+ARB = [
+    # (N, d, K, Hq, Hkv, causal)
+    (5000, 128, 16, 1, 1, True),
+    (4133, 64, 8, 4, 2, True),
+    (3000, 128, 12, 2, 1, False),
+    (2500, 128, 16, 16, 1, True),
+    (700, 128, 5, 8, 1, True),
+]
+
+
+def arbitrary_block_lists(n, hkv, k, causal, seed):
+    """Caller-made lists: unsorted rows mixing the always-attended blocks
+    (0, c - 1, c) with others, -1 and out-of-range entries, future blocks and
+    empty rows."""
+    rng = np.random.default_rng(seed)
+    m1 = -(-n // 64)
+    idx = np.full((1, hkv, n, k), -1, np.int32)
+    for h in range(hkv):
+        for t in range(n):
+            c = t // 64
+            hi = c if causal else m1 - 1
+            kind = rng.integers(0, 10)
+            if kind < 4:  # the forced blocks plus random others
+                base = sorted({0, max(c - 1, 0), c})
+                rest = [x for x in rng.permutation(hi + 1)[:k] if x not in base]
+                row = (base + rest)[:k]
+            elif kind < 7:  # random subset, forced blocks only by chance
+                row = list(rng.permutation(hi + 1)[:rng.integers(1, k + 1)])
+            elif kind < 9:  # random subset with junk and (causal) future blocks
+                row = list(rng.permutation(hi + 1)[:rng.integers(1, k)])
+                junk = [-1, -7, m1, m1 + 5] + ([min(c + 1 + int(rng.integers(0, 3)), m1 - 1)]
+                                              if causal and c + 1 < m1 else [])
+                row = (row + [int(x) for x in rng.choice(junk, size=k - len(row))])[:k]
+                vals = [x for x in row if 0 <= x < m1]
+                if len(vals) != len(set(vals)):  # keep valid entries distinct
+                    seen, dedup = set(), []
+                    for x in row:
+                        if 0 <= x < m1 and x in seen:
+                            x = -1
+                        seen.add(x)
+                        dedup.append(x)
+                    row = dedup
+            else:  # nothing attendable
+                row = [-1] * (k - 1) + [m1]
+            row = [int(x) for x in rng.permutation(np.array(row + [-1] * (k - len(row))))]
+            idx[0, h, t] = row
+    return idx
+
+
+@pytest.mark.parametrize("case", ARB, ids=[f"N{c[0]}_d{c[1]}_K{c[2]}_G{c[3]//c[4]}_"
+                                           f"{'causal' if c[5] else 'full'}" for c in ARB])
+def test_attention_arbitrary_block_lists(case):
+    """bf16 block attention (C = 64) on block lists made by the caller."""
+    n, d, k, hq, hkv, causal = case
+    prob = Problem(1, hq, hkv, n, d, block=64, topk=k, dtype=torch.bfloat16, causal=causal,
+                   force_first_prev=causal)
+    announce(f"arbitrary lists {case}")
+    inp = prefill_inputs(1, hq, hkv, n, d, torch.bfloat16, seed=500 + n, recipe="unit",
+                         device=DEV)
+    idx_np = arbitrary_block_lists(n, hkv, k, causal, seed=n)
+    idx = torch.from_numpy(idx_np).to(DEV)
+    out, lse = pisa_block_sparse_attn(prob, inp.q, inp.k, inp.v, idx)
+    torch.cuda.synchronize()
+    g = hq // hkv
+    m1 = -(-n // 64)
+    rows = list(range(0, n, 2)) + [n - 1]
+    for h in range(hkv):
+        keys, vals = parity.to_np(inp.k[0, h]), parity.to_np(inp.v[0, h])
+        qg = parity.to_np(inp.q[0, h * g:(h + 1) * g])
+        o = parity.to_np(out[0, h * g:(h + 1) * g])
+        ls = lse[0, h * g:(h + 1) * g].cpu().numpy()
+        full, empty = [], []
+        for t in rows:
+            leaves = [int(x) for x in idx_np[0, h, t] if 0 <= x < m1]
+            live = [x for x in leaves if not causal or x * 64 <= t]
+            (full if live else empty).append(t)
+        for t in empty:
+            assert np.all(o[:, t] == 0.0) and np.all(np.isneginf(ls[:, t])), t
+        sub = np.where(idx_np[0, h] >= m1, -1, idx_np[0, h])
+        parity.compare_attention(o, ls, qg, keys, vals, sub, full, 64, causal,
+                                 prob.logit_scale, fp32=False)
+        assert len(empty) > 0 and len(full) > len(rows) // 2

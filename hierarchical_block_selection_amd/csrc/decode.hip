@@ -67,7 +67,7 @@ __global__ __launch_bounds__(kWave) void decode_kernel(
 
 namespace {
 
-constexpr int kDecThreads = 256;
+constexpr int kDecThreads = 512;
 constexpr int kDecWaves = kDecThreads / kWave;
 constexpr int kDecMaxK = 16;  // 2K candidates fit one 32-lane half-wave
 
@@ -134,7 +134,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_wg_kernel(
     float scale_log2, LevelTable lv) {
   constexpr int C = 64;
   constexpr int KSTEPS = D / 16;
-  constexpr int DP = D / 4;           // dims per thread in the child-summary dots
+  constexpr int TPR = kDecThreads / 64;  // threads per child row (64 rows)
+  constexpr int DP = D / TPR;             // dims per thread in the child-summary dots
   constexpr int DL = D / kWave;       // output dims per lane in P V
   __shared__ float q_s[G][D];
   __shared__ float z_s[64][G];
@@ -195,8 +196,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_wg_kernel(
     }
     const int m_child = lv.size[l - 2];
     if (n_valid > topk) {
-      // child row r = tid / 4 of candidate r / 2; 4 threads per row
-      const int r = tid >> 2, part = tid & 3;
+      // child row r of candidate r / 2; TPR threads per row
+      const int r = tid / TPR, part = tid % TPR;
       const int j = r >> 1;
       const int cnode = 2 * kept_s[min(j >> 1, kDecMaxK)] + (j & 1);
       const int crow = 2 * cnode + (r & 1);
@@ -217,8 +218,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_wg_kernel(
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float v = acc[h];
-        v += __shfl_xor(v, 1, kWave);
-        v += __shfl_xor(v, 2, kWave);
+#pragma unroll
+        for (int o = 1; o < TPR; o <<= 1) v += __shfl_xor(v, o, kWave);
         if (part == 0) z_s[r][h] = live ? v * scale_log2 : neg_inf();
       }
     }
@@ -259,41 +260,60 @@ __global__ __launch_bounds__(kDecThreads) void decode_wg_kernel(
   }
   const bool ranked = n_valid > topk;
   if (ranked) {
-    for (int jj = 0; jj < 32 / kDecWaves; ++jj) {
-      const int j = wave * (32 / kDecWaves) + jj;
-      if (j >= n_valid) break;
-      const int leaf = 2 * kept_s[j >> 1] + (j & 1);
-      f32x16_t acc[2] = {};
+    // Wave w scores candidates w * PER .. ; the raw keys of two candidates are
+    // requested together (a candidate past the list loads a valid leaf and
+    // its result is dropped).
+    constexpr int PER = 32 / kDecWaves;
+    const int last_leaf = 2 * kept_s[(n_valid - 1) >> 1] + ((n_valid - 1) & 1);
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const int tok = min(leaf * C + 32 * rb + col, capacity - 1);
-        const bf16_t* kr = kb + (size_t)tok * D + 8 * kh;
+    for (int jj = 0; jj < PER; jj += 2) {
+      uint4 kr[2][2][KSTEPS];
+      int leaf2[2];
 #pragma unroll
-        for (int s = 0; s < KSTEPS; ++s)
-          acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              as_bf16x8(*reinterpret_cast<const uint4*>(kr + 16 * s)), bq[s], acc[rb], 0, 0, 0);
-      }
-      // lane: head col, keys (i/4)*8 + 4kh + i%4 (+32 in acc[1])
-      float m = neg_inf();
+      for (int u = 0; u < 2; ++u) {
+        const int j = wave * PER + jj + u;
+        leaf2[u] = j < n_valid ? 2 * kept_s[j >> 1] + (j & 1) : last_leaf;
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
+        for (int rb = 0; rb < 2; ++rb) {
+          const int tok = min(leaf2[u] * C + 32 * rb + col, capacity - 1);
+          const bf16_t* kp = kb + (size_t)tok * D + 8 * kh;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int tok = leaf * C + 32 * rb + (i / 4) * 8 + 4 * kh + (i % 4);
-          acc[rb][i] = tok <= t ? acc[rb][i] * scale_log2 : neg_inf();
-          m = fmaxf(m, acc[rb][i]);
+          for (int s2 = 0; s2 < KSTEPS; ++s2) kr[u][rb][s2] = *reinterpret_cast<const uint4*>(kp + 16 * s2);
         }
-      m = fmaxf(m, __shfl_xor(m, 32, kWave));
-      float se = 0.f;
+      }
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
+      for (int u = 0; u < 2; ++u) {
+        const int j = wave * PER + jj + u;
+        const int leaf = leaf2[u];
+        f32x16_t acc[2] = {};
 #pragma unroll
-        for (int i = 0; i < 16; ++i) se += fast_exp2(acc[rb][i] - m);
-      se += __shfl_xor(se, 32, kWave);
-      float v = col < G ? m + fast_log2(se) : 0.f;
+        for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-      for (int o = 1; o < 32; o <<= 1) v += __shfl_xor(v, o, kWave);
-      if (lane == 0) leaf_s[j] = v;
+          for (int s2 = 0; s2 < KSTEPS; ++s2)
+            acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kr[u][rb][s2]), bq[s2],
+                                                              acc[rb], 0, 0, 0);
+        // lane: head col, keys (i/4)*8 + 4kh + i%4 (+32 in acc[1])
+        float m = neg_inf();
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int tok = leaf * C + 32 * rb + (i / 4) * 8 + 4 * kh + (i % 4);
+            acc[rb][i] = tok <= t ? acc[rb][i] * scale_log2 : neg_inf();
+            m = fmaxf(m, acc[rb][i]);
+          }
+        m = fmaxf(m, __shfl_xor(m, 32, kWave));
+        float se = 0.f;
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) se += fast_exp2(acc[rb][i] - m);
+        se += __shfl_xor(se, 32, kWave);
+        float v = col < G ? m + fast_log2(se) : 0.f;
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) v += __shfl_xor(v, o, kWave);
+        if (lane == 0 && j < n_valid) leaf_s[j] = v;
+      }
     }
   }
   __syncthreads();
@@ -377,16 +397,27 @@ __global__ __launch_bounds__(kDecThreads) void decode_wg_kernel(
 #pragma unroll
       for (int e = 0; e < DL; ++e) o[h][e] *= alpha;
     }
+    // All C value rows are requested at once; rows after t (probability 0)
+    // repeat row t, which is inside the cache.
     const bf16_t* vr = vb + (size_t)leaf * C * D + lane * DL;
-    const int rows = min(C, t - leaf * C + 1);
-    for (int r = 0; r < rows; ++r) {
+    const int last = t - leaf * C;  // >= 0: a kept leaf is never in the future
+    uint32_t vw[C];
+#pragma unroll
+    for (int r = 0; r < C; ++r) {
+      const int rr = min(r, last);
+      if constexpr (DL == 2)
+        vw[r] = *reinterpret_cast<const uint32_t*>(vr + (size_t)rr * D);
+      else
+        vw[r] = uint32_t(vr[(size_t)rr * D]) << 16;
+    }
+#pragma unroll
+    for (int r = 0; r < C; ++r) {
       float vv[DL];
-      if (DL == 2) {
-        const uint32_t w2 = *reinterpret_cast<const uint32_t*>(vr + (size_t)r * D);
-        vv[0] = __uint_as_float(w2 << 16);
-        vv[DL - 1] = __uint_as_float(w2 & 0xffff0000u);
+      if constexpr (DL == 2) {
+        vv[0] = __uint_as_float(vw[r] << 16);
+        vv[1] = __uint_as_float(vw[r] & 0xffff0000u);
       } else {
-        vv[0] = bf16_to_f32(vr[(size_t)r * D]);
+        vv[0] = __uint_as_float(vw[r]);
       }
 #pragma unroll
       for (int h = 0; h < G; ++h) {

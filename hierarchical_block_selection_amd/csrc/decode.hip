@@ -142,9 +142,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_wg_kernel(
   __shared__ float leaf_s[32];
   __shared__ int kept_s[kDecMaxK + 1];
   __shared__ int nk_s;
-  __shared__ float p_s[kDecWaves][C][G];
+  __shared__ float lg_s[32][C][G];  // candidate logits (log2 units), later probabilities
+  __shared__ float cm_s[32][G];      // candidate max logit per head
+  __shared__ int kept_j_s[kDecMaxK];
   __shared__ float po_s[kDecWaves][G][D];
-  __shared__ float pm_s[kDecWaves][G], pl_s[kDecWaves][G];
+  __shared__ float pl_s[kDecWaves][G];
+  __shared__ float mh_s[G];
   const int bh = blockIdx.x;
   const int b = bh / heads_kv, kvh = bh % heads_kv;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
@@ -259,10 +262,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_wg_kernel(
     n_valid += int(c <= cur) + int(c + 1 <= cur);
   }
   const bool ranked = n_valid > topk;
-  if (ranked) {
+  {
     // Wave w scores candidates w * PER .. ; the raw keys of two candidates are
     // requested together (a candidate past the list loads a valid leaf and
-    // its result is dropped).
+    // its result is dropped).  The logits stay in LDS for the attention.
     constexpr int PER = 32 / kDecWaves;
     const int last_leaf = 2 * kept_s[(n_valid - 1) >> 1] + ((n_valid - 1) & 1);
 #pragma unroll
@@ -303,6 +306,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_wg_kernel(
             m = fmaxf(m, acc[rb][i]);
           }
         m = fmaxf(m, __shfl_xor(m, 32, kWave));
+        if (col < G && j < n_valid) {
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              lg_s[j][32 * rb + (i / 4) * 8 + 4 * kh + (i % 4)][col] = acc[rb][i];
+          if (kh == 0) cm_s[j][col] = m;
+        }
         float se = 0.f;
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
@@ -330,6 +341,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_wg_kernel(
     wave_lds_sync();
     if (k && pos < kDecMaxK) {
       kept_s[pos] = leaf;
+      kept_j_s[pos] = j;
       idx_row[pos] = leaf;
       if (score_row) score_row[pos] = (ranked && !forced) ? sc * kLn2 : pos_inf();
     }
@@ -341,120 +353,96 @@ __global__ __launch_bounds__(kDecThreads) void decode_wg_kernel(
   }
   __syncthreads();
 
-  // Attention over the kept leaves: wave w takes kept leaves w, w + 4, ...
+  // Attention over the kept leaves, from the logits kept in LDS: one shared
+  // maximum per head, so the waves' partial sums add without rescaling.
+  // Wave w takes kept leaves w, w + kDecWaves; their value rows are all
+  // requested before use.
   const int nsel = nk_s;
-  float mh[G], lh[G], o[G][DL];
+  float Mh[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    mh[h] = neg_inf();
-    lh[h] = 0.f;
+    Mh[h] = neg_inf();
+    for (int i = 0; i < nsel; ++i) Mh[h] = fmaxf(Mh[h], cm_s[kept_j_s[i]][h]);
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+    if (tid == h) mh_s[h] = Mh[h];
+  float lsum[G], o[G][DL];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    lsum[h] = 0.f;
 #pragma unroll
     for (int e = 0; e < DL; ++e) o[h][e] = 0.f;
   }
-  for (int i = wave; i < nsel; i += kDecWaves) {
+  constexpr int PERW = (kDecMaxK + kDecWaves - 1) / kDecWaves;
+  uint32_t vw[PERW][C];
+#pragma unroll
+  for (int u = 0; u < PERW; ++u) {
+    const int i = min(wave + u * kDecWaves, nsel - 1);
     const int leaf = kept_s[i];
-    f32x16_t acc[2] = {};
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const int tok = min(leaf * C + 32 * rb + col, capacity - 1);
-      const bf16_t* kr = kb + (size_t)tok * D + 8 * kh;
-#pragma unroll
-      for (int s = 0; s < KSTEPS; ++s)
-        acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            as_bf16x8(*reinterpret_cast<const uint4*>(kr + 16 * s)), bq[s], acc[rb], 0, 0, 0);
-    }
-    float m = neg_inf();
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int tok = leaf * C + 32 * rb + (e / 4) * 8 + 4 * kh + (e % 4);
-        acc[rb][e] = tok <= t ? acc[rb][e] * scale_log2 : neg_inf();
-        m = fmaxf(m, acc[rb][e]);
-      }
-    m = fmaxf(m, __shfl_xor(m, 32, kWave));
-    // per head: new max, rescale, probabilities to LDS
-    float mnew = fmaxf(m, col < G ? mh[0] : neg_inf());
-#pragma unroll
-    for (int h = 1; h < G; ++h) mnew = col == h ? fmaxf(m, mh[h]) : mnew;
-    float psum = 0.f;
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float pv = fast_exp2(acc[rb][e] - mnew);
-        psum += pv;
-        if (col < G) p_s[wave][32 * rb + (e / 4) * 8 + 4 * kh + (e % 4)][col] = pv;
-      }
-    psum += __shfl_xor(psum, 32, kWave);
-    wave_lds_sync();
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float mn = __shfl(mnew, h, kWave);
-      const float alpha = fast_exp2(mh[h] - mn);
-      lh[h] = lh[h] * alpha + __shfl(psum, h, kWave);
-      mh[h] = mn;
-#pragma unroll
-      for (int e = 0; e < DL; ++e) o[h][e] *= alpha;
-    }
-    // All C value rows are requested at once; rows after t (probability 0)
-    // repeat row t, which is inside the cache.
-    const bf16_t* vr = vb + (size_t)leaf * C * D + lane * DL;
+    // rows after t (probability 0) repeat row t, which is inside the cache
     const int last = t - leaf * C;  // >= 0: a kept leaf is never in the future
-    uint32_t vw[C];
+    const bf16_t* vr = vb + (size_t)leaf * C * D + lane * DL;
 #pragma unroll
     for (int r = 0; r < C; ++r) {
       const int rr = min(r, last);
       if constexpr (DL == 2)
-        vw[r] = *reinterpret_cast<const uint32_t*>(vr + (size_t)rr * D);
+        vw[u][r] = *reinterpret_cast<const uint32_t*>(vr + (size_t)rr * D);
       else
-        vw[r] = uint32_t(vr[(size_t)rr * D]) << 16;
+        vw[u][r] = uint32_t(vr[(size_t)rr * D]) << 16;
     }
+  }
+#pragma unroll
+  for (int u = 0; u < PERW; ++u) {
+    const int i = wave + u * kDecWaves;
+    if (i >= nsel) break;
+    const int j = kept_j_s[i];
+    // probabilities in place: lane = key, every head
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float pv = fast_exp2(lg_s[j][lane][h] - Mh[h]);
+      lg_s[j][lane][h] = pv;
+      lsum[h] += pv;
+    }
+    wave_lds_sync();
 #pragma unroll
     for (int r = 0; r < C; ++r) {
       float vv[DL];
       if constexpr (DL == 2) {
-        vv[0] = __uint_as_float(vw[r] << 16);
-        vv[1] = __uint_as_float(vw[r] & 0xffff0000u);
+        vv[0] = __uint_as_float(vw[u][r] << 16);
+        vv[1] = __uint_as_float(vw[u][r] & 0xffff0000u);
       } else {
-        vv[0] = __uint_as_float(vw[r]);
+        vv[0] = __uint_as_float(vw[u][r]);
       }
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float pr = p_s[wave][r][h];
+        const float pr = lg_s[j][r][h];
 #pragma unroll
         for (int e = 0; e < DL; ++e) o[h][e] += pr * vv[e];
       }
     }
-    wave_lds_sync();
   }
-  // Merge the waves' partial results.
+  // Merge the waves' partial sums.
 #pragma unroll
   for (int h = 0; h < G; ++h) {
+    float v = lsum[h];
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) v += __shfl_xor(v, off, kWave);
 #pragma unroll
     for (int e = 0; e < DL; ++e) po_s[wave][h][lane * DL + e] = o[h][e];
-    if (lane == 0) {
-      pm_s[wave][h] = mh[h];
-      pl_s[wave][h] = lh[h];
-    }
+    if (lane == 0) pl_s[wave][h] = v;
   }
   __syncthreads();
   for (int x = tid; x < G * D; x += kDecThreads) {
     const int h = x / D, d = x % D;
-    float M = neg_inf();
-#pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, pm_s[w][h]);
     float L = 0.f, O = 0.f;
-    if (M != neg_inf()) {
 #pragma unroll
-      for (int w = 0; w < kDecWaves; ++w) {
-        const float a = fast_exp2(pm_s[w][h] - M);
-        L += a * pl_s[w][h];
-        O += a * po_s[w][h][d];
-      }
+    for (int w = 0; w < kDecWaves; ++w) {
+      L += pl_s[w][h];
+      O += po_s[w][h][d];
     }
     out[(head0 + h) * D + d] = f32_to_bf16(L > 0.f ? O / L : 0.f);
-    if (lse && d == 0) lse[head0 + h] = L > 0.f ? (M + fast_log2(L)) * kLn2 : neg_inf();
+    if (lse && d == 0) lse[head0 + h] = L > 0.f ? (mh_s[h] + fast_log2(L)) * kLn2 : neg_inf();
   }
 }
 

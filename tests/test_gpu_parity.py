@@ -244,9 +244,11 @@ def decode_compare(prob, inp, pyr, pairs, fp32=False, min_compared=None):
         keys = parity.to_np(inp.k_cache[b, h, :n])
         vals = parity.to_np(inp.v_cache[b, h, :n])
         qg = parity.to_np(inp.q[b, h * g:(h + 1) * g])
-        sel, ref, ref_lse = oracle.decode_row(qg, keys, vals, n, prob.block, prob.topk)
+        force = prob.force_first_prev
+        sel, ref, ref_lse = oracle.decode_row(qg, keys, vals, n, prob.block, prob.topk,
+                                              force_first_prev=force)
         got = [int(x) for x in idx[b, h].cpu()]
-        parity.check_structure(got, n - 1, prob.block, prob.topk, -(-n // prob.block), True, True)
+        parity.check_structure(got, n - 1, prob.block, prob.topk, -(-n // prob.block), True, force)
         tally.rows += 1
         if sel.min_margin > parity.MARGIN:
             tally.compared += 1
@@ -285,6 +287,33 @@ def test_decode_unit_variant_ragged_lengths():
                         cache_len=[1, 63, 3001, 8192], device=DEV)
     pyr = pisa_build_pyramid(prob, inp.k_cache)
     decode_compare(prob, inp, pyr, [(b, h) for b in range(4) for h in range(2)], min_compared=0.5)
+
+
+DECODE_SHAPES = [
+    # (B, Hq, Hkv, capacity, d, K, force, cache lengths)
+    (3, 8, 1, 8192, 128, 16, True, [1, 4000, 8192]),
+    (2, 2, 2, 8192, 64, 8, False, [700, 8192]),
+    (2, 4, 2, 6000, 128, 5, True, [65, 6000]),
+    (2, 4, 4, 16384, 128, 16, True, [16384, 9999]),
+    (2, 8, 2, 4096, 64, 16, True, [4096, 130]),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_SHAPES, ids=[f"B{c[0]}_G{c[1]//c[2]}_d{c[4]}_K{c[5]}"
+                                                     f"{'_force' if c[6] else ''}"
+                                                     for c in DECODE_SHAPES])
+def test_decode_group_sizes(case):
+    """The bf16 workgroup decode for every group size it serves (1, 2, 4, 8),
+    d = 64 and 128, budgets below 16 and with and without first/previous
+    forcing, on ragged cache lengths."""
+    bsz, hq, hkv, cap, d, k, force, lens = case
+    prob = Problem(bsz, hq, hkv, cap, d, block=64, topk=k, dtype=torch.bfloat16,
+                   force_first_prev=force)
+    announce(f"decode {case}")
+    inp = decode_inputs(bsz, hq, hkv, cap, d, torch.bfloat16, seed=41 + cap, recipe="unit",
+                        cache_len=lens, device=DEV)
+    pyr = pisa_build_pyramid(prob, inp.k_cache)
+    decode_compare(prob, inp, pyr, [(b, h) for b in range(bsz) for h in range(hkv)])
 
 
 def test_decode_equals_prefill_row():

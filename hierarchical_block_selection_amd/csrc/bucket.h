@@ -24,6 +24,7 @@ namespace bucket {
 
 constexpr int kRowsPerGroup = 512;    // rows of one head per count/scatter workgroup
 constexpr int kMaxLocalBuckets = 8192;  // LDS histogram limit (two int arrays = 64 KB)
+constexpr int kBatch = 16;  // slots per thread whose loads are issued together
 
 namespace {  // each translation unit keeps its own copy of these kernels
 
@@ -40,9 +41,14 @@ __global__ __launch_bounds__(256) void count_kernel(const int* __restrict__ node
   const int bh = blockIdx.y;
   const int t0 = blockIdx.x * kRowsPerGroup, t1 = min(t0 + kRowsPerGroup, n_tok);
   const int* src = node + ((size_t)bh * n_tok) * topk;
-  for (int i = t0 * topk + threadIdx.x; i < t1 * topk; i += blockDim.x) {
-    const int x = src[i];
-    if (x >= 0 && x < m) atomicAdd(&hist[x], 1);
+  const int i1 = t1 * topk;
+  for (int ib = t0 * topk + threadIdx.x; ib < i1; ib += kBatch * blockDim.x) {
+    int xs[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) xs[k] = src[min(ib + k * (int)blockDim.x, i1 - 1)];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k)
+      if (ib + k * (int)blockDim.x < i1 && xs[k] >= 0 && xs[k] < m) atomicAdd(&hist[xs[k]], 1);
   }
   __syncthreads();
   for (int i = threadIdx.x; i < m; i += blockDim.x)
@@ -60,9 +66,16 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ coun
   const int per = (n_buckets + 1023) / 1024;
   const int lo = min(tid * per, n_buckets), hi = min(lo + per, n_buckets);
   int sp = 0, si = 0;
-  for (int i = lo; i < hi; ++i) {
-    sp += counts[i];
-    si += (counts[i] + per_item - 1) / per_item;
+  for (int i0 = lo; i0 < hi; i0 += 8) {  // 8 loads in flight
+    int c8[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) c8[k] = counts[min(i0 + k, hi - 1)];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (i0 + k < hi) {
+        sp += c8[k];
+        si += (c8[k] + per_item - 1) / per_item;
+      }
   }
   part_pairs[tid] = sp;
   part_items[tid] = si;
@@ -108,20 +121,32 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int* __restrict__ no
   const int t0 = blockIdx.x * kRowsPerGroup, t1 = min(t0 + kRowsPerGroup, n_tok);
   const size_t row0 = (size_t)bh * n_tok;
   const int* src = node + row0 * topk;
-  for (int i = t0 * topk + threadIdx.x; i < t1 * topk; i += blockDim.x) {
-    const int x = src[i];
-    if (x >= 0 && x < m) atomicAdd(&base[x], 1);
+  const int i1 = t1 * topk;
+  for (int ib = t0 * topk + threadIdx.x; ib < i1; ib += kBatch * blockDim.x) {
+    int xs[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) xs[k] = src[min(ib + k * (int)blockDim.x, i1 - 1)];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k)
+      if (ib + k * (int)blockDim.x < i1 && xs[k] >= 0 && xs[k] < m) atomicAdd(&base[xs[k]], 1);
   }
   __syncthreads();
   for (int i = threadIdx.x; i < m; i += blockDim.x)
     if (base[i]) base[i] = atomicAdd(&cursors[(size_t)bh * m + i], base[i]);
   __syncthreads();
-  for (int i = t0 * topk + threadIdx.x; i < t1 * topk; i += blockDim.x) {
-    const int x = src[i];
-    if (x >= 0 && x < m) {
-      const int pos = base[x] + atomicAdd(&cur[x], 1);
-      pairs[pos] = (int)(((row0 + i / topk) << 5) | (i % topk));
-      if (inv) inv[row0 * topk + i] = pos;
+  for (int ib = t0 * topk + threadIdx.x; ib < i1; ib += kBatch * blockDim.x) {
+    int xs[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) xs[k] = src[min(ib + k * (int)blockDim.x, i1 - 1)];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int i = ib + k * (int)blockDim.x;
+      const int x = xs[k];
+      if (i < i1 && x >= 0 && x < m) {
+        const int pos = base[x] + atomicAdd(&cur[x], 1);
+        pairs[pos] = (int)(((row0 + i / topk) << 5) | (i % topk));
+        if (inv) inv[row0 * topk + i] = pos;
+      }
     }
   }
 }

@@ -251,7 +251,34 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void stage1_kernel(
         const Column<float> scol[2] = {{&score_s[wave][0][(32 * 0 + col) / G], T},
                                        {&score_s[wave][0][(32 * 1 + col) / G], T}};
         const bool writer = (col % G) == 0;
-        for (int r0 = 0; r0 < rows_needed; r0 += 32) {
+        // The next chunk at or after row r whose parents some query of the
+        // wave keeps (rows_needed when there is none).
+        auto next_chunk = [&](int r) __attribute__((always_inline)) {
+          for (; r < rows_needed; r += 32) {
+            const int p = r >> 2;
+            uint32_t any = 0;
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) any |= (mcol[cb][p >> 5] >> (p & 31)) & 0xffu;
+            if (__ballot(any != 0u) != 0) break;
+          }
+          return r;
+        };
+        // Summary rows r0 + col of a chunk (rows past the level end repeat its
+        // last row; their logits are never used: see the ragged-chunk masking).
+        uint4 hv[KSTEPS], lv4[KSTEPS];
+        auto fetch = [&](int r0) __attribute__((always_inline)) {
+          const int r = min(r0 + col, m_child - 1);
+          const bf16_t* hrow = phi + (child0 + r) * D + 8 * kh;
+          const bf16_t* lrow2 = plo + (child0 + r) * D + 8 * kh;
+#pragma unroll
+          for (int s = 0; s < KSTEPS; ++s) {
+            hv[s] = *reinterpret_cast<const uint4*>(hrow + 16 * s);
+            lv4[s] = *reinterpret_cast<const uint4*>(lrow2 + 16 * s);
+          }
+        };
+        // One chunk: S = summaries x queries on MFMA (hv, lv4 hold its rows),
+        // then the candidates' LSEs picked up into the slot arrays.
+        auto chunk = [&](int r0, auto&& between) __attribute__((always_inline)) {
           // Rows of this chunk: r0 + 8g + 4kh + i%4 (acc element 4g + i%4);
           // level-l candidates n = r0/2 + 4g + 2kh + m own rows 2n, 2n+1;
           // their parents p = r0/4 + 2g + kh (bits p0..p0+7 of the masks).
@@ -259,18 +286,6 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void stage1_kernel(
           uint32_t byte[2];
 #pragma unroll
           for (int cb = 0; cb < 2; ++cb) byte[cb] = (mcol[cb][p0 >> 5] >> (p0 & 31)) & 0xffu;
-          if (__ballot((byte[0] | byte[1]) != 0u) == 0) continue;  // no query keeps these parents
-          // Rows past the level end repeat its last row (their logits are
-          // never used: see the ragged-chunk masking below).
-          const int r = min(r0 + col, m_child - 1);
-          const bf16_t* hrow = phi + (child0 + r) * D + 8 * kh;
-          const bf16_t* lrow2 = plo + (child0 + r) * D + 8 * kh;
-          uint4 hv[KSTEPS], lv4[KSTEPS];
-#pragma unroll
-          for (int s = 0; s < KSTEPS; ++s) {
-            hv[s] = *reinterpret_cast<const uint4*>(hrow + 16 * s);
-            lv4[s] = *reinterpret_cast<const uint4*>(lrow2 + 16 * s);
-          }
           f32x16_t acc[2] = {};
 #pragma unroll
           for (int s = 0; s < KSTEPS; ++s) {
@@ -282,6 +297,7 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void stage1_kernel(
                                                                 acc[cb], 0, 0, 0);
             }
           }
+          between();
           auto pickup = [&](auto full_tag) {
             constexpr bool kFull = decltype(full_tag)::value;  // every row of the chunk exists
 #pragma unroll
@@ -316,6 +332,21 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void stage1_kernel(
             pickup(std::true_type{});
           else
             pickup(std::false_type{});
+        };
+        if constexpr (G == 1) {
+          // the next chunk's rows are in flight while this one is picked up
+          int r0 = next_chunk(0);
+          if (r0 < rows_needed) fetch(r0);
+          while (r0 < rows_needed) {
+            const int rn = next_chunk(r0 + 32);
+            chunk(r0, [&] { if (rn < rows_needed) fetch(rn); });
+            r0 = rn;
+          }
+        } else {  // larger groups need the registers: fetch, then compute
+          for (int r0 = next_chunk(0); r0 < rows_needed; r0 = next_chunk(r0 + 32)) {
+            fetch(r0);
+            chunk(r0, [] {});
+          }
         }
       } else {
         // Gather: one query at a time; lane L scores child row L of the

@@ -325,6 +325,11 @@ def decode_bench(args):
                               None, out, None, workspace=ws if ws_n else None)
 
     ms = timed_call(step, 20, 3)
+    # Pyramid upkeep for the token each sequence appends (its leaf and the
+    # ancestors rewritten), timed separately: the decode step above reads a
+    # pyramid that is current.
+    append_ms = timed_call(lambda: pisa.pisa_pyramid_append(prob, inp.cache_len, inp.k_cache, pyr),
+                           20, 3)
     # compulsory bytes per step: the level summaries the descent scores, the
     # raw keys of the scored leaves and the K/V rows of the kept leaves
     summaries = 0
@@ -343,6 +348,7 @@ def decode_bench(args):
     return {"ms_per_step": ms, "tokens_per_s": prob.batch / (ms * 1e-3),
             "compulsory_mb": bytes_step / 1e6,
             "achieved_gbs": bytes_step / (ms * 1e-3) / 1e9,
+            "pyramid_append_ms": append_ms,
             "workload": "decode B=32 cache=131072 Hq=32 Hkv=8 d=128 C=64 K=16 bf16, "
                         "pyramid prebuilt"}
 

@@ -7,7 +7,8 @@ There is no CPU fallback: without the built library every call raises.
 
 Entry points (see include/pisa.h for layouts and semantics):
   pisa_build_pyramid, pisa_select, pisa_bsa_select, pisa_block_sparse_attn,
-  pisa_decode_step, plus pisa_pyramid_layout and pisa_workspace_bytes.
+  pisa_pyramid_append, pisa_decode_step, plus pisa_pyramid_layout and
+  pisa_workspace_bytes.
 """
 from __future__ import annotations
 
@@ -22,7 +23,8 @@ from ._lib import PisaError  # noqa: F401
 
 __all__ = [
     "Problem", "PisaError", "pisa_pyramid_layout", "pisa_workspace_bytes", "pisa_build_pyramid",
-    "pisa_select", "pisa_bsa_select", "pisa_block_sparse_attn", "pisa_decode_step",
+    "pisa_select", "pisa_bsa_select", "pisa_block_sparse_attn", "pisa_pyramid_append",
+    "pisa_decode_step",
     "pisa_profile_enable", "pisa_profile_report",
 ]
 
@@ -205,6 +207,19 @@ def pisa_block_sparse_attn(problem: Problem, q, k, v, block_idx, out=None, row_l
         ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(block_idx), _ptr(out), _ptr(row_lse),
         _ptr(ws), ws_bytes, _stream(stream)))
     return out, row_lse
+
+
+def pisa_pyramid_append(problem: Problem, cache_len, k_cache, pyramid, stream=None):
+    """Rewrite the pyramid rows on the path of token cache_len[b] - 1 (already in
+    k_cache) to those of the pyramid over cache_len[b] tokens; in place."""
+    p = problem
+    _need(cache_len, "cache_len", (p.batch,), torch.int32)
+    _need(k_cache, "k_cache", (p.batch, p.heads_kv, p.seq_len, p.head_dim), p.dtype)
+    _need(pyramid, "pyramid", (p.batch, p.heads_kv, pyramid_rows(p), p.head_dim), torch.float32)
+    c = p.to_c()
+    _lib.check("pisa_pyramid_append", _lib.load().pisa_pyramid_append(
+        ctypes.byref(c), _ptr(cache_len), _ptr(k_cache), _ptr(pyramid), _stream(stream)))
+    return pyramid
 
 
 def pisa_decode_step(problem: Problem, cache_len, q, k_cache, v_cache, pyramid, block_idx=None,

@@ -24,7 +24,8 @@ PISA_SELECT_AUTO, PISA_SELECT_FUSED, PISA_SELECT_TWO_STAGE = range(3)
 
 EXPORTED = (
     "pisa_pyramid_layout", "pisa_workspace_bytes", "pisa_build_pyramid", "pisa_select",
-    "pisa_bsa_select", "pisa_block_sparse_attn", "pisa_decode_step", "pisa_status_string",
+    "pisa_bsa_select", "pisa_block_sparse_attn", "pisa_pyramid_append", "pisa_decode_step",
+    "pisa_status_string",
     "pisa_last_error", "pisa_profile_enable", "pisa_profile_report",
 )
 
@@ -63,6 +64,7 @@ def load(path: str = LIB_PATH):
         "pisa_pyramid_layout": [i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_int64), i32],
         "pisa_workspace_bytes": [pp, i32, ctypes.POINTER(sz)],
         "pisa_build_pyramid": [pp, vp, vp, vp],
+        "pisa_pyramid_append": [pp, vp, vp, vp, vp],
         "pisa_select": [pp, vp, vp, vp, vp, vp, i32, vp, sz, vp],
         "pisa_bsa_select": [pp, vp, vp, vp, vp, vp, sz, vp],
         "pisa_block_sparse_attn": [pp, vp, vp, vp, vp, vp, vp, vp, sz, vp],

@@ -199,6 +199,17 @@ int pisa_block_sparse_attn(const pisa_problem* problem, const void* q, const voi
   return e == hipSuccess ? PISA_OK : fail_hip(e, "pisa_block_sparse_attn");
 }
 
+int pisa_pyramid_append(const pisa_problem* problem, const int32_t* cache_len,
+                        const void* k_cache, float* pyramid, void* stream) {
+  pisa::LaunchShape s;
+  const int rc = check_problem(problem, PISA_OP_PYRAMID, &s);
+  if (rc != PISA_OK) return rc;
+  if (!cache_len || !k_cache || !pyramid) return fail(PISA_ERR_INVALID, "null tensor pointer");
+  const hipError_t e =
+      pisa::launch_pyramid_append(s, cache_len, k_cache, pyramid, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PISA_OK : fail_hip(e, "pisa_pyramid_append");
+}
+
 int pisa_decode_step(const pisa_problem* problem, const int32_t* cache_len, const void* q,
                      const void* k_cache, const void* v_cache, const float* pyramid,
                      int32_t* block_idx, float* block_score, void* out, float* row_lse,

@@ -35,6 +35,8 @@ struct LaunchShape {
 };
 
 hipError_t launch_pyramid(const LaunchShape& s, const void* k, float* pyr, hipStream_t st);
+hipError_t launch_pyramid_append(const LaunchShape& s, const int32_t* cache_len, const void* kc,
+                                 float* pyr, hipStream_t st);
 
 // Per-query fused selection (leaf level included).
 hipError_t launch_select_fused(const LaunchShape& s, const void* q, const void* k,

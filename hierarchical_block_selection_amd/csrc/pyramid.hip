@@ -151,4 +151,121 @@ hipError_t launch_pyramid(const LaunchShape& s, const void* k, float* pyr, hipSt
                            : launch_pyramid_t<float, 64>(s, k, pyr, st);
 }
 
+// Pyramid cache upkeep for decode (PISA reading page §5.3, decode cache): the
+// key of token t = cache_len - 1 has just been written to the cache; the
+// nodes on t's path (leaf t / C and its ancestors) become those of the
+// pyramid over exactly t + 1 tokens.  One wavefront per (sequence, KV head).
+// The leaf mean uses the chunk kernel's lane mapping and summation order and
+// every level the same (left + right) / 2, so the rows written are bit for
+// bit those pisa_build_pyramid writes over t + 1 tokens; rows off the path
+// are not touched.  The complete left siblings on the path are read into LDS
+// before the levels are folded.
+constexpr int kAppendWaves = 4;
+
+template <typename T, int D>
+__global__ __launch_bounds__(kAppendWaves * kWave) void pyramid_append_kernel(
+    const int32_t* __restrict__ cache_len, const T* __restrict__ kc, float* __restrict__ pyr,
+    int heads_kv, int capacity, int block, LevelTable lv, int n_units) {
+  constexpr int VEC = Vec16<T>::n;
+  constexpr int LPR = D / VEC;      // lanes per key row
+  constexpr int RPI = kWave / LPR;  // key rows per load instruction
+  __shared__ float sib_s[kAppendWaves][PISA_MAX_LEVELS][D];
+  const int wave = threadIdx.x / kWave, lane = lane_id();
+  const int unit = blockIdx.x * kAppendWaves + wave;  // b * heads_kv + kvh
+  if (unit >= n_units) return;
+  const int n = cache_len[unit / heads_kv];
+  if (n < 1 || n > capacity) return;
+  const int t = n - 1, c = t / block;
+  const int r0 = c * block, r1 = t + 1;
+  const T* kb = kc + (size_t)unit * capacity * D;
+  float* pb = pyr + (size_t)unit * lv.rows * D;
+  // Left siblings of the path (node at level l - 1 odd): all lanes, to LDS.
+  for (int l = 2; l <= lv.n; ++l) {
+    const int node = c >> (l - 2);
+    if (node & 1) {
+      const float* src = pb + (size_t)(lv.off[l - 2] + node - 1) * D;
+      for (int x = lane; x < D; x += kWave) sib_s[wave][l - 1][x] = src[x];
+    }
+  }
+  // Leaf mean: rows r0 + sub, r0 + sub + RPI, ... added in order; 16 loads
+  // are requested before the first is added.
+  const int sub = lane / LPR, col = (lane % LPR) * VEC;
+  float acc[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+  for (int rb = r0 + sub; rb < r1; rb += 16 * RPI) {
+    uint4 raw[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      raw[k] = *reinterpret_cast<const uint4*>(kb + (size_t)min(rb + k * RPI, r1 - 1) * D + col);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      if (rb + k * RPI >= r1) break;
+      float v[VEC];
+      if constexpr (VEC == 8) {
+        const uint32_t w[4] = {raw[k].x, raw[k].y, raw[k].z, raw[k].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[2 * i] = __uint_as_float(w[i] << 16);
+          v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+      } else {
+        v[0] = __uint_as_float(raw[k].x);
+        v[1] = __uint_as_float(raw[k].y);
+        v[2] = __uint_as_float(raw[k].z);
+        v[3] = __uint_as_float(raw[k].w);
+      }
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[e] += v[e];
+    }
+  }
+#pragma unroll
+  for (int o = LPR; o < kWave; o <<= 1)
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] += __shfl_xor(acc[e], o, kWave);
+  wave_lds_sync();
+  if (sub != 0) return;  // lanes 0 .. LPR - 1 carry the path
+  const float inv = 1.f / float(r1 - r0);
+  float v[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) v[e] = acc[e] * inv;
+  auto store = [&](int level_index, int node) {
+    float* dst = pb + (size_t)(lv.off[level_index] + node) * D + col;
+#pragma unroll
+    for (int e = 0; e < VEC; e += 4)
+      *reinterpret_cast<float4*>(dst + e) = make_float4(v[e], v[e + 1], v[e + 2], v[e + 3]);
+  };
+  store(0, c);
+  for (int l = 2; l <= lv.n; ++l) {
+    const int node = c >> (l - 2);  // path node one level down (the last there)
+    if (node & 1) {  // its left sibling exists: mean of both
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) v[e] = 0.5f * (sib_s[wave][l - 1][col + e] + v[e]);
+    }  // else it has no right sibling yet: the parent equals it
+    store(l - 1, node >> 1);
+  }
+}
+
+template <typename T, int D>
+static hipError_t launch_append_t(const LaunchShape& s, const int32_t* cache_len, const void* kc,
+                                  float* pyr, hipStream_t st) {
+  const int units = s.batch * s.heads_kv;
+  prof::Scope ps("pyramid_append", st);
+  hipLaunchKernelGGL((pyramid_append_kernel<T, D>),
+                     dim3((units + kAppendWaves - 1) / kAppendWaves), dim3(kAppendWaves * kWave),
+                     0, st, cache_len, static_cast<const T*>(kc), pyr, s.heads_kv, s.seq_len,
+                     s.block, s.lv, units);
+  return hipGetLastError();
+}
+
+hipError_t launch_pyramid_append(const LaunchShape& s, const int32_t* cache_len, const void* kc,
+                                 float* pyr, hipStream_t st) {
+  if (s.bf16) {
+    return s.head_dim == 128 ? launch_append_t<bf16_t, 128>(s, cache_len, kc, pyr, st)
+                             : launch_append_t<bf16_t, 64>(s, cache_len, kc, pyr, st);
+  }
+  return s.head_dim == 128 ? launch_append_t<float, 128>(s, cache_len, kc, pyr, st)
+                           : launch_append_t<float, 64>(s, cache_len, kc, pyr, st);
+}
+
 }  // namespace pisa

@@ -123,6 +123,24 @@ int pisa_workspace_bytes(const pisa_problem* problem, int32_t op, size_t* bytes)
  *   pyramid:  [B, Hkv, R, d] float32, out */
 int pisa_build_pyramid(const pisa_problem* problem, const void* k, float* pyramid, void* stream);
 
+/* Pyramid cache upkeep for decode (§5.3, decode cache; §4.1 eqs. (3), (4)):
+ * for each sequence b, the key of token t = cache_len[b] - 1 is already in
+ * k_cache; the rows on t's path (leaf t / C and every ancestor) are rewritten
+ * to those of the pyramid over exactly t + 1 tokens: the leaf is the mean of
+ * keys [cC, t], each ancestor the mean of its existing children.  The rows
+ * written equal bit for bit what pisa_build_pyramid writes for a sequence of
+ * t + 1 tokens; rows off the path are not touched.  O(C d + L d) per
+ * (sequence, KV head).  Call once per appended token, after writing it.
+ *   problem.seq_len: cache capacity (the pyramid's layout); flags and topk
+ *                    are not used
+ *   cache_len: [B] int32 device, length after the append; values outside
+ *              [1, capacity] leave that sequence's pyramid unchanged
+ *   k_cache:   [B, Hkv, capacity, d] dtype
+ *   pyramid:   [B, Hkv, R(capacity), d] float32, updated in place
+ * Errors: as pisa_build_pyramid; PISA_ERR_INVALID for NULL pointers. */
+int pisa_pyramid_append(const pisa_problem* problem, const int32_t* cache_len,
+                        const void* k_cache, float* pyramid, void* stream);
+
 /* PISA selection (§4.2 eqs. (5), (6); §4.3 eq. (7); §4.4 eq. (11); §5.3):
  * per (b, kv head, t), descend from the root; at each level drop future nodes,
  * keep all candidates if there are at most K, else keep the forced nodes plus

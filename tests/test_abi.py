@@ -104,6 +104,7 @@ def test_invalid_problems_rejected_by_every_entry_point(kw, code):
     assert L.pisa_block_sparse_attn(pp, ptr, ptr, ptr, ptr, ptr, ptr, ptr, 1 << 40, None) == code
     assert L.pisa_decode_step(pp, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, 1 << 40,
                               None) == code
+    assert L.pisa_pyramid_append(pp, ptr, ptr, ptr, None) == code
     sz = ctypes.c_size_t()
     assert L.pisa_workspace_bytes(pp, 0, ctypes.byref(sz)) == code
     assert L.pisa_last_error()
@@ -117,6 +118,8 @@ def test_null_pointers_and_workspace_rejected():
     ptr = ctypes.cast(dummy, ctypes.c_void_p)
     assert L.pisa_build_pyramid(None, ptr, ptr, None) == _lib.PISA_ERR_INVALID
     assert L.pisa_build_pyramid(pp, None, ptr, None) == _lib.PISA_ERR_INVALID
+    assert L.pisa_pyramid_append(pp, None, ptr, ptr, None) == _lib.PISA_ERR_INVALID
+    assert L.pisa_pyramid_append(pp, ptr, ptr, None, None) == _lib.PISA_ERR_INVALID
     assert L.pisa_select(pp, None, ptr, ptr, ptr, None, 0, None, 0, None) == _lib.PISA_ERR_INVALID
     assert L.pisa_select(pp, ptr, ptr, ptr, ptr, None, 9, None, 0, None) == _lib.PISA_ERR_INVALID
     assert L.pisa_bsa_select(pp, ptr, ptr, None, None, ptr, 1 << 40, None) == _lib.PISA_ERR_INVALID

@@ -31,6 +31,7 @@ __all__ = [
 _DTYPES = {torch.float32: _lib.PISA_F32, torch.bfloat16: _lib.PISA_BF16}
 _STRATEGIES = {"auto": _lib.PISA_SELECT_AUTO, "fused": _lib.PISA_SELECT_FUSED,
                "two_stage": _lib.PISA_SELECT_TWO_STAGE}
+_SCORES = {"lse": 0, "mean": _lib.PISA_SCORE_MEAN, "mean_var": _lib.PISA_SCORE_MEAN_VAR}
 _OPS = {"pyramid": _lib.PISA_OP_PYRAMID, "select": _lib.PISA_OP_SELECT, "bsa": _lib.PISA_OP_BSA,
         "attn": _lib.PISA_OP_ATTN, "decode": _lib.PISA_OP_DECODE}
 
@@ -50,12 +51,15 @@ class Problem:
     force_first_prev: bool = True
     dtype: torch.dtype = torch.bfloat16
     scale: float = 0.0  # <= 0 -> 1/sqrt(head_dim)
+    score: str = "lse"  # "lse" (eq. 7), "mean" (PISA-1) or "mean_var" (PISA-2)
 
     def to_c(self) -> _lib.PisaProblem:
         if self.dtype not in _DTYPES:
             raise ValueError(f"unsupported dtype {self.dtype}")
+        if self.score not in _SCORES:
+            raise ValueError(f"unknown score {self.score!r}")
         flags = (_lib.PISA_CAUSAL if self.causal else 0) | (
-            _lib.PISA_FORCE_FIRST_PREV if self.force_first_prev else 0)
+            _lib.PISA_FORCE_FIRST_PREV if self.force_first_prev else 0) | _SCORES[self.score]
         return _lib.PisaProblem(self.batch, self.heads_q, self.heads_kv, self.seq_len,
                                 self.head_dim, self.block, self.topk, self.branch, flags,
                                 _DTYPES[self.dtype], float(self.scale))

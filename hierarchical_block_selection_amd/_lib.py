@@ -17,6 +17,8 @@ PISA_F32 = 0
 PISA_BF16 = 1
 PISA_CAUSAL = 1
 PISA_FORCE_FIRST_PREV = 2
+PISA_SCORE_MEAN = 4
+PISA_SCORE_MEAN_VAR = 8
 PISA_MAX_LEVELS = 32
 
 PISA_OP_PYRAMID, PISA_OP_SELECT, PISA_OP_BSA, PISA_OP_ATTN, PISA_OP_DECODE = range(5)

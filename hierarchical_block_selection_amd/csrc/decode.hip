@@ -16,8 +16,8 @@ __global__ __launch_bounds__(kWave) void decode_kernel(
     const int32_t* __restrict__ cache_len, const T* __restrict__ q, const T* __restrict__ kc,
     const T* __restrict__ vc, const float* __restrict__ pyr, int32_t* __restrict__ idx,
     float* __restrict__ score, T* __restrict__ out, float* __restrict__ lse, int heads_q,
-    int heads_kv, int capacity, int block, int topk, int group, int force, float scale_log2,
-    LevelTable lv) {
+    int heads_kv, int capacity, int block, int topk, int group, int force, int variant,
+    float scale_log2, LevelTable lv) {
   extern __shared__ float smem[];
   float* q_s = smem;                                        // group * D
   float* p_s = q_s + group * D;                             // 64
@@ -45,7 +45,7 @@ __global__ __launch_bounds__(kWave) void decode_kernel(
   const T* vb = vc + (size_t)bh * capacity * D;
   const float* pb = pyr + (size_t)bh * lv.rows * D;
   const SelectResult r = select_descend<T, D>(q_s, group, kb, pb, lv, capacity, block, topk, t,
-                                              true, force != 0, scale_log2, nbuf);
+                                              true, force != 0, scale_log2, nbuf, false, variant);
   write_selection(r, topk, idx_row, score_row);
   // Same ascending list into LDS for the attention loop.
   const uint64_t km = ballot(r.keep);
@@ -449,7 +449,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_wg_kernel(
 bool decode_wg_supported(const LaunchShape& s) {
   const bool g_ok = s.group == 1 || s.group == 2 || s.group == 4 || s.group == 8;
   return s.bf16 && s.block == 64 && (s.head_dim == 64 || s.head_dim == 128) && g_ok &&
-         s.topk <= kDecMaxK && s.causal && s.lv.n >= 2;
+         s.topk <= kDecMaxK && s.causal && s.lv.n >= 2 && s.variant == 0;
 }
 
 template <int D, int G>
@@ -489,7 +489,7 @@ static hipError_t launch_decode_t(const LaunchShape& s, const int32_t* cache_len
                      cache_len, static_cast<const T*>(q), static_cast<const T*>(kc),
                      static_cast<const T*>(vc), pyr, idx, score, static_cast<T*>(out), lse,
                      s.heads_q, s.heads_kv, s.seq_len, s.block, s.topk, s.group, s.force ? 1 : 0,
-                     s.scale * kLog2e, s.lv);
+                     s.variant, s.scale * kLog2e, s.lv);
   return hipGetLastError();
 }
 

@@ -51,8 +51,11 @@ int check_problem(const pisa_problem* p, int op, pisa::LaunchShape* s) {
     return fail(PISA_ERR_INVALID, "batch, heads, seq_len, head_dim, block and topk must be >= 1");
   if (p->heads_q % p->heads_kv != 0) return fail(PISA_ERR_INVALID, "heads_q % heads_kv != 0");
   if (p->dtype != PISA_F32 && p->dtype != PISA_BF16) return fail(PISA_ERR_INVALID, "bad dtype");
-  if (p->flags & ~(uint32_t)(PISA_CAUSAL | PISA_FORCE_FIRST_PREV))
+  if (p->flags & ~(uint32_t)(PISA_CAUSAL | PISA_FORCE_FIRST_PREV | PISA_SCORE_MEAN |
+                             PISA_SCORE_MEAN_VAR))
     return fail(PISA_ERR_INVALID, "unknown flag bits");
+  if ((p->flags & PISA_SCORE_MEAN) && (p->flags & PISA_SCORE_MEAN_VAR))
+    return fail(PISA_ERR_INVALID, "PISA_SCORE_MEAN and PISA_SCORE_MEAN_VAR are exclusive");
   if ((p->flags & PISA_FORCE_FIRST_PREV) && !(p->flags & PISA_CAUSAL))
     return fail(PISA_ERR_INVALID, "PISA_FORCE_FIRST_PREV requires PISA_CAUSAL");
   if (!std::isfinite(p->scale)) return fail(PISA_ERR_INVALID, "scale is not finite");
@@ -82,6 +85,7 @@ int check_problem(const pisa_problem* p, int op, pisa::LaunchShape* s) {
   s->bf16 = p->dtype == PISA_BF16;
   s->causal = (p->flags & PISA_CAUSAL) != 0;
   s->force = (p->flags & PISA_FORCE_FIRST_PREV) != 0;
+  s->variant = (p->flags & PISA_SCORE_MEAN) ? 1 : (p->flags & PISA_SCORE_MEAN_VAR) ? 2 : 0;
   s->scale = p->scale > 0.f ? p->scale : 1.0f / std::sqrt((float)p->head_dim);
   if (!layout(p->seq_len, p->block, &s->lv)) return fail(PISA_ERR_INVALID, "pyramid too tall");
   if (op == PISA_OP_BSA && s->lv.size[0] > 4096)

@@ -30,6 +30,7 @@ class Scope {
 struct LaunchShape {
   int batch, heads_q, heads_kv, seq_len, head_dim, block, topk, group;
   bool bf16, causal, force;
+  int variant;  // candidate score: 0 LSE (eq. 7), 1 mean (PISA-1), 2 mean + var/2 (PISA-2)
   float scale;
   LevelTable lv;
 };

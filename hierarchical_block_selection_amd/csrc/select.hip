@@ -14,7 +14,8 @@ template <typename T, int D>
 __global__ __launch_bounds__(kSelWaves * kWave) void select_fused_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ pyr,
     int32_t* __restrict__ idx, float* __restrict__ score, int heads_q, int heads_kv, int n_tok,
-    int block, int topk, int group, int causal, int force, float scale_log2, LevelTable lv) {
+    int block, int topk, int group, int causal, int force, int variant, float scale_log2,
+    LevelTable lv) {
   extern __shared__ float smem[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   float* q_s = smem + wave * (group * D + kWave);
@@ -28,7 +29,8 @@ __global__ __launch_bounds__(kSelWaves * kWave) void select_fused_kernel(
   const T* kb = k + (size_t)bh * n_tok * D;
   const float* pb = pyr + (size_t)bh * lv.rows * D;
   const SelectResult r = select_descend<T, D>(q_s, group, kb, pb, lv, n_tok, block, topk, t,
-                                              causal != 0, force != 0, scale_log2, nbuf);
+                                              causal != 0, force != 0, scale_log2, nbuf, false,
+                                              variant);
   const size_t orow = ((size_t)bh * n_tok + t) * topk;
   write_selection(r, topk, idx + orow, score ? score + orow : nullptr);
 }
@@ -42,7 +44,7 @@ static hipError_t launch_fused_t(const LaunchShape& s, const void* q, const void
   hipLaunchKernelGGL((select_fused_kernel<T, D>), grid, dim3(kSelWaves * kWave), lds, st,
                      static_cast<const T*>(q), static_cast<const T*>(k), pyr, idx, score,
                      s.heads_q, s.heads_kv, s.seq_len, s.block, s.topk, s.group, s.causal ? 1 : 0,
-                     s.force ? 1 : 0, s.scale * kLog2e, s.lv);
+                     s.force ? 1 : 0, s.variant, s.scale * kLog2e, s.lv);
   return hipGetLastError();
 }
 

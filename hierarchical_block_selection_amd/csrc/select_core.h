@@ -45,7 +45,7 @@ __device__ __forceinline__ void stage_queries(const T* __restrict__ q0, size_t h
 template <int D>
 __device__ __forceinline__ float score_node_lse(const float* __restrict__ child_rows, int m_child,
                                                 int node, const float* q_s, int group,
-                                                float scale_log2) {
+                                                float scale_log2, int variant = 0) {
   const int c0 = 2 * node;
   const bool has1 = c0 + 1 < m_child;
   const float* r0 = child_rows + (size_t)c0 * D;
@@ -65,6 +65,19 @@ __device__ __forceinline__ float score_node_lse(const float* __restrict__ child_
         a1[h] += qq.x * x1.x + qq.y * x1.y + qq.z * x1.z + qq.w * x1.w;
       }
     }
+  }
+  if (variant != 0) {  // eq. (9) over the (one or two) children, in nats
+    const float sc = scale_log2 * kLn2;
+    float total = 0.f;
+#pragma unroll
+    for (int h = 0; h < kMaxGroup; ++h) {
+      if (h < group) {
+        const float z0 = a0[h] * sc, z1 = has1 ? a1[h] * sc : z0;
+        const float half = 0.5f * (z0 - z1);
+        total += 0.5f * (z0 + z1) + (variant == 2 ? 0.5f * half * half : 0.f);
+      }
+    }
+    return total;
   }
   float total = 0.f;
 #pragma unroll
@@ -88,7 +101,7 @@ __device__ __forceinline__ float score_node_lse(const float* __restrict__ child_
 template <typename T, int D>
 __device__ __forceinline__ float score_leaf_lse_wave(const T* __restrict__ kb, int n_tok, int block,
                                                      int leaf, const float* q_s, int group,
-                                                     float scale_log2) {
+                                                     float scale_log2, int variant = 0) {
   constexpr int VEC = Vec16<T>::n;
   const int lane = lane_id();
   const int tok = leaf * block + lane;
@@ -111,6 +124,24 @@ __device__ __forceinline__ float score_leaf_lse_wave(const T* __restrict__ kb, i
       }
     }
   }
+  if (variant != 0) {  // eq. (9) over the leaf's raw keys, in nats
+    const float sc = scale_log2 * kLn2;
+    const float cnt = float(min(block, n_tok - leaf * block));
+    float total = 0.f;
+#pragma unroll
+    for (int h = 0; h < kMaxGroup; ++h) {
+      if (h < group) {
+        const float z = acc[h] * sc;
+        const float mean = wave_sum(ok ? z : 0.f) / cnt;
+        total += mean;
+        if (variant == 2) {
+          const float dz = z - mean;
+          total += 0.5f * wave_sum(ok ? dz * dz : 0.f) / cnt;
+        }
+      }
+    }
+    return total;
+  }
   float total = 0.f;
 #pragma unroll
   for (int h = 0; h < kMaxGroup; ++h) {
@@ -132,7 +163,7 @@ __device__ SelectResult select_descend(const float* q_s, int group, const T* __r
                                        const float* __restrict__ pb, const LevelTable& lv,
                                        int n_tok, int block, int topk, int t, bool causal,
                                        bool force, float scale_log2, int* nbuf,
-                                       bool intermediate_only = false) {
+                                       bool intermediate_only = false, int variant = 0) {
   const int lane = lane_id();
   const int cur = t / block;
   int node = lane == 0 ? 0 : -1;
@@ -167,14 +198,15 @@ __device__ SelectResult select_descend(const float* q_s, int group, const T* __r
       if (l >= 2) {
         if (rankable)
           s = score_node_lse<D>(pb + (size_t)lv.off[l - 2] * D, lv.size[l - 2], node, q_s, group,
-                                scale_log2);
+                                scale_log2, variant);
       } else {
         uint64_t todo = rm;
         while (todo) {
           const int j = __builtin_ctzll(todo);
           todo &= todo - 1;
           const int leaf = readlane_i(node, j);
-          const float sj = score_leaf_lse_wave<T, D>(kb, n_tok, block, leaf, q_s, group, scale_log2);
+          const float sj =
+              score_leaf_lse_wave<T, D>(kb, n_tok, block, leaf, q_s, group, scale_log2, variant);
           if (lane == j) s = sj;
         }
       }

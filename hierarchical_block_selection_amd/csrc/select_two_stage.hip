@@ -596,6 +596,7 @@ bool select_two_stage_supported(const LaunchShape& s) {
   const bool pow2_group = (s.group & (s.group - 1)) == 0;
   // pairs are stored as (row << 5) | slot in an int32
   const int64_t rows = (int64_t)s.batch * s.heads_kv * s.seq_len;
+  if (s.variant != 0) return false;  // LSE scores only
   return s.bf16 && s.block == 64 && (s.head_dim == 64 || s.head_dim == 128) &&
          s.lv.n >= kSplitLevel + 1 && pow2_group && s.group <= 4 && s.topk <= 32 &&
          rows < (int64_t(1) << 26);

@@ -66,7 +66,15 @@ enum {
   PISA_CAUSAL = 1u,
   /* Also keep leaf 0 and leaf c-1 (and their ancestors) for query t in leaf c,
      as the NSA/FLA policy of §5.3; they take slots of the budget K. */
-  PISA_FORCE_FIRST_PREV = 2u
+  PISA_FORCE_FIRST_PREV = 2u,
+  /* Rank candidates by a truncation of eq. (8) (§4.3 eq. (9)) instead of eq.
+     (7)'s LSE: PISA-1 scores a node by the mean of its children's logits,
+     PISA-2 by that mean plus half their population variance (at the leaf
+     level, over the raw keys).  At most one of the two.  Used by pisa_select
+     (per-query selector; PISA_SELECT_TWO_STAGE is then unsupported) and
+     pisa_decode_step; the other entry points ignore them. */
+  PISA_SCORE_MEAN = 4u,
+  PISA_SCORE_MEAN_VAR = 8u
 };
 
 enum { PISA_MAX_LEVELS = 32 };
@@ -80,7 +88,7 @@ typedef struct {
   int32_t block;     /* C, leaf block size */
   int32_t topk;      /* K, blocks kept per query and KV head */
   int32_t branch;    /* g, must be 2 */
-  uint32_t flags;    /* PISA_CAUSAL | PISA_FORCE_FIRST_PREV */
+  uint32_t flags;    /* PISA_CAUSAL | PISA_FORCE_FIRST_PREV | PISA_SCORE_* */
   int32_t dtype;     /* pisa_dtype of Q/K/V/O */
   float scale;       /* logit scale; <= 0 selects 1/sqrt(d) */
 } pisa_problem;

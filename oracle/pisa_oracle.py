@@ -378,7 +378,7 @@ def attend_row(q_heads, keys, values, leaves, t, block, causal=True, scale=None)
 
 
 def decode_row(q_heads, k_cache, v_cache, cache_len, block, topk, causal=True,
-               force_first_prev=True, scale=None, branch=2):
+               force_first_prev=True, scale=None, branch=2, variant="lse"):
     """One decode step for one (sequence, KV head): the new query at
     t = cache_len - 1 (reading R10) selects over the pyramid of the first
     cache_len keys and attends to the selected blocks.
@@ -390,7 +390,7 @@ def decode_row(q_heads, k_cache, v_cache, cache_len, block, topk, causal=True,
     vals = np.asarray(v_cache, dtype=np.float64)[:n]
     levels = build_pyramid(keys, block, branch)
     sel = select_pisa_row(q_heads, keys, levels, n - 1, block, topk, causal,
-                          force_first_prev, scale, branch)
+                          force_first_prev, scale, branch, variant)
     out, lse = attend_row(q_heads, keys, vals, sel.leaves, n - 1, block, causal, scale)
     return sel, out, lse
 

@@ -52,14 +52,15 @@ def check_structure(row, t, block, topk, n_leaves, causal, force):
 
 
 def compare_selection(kind, gpu_idx, gpu_score, q_group, keys, levels, rows, block, topk,
-                      causal, force, scale, tally: Tally):
+                      causal, force, scale, tally: Tally, variant: str = "lse"):
     """gpu_idx / gpu_score: [N, K] arrays of one (b, kv head).  Returns tally."""
     n_leaves = len(levels[0])
     for t in rows:
         check_structure(gpu_idx[t], t, block, topk, n_leaves, causal, force)
         qh = q_group[:, t, :]
         if kind == "pisa":
-            sel = oracle.select_pisa_row(qh, keys, levels, t, block, topk, causal, force, scale)
+            sel = oracle.select_pisa_row(qh, keys, levels, t, block, topk, causal, force, scale,
+                                         variant=variant)
         else:
             sel = oracle.select_bsa_row(qh, levels, t, block, topk, causal, force, scale)
         tally.rows += 1

@@ -80,7 +80,9 @@ BAD = [
     (dict(topk=0), _lib.PISA_ERR_INVALID),
     (dict(dtype=7), _lib.PISA_ERR_INVALID),
     (dict(flags=_lib.PISA_FORCE_FIRST_PREV), _lib.PISA_ERR_INVALID),
-    (dict(flags=8), _lib.PISA_ERR_INVALID),
+    (dict(flags=16), _lib.PISA_ERR_INVALID),
+    (dict(flags=_lib.PISA_CAUSAL | _lib.PISA_SCORE_MEAN | _lib.PISA_SCORE_MEAN_VAR),
+     _lib.PISA_ERR_INVALID),
     (dict(scale=float("nan")), _lib.PISA_ERR_INVALID),
     (dict(branch=4), _lib.PISA_ERR_UNSUPPORTED),
     (dict(head_dim=96), _lib.PISA_ERR_UNSUPPORTED),
@@ -153,3 +155,18 @@ def test_binding_fails_loudly_without_library(tmp_path):
             _lib.load(missing)
     finally:
         _lib._lib = saved
+
+
+def test_score_variants_need_the_per_query_selector():
+    """PISA-1 / PISA-2 scores run on the per-query selector; asking for the
+    two-stage selector with them is refused before anything is launched."""
+    L = lib()
+    dummy = ctypes.create_string_buffer(64)
+    ptr = ctypes.cast(dummy, ctypes.c_void_p)
+    for bit in (_lib.PISA_SCORE_MEAN, _lib.PISA_SCORE_MEAN_VAR):
+        p = problem(seq_len=131072, flags=_lib.PISA_CAUSAL | _lib.PISA_FORCE_FIRST_PREV | bit)
+        assert L.pisa_select(ctypes.byref(p), ptr, ptr, ptr, ptr, None, _lib.PISA_SELECT_TWO_STAGE,
+                             ptr, 1 << 40, None) == _lib.PISA_ERR_UNSUPPORTED
+    with pytest.raises(ValueError):
+        from hierarchical_block_selection_amd import Problem
+        Problem(1, 1, 1, 64, 64, score="max").to_c()

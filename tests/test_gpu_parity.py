@@ -246,7 +246,7 @@ def decode_compare(prob, inp, pyr, pairs, fp32=False, min_compared=None):
         qg = parity.to_np(inp.q[b, h * g:(h + 1) * g])
         force = prob.force_first_prev
         sel, ref, ref_lse = oracle.decode_row(qg, keys, vals, n, prob.block, prob.topk,
-                                              force_first_prev=force)
+                                              force_first_prev=force, variant=prob.score)
         got = [int(x) for x in idx[b, h].cpu()]
         parity.check_structure(got, n - 1, prob.block, prob.topk, -(-n // prob.block), True, force)
         tally.rows += 1
@@ -421,3 +421,44 @@ def test_attention_arbitrary_block_lists(case):
         parity.compare_attention(o, ls, qg, keys, vals, sub, full, 64, causal,
                                  prob.logit_scale, fp32=False)
         assert len(empty) > 0 and len(full) > len(rows) // 2
+
+
+SCORE_CASES = [
+    # (score, N, C, d, K, Hq, Hkv, dtype)
+    ("mean", 3000, 64, 128, 8, 2, 1, torch.bfloat16),
+    ("mean_var", 3000, 64, 128, 8, 2, 1, torch.bfloat16),
+    ("mean", 2500, 32, 64, 16, 4, 4, torch.float32),
+    ("mean_var", 2065, 16, 64, 5, 4, 2, torch.float32),
+]
+
+
+@pytest.mark.parametrize("case", SCORE_CASES, ids=[f"{c[0]}_N{c[1]}_C{c[2]}_d{c[3]}_K{c[4]}_"
+                                                   f"G{c[5]//c[6]}" for c in SCORE_CASES])
+def test_score_variants(case):
+    """PISA-1 (mean) and PISA-2 (mean + var/2) candidate scores (eq. (9)) on
+    the per-query selector, prefill rows and a decode step, against the
+    oracle's same variant."""
+    score, n, c, d, k, hq, hkv, dtype = case
+    prob = Problem(1, hq, hkv, n, d, block=c, topk=k, dtype=dtype, score=score)
+    announce(f"score variant {case}")
+    inp = prefill_inputs(1, hq, hkv, n, d, dtype, seed=91 + n, recipe="unit", device=DEV)
+    pyr = pisa_build_pyramid(prob, inp.k)
+    idx, sc = pisa_select(prob, inp.q, inp.k, pyr)
+    torch.cuda.synchronize()
+    g = hq // hkv
+    rows = list(range(0, n, 2)) + [n - 1]
+    for h in range(hkv):
+        keys = parity.to_np(inp.k[0, h])
+        qg = parity.to_np(inp.q[0, h * g:(h + 1) * g])
+        levels = oracle.build_pyramid(keys, c)
+        tl = parity.compare_selection("pisa", idx[0, h].cpu().numpy(), sc[0, h].cpu().numpy(), qg,
+                                      keys, levels, rows, c, k, True, True, prob.logit_scale,
+                                      parity.Tally(), variant=score)
+        print(f"  {score}: compared {tl.compared}/{tl.rows}", flush=True)
+        assert not tl.mismatches, tl.mismatches[:3]
+        assert tl.frac() > 0.6
+    dprob = Problem(2, hq, hkv, n, d, block=c, topk=k, dtype=dtype, score=score)
+    dinp = decode_inputs(2, hq, hkv, n, d, dtype, seed=93 + n, recipe="unit",
+                         cache_len=[n, n // 2 + 7], device=DEV)
+    dpyr = pisa_build_pyramid(dprob, dinp.k_cache)
+    decode_compare(dprob, dinp, dpyr, [(b, h) for b in range(2) for h in range(hkv)])

@@ -3,7 +3,8 @@
 The selection-quality diagnostic of the PISA reading page (§7.2, Table 7)
 needs a trained model and its prompts, which are not available; planted
 needles stand in for them (see hierarchical_block_selection_amd.inputs).  For
-PISA (GPU) and the flat BSA selector (GPU), against the exhaustive reference
+PISA, its eq. (9) ablations PISA-1 and PISA-2, and the flat BSA selector (all
+on the GPU), against the exhaustive reference
 (the oracle's flat selection by the exact leaf LSE over raw keys, summed over
 the group's heads, with the same forcing), on sampled rows:
 
@@ -19,6 +20,7 @@ import json
 import math
 import os
 import sys
+from dataclasses import replace
 
 import numpy as np
 import pytest
@@ -32,22 +34,27 @@ from hierarchical_block_selection_amd.inputs import WORKLOADS, prefill_inputs
 pytestmark = pytest.mark.gpu
 
 
-def _quality(cfg_name, heads, rows_per_head, seed_rows=0):
+def _quality(cfg_name, heads, rows_per_head, seed_rows=0, recipe=None):
     cfg = WORKLOADS[cfg_name]
+    recipe = recipe or cfg["recipe"]
     prob = Problem(cfg["batch"], cfg["heads_q"], cfg["heads_kv"], cfg["seq_len"], cfg["head_dim"],
                    block=cfg["block"], topk=cfg["topk"], dtype=cfg["dtype"])
-    print(f"[case] quality {cfg_name} heads={heads}", flush=True)
+    print(f"[case] quality {cfg_name} {recipe} heads={heads}", flush=True)
     inp = prefill_inputs(prob.batch, prob.heads_q, prob.heads_kv, prob.seq_len, prob.head_dim,
-                         prob.dtype, seed=cfg["seed"], recipe=cfg["recipe"],
+                         prob.dtype, seed=cfg["seed"], recipe=recipe,
                          n_needles=cfg["n_needles"], block=prob.block, device="cuda")
     pyr = pisa_build_pyramid(prob, inp.k)
     pidx, _ = pisa_select(prob, inp.q, inp.k, pyr, want_score=False)
+    # the eq. (9) ablations PISA-1 (mean) and PISA-2 (mean + var/2)
+    p1idx, _ = pisa_select(replace(prob, score="mean"), inp.q, inp.k, pyr, want_score=False)
+    p2idx, _ = pisa_select(replace(prob, score="mean_var"), inp.q, inp.k, pyr, want_score=False)
     bidx, _ = pisa_bsa_select(prob, inp.q, pyr, want_score=False)
     torch.cuda.synchronize()
     C, K, G = prob.block, prob.topk, prob.group
     rng = np.random.default_rng(seed_rows)
-    stats = {"pisa": [], "bsa": [], "exhaustive": []}
-    hits = {"pisa": 0, "bsa": 0, "exhaustive": 0}
+    names = ("pisa", "pisa1", "pisa2", "bsa", "exhaustive")
+    stats = {name: [] for name in names}
+    hits = {name: 0 for name in names}
     n_needles = 0
     for h in heads:
         keys = inp.k[0, h].double().cpu().numpy()
@@ -56,18 +63,20 @@ def _quality(cfg_name, heads, rows_per_head, seed_rows=0):
                        if nd.batch == 0 and nd.kv_head == h}
         rows = sorted(set(needle_rows) | set(
             int(x) for x in rng.integers(K * C, prob.seq_len, rows_per_head)))
-        p_rows = pidx[0, h].cpu().numpy()
-        b_rows = bidx[0, h].cpu().numpy()
+        got = {"pisa": pidx[0, h].cpu().numpy(), "pisa1": p1idx[0, h].cpu().numpy(),
+               "pisa2": p2idx[0, h].cpu().numpy(), "bsa": bidx[0, h].cpu().numpy()}
         for t in rows:
             ref = oracle.select_exhaustive_row(qg[:, t], keys, t, C, K, True, True).leaves
-            sets = {"pisa": p_rows[t], "bsa": b_rows[t], "exhaustive": ref}
+            sets = {name: v[t] for name, v in got.items()}
+            sets["exhaustive"] = ref
             for name, sel in sets.items():
                 stats[name].append(oracle.selection_quality(sel, ref, qg[:, t], keys, t, C, K))
             if t in needle_rows:
                 n_needles += 1
                 for name, sel in sets.items():
                     hits[name] += int(needle_rows[t] in set(int(x) for x in sel))
-    out = {"workload": cfg_name, "rows": len(stats["pisa"]), "needle_rows": n_needles}
+    out = {"workload": cfg_name, "recipe": recipe, "rows": len(stats["pisa"]),
+           "needle_rows": n_needles}
     for name in stats:
         arr = {k: float(np.mean([s[k] for s in stats[name]])) for k in stats[name][0]}
         arr["needle_hit_rate"] = hits[name] / max(n_needles, 1)
@@ -83,17 +92,19 @@ def _report(res):
             f.write(json.dumps(res) + "\n")
 
 
-def _check(res):
-    for name in ("pisa", "bsa", "exhaustive"):
+def _check(res, needles_clear=True):
+    for name in ("pisa", "pisa1", "pisa2", "bsa", "exhaustive"):
         m = res[name]
         for key in ("recall", "net_recall", "retained_mass", "mass_ratio", "needle_hit_rate"):
             assert 0.0 <= m[key] <= 1.0 + 1e-9 or key == "mass_ratio", (name, key, m[key])
     assert res["exhaustive"]["recall"] == pytest.approx(1.0)
     # A needle block's keys point along its target query: the exact reference
     # and the flat mean-summary selector both find it.
-    assert res["exhaustive"]["needle_hit_rate"] >= 0.9
-    assert res["bsa"]["needle_hit_rate"] >= 0.9
-    assert res["pisa"]["recall"] > 0.0
+    if needles_clear:
+        assert res["exhaustive"]["needle_hit_rate"] >= 0.9
+        assert res["bsa"]["needle_hit_rate"] >= 0.9
+    for name in ("pisa", "pisa1", "pisa2"):
+        assert res[name]["recall"] > 0.0
 
 
 def test_quality_needles_c2():
@@ -106,3 +117,14 @@ def test_quality_needles_c3():
     res = _quality("c3", heads=range(0, 8, 2), rows_per_head=16, seed_rows=1)
     _report(res)
     _check(res)
+
+
+def test_quality_needles_c2_unit_variance():
+    """The same shape with N(0,1) entries: logits spread widely, so the LSE of
+    a node's children and their mean part ways (the regime where eq. (9)'s
+    truncations and eq. (7) differ)."""
+    res = _quality("c2", heads=range(0, 16, 4), rows_per_head=24, seed_rows=2, recipe="unit")
+    _report(res)
+    # with N(0,1) noise the planted blocks no longer stand out from the
+    # strongest random blocks, so only the metrics' ranges are checked
+    _check(res, needles_clear=False)

@@ -322,6 +322,8 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void stage1_kernel(
                       fmaf(mx, scale_log2, fast_log2(1.f + fast_exp2((mn - mx) * scale_log2)));
                   if (G >= 2) v += __shfl_xor(v, 1, kWave);
                   if (G >= 4) v += __shfl_xor(v, 2, kWave);
+                  if (G >= 8) v += __shfl_xor(v, 4, kWave);
+                  if (G >= 16) v += __shfl_xor(v, 8, kWave);
                   scol[cb][w ? 2 * pslot + m : kSlots] = v;
                 }
               }

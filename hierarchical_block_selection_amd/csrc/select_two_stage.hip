@@ -598,8 +598,9 @@ bool select_two_stage_supported(const LaunchShape& s) {
   const int64_t rows = (int64_t)s.batch * s.heads_kv * s.seq_len;
   if (s.variant != 0) return false;  // LSE scores only
   return s.bf16 && s.block == 64 && (s.head_dim == 64 || s.head_dim == 128) &&
-         s.lv.n >= kSplitLevel + 1 && pow2_group && s.group <= 4 && s.topk <= 32 &&
-         rows < (int64_t(1) << 26);
+         s.lv.n >= kSplitLevel + 1 && pow2_group && s.topk <= 32 &&
+         // the lane-per-query kernels (K <= 16) take every group size
+         (s.group <= 4 || s.topk <= lpq::kMaxK) && rows < (int64_t(1) << 26);
 }
 
 size_t select_two_stage_ws_bytes(const LaunchShape& s) {
@@ -620,7 +621,11 @@ hipError_t launch_select_two_stage(const LaunchShape& s, const void* q, const vo
       case 2128: e = stage1_lpq_launch<128, 2>(s, q, pyr, w, st); break;
       case 2064: e = stage1_lpq_launch<64, 2>(s, q, pyr, w, st); break;
       case 4128: e = stage1_lpq_launch<128, 4>(s, q, pyr, w, st); break;
-      default: e = stage1_lpq_launch<64, 4>(s, q, pyr, w, st); break;
+      case 4064: e = stage1_lpq_launch<64, 4>(s, q, pyr, w, st); break;
+      case 8128: e = stage1_lpq_launch<128, 8>(s, q, pyr, w, st); break;
+      case 8064: e = stage1_lpq_launch<64, 8>(s, q, pyr, w, st); break;
+      case 16128: e = stage1_lpq_launch<128, 16>(s, q, pyr, w, st); break;
+      default: e = stage1_lpq_launch<64, 16>(s, q, pyr, w, st); break;
     }
   } else {
     e = s.group == 1 ? (s.head_dim == 128 ? stage1_launch<bf16_t, 128, 1>(s, q, pyr, w, st)
@@ -652,7 +657,11 @@ hipError_t launch_select_two_stage(const LaunchShape& s, const void* q, const vo
       case 2128: PISA_S2(128, 2); break;
       case 2064: PISA_S2(64, 2); break;
       case 4128: PISA_S2(128, 4); break;
-      default: PISA_S2(64, 4); break;
+      case 4064: PISA_S2(64, 4); break;
+      case 8128: PISA_S2(128, 8); break;
+      case 8064: PISA_S2(64, 8); break;
+      case 16128: PISA_S2(128, 16); break;
+      default: PISA_S2(64, 16); break;
     }
 #undef PISA_S2
   }

@@ -169,6 +169,10 @@ EDGE = [
     (3000, 64, 128, 5, 1, 1, torch.bfloat16, False, False),
     (1100, 64, 128, 4, 4, 1, torch.bfloat16, True, True),
     (8192, 64, 128, 16, 1, 1, torch.bfloat16, True, False),
+    # two-stage selection with 8 and 16 query heads per KV head (the pages'
+    # latency shape is G = 16, d = 64, K = 8)
+    (6000, 64, 64, 8, 16, 1, torch.bfloat16, True, True),
+    (5000, 64, 128, 16, 16, 2, torch.bfloat16, True, True),
 ]
 
 

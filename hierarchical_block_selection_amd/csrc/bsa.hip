@@ -6,8 +6,11 @@
 // Scores: s[t, i] = scale * sum over the group's heads of q_h,t . kbar_i
 // (eq. (1) summed over the group's heads).
 // bf16 inputs: the leaf summaries are split once into three bf16 planes
-// (hi + mid + lo carries the fp32 value).  A workgroup owns 128 queries (32 per
-// wave, held as MFMA A operands in registers) and walks the leaves 32 at a
+// (hi + mid + lo carries the fp32 value).  The score is linear in the query,
+// so for a group of G > 1 heads the heads' queries are added in fp32 first and
+// the sum enters as two bf16 parts (hi + lo): the MFMA count does not grow
+// with G.  A workgroup owns 128 queries (32 per wave, held as MFMA A operands
+// in registers) and walks the leaves 32 at a
 // time up to its causal limit; the three planes of each 32-leaf tile are
 // staged in LDS (double-buffered) and shared by the four waves.  Each output
 // row segment is a coalesced 128-byte store.  fp32 inputs use an LDS-tiled
@@ -132,14 +135,38 @@ __global__ __launch_bounds__(256, 2) void bsa_scores_mfma_kernel(
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
   const int col = lane & 31, kh = lane >> 5;
   const int tq0 = t0 + 32 * wave;
-  // A operands: this lane's query row (clamped), all heads of the group.
+  // A operands: this lane's query row (clamped).  Eq. (1) summed over the
+  // group is linear in the query, so a group's heads are added first (fp32)
+  // and the sum enters as bf16 hi and lo parts: 2 operands for any G.
+  constexpr int NQ = G == 1 ? 1 : 2;
   const int tq = min(tq0 + col, n_tok - 1);
-  bf16x8_t a[G][KSTEPS];
+  bf16x8_t a[NQ][KSTEPS];
+  if constexpr (G == 1) {
+    const bf16_t* qr = q + (((size_t)b * heads_q + (size_t)kvh) * n_tok + tq) * D + 8 * kh;
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const bf16_t* qr = q + (((size_t)b * heads_q + (size_t)kvh * G + h) * n_tok + tq) * D + 8 * kh;
+    for (int s = 0; s < KSTEPS; ++s) a[0][s] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qr + 16 * s));
+  } else {
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) a[h][s] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qr + 16 * s));
+    for (int s = 0; s < KSTEPS; ++s) {
+      float sum[8] = {};
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const bf16_t* qr =
+            q + (((size_t)b * heads_q + (size_t)kvh * G + h) * n_tok + tq) * D + 8 * kh + 16 * s;
+        const u32x4_t w = *reinterpret_cast<const u32x4_t*>(qr);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sum[2 * e] += __uint_as_float(w[e] << 16);
+          sum[2 * e + 1] += __uint_as_float(w[e] & 0xffff0000u);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const __bf16 hi = (__bf16)sum[e];
+        a[0][s][e] = hi;
+        a[1][s][e] = (__bf16)(sum[e] - (float)hi);
+      }
+    }
   }
   const bf16_t* pb = planes + (size_t)bh * m1 * D;
   u32x4_t stage[PER_THREAD];
@@ -177,7 +204,7 @@ __global__ __launch_bounds__(256, 2) void bsa_scores_mfma_kernel(
         const bf16x8_t bb =
             as_bf16x8(*reinterpret_cast<const u32x4_t*>(&bs[buf][p][col * ROW + 16 * s + 8 * kh]));
 #pragma unroll
-        for (int h = 0; h < G; ++h)
+        for (int h = 0; h < NQ; ++h)
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[h][s], bb, acc, 0, 0, 0);
       }
     // acc[i] = S[query tq0 + (i/4)*8 + 4kh + i%4][leaf lt*32 + col]
@@ -417,7 +444,9 @@ static hipError_t launch_bsa_mfma_d(const LaunchShape& s, const void* q, const f
   switch (s.group) {
     case 1: return launch_bsa_mfma_t<D, 1>(s, q, pyr, S, planes, st);
     case 2: return launch_bsa_mfma_t<D, 2>(s, q, pyr, S, planes, st);
-    default: return launch_bsa_mfma_t<D, 4>(s, q, pyr, S, planes, st);
+    case 4: return launch_bsa_mfma_t<D, 4>(s, q, pyr, S, planes, st);
+    case 8: return launch_bsa_mfma_t<D, 8>(s, q, pyr, S, planes, st);
+    default: return launch_bsa_mfma_t<D, 16>(s, q, pyr, S, planes, st);
   }
 }
 
@@ -425,8 +454,8 @@ hipError_t launch_bsa(const LaunchShape& s, const void* q, const float* pyr, int
                       float* score, void* ws, hipStream_t st) {
   float* S = static_cast<float*>(ws);
   hipError_t e;
-  // MFMA scores for bf16 with a group of 1, 2 or 4 query heads; else fp32 FMA tiles.
-  if (s.bf16 && (s.group == 1 || s.group == 2 || s.group == 4)) {
+  // MFMA scores for bf16 with a power-of-two group; else fp32 FMA tiles.
+  if (s.bf16 && (s.group & (s.group - 1)) == 0) {
     bf16_t* planes = reinterpret_cast<bf16_t*>(static_cast<char*>(ws) + scores_bytes(s));
     e = s.head_dim == 128 ? launch_bsa_mfma_d<128>(s, q, pyr, S, planes, st)
                           : launch_bsa_mfma_d<64>(s, q, pyr, S, planes, st);

@@ -294,6 +294,10 @@ def run(args):
         result["decode"] = decode_bench(args)
     if not args.no_sweep:
         result["selection_sweep"] = selection_sweep(args)
+        # the pages' own latency shape: 16 query heads per KV head, d=64, K=8
+        result["selection_sweep_g16"] = selection_sweep(
+            args, heads_q=16, heads_kv=1, head_dim=64, topk=8,
+            sizes=(16384, 65536, 131072, 262144), seed=4100)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(args, inp, prob)
     return result
@@ -353,9 +357,10 @@ def decode_bench(args):
                         "pyramid prebuilt"}
 
 
-def selection_sweep(args):
+def selection_sweep(args, heads_q=4, heads_kv=4, head_dim=128, topk=16,
+                    sizes=(16384, 32768, 65536, 131072, 262144), seed=4000):
     """Selection latency (pyramid + selection, attention excluded) of PISA and
-    of the GPU BSA baseline at H=4, d=128, K=16 for N = 16K .. 256K."""
+    of the GPU BSA baseline for N over `sizes` (default: H=4, d=128, K=16)."""
     import torch
 
     import hierarchical_block_selection_amd as pisa
@@ -363,12 +368,14 @@ def selection_sweep(args):
 
     dev = torch.device("cuda:0")
     pts = []
-    for i, n in enumerate((16384, 32768, 65536, 131072, 262144)):
-        prob = pisa.Problem(1, 4, 4, n, 128, block=64, topk=16, dtype=torch.bfloat16)
-        inp = prefill_inputs(1, 4, 4, n, 128, torch.bfloat16, seed=4000 + 10 * i, device=dev)
+    for i, n in enumerate(sizes):
+        prob = pisa.Problem(1, heads_q, heads_kv, n, head_dim, block=64, topk=topk,
+                            dtype=torch.bfloat16)
+        inp = prefill_inputs(1, heads_q, heads_kv, n, head_dim, torch.bfloat16,
+                             seed=seed + 10 * i, device=dev)
         rows = pisa.pisa_pyramid_layout(n, 64)[-1]
-        pyr = torch.empty((1, 4, rows, 128), dtype=torch.float32, device=dev)
-        idx = torch.empty((1, 4, n, 16), dtype=torch.int32, device=dev)
+        pyr = torch.empty((1, heads_kv, rows, head_dim), dtype=torch.float32, device=dev)
+        idx = torch.empty((1, heads_kv, n, topk), dtype=torch.int32, device=dev)
         ws_s = pisa.pisa_workspace_bytes(prob, "select")
         wsel = torch.empty(max(ws_s, 1), dtype=torch.uint8, device=dev)
         ws_b = pisa.pisa_workspace_bytes(prob, "bsa")
@@ -397,9 +404,12 @@ def selection_sweep(args):
             cross = math.exp(la + (lb - la) * (0 - ra) / (rb - ra))
     if pts and pts[0]["speedup_vs_bsa"] >= 1.0:
         cross = f"<= {pts[0]['N']}"
+    if cross is None and pts:
+        cross = f"> {pts[-1]['N']}"
     return {"points": pts, "crossover_N": cross,
-            "note": "timings include pyramid construction (all levels) for both selectors; "
-                    "attention excluded; H=4 MHA, d=128, C=64, K=16, bf16"}
+            "note": f"timings include pyramid construction (all levels) for both selectors; "
+                    f"attention excluded; Hq={heads_q} Hkv={heads_kv}, d={head_dim}, C=64, "
+                    f"K={topk}, bf16"}
 
 
 def cpu_baseline(args, inp, prob):

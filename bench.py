@@ -46,48 +46,33 @@ def level_sizes(n, c):
 def descent_counts(n, c, k, force=True):
     """For every query row t of a causal prefill, the dot products the PISA
     descent performs per head, by level: rankable candidates at level l >= 2
-    score their two child summaries, rankable leaves score their C raw keys.
-    Candidate counts are data-independent: every level keeps min(K, #A) nodes,
-    one of which is the current-path node, whose right child may be future.
+    score their two child summaries, rankable leaves score their C raw keys
+    (descent_row_counts; the counts depend on t only through its leaf t // C).
     Returns {level: int64 array over t}."""
     import numpy as np
     sizes = level_sizes(n, c)
     L = len(sizes)
     out = {lvl: np.zeros(n, dtype=np.int64) for lvl in range(1, L + 1)}
-    for t in range(n):
-        cur = t // c
-        cand = 1
-        for lvl in range(L, 0, -1):
-            sh = lvl - 1
-            lim = cur >> sh
-            cand = min(cand, lim + 1)
-            forced = {lim}
-            if force:
-                forced |= {0}
-                if cur >= 1:
-                    forced |= {(cur - 1) >> sh}
-            if cand > k:
-                ranked = cand - len(forced)
-                out[lvl][t] = 2 * ranked if lvl >= 2 else c * ranked
-                kept = k
-            else:
-                kept = cand
-            if lvl > 1:
-                cand = 2 * kept
+    for cur in range(sizes[0]):
+        t0, t1 = cur * c, min((cur + 1) * c, n)
+        for lvl, v in descent_row_counts(n, c, k, t0, force).items():
+            out[lvl][t0:t1] = v
     return out
 
 
 def descent_row_counts(n, c, k, t, force=True):
-    """descent_counts for the single query row t: {level: dot products}."""
+    """Child rows (levels >= 2) or raw keys (level 1) scored for query row t of
+    the causal descent, {level: count}.  Exact, and data-independent: every
+    ranked candidate lies strictly left of t's path, so it has all its
+    children; only the path node's right child can lie in the future."""
     sizes = level_sizes(n, c)
     L = len(sizes)
     out = {}
     cur = t // c
-    cand = 1
+    cand = 1  # level L: the root's only candidate, node 0
     for lvl in range(L, 0, -1):
         sh = lvl - 1
         lim = cur >> sh
-        cand = min(cand, lim + 1)
         forced = {lim}
         if force:
             forced |= {0}
@@ -101,7 +86,9 @@ def descent_row_counts(n, c, k, t, force=True):
             out[lvl] = 0
             kept = cand
         if lvl > 1:
-            cand = 2 * kept
+            # children of the kept nodes; the path node's right child is in
+            # the future when t's path continues through its left child
+            cand = 2 * kept - (1 if (cur >> (lvl - 2)) == 2 * lim else 0)
     return out
 
 

@@ -1,4 +1,5 @@
-"""Plain, slow CPU oracle of PISA's forward path (NumPy, float64).
+"""Plain, slow CPU oracle of PISA's forward path and of the block-sparse
+attention's backward (NumPy, float64).
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import this module.  The product path
@@ -25,6 +26,8 @@ equation.  Where the page is silent the reading taken is stated at the spot.
 * BSA baseline: eq. (1) block scores over mean-pooled leaf summaries + Top-K
   (§02, Table 1 row 5).
 * Block-sparse attention: eq. (2) (§02), with the causal mask of §5.3.
+* Its backward with the block lists held fixed (§5.3): the softmax chain rule
+  written out per row.
 
 Readings taken where the page leaves a step open (each also listed in the design doc):
 
@@ -45,6 +48,10 @@ R10 Decode: the new query sits at t = cache_len - 1; its own key is already in
     the cache and in the pyramid.
 R11 Var(z) in eq. (9) is the population variance (1/m), as the cumulant
     expansion of eq. (8) implies.
+R13 Backward (§5.3): the leaf lists are inputs, not functions of Q and K; the
+    gradients are those of eq. (2) over the fixed token set, so nothing reaches
+    the pyramid or the scores.  dK and dV of a key sum over every query head
+    of the group and every row whose list holds the key's block.
 
 Parity unpinned: outcomes at exact or near ties (several answers are then
 correct); the ragged-tail reading R1 in non-causal mode has no worked example
@@ -370,6 +377,105 @@ def attend_row(q_heads, keys, values, leaves, t, block, causal=True, scale=None)
         outs.append((p @ vv) / p.sum())
         lses.append(m + math.log(float(p.sum())))
     return np.stack(outs), np.array(lses)
+
+
+# --------------------------------------------------------------------------
+# Backward of the block-sparse attention (PISA reading page §5.3 "backward":
+# the selected block indices are held fixed and gradients flow only through
+# the attention entries they select; the forward is eq. (2) of §02)
+# --------------------------------------------------------------------------
+
+
+def attended_tokens(leaves, t, block, n_tok, causal=True):
+    """Token positions attend_row uses for position t: the union of the listed
+    leaf blocks (entries < 0 skipped, in list order sorted ascending), clipped
+    to the sequence and to j <= t in causal mode (reading R6)."""
+    return [j for i in sorted(x for x in leaves if x >= 0)
+            for j in range(i * block, min((i + 1) * block, n_tok))
+            if (not causal) or j <= t]
+
+
+def attend_row_grad(q_heads, keys, values, leaves, t, block, dout, causal=True, scale=None):
+    """Gradient of sum_h dout[h] . out[h] for the rows of attend_row at t.
+
+    The token set J is fixed (reading R13).  Per head, with z_j = scale q.k_j,
+    p = softmax(z) over J and out = sum_j p_j v_j, the chain rule through the
+    softmax gives
+        dv_j = p_j dout,
+        dz_j = p_j (dout . v_j - dout . out),
+        dq   = scale sum_j dz_j k_j,
+        dk_j = scale dz_j q.
+    Returns (cols, dq [G, d], dk [len(cols), d], dv [len(cols), d]); dk and dv
+    are summed over the group's heads, which read the same keys and values.
+    A row with no token gets zero gradients.
+    """
+    q_heads = np.atleast_2d(np.asarray(q_heads, dtype=np.float64))
+    dout = np.atleast_2d(np.asarray(dout, dtype=np.float64))
+    keys = np.asarray(keys, dtype=np.float64)
+    values = np.asarray(values, dtype=np.float64)
+    n_tok, d = keys.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    cols = attended_tokens(leaves, t, block, n_tok, causal)
+    dq = np.zeros_like(q_heads)
+    dk = np.zeros((len(cols), d))
+    dv = np.zeros((len(cols), d))
+    if not cols:
+        return cols, dq, dk, dv
+    kk, vv = keys[cols], values[cols]
+    for h, (q, g) in enumerate(zip(q_heads, dout)):
+        z = scale * (kk @ q)
+        p = np.exp(z - np.max(z))
+        p /= p.sum()
+        out = p @ vv
+        dz = p * (vv @ g - g @ out)
+        dq[h] = scale * (dz @ kk)
+        dk += scale * np.outer(dz, q)
+        dv += np.outer(p, g)
+    return cols, dq, dk, dv
+
+
+def attention_backward(q_group, keys, values, idx_rows, dout_group, block, causal=True,
+                       scale=None):
+    """Whole-head backward for one (batch, KV head) by summing attend_row_grad
+    over every row.  q_group, dout_group: [G, N, d]; keys, values: [N, d];
+    idx_rows: [N, K] leaf lists (entries < 0 or beyond the last block skipped).
+    Returns dq [G, N, d], dk [N, d], dv [N, d]."""
+    q_group = np.asarray(q_group, dtype=np.float64)
+    keys = np.asarray(keys, dtype=np.float64)
+    n_tok = keys.shape[0]
+    dq = np.zeros_like(q_group)
+    dk = np.zeros_like(keys)
+    dv = np.zeros_like(keys)
+    for t in range(n_tok):
+        cols, gq, gk, gv = attend_row_grad(q_group[:, t], keys, values, idx_rows[t], t, block,
+                                           np.asarray(dout_group)[:, t], causal, scale)
+        dq[:, t] = gq
+        if cols:
+            np.add.at(dk, cols, gk)
+            np.add.at(dv, cols, gv)
+    return dq, dk, dv
+
+
+def key_block_grad(q_group, keys, values, idx_rows, dout_group, blk, block, causal=True,
+                   scale=None):
+    """dk, dv of the keys of leaf block ``blk`` alone: the contributions of the
+    rows whose list holds ``blk``, computed row by row.  Returns two
+    [n_keys, d] arrays (n_keys = keys of the block inside the sequence)."""
+    keys = np.asarray(keys, dtype=np.float64)
+    n_tok, d = keys.shape
+    lo, hi = blk * block, min((blk + 1) * block, n_tok)
+    dk = np.zeros((hi - lo, d))
+    dv = np.zeros((hi - lo, d))
+    rows = np.nonzero((np.asarray(idx_rows) == blk).any(axis=1))[0]
+    for t in rows:
+        cols, _, gk, gv = attend_row_grad(np.asarray(q_group)[:, t], keys, values, idx_rows[t],
+                                          int(t), block, np.asarray(dout_group)[:, t], causal,
+                                          scale)
+        for c, j in enumerate(cols):
+            if lo <= j < hi:
+                dk[j - lo] += gk[c]
+                dv[j - lo] += gv[c]
+    return dk, dv
 
 
 # --------------------------------------------------------------------------

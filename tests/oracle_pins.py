@@ -12,7 +12,9 @@ Independent routes used here (none of them calls the oracle's own scoring):
     NumPy GEMM plus a lexsort for BSA);
   * a dense brute force on tiny inputs (S = scale Q K^T, node logits as block
     means of S, descent by boolean masks);
-  * invariants (eq. (6) bounds, eq. (10) sandwich, GQA duplication, causality).
+  * invariants (eq. (6) bounds, eq. (10) sandwich, GQA duplication, causality);
+  * for the backward: central differences of a dense masked attention written
+    here, torch autograd of the same, and softmax invariants.
 """
 from __future__ import annotations
 
@@ -457,9 +459,145 @@ def pin_tie_rule(O):
     assert ts[0] == [5] and ts[1] == 0.0
 
 
+# ---------------------------------------------------------------- P15 backward
+def random_lists(r, n, c, k, causal, junk=False):
+    """Leaf lists of K entries per row: the forced blocks {0, c-1, c} (causal)
+    plus distinct random others, -1 padded; with junk, also out-of-range
+    entries and, in causal mode, a future block."""
+    m1 = -(-n // c)
+    out = np.full((n, k), -1, np.int64)
+    for t in range(n):
+        cur = t // c
+        hi = cur if causal else m1 - 1
+        base = sorted({0, max(cur - 1, 0), cur}) if causal else []
+        rest = [int(x) for x in r.permutation(hi + 1) if int(x) not in base]
+        row = (base + rest)[:k - (1 if junk else 0)]
+        if junk:
+            row.append(int(r.choice([-1, m1, m1 + 3] + ([cur + 1] if causal and cur + 1 < m1 else []))))
+        out[t, :len(row)] = row
+    return out
+
+
+def dense_mask(lists, n, c, causal):
+    """mask[t, j]: token j is attended by row t (its block is listed and, in
+    causal mode, j <= t), built without the oracle."""
+    mask = np.zeros((n, n), bool)
+    blk = np.arange(n) // c
+    for t in range(n):
+        listed = [x for x in lists[t] if 0 <= x]
+        mask[t] = np.isin(blk, listed)
+        if causal:
+            mask[t, t + 1:] = False
+    return mask
+
+
+def dense_loss_np(q, keys, vals, dout, mask, scale):
+    """sum over heads and rows of dout . out for masked dense attention (rows
+    with no token contribute nothing)."""
+    total = 0.0
+    for h in range(q.shape[0]):
+        s = scale * q[h] @ keys.T
+        s = np.where(mask, s, -np.inf)
+        for t in range(q.shape[1]):
+            if not mask[t].any():
+                continue
+            p = np.exp(s[t] - s[t].max())
+            p /= p.sum()
+            total += float(dout[h, t] @ (p @ vals))
+    return total
+
+
+def pin_attention_grad_finite_differences(O):
+    """The backward is the derivative of the forward: central differences of a
+    dense masked softmax attention written here (fp64, step 1e-6) against
+    every entry of dq, dk and dv, causal and not, with junk list entries."""
+    r = rng(21)
+    n, c, d, k, g = 22, 4, 5, 3, 2
+    for causal in (True, False):
+        q = r.standard_normal((g, n, d))
+        keys = r.standard_normal((n, d))
+        vals = r.standard_normal((n, d))
+        dout = r.standard_normal((g, n, d))
+        lists = random_lists(r, n, c, k, causal, junk=True)
+        scale = 0.7
+        mask = dense_mask(lists, n, c, causal)
+        dq, dk, dv = O.attention_backward(q, keys, vals, lists, dout, c, causal, scale)
+        eps = 1e-6
+        for name, arr, grad in (("q", q, dq), ("k", keys, dk), ("v", vals, dv)):
+            num = np.zeros_like(arr)
+            for ix in np.ndindex(arr.shape):
+                old = arr[ix]
+                arr[ix] = old + eps
+                up = dense_loss_np(q, keys, vals, dout, mask, scale)
+                arr[ix] = old - eps
+                dn = dense_loss_np(q, keys, vals, dout, mask, scale)
+                arr[ix] = old
+                num[ix] = (up - dn) / (2 * eps)
+            err = np.max(np.abs(num - grad))
+            assert err <= 1e-6 * (1 + np.max(np.abs(num))), (name, causal, err)
+
+
+def pin_attention_grad_autograd(O):
+    """torch autograd (float64, CPU) of dense attention masked by the lists,
+    with GQA heads sharing K/V, rows without tokens included (zero gradient)."""
+    r = rng(22)
+    n, c, d, k, g = 160, 16, 8, 4, 4
+    for causal in (True, False):
+        lists = random_lists(r, n, c, k, causal, junk=True)
+        if not causal:
+            lists[5] = -1  # a row with nothing to attend
+        mask = torch.from_numpy(dense_mask(lists, n, c, causal))
+        q = torch.from_numpy(r.standard_normal((g, n, d))).requires_grad_()
+        kk = torch.from_numpy(r.standard_normal((n, d))).requires_grad_()
+        vv = torch.from_numpy(r.standard_normal((n, d))).requires_grad_()
+        dout = torch.from_numpy(r.standard_normal((g, n, d)))
+        s = (q @ kk.T) / math.sqrt(d)
+        s = s.masked_fill(~mask, -math.inf)
+        live = mask.any(dim=1)
+        p = torch.softmax(s.masked_fill(~live[:, None], 0.0), dim=-1) * live[:, None]
+        out = p @ vv
+        (out * dout).sum().backward()
+        dq, dk, dv = O.attention_backward(q.detach().numpy(), kk.detach().numpy(),
+                                          vv.detach().numpy(), lists, dout.numpy(), c, causal)
+        for name, a, b in (("q", dq, q.grad), ("k", dk, kk.grad), ("v", dv, vv.grad)):
+            assert np.max(np.abs(a - b.numpy())) <= 1e-11, (name, causal)
+        if not causal:
+            assert np.all(dq[:, 5] == 0.0)
+
+
+def pin_attention_grad_invariants(O):
+    """Facts fixed by the softmax: per row the dv contributions sum to the
+    group's dout (the weights sum to one); sum_t dq_t.q_t = sum_j dk_j.k_j (both
+    are scale * sum dz q.k); a row that sees one token gets dq = 0, dk = 0 and
+    dv = dout; key_block_grad agrees with the whole-head sums."""
+    r = rng(23)
+    n, c, d, k, g = 96, 8, 6, 4, 2
+    q = r.standard_normal((g, n, d))
+    keys = r.standard_normal((n, d))
+    vals = r.standard_normal((n, d))
+    dout = r.standard_normal((g, n, d))
+    lists = random_lists(r, n, c, k, True)
+    for t in (0, 17, 95):
+        cols, gq, gk, gv = O.attend_row_grad(q[:, t], keys, vals, lists[t], t, c, dout[:, t])
+        assert np.allclose(gv.sum(axis=0), dout[:, t].sum(axis=0), atol=1e-12)
+        assert np.allclose(np.sum(gq * q[:, t]), np.sum(gk * keys[cols]), atol=1e-12)
+    cols, gq, gk, gv = O.attend_row_grad(q[:, 0], keys, vals, [0], 0, c, dout[:, 0])
+    assert cols == [0] and np.all(np.abs(gq) < 1e-15) and np.all(np.abs(gk) < 1e-15)
+    assert np.allclose(gv[0], dout[:, 0].sum(axis=0), atol=1e-15)
+    dq, dk, dv = O.attention_backward(q, keys, vals, lists, dout, c, True)
+    assert np.allclose(np.sum(dq * q), np.sum(dk * keys), atol=1e-10)
+    assert np.allclose(dv.sum(axis=0), dout.sum(axis=(0, 1)), atol=1e-10)
+    for blk in (0, 3, n // c - 1):
+        bk, bv = O.key_block_grad(q, keys, vals, lists, dout, blk, c, True)
+        assert np.allclose(bk, dk[blk * c:(blk + 1) * c], atol=1e-12)
+        assert np.allclose(bv, dv[blk * c:(blk + 1) * c], atol=1e-12)
+
+
 ALL_PINS = [
     pin_tower_tables, pin_eq6_bounds, pin_pyramid_closed_form, pin_leaf_lse_is_logsumexp,
     pin_jensen_sandwich, pin_taylor_expansion, pin_no_pruning_equals_exhaustive,
     pin_dense_attention_recovered, pin_brute_force_tiny, pin_bsa_is_gemm_topk,
     pin_gqa_duplication, pin_causality_and_decode, pin_worked_causal_example, pin_tie_rule,
+    pin_attention_grad_finite_differences, pin_attention_grad_autograd,
+    pin_attention_grad_invariants,
 ]

@@ -33,7 +33,8 @@ MUTATIONS = [
     ("bsa_forced_not_charged",
      "best, margin = top_by_score(rankable, scores, topk - len(forced))\n    return RowSelection(",
      "best, margin = top_by_score(rankable, scores, topk)\n    return RowSelection("),
-    ("attention_mask_off_by_one", "if (not causal) or j <= t]", "if (not causal) or j < t]"),
+    ("attention_mask_off_by_one", "if (not causal) or j <= t]\n    kk, vv = keys[cols], values[cols]\n    outs",
+     "if (not causal) or j < t]\n    kk, vv = keys[cols], values[cols]\n    outs"),
     ("gqa_heads_averaged", "        total += reduce_logits(z, variant)\n    return total",
      "        total += reduce_logits(z, variant)\n    return total / len(q_heads)"),
     ("softmax_unnormalised", "outs.append((p @ vv) / p.sum())", "outs.append(p @ vv)"),
@@ -42,6 +43,14 @@ MUTATIONS = [
     ("pisa2_sample_variance", "np.mean(z) + 0.5 * np.var(z)", "np.mean(z) + 0.5 * np.var(z, ddof=1)"),
     ("bsa_scale_dropped", "lambda i: float(sum(scale * (leaf_sum[i] @ q) for q in q_heads))",
      "lambda i: float(sum((leaf_sum[i] @ q) for q in q_heads))"),
+    ("grad_delta_dropped", "dz = p * (vv @ g - g @ out)", "dz = p * (vv @ g)"),
+    ("grad_dk_scale_dropped", "dk += scale * np.outer(dz, q)", "dk += np.outer(dz, q)"),
+    ("grad_dq_uses_values", "dq[h] = scale * (dz @ kk)", "dq[h] = scale * (dz @ vv)"),
+    ("grad_dv_heads_not_summed", "dv += np.outer(p, g)", "dv = np.outer(p, g)"),
+    ("grad_mask_off_by_one", "if (not causal) or j <= t]\n\n\ndef attend_row_grad",
+     "if (not causal) or j < t]\n\n\ndef attend_row_grad"),
+    ("grad_block_rows_dropped", "rows = np.nonzero((np.asarray(idx_rows) == blk).any(axis=1))[0]",
+     "rows = np.nonzero((np.asarray(idx_rows) == blk).any(axis=1))[0][1:]"),
 ]
 
 

@@ -1,4 +1,4 @@
-"""PISA forward path on MI355X (gfx950): Python binding of libpisa's C ABI.
+"""PISA on MI355X (gfx950): Python binding of libpisa's C ABI.
 
 Every function here only marshals arguments (tensor pointers, sizes, the
 current HIP stream) into the C entry point of the same name; all computation
@@ -7,8 +7,8 @@ There is no CPU fallback: without the built library every call raises.
 
 Entry points (see include/pisa.h for layouts and semantics):
   pisa_build_pyramid, pisa_select, pisa_bsa_select, pisa_block_sparse_attn,
-  pisa_pyramid_append, pisa_decode_step, plus pisa_pyramid_layout and
-  pisa_workspace_bytes.
+  pisa_block_sparse_attn_backward, pisa_pyramid_append, pisa_decode_step, plus
+  pisa_pyramid_layout and pisa_workspace_bytes.
 """
 from __future__ import annotations
 
@@ -23,8 +23,8 @@ from ._lib import PisaError  # noqa: F401
 
 __all__ = [
     "Problem", "PisaError", "pisa_pyramid_layout", "pisa_workspace_bytes", "pisa_build_pyramid",
-    "pisa_select", "pisa_bsa_select", "pisa_block_sparse_attn", "pisa_pyramid_append",
-    "pisa_decode_step",
+    "pisa_select", "pisa_bsa_select", "pisa_block_sparse_attn",
+    "pisa_block_sparse_attn_backward", "pisa_pyramid_append", "pisa_decode_step",
     "pisa_profile_enable", "pisa_profile_report",
 ]
 
@@ -33,7 +33,8 @@ _STRATEGIES = {"auto": _lib.PISA_SELECT_AUTO, "fused": _lib.PISA_SELECT_FUSED,
                "two_stage": _lib.PISA_SELECT_TWO_STAGE}
 _SCORES = {"lse": 0, "mean": _lib.PISA_SCORE_MEAN, "mean_var": _lib.PISA_SCORE_MEAN_VAR}
 _OPS = {"pyramid": _lib.PISA_OP_PYRAMID, "select": _lib.PISA_OP_SELECT, "bsa": _lib.PISA_OP_BSA,
-        "attn": _lib.PISA_OP_ATTN, "decode": _lib.PISA_OP_DECODE}
+        "attn": _lib.PISA_OP_ATTN, "decode": _lib.PISA_OP_DECODE,
+        "attn_bwd": _lib.PISA_OP_ATTN_BWD}
 
 
 @dataclass
@@ -211,6 +212,33 @@ def pisa_block_sparse_attn(problem: Problem, q, k, v, block_idx, out=None, row_l
         ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(block_idx), _ptr(out), _ptr(row_lse),
         _ptr(ws), ws_bytes, _stream(stream)))
     return out, row_lse
+
+
+def pisa_block_sparse_attn_backward(problem: Problem, q, k, v, block_idx, out, row_lse, dout,
+                                    dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Gradients of the block-sparse attention with block_idx held fixed ->
+    (dq [B,Hq,N,d], dk [B,Hkv,N,d], dv [B,Hkv,N,d]).  out and row_lse are the
+    forward's outputs for these inputs."""
+    p = problem
+    _need(q, "q", (p.batch, p.heads_q, p.seq_len, p.head_dim), p.dtype)
+    _need(k, "k", (p.batch, p.heads_kv, p.seq_len, p.head_dim), p.dtype)
+    _need(v, "v", (p.batch, p.heads_kv, p.seq_len, p.head_dim), p.dtype)
+    _need(block_idx, "block_idx", (p.batch, p.heads_kv, p.seq_len, p.topk), torch.int32)
+    _need(out, "out", tuple(q.shape), p.dtype)
+    _need(row_lse, "row_lse", (p.batch, p.heads_q, p.seq_len), torch.float32)
+    _need(dout, "dout", tuple(q.shape), p.dtype)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _need(dq, "dq", tuple(q.shape), p.dtype)
+    _need(dk, "dk", tuple(k.shape), p.dtype)
+    _need(dv, "dv", tuple(v.shape), p.dtype)
+    ws, ws_bytes = _workspace(p, "attn_bwd", workspace, q.device)
+    c = p.to_c()
+    _lib.check("pisa_block_sparse_attn_backward", _lib.load().pisa_block_sparse_attn_backward(
+        ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(block_idx), _ptr(out), _ptr(row_lse),
+        _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws_bytes, _stream(stream)))
+    return dq, dk, dv
 
 
 def pisa_pyramid_append(problem: Problem, cache_len, k_cache, pyramid, stream=None):

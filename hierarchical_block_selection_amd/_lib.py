@@ -21,12 +21,13 @@ PISA_SCORE_MEAN = 4
 PISA_SCORE_MEAN_VAR = 8
 PISA_MAX_LEVELS = 32
 
-PISA_OP_PYRAMID, PISA_OP_SELECT, PISA_OP_BSA, PISA_OP_ATTN, PISA_OP_DECODE = range(5)
+PISA_OP_PYRAMID, PISA_OP_SELECT, PISA_OP_BSA, PISA_OP_ATTN, PISA_OP_DECODE, PISA_OP_ATTN_BWD = range(6)
 PISA_SELECT_AUTO, PISA_SELECT_FUSED, PISA_SELECT_TWO_STAGE = range(3)
 
 EXPORTED = (
     "pisa_pyramid_layout", "pisa_workspace_bytes", "pisa_build_pyramid", "pisa_select",
-    "pisa_bsa_select", "pisa_block_sparse_attn", "pisa_pyramid_append", "pisa_decode_step",
+    "pisa_bsa_select", "pisa_block_sparse_attn", "pisa_block_sparse_attn_backward",
+    "pisa_pyramid_append", "pisa_decode_step",
     "pisa_status_string",
     "pisa_last_error", "pisa_profile_enable", "pisa_profile_report",
 )
@@ -70,6 +71,7 @@ def load(path: str = LIB_PATH):
         "pisa_select": [pp, vp, vp, vp, vp, vp, i32, vp, sz, vp],
         "pisa_bsa_select": [pp, vp, vp, vp, vp, vp, sz, vp],
         "pisa_block_sparse_attn": [pp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "pisa_block_sparse_attn_backward": [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "pisa_decode_step": [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
     }
     for name, args in sig.items():

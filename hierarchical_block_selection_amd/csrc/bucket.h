@@ -175,6 +175,96 @@ __global__ void scatter_global_kernel(const int* __restrict__ node, int* __restr
   }
 }
 
+// Stable variant: each bucket lists its pairs in increasing (row, slot) order,
+// so the pairs, their grouping into work items and every sum taken over them
+// in that order are the same run to run.
+//   count_wg:  per (row chunk, head), the chunk's histogram written out whole
+//              to wgc[head][chunk][node] (no global atomics);
+//   wg_prefix: per bucket, exclusive prefix of wgc over the chunks (in place)
+//              and the bucket's total;
+//   scatter_stable: one wave per (row chunk, head) walks its slots in order,
+//              64 at a time; lanes holding the same node are ranked by lane
+//              (ballot), and a running base per node lives in LDS.
+__global__ __launch_bounds__(256) void count_wg_kernel(const int* __restrict__ node,
+                                                       int* __restrict__ wgc, int n_tok, int topk,
+                                                       int m) {
+  extern __shared__ int hist[];  // [m]
+  for (int i = threadIdx.x; i < m; i += blockDim.x) hist[i] = 0;
+  __syncthreads();
+  const int bh = blockIdx.y;
+  const int t0 = blockIdx.x * kRowsPerGroup, t1 = min(t0 + kRowsPerGroup, n_tok);
+  const int* src = node + ((size_t)bh * n_tok) * topk;
+  const int i1 = t1 * topk;
+  for (int ib = t0 * topk + threadIdx.x; ib < i1; ib += kBatch * blockDim.x) {
+    int xs[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) xs[k] = src[min(ib + k * (int)blockDim.x, i1 - 1)];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k)
+      if (ib + k * (int)blockDim.x < i1 && xs[k] >= 0 && xs[k] < m) atomicAdd(&hist[xs[k]], 1);
+  }
+  __syncthreads();
+  int* dst = wgc + ((size_t)bh * gridDim.x + blockIdx.x) * m;
+  for (int i = threadIdx.x; i < m; i += blockDim.x) dst[i] = hist[i];
+}
+
+__global__ __launch_bounds__(256) void wg_prefix_kernel(int* __restrict__ wgc,
+                                                        int* __restrict__ counts, int n_chunks,
+                                                        int m, int n_buckets) {
+  const int bucket = blockIdx.x * blockDim.x + threadIdx.x;
+  if (bucket >= n_buckets) return;
+  const int bh = bucket / m, x = bucket % m;
+  int* col = wgc + (size_t)bh * n_chunks * m + x;
+  int run = 0;
+  for (int c = 0; c < n_chunks; ++c) {
+    const int v = col[(size_t)c * m];
+    col[(size_t)c * m] = run;
+    run += v;
+  }
+  counts[bucket] = run;
+}
+
+__global__ __launch_bounds__(64) void scatter_stable_kernel(
+    const int* __restrict__ node, const int* __restrict__ offsets, const int* __restrict__ wgc,
+    int* __restrict__ pairs, int* __restrict__ inv, int n_tok, int topk, int m) {
+  extern __shared__ int base[];  // [m]: next position of each node's pairs
+  const int bh = blockIdx.y;
+  const int* pre = wgc + ((size_t)bh * gridDim.x + blockIdx.x) * m;
+  for (int i = threadIdx.x; i < m; i += blockDim.x) base[i] = offsets[(size_t)bh * m + i] + pre[i];
+  __syncthreads();
+  const int lane = threadIdx.x;
+  const int t0 = blockIdx.x * kRowsPerGroup, t1 = min(t0 + kRowsPerGroup, n_tok);
+  const size_t row0 = (size_t)bh * n_tok;
+  const int* src = node + row0 * topk;
+  const int i1 = t1 * topk;
+  const uint64_t below = (uint64_t(1) << lane) - 1;
+  for (int ib = t0 * topk; ib < i1; ib += 64) {
+    const int i = ib + lane;
+    const int x = i < i1 ? src[i] : -1;
+    const bool live = x >= 0 && x < m;
+    uint64_t pending = __ballot(live);
+    int rank = 0, cnt = 0;
+    while (pending) {
+      const int v = __builtin_amdgcn_readlane(x, (int)__builtin_ctzll(pending));
+      const uint64_t same = __ballot(live && x == v);
+      if (live && x == v) {
+        rank = __popcll(same & below);
+        cnt = __popcll(same);
+      }
+      pending &= ~same;
+    }
+    int pos = 0;
+    if (live) pos = base[x] + rank;
+    wave_lds_sync();  // every lane has read base[] before the leaders move it
+    if (live && rank == 0) base[x] += cnt;
+    wave_lds_sync();
+    if (live) {
+      pairs[pos] = (int)(((row0 + i / topk) << 5) | (i % topk));
+      if (inv) inv[row0 * topk + i] = pos;
+    }
+  }
+}
+
 }  // namespace
 
 // Work item -> (bucket, first pair, pair count) from the scan's offsets.
@@ -229,6 +319,32 @@ inline hipError_t sort_pairs(const int* node, int batch_heads, int n_tok, int to
   else
     hipLaunchKernelGGL(scatter_global_kernel, dim3(grid_for(n_slots)), dim3(256), 0, st, node,
                        cursors, pairs, inv, n_tok, topk, m, n_slots);
+  return hipGetLastError();
+}
+
+// Rows handled per count/scatter workgroup, and the per-chunk count matrix
+// the stable sort needs (ints).
+inline int row_chunks(int n_tok) { return (n_tok + kRowsPerGroup - 1) / kRowsPerGroup; }
+inline size_t stable_wgc_ints(int batch_heads, int n_tok, int m) {
+  return (size_t)batch_heads * row_chunks(n_tok) * m;
+}
+
+// sort_pairs with each bucket in increasing (row, slot) order (m <=
+// kMaxLocalBuckets; callers check).  wgc: stable_wgc_ints(...) ints.
+inline hipError_t sort_pairs_stable(const int* node, int batch_heads, int n_tok, int topk, int m,
+                                    int per_item, int* counts, int* offsets, int* cursors,
+                                    int* item_offsets, int* wgc, int* pairs, int* inv,
+                                    hipStream_t st) {
+  const int n_buckets = batch_heads * m;
+  const dim3 grid(row_chunks(n_tok), batch_heads);
+  hipLaunchKernelGGL(count_wg_kernel, grid, dim3(256), sizeof(int) * m, st, node, wgc, n_tok, topk,
+                     m);
+  hipLaunchKernelGGL(wg_prefix_kernel, dim3((n_buckets + 255) / 256), dim3(256), 0, st, wgc, counts,
+                     (int)grid.x, m, n_buckets);
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, counts, offsets, cursors,
+                     item_offsets, n_buckets, per_item);
+  hipLaunchKernelGGL(scatter_stable_kernel, grid, dim3(64), sizeof(int) * m, st, node, offsets, wgc,
+                     pairs, inv, n_tok, topk, m);
   return hipGetLastError();
 }
 

@@ -88,6 +88,8 @@ int check_problem(const pisa_problem* p, int op, pisa::LaunchShape* s) {
   s->variant = (p->flags & PISA_SCORE_MEAN) ? 1 : (p->flags & PISA_SCORE_MEAN_VAR) ? 2 : 0;
   s->scale = p->scale > 0.f ? p->scale : 1.0f / std::sqrt((float)p->head_dim);
   if (!layout(p->seq_len, p->block, &s->lv)) return fail(PISA_ERR_INVALID, "pyramid too tall");
+  if (op == PISA_OP_ATTN_BWD && !pisa::attn_bwd_supported(*s))
+    return fail(PISA_ERR_UNSUPPORTED, "the backward needs bf16, block 64 and a power-of-two group");
   if (op == PISA_OP_BSA && s->lv.size[0] > 4096)
     return fail(PISA_ERR_UNSUPPORTED, "BSA supports at most 4096 leaf blocks");
   return PISA_OK;
@@ -99,6 +101,7 @@ size_t ws_bytes_for(const pisa::LaunchShape& s, int op) {
     case PISA_OP_BSA: return pisa::bsa_ws_bytes(s);
     case PISA_OP_ATTN: return pisa::attn_ws_bytes(s);
     case PISA_OP_DECODE: return pisa::decode_ws_bytes(s);
+    case PISA_OP_ATTN_BWD: return pisa::attn_bwd_ws_bytes(s);
     default: return 0;
   }
 }
@@ -131,7 +134,7 @@ int pisa_pyramid_layout(int32_t seq_len, int32_t block, int32_t branch, int32_t*
 
 int pisa_workspace_bytes(const pisa_problem* problem, int32_t op, size_t* bytes) {
   if (!bytes) return fail(PISA_ERR_INVALID, "bytes is NULL");
-  if (op < PISA_OP_PYRAMID || op > PISA_OP_DECODE) return fail(PISA_ERR_INVALID, "bad op");
+  if (op < PISA_OP_PYRAMID || op > PISA_OP_ATTN_BWD) return fail(PISA_ERR_INVALID, "bad op");
   pisa::LaunchShape s;
   const int rc = check_problem(problem, op, &s);
   if (rc != PISA_OK) return rc;
@@ -201,6 +204,21 @@ int pisa_block_sparse_attn(const pisa_problem* problem, const void* q, const voi
   const hipError_t e = pisa::launch_attn(s, q, k, v, block_idx, out, row_lse, ws,
                                          static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PISA_OK : fail_hip(e, "pisa_block_sparse_attn");
+}
+
+int pisa_block_sparse_attn_backward(const pisa_problem* problem, const void* q, const void* k,
+                                    const void* v, const int32_t* block_idx, const void* out,
+                                    const float* row_lse, const void* dout, void* dq, void* dk,
+                                    void* dv, void* ws, size_t ws_bytes, void* stream) {
+  pisa::LaunchShape s;
+  int rc = check_problem(problem, PISA_OP_ATTN_BWD, &s);
+  if (rc != PISA_OK) return rc;
+  if (!q || !k || !v || !block_idx || !out || !row_lse || !dout || !dq || !dk || !dv)
+    return fail(PISA_ERR_INVALID, "null tensor pointer");
+  if ((rc = check_ws(s, PISA_OP_ATTN_BWD, ws, ws_bytes)) != PISA_OK) return rc;
+  const hipError_t e = pisa::launch_attn_bwd(s, q, k, v, block_idx, out, row_lse, dout, dq, dk, dv,
+                                             ws, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PISA_OK : fail_hip(e, "pisa_block_sparse_attn_backward");
 }
 
 int pisa_pyramid_append(const pisa_problem* problem, const int32_t* cache_len,

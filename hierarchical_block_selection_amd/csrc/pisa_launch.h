@@ -60,6 +60,14 @@ size_t attn_ws_bytes(const LaunchShape& s);
 hipError_t launch_attn(const LaunchShape& s, const void* q, const void* k, const void* v,
                        const int32_t* idx, void* out, float* lse, void* ws, hipStream_t st);
 
+// Backward of the block-sparse attention (block lists held fixed).
+bool attn_bwd_supported(const LaunchShape& s);
+size_t attn_bwd_ws_bytes(const LaunchShape& s);
+hipError_t launch_attn_bwd(const LaunchShape& s, const void* q, const void* k, const void* v,
+                           const int32_t* idx, const void* out, const float* lse,
+                           const void* dout, void* dq, void* dk, void* dv, void* ws,
+                           hipStream_t st);
+
 // Decode step.
 size_t decode_ws_bytes(const LaunchShape& s);
 hipError_t launch_decode(const LaunchShape& s, const int32_t* cache_len, const void* q,

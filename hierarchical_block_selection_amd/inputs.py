@@ -123,6 +123,49 @@ def decode_inputs(batch, heads_q, heads_kv, capacity, head_dim, dtype=torch.bflo
     return DecodeInputs(q, kc, vc, torch.tensor(lens, dtype=torch.int32, device=device))
 
 
+def block_lists(batch, heads_kv, seq_len, block, topk, seed, causal=True, device="cpu"):
+    """Leaf lists shaped like a selector's output, for the attention and its
+    backward when the lists are an input: [B, Hkv, N, K] int32, each row
+    ascending and padded with -1.  Causal: row t (leaf c = t // C) holds the
+    blocks 0, c - 1 and c plus distinct blocks drawn uniformly from [0, c];
+    otherwise K distinct blocks from all leaves.  Each row draws 2K candidates
+    and keeps the first distinct ones, so a row may hold fewer than
+    min(K, eligible) blocks when draws collide."""
+    import numpy as np
+
+    n_leaves = -(-seq_len // block)
+    rows = batch * heads_kv * seq_len
+    rng = np.random.default_rng(seed)
+    t = np.tile(np.arange(seq_len), batch * heads_kv)
+    cur = t // block
+    hi = cur if causal else np.full_like(cur, n_leaves - 1)
+    draws = (rng.random((rows, 2 * topk)) * (hi[:, None] + 1)).astype(np.int64)
+    if causal:
+        forced = np.stack([np.zeros_like(cur), np.maximum(cur - 1, 0), cur], axis=1)
+        vals = np.concatenate([forced, draws], axis=1)
+    else:
+        vals = draws
+    width = vals.shape[1]
+    pri = np.broadcast_to(np.arange(width), vals.shape)
+    order = np.lexsort((pri, vals), axis=1)
+    sv = np.take_along_axis(vals, order, axis=1)
+    sp = np.take_along_axis(pri, order, axis=1).copy()
+    dup = np.zeros_like(sv, dtype=bool)
+    dup[:, 1:] = sv[:, 1:] == sv[:, :-1]
+    big = width + 1
+    sp[dup] = big
+    keep = np.argsort(sp, axis=1, kind="stable")[:, :topk]
+    kv = np.take_along_axis(sv, keep, axis=1)
+    kp = np.take_along_axis(sp, keep, axis=1)
+    kv = np.where(kp == big, np.iinfo(np.int64).max, kv)
+    kv.sort(axis=1)
+    kv[kv == np.iinfo(np.int64).max] = -1
+    if kv.shape[1] < topk:
+        kv = np.concatenate([kv, np.full((rows, topk - kv.shape[1]), -1)], axis=1)
+    out = torch.from_numpy(kv.astype(np.int32)).reshape(batch, heads_kv, seq_len, topk)
+    return out.to(device)
+
+
 # Workload shapes of the five configurations: prefill c1-c4 (c4 sweeps N) and
 # the decode step c5.  Sizes only; inputs come from prefill_inputs /
 # decode_inputs with the given seed and recipe.

@@ -1,8 +1,9 @@
 /*
- * pisa.h - C ABI of the MI355X (gfx950) implementation of PISA's forward path:
+ * pisa.h - C ABI of the MI355X (gfx950) implementation of PISA:
  * the mean-pooled key pyramid, coarse-to-fine pyramid Top-K block selection
  * with LogSumExp scoring, the flat BSA selector it is compared with,
- * block-sparse attention over the selected blocks, and a GQA decode step.
+ * block-sparse attention over the selected blocks and its backward with the
+ * block lists held fixed, pyramid upkeep for decode, and a GQA decode step.
  *
  * Source of the method: "Block Sparse Attention with Log-Linear Complexity"
  * (PISA), as laid out by the close-reading page "论文精读 · Block Sparse
@@ -99,7 +100,8 @@ enum {
   PISA_OP_SELECT = 1,
   PISA_OP_BSA = 2,
   PISA_OP_ATTN = 3,
-  PISA_OP_DECODE = 4
+  PISA_OP_DECODE = 4,
+  PISA_OP_ATTN_BWD = 5
 };
 
 /* Selection strategies for pisa_select (problem-independent hint). */
@@ -191,6 +193,31 @@ int pisa_bsa_select(const pisa_problem* problem, const void* q, const float* pyr
 int pisa_block_sparse_attn(const pisa_problem* problem, const void* q, const void* k,
                            const void* v, const int32_t* block_idx, void* out, float* row_lse,
                            void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of pisa_block_sparse_attn with block_idx held fixed (§5.3,
+ * "backward": the selected indices do not move and gradients flow only
+ * through the attention entries they select).  For every query head h and row
+ * t with token set J (the tokens pisa_block_sparse_attn attends), with
+ * P_j = exp(scale q.k_j - row_lse) and D = dout . out:
+ *   dq      = scale * sum_j P_j (dout . v_j - D) k_j
+ *   dk_j   += scale * P_j (dout . v_j - D) q
+ *   dv_j   += P_j dout
+ * dk and dv sum over every query head of the KV group and every row whose
+ * list holds the key's block; keys no row attends get zeros.
+ *   q, k, v, block_idx: the forward's inputs (same rules for block_idx)
+ *   out, row_lse:       the forward's outputs for exactly these inputs
+ *                       (row_lse is required)
+ *   dout:      [B, Hq, N, d] dtype, gradient of the loss w.r.t. out
+ *   dq:        [B, Hq, N, d] dtype, out (every row written)
+ *   dk, dv:    [B, Hkv, N, d] dtype, out (every row written)
+ *   ws/ws_bytes: pisa_workspace_bytes(PISA_OP_ATTN_BWD) bytes
+ * Supported: bf16, C = 64, d in {64, 128}, Hq / Hkv a power of two <= 16,
+ * ceil(N / C) <= 8192 (PISA_ERR_UNSUPPORTED otherwise).  Deterministic: each
+ * block's rows are visited in row order and every sum has a fixed order. */
+int pisa_block_sparse_attn_backward(const pisa_problem* problem, const void* q, const void* k,
+                                    const void* v, const int32_t* block_idx, const void* out,
+                                    const float* row_lse, const void* dout, void* dq, void* dk,
+                                    void* dv, void* ws, size_t ws_bytes, void* stream);
 
 /* One decode step (§5.1: single fused stage for decode; §5.3 pyramid cache):
  * for each sequence b the new query sits at t = cache_len[b] - 1 and its key

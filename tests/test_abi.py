@@ -107,6 +107,8 @@ def test_invalid_problems_rejected_by_every_entry_point(kw, code):
     assert L.pisa_decode_step(pp, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, 1 << 40,
                               None) == code
     assert L.pisa_pyramid_append(pp, ptr, ptr, ptr, None) == code
+    assert L.pisa_block_sparse_attn_backward(pp, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr,
+                                             ptr, 1 << 40, None) == code
     sz = ctypes.c_size_t()
     assert L.pisa_workspace_bytes(pp, 0, ctypes.byref(sz)) == code
     assert L.pisa_last_error()
@@ -170,3 +172,44 @@ def test_score_variants_need_the_per_query_selector():
     with pytest.raises(ValueError):
         from hierarchical_block_selection_amd import Problem
         Problem(1, 1, 1, 64, 64, score="max").to_c()
+
+
+def test_backward_arguments():
+    """The backward refuses shapes outside its kernels (fp32, C != 64, a group
+    that is not a power of two, more than 8192 leaf blocks), a missing row_lse
+    or output, and a short
+    workspace; its workspace is the sort's maps, D, the bf16 dq partials and
+    the fp32 per-item dk/dv partials."""
+    L = lib()
+    dummy = ctypes.create_string_buffer(64)
+    ptr = ctypes.cast(dummy, ctypes.c_void_p)
+    bwd = L.pisa_block_sparse_attn_backward
+    for kw in (dict(dtype=_lib.PISA_F32), dict(block=32), dict(heads_q=6, heads_kv=2),
+               dict(seq_len=64 * 8192 + 1)):
+        p = problem(**kw)
+        assert bwd(ctypes.byref(p), ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, 1 << 40,
+                   None) == _lib.PISA_ERR_UNSUPPORTED, kw
+        sz = ctypes.c_size_t()
+        assert L.pisa_workspace_bytes(ctypes.byref(p), _lib.PISA_OP_ATTN_BWD,
+                                      ctypes.byref(sz)) == _lib.PISA_ERR_UNSUPPORTED
+    p = problem(heads_q=8, heads_kv=2, seq_len=3000, topk=8)
+    pp = ctypes.byref(p)
+    sz = ctypes.c_size_t()
+    assert L.pisa_workspace_bytes(pp, _lib.PISA_OP_ATTN_BWD, ctypes.byref(sz)) == 0
+
+    def a256(x):
+        return (x + 255) // 256 * 256
+    g, slots, m1 = 4, 1 * 2 * 3000 * 8, 2 * 47
+    items = (slots + 256 - 1) // 256 + m1  # 1024 columns per item = 256 pairs at G = 4
+    chunks = -(-3000 // 512)  # row chunks of the stable sort
+    want = (a256(4 * m1) + a256(4 * (m1 + 1)) + a256(4 * m1) + a256(4 * (m1 + 1))
+            + a256(4 * 2 * chunks * 47) + a256(4 * slots) + a256(4 * slots) + a256(4 * 8 * 3000) + a256(2 * slots * g * 128)
+            + a256(4 * items * 2 * 64 * 128))
+    assert sz.value == want
+    args = [ptr] * 10
+    for i in range(10):
+        a = list(args)
+        a[i] = None
+        assert bwd(pp, *a, ptr, sz.value, None) == _lib.PISA_ERR_INVALID, i
+    assert bwd(pp, *args, ptr, sz.value - 1, None) == _lib.PISA_ERR_WORKSPACE
+    assert bwd(pp, *args, None, sz.value, None) == _lib.PISA_ERR_WORKSPACE

@@ -51,8 +51,11 @@ typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
 typedef __attribute__((ext_vector_type(2))) unsigned int u32x2_t;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+// Word i (0..3, may differ per lane) of v.
 __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
-  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+  const uint32_t a = (i & 1) ? v.y : v.x;
+  const uint32_t b = (i & 1) ? v.w : v.z;
+  return (i & 2) ? b : a;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -131,11 +134,11 @@ struct ChunkRegs {
 };
 
 template <int D, int G>
-__device__ __forceinline__ void chunk_fetch(ChunkRegs<D, G>& cr, int chunk, const int* __restrict__ pairs,
-                                            int start, int rows, const bf16_t* __restrict__ qh,
+__device__ __forceinline__ void chunk_fetch(ChunkRegs<D, G>& cr, int chunk, const int* tok_s,
+                                            int rows, const bf16_t* __restrict__ qh,
                                             const bf16_t* __restrict__ doh,
                                             const float* __restrict__ lse_h,
-                                            const float* __restrict__ delta_h, int bh, int n_tok,
+                                            const float* __restrict__ delta_h, int n_tok,
                                             int tok0, int n_keys, bool causal) {
   constexpr int R = D / 32;
   constexpr int PIECES = D / 8;  // 16-byte pieces per row
@@ -147,16 +150,14 @@ __device__ __forceinline__ void chunk_fetch(ChunkRegs<D, G>& cr, int chunk, cons
 #pragma unroll
   for (int i = 0; i < R; ++i) {
     const int r = min(chunk * kBwdCols + R * cg + i, rows - 1);
-    const int pid = pairs[start + r / G];
-    const int t = (pid >> 5) - bh * n_tok;  // pair = (row << 5) | slot
+    const int t = tok_s[r / G];
     const int h = r % G;
     cr.x[i] = *reinterpret_cast<const uint4*>(src + ((size_t)h * n_tok + t) * D + c8);
   }
   if (tid < kBwdCols) {
     const int r0 = chunk * kBwdCols + tid;
     const int r = min(r0, rows - 1);
-    const int pid = pairs[start + r / G];
-    const int t = (pid >> 5) - bh * n_tok;
+    const int t = tok_s[r / G];
     const int h = r % G;
     cr.lse2 = lse_h[(size_t)h * n_tok + t] * kLog2e;
     cr.dl = delta_h[(size_t)h * n_tok + t];
@@ -181,6 +182,7 @@ struct BwdLds {
   float lse2[kBwdCols];
   float dl[kBwdCols];
   int lim[kBwdCols];
+  int tok[kBwdItemCols];  // query position of each pair of the work item
 };
 
 template <int D, int G>
@@ -197,16 +199,20 @@ __device__ __forceinline__ void chunk_stage(const ChunkRegs<D, G>& cr, BwdLds<D>
 #pragma unroll
   for (int i = 0; i < R; ++i)
     *reinterpret_cast<uint4*>(&rows[(R * cg + i) * KROW + c8]) = cr.x[i];
-  // transposed: dims c8..c8+7, columns R*cg..R*cg+R-1 (R consecutive bf16)
+  // transposed: dims c8..c8+7, columns R*cg..R*cg+R-1 (R consecutive bf16).
+  // Lane p writes dim c8 + (e + p) % 8 at step e: without the rotation the
+  // lanes of one store would sit 8 rows apart, on the same few banks.
+  const int p = tt % PIECES;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
+    const int ee = (e + p) & 7;
     uint32_t h[R];
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-      const uint32_t w = word(cr.x[i], e / 2);
-      h[i] = (e & 1) ? (w >> 16) : (w & 0xffffu);
+      const uint32_t w = word(cr.x[i], ee >> 1);
+      h[i] = (ee & 1) ? (w >> 16) : (w & 0xffffu);
     }
-    bf16_t* dst = &tr[(c8 + e) * CT + R * cg];
+    bf16_t* dst = &tr[(c8 + ee) * CT + R * cg];
     if (R == 4)
       *reinterpret_cast<uint2*>(dst) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
     else
@@ -258,10 +264,16 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_kernel(
   const bf16_t* doh = dout + head0 * n_tok * D;
   const float* lse_h = lse + head0 * n_tok;
   const float* delta_h = delta + head0 * n_tok;
+  for (int i = tid; i < len; i += kBwdThreads)
+    L.tok[i] = (pairs[start + i] >> 5) - bh * n_tok;  // pair = (row << 5) | slot
+  __syncthreads();
 
-  ChunkRegs<D, G> cr;
-  chunk_fetch<D, G>(cr, 0, pairs, start, rows, qh, doh, lse_h, delta_h, bh, n_tok, tok0, n_keys,
-                    causal != 0);
+  // Two chunks in flight: chunk c + 2 is requested while chunk c computes.
+  ChunkRegs<D, G> cra, crb;
+  chunk_fetch<D, G>(cra, 0, L.tok, rows, qh, doh, lse_h, delta_h, n_tok, tok0, n_keys, causal != 0);
+  if (n_chunks > 1)
+    chunk_fetch<D, G>(crb, 1, L.tok, rows, qh, doh, lse_h, delta_h, n_tok, tok0, n_keys,
+                      causal != 0);
 
   // This wave's keys as B operands (K rows for S, V rows for dP), rows past
   // the sequence end repeat the last key (masked below).
@@ -305,12 +317,12 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_kernel(
     dv_acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  for (int ch = 0; ch < n_chunks; ++ch) {
+  auto chunk = [&](int ch, ChunkRegs<D, G>& cr) {
     chunk_stage<D, G>(cr, L);
     __syncthreads();
-    if (ch + 1 < n_chunks)
-      chunk_fetch<D, G>(cr, ch + 1, pairs, start, rows, qh, doh, lse_h, delta_h, bh, n_tok, tok0,
-                        n_keys, causal != 0);
+    if (ch + 2 < n_chunks)
+      chunk_fetch<D, G>(cr, ch + 2, L.tok, rows, qh, doh, lse_h, delta_h, n_tok, tok0, n_keys,
+                        causal != 0);
     // S and dP for columns 16ct + 4g + e, key my_key.
     f32x4_t sacc[2], pacc[2];
 #pragma unroll
@@ -384,6 +396,10 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_kernel(
         }
       }
     }
+  };
+  for (int ch = 0; ch < n_chunks; ch += 2) {
+    chunk(ch, cra);
+    if (ch + 1 < n_chunks) chunk(ch + 1, crb);
   }
 
   // dK (times scale) and dV of keys my_key: lane holds d = 16m + 4g + e.

@@ -216,10 +216,16 @@ __global__ __launch_bounds__(256) void wg_prefix_kernel(int* __restrict__ wgc,
   const int bh = bucket / m, x = bucket % m;
   int* col = wgc + (size_t)bh * n_chunks * m + x;
   int run = 0;
-  for (int c = 0; c < n_chunks; ++c) {
-    const int v = col[(size_t)c * m];
-    col[(size_t)c * m] = run;
-    run += v;
+  for (int c0 = 0; c0 < n_chunks; c0 += kBatch) {  // kBatch loads in flight
+    int v[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) v[k] = col[(size_t)min(c0 + k, n_chunks - 1) * m];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k)
+      if (c0 + k < n_chunks) {
+        col[(size_t)(c0 + k) * m] = run;
+        run += v[k];
+      }
   }
   counts[bucket] = run;
 }
@@ -238,29 +244,41 @@ __global__ __launch_bounds__(64) void scatter_stable_kernel(
   const int* src = node + row0 * topk;
   const int i1 = t1 * topk;
   const uint64_t below = (uint64_t(1) << lane) - 1;
-  for (int ib = t0 * topk; ib < i1; ib += 64) {
-    const int i = ib + lane;
-    const int x = i < i1 ? src[i] : -1;
-    const bool live = x >= 0 && x < m;
-    uint64_t pending = __ballot(live);
-    int rank = 0, cnt = 0;
-    while (pending) {
-      const int v = __builtin_amdgcn_readlane(x, (int)__builtin_ctzll(pending));
-      const uint64_t same = __ballot(live && x == v);
-      if (live && x == v) {
-        rank = __popcll(same & below);
-        cnt = __popcll(same);
-      }
-      pending &= ~same;
+  constexpr int S = 8;  // steps whose node loads are issued together
+  for (int ib0 = t0 * topk; ib0 < i1; ib0 += S * 64) {
+    int xs[S];
+#pragma unroll
+    for (int u = 0; u < S; ++u) {
+      const int i = ib0 + u * 64 + lane;
+      xs[u] = i < i1 ? src[i] : -1;
     }
-    int pos = 0;
-    if (live) pos = base[x] + rank;
-    wave_lds_sync();  // every lane has read base[] before the leaders move it
-    if (live && rank == 0) base[x] += cnt;
-    wave_lds_sync();
-    if (live) {
-      pairs[pos] = (int)(((row0 + i / topk) << 5) | (i % topk));
-      if (inv) inv[row0 * topk + i] = pos;
+#pragma unroll
+    for (int u = 0; u < S; ++u) {
+      const int ib = ib0 + u * 64;
+      if (ib >= i1) break;
+      const int i = ib + lane;
+      const int x = xs[u];
+      const bool live = x >= 0 && x < m;
+      uint64_t pending = __ballot(live);
+      int rank = 0, cnt = 0;
+      while (pending) {
+        const int v = __builtin_amdgcn_readlane(x, (int)__builtin_ctzll(pending));
+        const uint64_t same = __ballot(live && x == v);
+        if (live && x == v) {
+          rank = __popcll(same & below);
+          cnt = __popcll(same);
+        }
+        pending &= ~same;
+      }
+      int pos = 0;
+      if (live) pos = base[x] + rank;
+      wave_lds_sync();  // every lane has read base[] before the leaders move it
+      if (live && rank == 0) base[x] += cnt;
+      wave_lds_sync();
+      if (live) {
+        pairs[pos] = (int)(((row0 + i / topk) << 5) | (i % topk));
+        if (inv) inv[row0 * topk + i] = pos;
+      }
     }
   }
 }
@@ -268,15 +286,26 @@ __global__ __launch_bounds__(64) void scatter_stable_kernel(
 }  // namespace
 
 // Work item -> (bucket, first pair, pair count) from the scan's offsets.
+// Called by every lane of a wave with the same item (the kernels call it
+// first thing, with all lanes active).  The bucket is the largest b with
+// item_offsets[b] <= item, found by a 64-way search: each round the wave's
+// lanes probe 64 evenly spaced entries at once, so 2^18 buckets take three
+// rounds of parallel loads instead of eighteen dependent ones.
 __device__ __forceinline__ bool locate_item(const int* __restrict__ item_offsets,
                                             const int* __restrict__ offsets, int n_buckets,
                                             int item, int per_item, int* bucket, int* start,
                                             int* len) {
   if (item >= item_offsets[n_buckets]) return false;
-  int lo = 0, hi = n_buckets - 1;  // largest bucket with item_offsets[b] <= item
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (item_offsets[mid] <= item) lo = mid; else hi = mid - 1;
+  const int lane = threadIdx.x & 63;
+  int lo = 0, hi = n_buckets;  // item_offsets[lo] <= item; answer in [lo, hi)
+  while (hi - lo > 1) {
+    const int step = (hi - lo + 63) >> 6;
+    const int probe = lo + lane * step;
+    const bool ok = probe < hi && item_offsets[probe] <= item;
+    const uint64_t m = __ballot(ok);  // a prefix of the lanes (item_offsets is sorted)
+    const int last = 63 - __builtin_clzll(m);
+    lo += last * step;
+    hi = min(hi, lo + step);
   }
   const int k = item - item_offsets[lo];
   *bucket = lo;

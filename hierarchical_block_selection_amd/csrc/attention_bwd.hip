@@ -25,7 +25,8 @@
 //       dV^T += dO^T P,  dK^T += Q^T dS  (the contraction runs over the chunk's
 //                                         columns; Q^T and dO^T come from LDS)
 //       dQ^T  = K^T dS^T for the wave's quarter of d (dS passes through LDS)
-//     Each column's dQ over this block is written (bf16) in bucket order.  At
+//     Each column's dQ over this block goes (bf16) through an LDS tile and
+//     leaves as whole rows, in bucket order.  At
 //     the end the block's dK, dV go straight to the outputs when its bucket is
 //     one work item, else to a per-item fp32 partial;
 //  4. dq combine: the row's K partials summed in slot order, times scale;
@@ -183,6 +184,7 @@ struct BwdLds {
   float dl[kBwdCols];
   int lim[kBwdCols];
   int tok[kBwdItemCols];  // query position of each pair of the work item
+  bf16_t dqt[kBwdCols * KROW];  // the chunk's dQ rows, stored out whole
 };
 
 template <int D, int G>
@@ -374,7 +376,6 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_kernel(
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
       const int col = 16 * ct + li;
-      const int r = ch * kBwdCols + col;
       bf16x8_t bs[2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
@@ -384,17 +385,25 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_kernel(
         f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ktop[m][0], bs[0], acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ktop[m][1], bs[1], acc, 0, 0, 0);
-        if (r < rows) {
-          bf16x4_t o4;
+        bf16x4_t o4;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o4[e] = (__bf16)acc[e];
-          // streamed out: read once, by the combine
-          __builtin_nontemporal_store(
-              __builtin_bit_cast(u32x2_t, o4),
-              reinterpret_cast<u32x2_t*>(part_dq + ((size_t)start * G + r) * D +
-                                         16 * (QMT * w + m) + 4 * g));
-        }
+        for (int e = 0; e < 4; ++e) o4[e] = (__bf16)acc[e];
+        *reinterpret_cast<uint2*>(&L.dqt[col * KROW + 16 * (QMT * w + m) + 4 * g]) =
+            __builtin_bit_cast(uint2, o4);
       }
+    }
+    __syncthreads();
+    // Whole rows leave as 16-byte pieces (1 KB per store instruction); each is
+    // read once, by the dq combine.
+#pragma unroll
+    for (int j = 0; j < kBwdCols * (D / 8) / kBwdThreads; ++j) {
+      const int x = tid + kBwdThreads * j;
+      const int row = x / (D / 8), c8 = (x % (D / 8)) * 8;
+      const int r = ch * kBwdCols + row;
+      if (r < rows)
+        __builtin_nontemporal_store(
+            *reinterpret_cast<const u32x4_t*>(&L.dqt[row * KROW + c8]),
+            reinterpret_cast<u32x4_t*>(part_dq + ((size_t)start * G + r) * D + c8));
     }
   };
   for (int ch = 0; ch < n_chunks; ch += 2) {

@@ -25,6 +25,7 @@ namespace bucket {
 constexpr int kRowsPerGroup = 512;    // rows of one head per count/scatter workgroup
 constexpr int kMaxLocalBuckets = 8192;  // LDS histogram limit (two int arrays = 64 KB)
 constexpr int kBatch = 16;  // slots per thread whose loads are issued together
+constexpr int kStableRows = 128;  // rows per chunk of the stable sort (one wave scatters a chunk)
 
 namespace {  // each translation unit keeps its own copy of these kernels
 
@@ -178,7 +179,8 @@ __global__ void scatter_global_kernel(const int* __restrict__ node, int* __restr
 // Stable variant: each bucket lists its pairs in increasing (row, slot) order,
 // so the pairs, their grouping into work items and every sum taken over them
 // in that order are the same run to run.
-//   count_wg:  per (row chunk, head), the chunk's histogram written out whole
+//   count_wg:  per (chunk of kStableRows rows, head), the chunk's histogram
+//              written out whole
 //              to wgc[head][chunk][node] (no global atomics);
 //   wg_prefix: per bucket, exclusive prefix of wgc over the chunks (in place)
 //              and the bucket's total;
@@ -192,7 +194,7 @@ __global__ __launch_bounds__(256) void count_wg_kernel(const int* __restrict__ n
   for (int i = threadIdx.x; i < m; i += blockDim.x) hist[i] = 0;
   __syncthreads();
   const int bh = blockIdx.y;
-  const int t0 = blockIdx.x * kRowsPerGroup, t1 = min(t0 + kRowsPerGroup, n_tok);
+  const int t0 = blockIdx.x * kStableRows, t1 = min(t0 + kStableRows, n_tok);
   const int* src = node + ((size_t)bh * n_tok) * topk;
   const int i1 = t1 * topk;
   for (int ib = t0 * topk + threadIdx.x; ib < i1; ib += kBatch * blockDim.x) {
@@ -239,14 +241,17 @@ __global__ __launch_bounds__(64) void scatter_stable_kernel(
   for (int i = threadIdx.x; i < m; i += blockDim.x) base[i] = offsets[(size_t)bh * m + i] + pre[i];
   __syncthreads();
   const int lane = threadIdx.x;
-  const int t0 = blockIdx.x * kRowsPerGroup, t1 = min(t0 + kRowsPerGroup, n_tok);
+  const int t0 = blockIdx.x * kStableRows, t1 = min(t0 + kStableRows, n_tok);
   const size_t row0 = (size_t)bh * n_tok;
   const int* src = node + row0 * topk;
   const int i1 = t1 * topk;
   const uint64_t below = (uint64_t(1) << lane) - 1;
-  constexpr int S = 8;  // steps whose node loads are issued together
+  // Steps of 64 slots, S at a time: their node loads are issued together and
+  // their stores after the last of them (loads and stores share one counter,
+  // so a store between two steps would hold up the next step's load).
+  constexpr int S = 8;
   for (int ib0 = t0 * topk; ib0 < i1; ib0 += S * 64) {
-    int xs[S];
+    int xs[S], ps[S];
 #pragma unroll
     for (int u = 0; u < S; ++u) {
       const int i = ib0 + u * 64 + lane;
@@ -254,9 +259,6 @@ __global__ __launch_bounds__(64) void scatter_stable_kernel(
     }
 #pragma unroll
     for (int u = 0; u < S; ++u) {
-      const int ib = ib0 + u * 64;
-      if (ib >= i1) break;
-      const int i = ib + lane;
       const int x = xs[u];
       const bool live = x >= 0 && x < m;
       uint64_t pending = __ballot(live);
@@ -270,14 +272,18 @@ __global__ __launch_bounds__(64) void scatter_stable_kernel(
         }
         pending &= ~same;
       }
-      int pos = 0;
-      if (live) pos = base[x] + rank;
+      const int b = base[live ? x : 0];
+      ps[u] = live ? b + rank : -1;
       wave_lds_sync();  // every lane has read base[] before the leaders move it
       if (live && rank == 0) base[x] += cnt;
       wave_lds_sync();
-      if (live) {
-        pairs[pos] = (int)(((row0 + i / topk) << 5) | (i % topk));
-        if (inv) inv[row0 * topk + i] = pos;
+    }
+#pragma unroll
+    for (int u = 0; u < S; ++u) {
+      const int i = ib0 + u * 64 + lane;
+      if (ps[u] >= 0) {
+        pairs[ps[u]] = (int)(((row0 + i / topk) << 5) | (i % topk));
+        if (inv) inv[row0 * topk + i] = ps[u];
       }
     }
   }
@@ -351,9 +357,8 @@ inline hipError_t sort_pairs(const int* node, int batch_heads, int n_tok, int to
   return hipGetLastError();
 }
 
-// Rows handled per count/scatter workgroup, and the per-chunk count matrix
-// the stable sort needs (ints).
-inline int row_chunks(int n_tok) { return (n_tok + kRowsPerGroup - 1) / kRowsPerGroup; }
+// Row chunks of the stable sort, and its per-chunk count matrix (ints).
+inline int row_chunks(int n_tok) { return (n_tok + kStableRows - 1) / kStableRows; }
 inline size_t stable_wgc_ints(int batch_heads, int n_tok, int m) {
   return (size_t)batch_heads * row_chunks(n_tok) * m;
 }

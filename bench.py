@@ -9,9 +9,11 @@ Prints ONE JSON line: tokens/s of the whole step, per-stage times, the
 selection-latency comparison with the GPU BSA baseline across N (crossover),
 the roofline of the dominant kernel (HIP events on the launch stream) and the
 CPU oracle timed on a bounded sample of the same workload (cpu_baseline).
+Beside it (not part of the step): the backward of the block-sparse attention
+with the step's block lists held fixed, and the GQA decode step.
 
 Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--no-sweep] [--no-cpu] [--no-decode]
-                       [--cpu-seconds 15] [--calibrate-copy-mb 0]
+                       [--no-backward] [--cpu-seconds 15] [--calibrate-copy-mb 0]
 """
 from __future__ import annotations
 
@@ -277,6 +279,8 @@ def run(args):
         "roofline": roof,
     }
 
+    if not args.no_backward:
+        result["backward"] = backward_bench(prob, inp, idx, dev)
     if not args.no_decode:
         result["decode"] = decode_bench(args)
     if not args.no_sweep:
@@ -288,6 +292,56 @@ def run(args):
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(args, inp, prob)
     return result
+
+
+def backward_bench(prob, inp, idx, dev):
+    """Backward of the block-sparse attention for the timed workload, with the
+    block lists of the last timed step held fixed: the forward is run once
+    more for out / row_lse, dO is a seeded N(0, 1/d) tensor, and one backward
+    (delta, stable sort, main kernel, dk/dv reduce, dq combine) is timed."""
+    import torch
+
+    import hierarchical_block_selection_amd as pisa
+    from hierarchical_block_selection_amd.inputs import seeded_normal
+
+    B, H, N, d, C = prob.batch, prob.heads_q, prob.seq_len, prob.head_dim, prob.block
+    G = prob.heads_q // prob.heads_kv
+    out, lse = pisa.pisa_block_sparse_attn(prob, inp.q, inp.k, inp.v, idx)
+    dout = seeded_normal(tuple(inp.q.shape), 4017, 1.0 / math.sqrt(d), prob.dtype, dev)
+    ws = torch.empty(pisa.pisa_workspace_bytes(prob, "attn_bwd"), dtype=torch.uint8, device=dev)
+    dq, dk, dv = torch.empty_like(inp.q), torch.empty_like(inp.k), torch.empty_like(inp.v)
+
+    def bwd():
+        pisa.pisa_block_sparse_attn_backward(prob, inp.q, inp.k, inp.v, idx, out, lse, dout,
+                                             dq, dk, dv, workspace=ws)
+
+    ms = timed_call(bwd, 5, 2)
+    pisa.pisa_profile_report()
+    pisa.pisa_profile_enable(True)
+    timed_call(bwd, 3, 0)
+    pisa.pisa_profile_enable(False)
+    kernels = {k: tot / cnt for k, (tot, cnt) in pisa.pisa_profile_report().items()}
+    m1 = -(-N // C)
+    live = int(((idx >= 0) & (idx < m1)).sum().item())
+    cols = live * G  # (row, slot, query head) columns
+    elt = 2
+    # per column: q, dO read, its dQ contribution written (bf16), lse and D;
+    # per leaf block: K and V read, dK and dV written once
+    main_bytes = cols * (3 * d * elt + 8) + B * prob.heads_kv * m1 * 4 * C * d * elt
+    main_flop = cols * 5 * 2.0 * C * d  # S, dP, dV, dK, dQ products over the block
+    main_ms = kernels.get("attn_bwd_main", float("nan"))
+    achieved = main_bytes / (main_ms * 1e-3) / 1e9
+    return {
+        "ms": ms,
+        "kernels_ms": kernels,
+        "columns": cols,
+        "roofline_main": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                          "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                          "traffic": stored_traffic("bwd_main"),
+                          "algorithmic_bytes": main_bytes,
+                          "mfma_tflops": main_flop / (main_ms * 1e-3) / 1e12},
+        "tokens_per_s": B * N / (ms * 1e-3),
+    }
 
 
 def decode_bench(args):
@@ -442,6 +496,7 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="launch one elementwise copy of this many MiB before the steps "

@@ -15,7 +15,7 @@
 //  1. delta:   D_i per (query head, row), fp32;
 //  2. the (row, slot) pairs are bucketed by leaf block with the stable
 //     counting sort of bucket.h (each block's pairs in row order), in work
-//     items of at most 1024 (pair, head) columns;
+//     items of at most 2048 (pair, head) columns;
 //  3. one workgroup per work item keeps its block's K and V as MFMA operands
 //     in registers and walks the item's columns 32 at a time.  Wave w owns the
 //     block's keys 16w..16w+15:
@@ -43,7 +43,7 @@ namespace {
 constexpr int kBwdBlock = 64;     // C
 constexpr int kBwdThreads = 256;  // 4 waves, one per 16 keys of the block
 constexpr int kBwdCols = 32;      // (pair, head) columns per chunk
-constexpr int kBwdItemCols = 1024;  // (pair, head) columns per work item
+constexpr int kBwdItemCols = 2048;  // (pair, head) columns per work item
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;

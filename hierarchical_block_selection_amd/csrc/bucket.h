@@ -186,7 +186,8 @@ __global__ void scatter_global_kernel(const int* __restrict__ node, int* __restr
 //              and the bucket's total;
 //   scatter_stable: one wave per (row chunk, head) walks its slots in order,
 //              64 at a time; lanes holding the same node are ranked by lane
-//              (ballot), and a running base per node lives in LDS.
+//              (ballot; LDS counters first single out the lanes whose node is
+//              unique in the step), and a running base per node lives in LDS.
 __global__ __launch_bounds__(256) void count_wg_kernel(const int* __restrict__ node,
                                                        int* __restrict__ wgc, int n_tok, int topk,
                                                        int m) {
@@ -210,35 +211,60 @@ __global__ __launch_bounds__(256) void count_wg_kernel(const int* __restrict__ n
   for (int i = threadIdx.x; i < m; i += blockDim.x) dst[i] = hist[i];
 }
 
+// 16 buckets x 16 chunk segments per workgroup: each thread sums its
+// segment, the segment offsets go through LDS, then each thread rewrites its
+// segment as running prefixes.
+constexpr int kPrefixBuckets = 16, kPrefixSegs = 16;
 __global__ __launch_bounds__(256) void wg_prefix_kernel(int* __restrict__ wgc,
                                                         int* __restrict__ counts, int n_chunks,
                                                         int m, int n_buckets) {
-  const int bucket = blockIdx.x * blockDim.x + threadIdx.x;
-  if (bucket >= n_buckets) return;
-  const int bh = bucket / m, x = bucket % m;
+  __shared__ int part[kPrefixSegs][kPrefixBuckets];
+  const int bl = threadIdx.x % kPrefixBuckets, seg = threadIdx.x / kPrefixBuckets;
+  const int bucket = blockIdx.x * kPrefixBuckets + bl;
+  const bool ok = bucket < n_buckets;
+  const int bh = ok ? bucket / m : 0, x = ok ? bucket % m : 0;
   int* col = wgc + (size_t)bh * n_chunks * m + x;
+  const int per = (n_chunks + kPrefixSegs - 1) / kPrefixSegs;
+  const int c0 = min(seg * per, n_chunks), c1 = min(c0 + per, n_chunks);
+  int sum = 0;
+  if (ok)
+    for (int c = c0; c < c1; c += kBatch) {
+      int v[kBatch];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) v[k] = col[(size_t)min(c + k, c1 - 1) * m];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k)
+        if (c + k < c1) sum += v[k];
+    }
+  part[seg][bl] = sum;
+  __syncthreads();
   int run = 0;
-  for (int c0 = 0; c0 < n_chunks; c0 += kBatch) {  // kBatch loads in flight
-    int v[kBatch];
+  for (int s2 = 0; s2 < seg; ++s2) run += part[s2][bl];
+  if (ok && seg == kPrefixSegs - 1) counts[bucket] = run + sum;
+  if (ok)
+    for (int c = c0; c < c1; c += kBatch) {
+      int v[kBatch];
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k) v[k] = col[(size_t)min(c0 + k, n_chunks - 1) * m];
+      for (int k = 0; k < kBatch; ++k) v[k] = col[(size_t)min(c + k, c1 - 1) * m];
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k)
-      if (c0 + k < n_chunks) {
-        col[(size_t)(c0 + k) * m] = run;
-        run += v[k];
-      }
-  }
-  counts[bucket] = run;
+      for (int k = 0; k < kBatch; ++k)
+        if (c + k < c1) {
+          col[(size_t)(c + k) * m] = run;
+          run += v[k];
+        }
+    }
 }
 
 __global__ __launch_bounds__(64) void scatter_stable_kernel(
     const int* __restrict__ node, const int* __restrict__ offsets, const int* __restrict__ wgc,
     int* __restrict__ pairs, int* __restrict__ inv, int n_tok, int topk, int m) {
-  extern __shared__ int base[];  // [m]: next position of each node's pairs
+  extern __shared__ int base[];  // [m] next position of each node's pairs, then
+                                 // [m / 4] byte counters of the current step
+  unsigned* cnt4 = reinterpret_cast<unsigned*>(base + m);
   const int bh = blockIdx.y;
   const int* pre = wgc + ((size_t)bh * gridDim.x + blockIdx.x) * m;
   for (int i = threadIdx.x; i < m; i += blockDim.x) base[i] = offsets[(size_t)bh * m + i] + pre[i];
+  for (int i = threadIdx.x; i < (m + 3) / 4; i += blockDim.x) cnt4[i] = 0;
   __syncthreads();
   const int lane = threadIdx.x;
   const int t0 = blockIdx.x * kStableRows, t1 = min(t0 + kStableRows, n_tok);
@@ -261,18 +287,24 @@ __global__ __launch_bounds__(64) void scatter_stable_kernel(
     for (int u = 0; u < S; ++u) {
       const int x = xs[u];
       const bool live = x >= 0 && x < m;
-      uint64_t pending = __ballot(live);
-      int rank = 0, cnt = 0;
+      const int xc = live ? x : 0;
+      const unsigned one = 1u << (8 * (xc & 3));
+      // How many of the step's lanes hold x (order-free LDS adds); lanes
+      // whose node is unique take rank 0 without the ranking loop below.
+      if (live) atomicAdd(&cnt4[xc >> 2], one);
+      wave_lds_sync();
+      const int c = live ? (int)((cnt4[xc >> 2] >> (8 * (xc & 3))) & 0xffu) : 0;
+      wave_lds_sync();
+      if (live) atomicSub(&cnt4[xc >> 2], one);
+      int rank = 0, cnt = c;
+      uint64_t pending = __ballot(c > 1);  // lanes ranked by lane among equal nodes
       while (pending) {
         const int v = __builtin_amdgcn_readlane(x, (int)__builtin_ctzll(pending));
         const uint64_t same = __ballot(live && x == v);
-        if (live && x == v) {
-          rank = __popcll(same & below);
-          cnt = __popcll(same);
-        }
+        if (live && x == v) rank = __popcll(same & below);
         pending &= ~same;
       }
-      const int b = base[live ? x : 0];
+      const int b = base[xc];
       ps[u] = live ? b + rank : -1;
       wave_lds_sync();  // every lane has read base[] before the leaders move it
       if (live && rank == 0) base[x] += cnt;
@@ -373,12 +405,12 @@ inline hipError_t sort_pairs_stable(const int* node, int batch_heads, int n_tok,
   const dim3 grid(row_chunks(n_tok), batch_heads);
   hipLaunchKernelGGL(count_wg_kernel, grid, dim3(256), sizeof(int) * m, st, node, wgc, n_tok, topk,
                      m);
-  hipLaunchKernelGGL(wg_prefix_kernel, dim3((n_buckets + 255) / 256), dim3(256), 0, st, wgc, counts,
-                     (int)grid.x, m, n_buckets);
+  hipLaunchKernelGGL(wg_prefix_kernel, dim3((n_buckets + kPrefixBuckets - 1) / kPrefixBuckets),
+                     dim3(256), 0, st, wgc, counts, (int)grid.x, m, n_buckets);
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, counts, offsets, cursors,
                      item_offsets, n_buckets, per_item);
-  hipLaunchKernelGGL(scatter_stable_kernel, grid, dim3(64), sizeof(int) * m, st, node, offsets, wgc,
-                     pairs, inv, n_tok, topk, m);
+  hipLaunchKernelGGL(scatter_stable_kernel, grid, dim3(64), sizeof(int) * (m + (m + 3) / 4), st,
+                     node, offsets, wgc, pairs, inv, n_tok, topk, m);
   return hipGetLastError();
 }
 

@@ -200,7 +200,7 @@ def test_backward_arguments():
     def a256(x):
         return (x + 255) // 256 * 256
     g, slots, m1 = 4, 1 * 2 * 3000 * 8, 2 * 47
-    items = (slots + 256 - 1) // 256 + m1  # 1024 columns per item = 256 pairs at G = 4
+    items = (slots + 512 - 1) // 512 + m1  # 2048 columns per item = 512 pairs at G = 4
     chunks = -(-3000 // 128)  # row chunks of the stable sort
     want = (a256(4 * m1) + a256(4 * (m1 + 1)) + a256(4 * m1) + a256(4 * (m1 + 1))
             + a256(4 * 2 * chunks * 47) + a256(4 * slots) + a256(4 * slots) + a256(4 * 8 * 3000) + a256(2 * slots * g * 128)

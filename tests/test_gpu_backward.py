@@ -65,8 +65,8 @@ def run_gpu(prob, inp, idx, dout):
 CASES = [
     # (N, d, K, Hq, Hkv, causal, lists)
     (3000, 128, 8, 2, 1, True, "selector"),     # ragged last block (56 keys), G = 2
-    (2048, 64, 16, 4, 4, True, "selector"),     # G = 1, d = 64, block 0 in 2 work items
-    (4160, 128, 16, 16, 1, True, "selector"),   # G = 16: 64 pairs per item, 65 items on block 0
+    (4160, 64, 16, 4, 4, True, "selector"),     # G = 1, d = 64, block 0 in 3 work items
+    (4160, 128, 16, 16, 1, True, "selector"),   # G = 16: 128 pairs per item, 33 items on block 0
     (1500, 64, 8, 8, 2, False, "selector"),     # non-causal, G = 4, unselected blocks
     (2100, 128, 12, 4, 2, True, "arbitrary"),   # unsorted rows, junk, future and empty rows
     (700, 64, 5, 2, 2, False, "arbitrary"),

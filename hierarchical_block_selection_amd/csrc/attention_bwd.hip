@@ -24,7 +24,8 @@
 //       P, dS  in the accumulators (masked entries are 0)
 //       dV^T += dO^T P,  dK^T += Q^T dS  (the contraction runs over the chunk's
 //                                         columns; Q^T and dO^T come from LDS)
-//       dQ^T  = K^T dS^T for the wave's quarter of d (dS passes through LDS)
+//       dQ^T  = K^T dS^T for the wave's quarter of d (dS passes through LDS;
+//               computed one chunk later, so each chunk needs two barriers)
 //     Each column's dQ over this block goes (bf16) through an LDS tile and
 //     leaves as whole rows, in bucket order.  At
 //     the end the block's dK, dV go straight to the outputs when its bucket is
@@ -174,17 +175,24 @@ struct BwdLds {
   static constexpr int TROW = kBwdBlock + 8;  // K^T [d][key]
   static constexpr int CT = kBwdCols + 4;     // Q^T, dO^T [d][column]
   static constexpr int SROW = kBwdBlock + 8;  // dS [column][key]
-  bf16_t kt[D * TROW];
   bf16_t qs[kBwdCols * KROW];
   bf16_t os[kBwdCols * KROW];
   bf16_t qt[D * CT];
   bf16_t ot[D * CT];
-  bf16_t ds[kBwdCols * SROW];
   float lse2[kBwdCols];
   float dl[kBwdCols];
   int lim[kBwdCols];
   int tok[kBwdItemCols];  // query position of each pair of the work item
-  bf16_t dqt[kBwdCols * KROW];  // the chunk's dQ rows, stored out whole
+  // K^T is read into registers once, before the first chunk; its space then
+  // holds two chunks' dS and dQ rows (chunk c is written while chunk c - 1's
+  // are still being read).
+  union {
+    bf16_t kt[D * TROW];
+    struct {
+      bf16_t ds[2][kBwdCols * SROW];
+      bf16_t dqt[2][kBwdCols * KROW];  // a chunk's dQ rows, stored out whole
+    } c;
+  } u;
 };
 
 template <int D, int G>
@@ -298,8 +306,8 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_kernel(
     const uint32_t w4[4] = {kv.x, kv.y, kv.z, kv.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      L.kt[(c + 2 * e) * TROW + r] = bf16_t(w4[e] & 0xffffu);
-      L.kt[(c + 2 * e + 1) * TROW + r] = bf16_t(w4[e] >> 16);
+      L.u.kt[(c + 2 * e) * TROW + r] = bf16_t(w4[e] & 0xffffu);
+      L.u.kt[(c + 2 * e + 1) * TROW + r] = bf16_t(w4[e] >> 16);
     }
   }
   __syncthreads();
@@ -310,7 +318,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_kernel(
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
       ktop[m][ks] = as_bf16x8(
-          *reinterpret_cast<const uint4*>(&L.kt[(16 * (QMT * w + m) + li) * TROW + 32 * ks + 8 * g]));
+          *reinterpret_cast<const uint4*>(&L.u.kt[(16 * (QMT * w + m) + li) * TROW + 32 * ks + 8 * g]));
 
   f32x4_t dk_acc[MT], dv_acc[MT];
 #pragma unroll
@@ -319,12 +327,57 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_kernel(
     dv_acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
+  // dQ^T of chunk cp for d tiles QMT*w.., all 32 columns; lane (column
+  // 16ct + li, g) receives dQ[column][16 (QMT w + m) + 4g + e], which goes to
+  // the chunk's dQ tile.
+  auto dq_phase = [&](int cp) {
+    const bf16_t* dsb = L.u.c.ds[cp & 1];
+    bf16_t* dqt = L.u.c.dqt[cp & 1];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      const int col = 16 * ct + li;
+      bf16x8_t bs[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        bs[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(&dsb[col * SROW + 32 * ks + 8 * g]));
+#pragma unroll
+      for (int m = 0; m < QMT; ++m) {
+        f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ktop[m][0], bs[0], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ktop[m][1], bs[1], acc, 0, 0, 0);
+        bf16x4_t o4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o4[e] = (__bf16)acc[e];
+        *reinterpret_cast<uint2*>(&dqt[col * KROW + 16 * (QMT * w + m) + 4 * g]) =
+            __builtin_bit_cast(uint2, o4);
+      }
+    }
+  };
+  // Whole dQ rows of chunk cp leave as 16-byte pieces (1 KB per store
+  // instruction); each is read once, by the dq combine.
+  auto store_phase = [&](int cp) {
+    const bf16_t* dqt = L.u.c.dqt[cp & 1];
+#pragma unroll
+    for (int j = 0; j < kBwdCols * (D / 8) / kBwdThreads; ++j) {
+      const int x = tid + kBwdThreads * j;
+      const int row = x / (D / 8), c8 = (x % (D / 8)) * 8;
+      const int r = cp * kBwdCols + row;
+      if (r < rows)
+        __builtin_nontemporal_store(
+            *reinterpret_cast<const u32x4_t*>(&dqt[row * KROW + c8]),
+            reinterpret_cast<u32x4_t*>(part_dq + ((size_t)start * G + r) * D + c8));
+    }
+  };
+  // Per chunk two barriers: after the staging (A) and after this chunk's
+  // reads of the staged rows (X).  Chunk c's dQ is computed after barrier A
+  // of chunk c + 1 (its dS is complete by then) and stored after barrier X.
   auto chunk = [&](int ch, ChunkRegs<D, G>& cr) {
     chunk_stage<D, G>(cr, L);
     __syncthreads();
     if (ch + 2 < n_chunks)
       chunk_fetch<D, G>(cr, ch + 2, L.tok, rows, qh, doh, lse_h, delta_h, n_tok, tok0, n_keys,
                         causal != 0);
+    if (ch > 0) dq_phase(ch - 1);
     // S and dP for columns 16ct + 4g + e, key my_key.
     f32x4_t sacc[2], pacc[2];
 #pragma unroll
@@ -345,6 +398,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_kernel(
     // 16+4g..16+4g+3} in k-slots 8g..8g+7 (the same permutation is used for
     // the A operands read from Q^T / dO^T).
     bf16x8_t pb, sb;
+    bf16_t* dsb = L.u.c.ds[ch & 1];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
@@ -355,7 +409,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_kernel(
         const float dsv = p * (pacc[ct][e] - L.dl[col]);
         pb[4 * ct + e] = (__bf16)p;
         sb[4 * ct + e] = (__bf16)dsv;
-        L.ds[col * SROW + my_key] = __builtin_bit_cast(bf16_t, (__bf16)dsv);
+        dsb[col * SROW + my_key] = __builtin_bit_cast(bf16_t, (__bf16)dsv);
       }
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
@@ -371,45 +425,15 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_kernel(
           as_bf16x8(make_uint4(q0.x, q0.y, q1.x, q1.y)), sb, dk_acc[m], 0, 0, 0);
     }
     __syncthreads();
-    // dQ^T for d tiles QMT*w.., all 32 columns; lane (column 16ct + li, g)
-    // receives dQ[column][16 (QMT w + m) + 4g + e].
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      const int col = 16 * ct + li;
-      bf16x8_t bs[2];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        bs[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(&L.ds[col * SROW + 32 * ks + 8 * g]));
-#pragma unroll
-      for (int m = 0; m < QMT; ++m) {
-        f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ktop[m][0], bs[0], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ktop[m][1], bs[1], acc, 0, 0, 0);
-        bf16x4_t o4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o4[e] = (__bf16)acc[e];
-        *reinterpret_cast<uint2*>(&L.dqt[col * KROW + 16 * (QMT * w + m) + 4 * g]) =
-            __builtin_bit_cast(uint2, o4);
-      }
-    }
-    __syncthreads();
-    // Whole rows leave as 16-byte pieces (1 KB per store instruction); each is
-    // read once, by the dq combine.
-#pragma unroll
-    for (int j = 0; j < kBwdCols * (D / 8) / kBwdThreads; ++j) {
-      const int x = tid + kBwdThreads * j;
-      const int row = x / (D / 8), c8 = (x % (D / 8)) * 8;
-      const int r = ch * kBwdCols + row;
-      if (r < rows)
-        __builtin_nontemporal_store(
-            *reinterpret_cast<const u32x4_t*>(&L.dqt[row * KROW + c8]),
-            reinterpret_cast<u32x4_t*>(part_dq + ((size_t)start * G + r) * D + c8));
-    }
+    if (ch > 0) store_phase(ch - 1);
   };
   for (int ch = 0; ch < n_chunks; ch += 2) {
     chunk(ch, cra);
     if (ch + 1 < n_chunks) chunk(ch + 1, crb);
   }
+  dq_phase(n_chunks - 1);
+  __syncthreads();
+  store_phase(n_chunks - 1);
 
   // dK (times scale) and dV of keys my_key: lane holds d = 16m + 4g + e.
   const int n_items = item_offsets[bucket + 1] - item_offsets[bucket];

@@ -455,37 +455,88 @@ def selection_sweep(args, heads_q=4, heads_kv=4, head_dim=128, topk=16,
 
 def cpu_baseline(args, inp, prob):
     """The CPU oracle on a bounded sample of the same workload: the full pyramid
-    of KV head 0 plus selection + attention for sampled rows, one thread."""
+    of KV head 0 plus selection + attention for random rows, on the host's
+    cores.  The inputs go to a temporary directory and a child process that
+    never touches the GPU runs a pool of single-threaded oracle workers (one
+    per core of this process's CPU share, at most 16)."""
+    import subprocess
+    import tempfile
+
     import numpy as np
-    from threadpoolctl import threadpool_limits
+
+    with tempfile.TemporaryDirectory() as tmp:
+        np.save(os.path.join(tmp, "keys.npy"), inp.k[0, 0].float().cpu().numpy())
+        np.save(os.path.join(tmp, "vals.npy"), inp.v[0, 0].float().cpu().numpy())
+        np.save(os.path.join(tmp, "q.npy"), inp.q[0, 0:1].float().cpu().numpy())
+        cmd = [sys.executable, os.path.abspath(__file__), "--cpu-worker", tmp,
+               "--cpu-seconds", str(args.cpu_seconds), "--cpu-block", str(prob.block),
+               "--cpu-topk", str(prob.topk)]
+        res = subprocess.run(cmd, capture_output=True, text=True, timeout=600,
+                             env=dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1",
+                                      MKL_NUM_THREADS="1"))
+    if res.returncode != 0:
+        raise RuntimeError(f"cpu baseline worker failed: {res.stderr[-2000:]}")
+    r = json.loads(res.stdout.strip().splitlines()[-1])
+    N, H = prob.seq_len, prob.heads_q
+    # per (token, head): the pyramid prorated per token plus one row's selection
+    # and attention; rows run concurrently on r["procs"] cores
+    per_token_head = r["row_seconds"] / r["rows"] + r["pyramid_seconds"] / N
+    value = r["procs"] / (H * per_token_head)
+    return {"value": value, "unit": "tokens/s", "cores": r["procs"], "kind": "oracle",
+            "sample": f"KV head 0 of the 128K workload: full pyramid ({r['pyramid_seconds']:.2f} s, "
+                      f"prorated per token) + selection and attention of {r['rows']} random rows "
+                      f"t >= K*C ({r['row_seconds']:.1f} core-s over {r['procs']} single-threaded "
+                      f"worker processes), scaled to all {H} heads",
+            "host_cpus": os.cpu_count(), "affinity_cpus": r["affinity"]}
+
+
+_CPU = {}
+
+
+def _cpu_rows(seed):
+    """One oracle worker: random rows for the time budget (no GPU in here)."""
+    import numpy as np
 
     import oracle
 
-    N, C, K, H = prob.seq_len, prob.block, prob.topk, prob.heads_q
-    with threadpool_limits(limits=1):
-        keys = inp.k[0, 0].double().cpu().numpy()
-        vals = inp.v[0, 0].double().cpu().numpy()
-        qh = inp.q[0, 0:1].double().cpu().numpy()
-        t0 = time.perf_counter()
-        levels = oracle.build_pyramid(keys, C)
-        t_pyr = time.perf_counter() - t0
-        rng = np.random.default_rng(0)
-        budget = args.cpu_seconds
-        done = 0
-        t_rows = 0.0
-        while t_rows < budget and done < 65536:
-            t = int(rng.integers(K * C, N))
-            t1 = time.perf_counter()
-            sel = oracle.select_pisa_row(qh[:, t], keys, levels, t, C, K, True, True)
-            oracle.attend_row(qh[:, t], keys, vals, sel.leaves, t, C, True)
-            t_rows += time.perf_counter() - t1
-            done += 1
-    per_token_head = t_rows / done + t_pyr / N
-    return {"value": 1.0 / (H * per_token_head), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"KV head 0 of the 128K workload: full pyramid ({t_pyr:.2f} s, prorated "
-                      f"per token) + selection and attention of {done} random rows t >= K*C "
-                      f"({t_rows:.1f} s), one thread, scaled to all {H} heads",
-            "host_cpus": os.cpu_count()}
+    keys, vals, qh, levels = _CPU["keys"], _CPU["vals"], _CPU["q"], _CPU["levels"]
+    C, K, budget = _CPU["block"], _CPU["topk"], _CPU["seconds"]
+    n = keys.shape[0]
+    rng = np.random.default_rng(seed)
+    done, spent = 0, 0.0
+    while spent < budget and done < 65536:
+        t = int(rng.integers(K * C, n))
+        t1 = time.perf_counter()
+        sel = oracle.select_pisa_row(qh[:, t], keys, levels, t, C, K, True, True)
+        oracle.attend_row(qh[:, t], keys, vals, sel.leaves, t, C, True)
+        spent += time.perf_counter() - t1
+        done += 1
+    return done, spent
+
+
+def cpu_worker(args):
+    """--cpu-worker DIR: load the sample, build the pyramid once, then fork the
+    oracle workers and print one JSON line with the totals."""
+    import multiprocessing
+
+    import numpy as np
+
+    import oracle
+
+    d = args.cpu_worker
+    keys = np.load(os.path.join(d, "keys.npy")).astype(np.float64)
+    _CPU.update(keys=keys, vals=np.load(os.path.join(d, "vals.npy")).astype(np.float64),
+                q=np.load(os.path.join(d, "q.npy")).astype(np.float64), block=args.cpu_block,
+                topk=args.cpu_topk, seconds=args.cpu_seconds)
+    t0 = time.perf_counter()
+    _CPU["levels"] = oracle.build_pyramid(keys, args.cpu_block)
+    t_pyr = time.perf_counter() - t0
+    affinity = len(os.sched_getaffinity(0))
+    procs = max(1, min(16, affinity))
+    with multiprocessing.get_context("fork").Pool(procs) as pool:
+        out = pool.map(_cpu_rows, range(procs))
+    print(json.dumps({"rows": sum(o[0] for o in out), "row_seconds": sum(o[1] for o in out),
+                      "pyramid_seconds": t_pyr, "procs": procs, "affinity": affinity}), flush=True)
 
 
 def main():
@@ -498,10 +549,16 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-worker", default=None, help=argparse.SUPPRESS)
+    ap.add_argument("--cpu-block", type=int, default=64, help=argparse.SUPPRESS)
+    ap.add_argument("--cpu-topk", type=int, default=16, help=argparse.SUPPRESS)
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="launch one elementwise copy of this many MiB before the steps "
                          "(HBM counter calibration)")
     args = ap.parse_args()
+    if args.cpu_worker:
+        cpu_worker(args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the (batch, KV head) units would shard across GPUs without communication)",

@@ -11,7 +11,8 @@
 //   dQ_i  = scale sum_j dS_ij k_j,       dK_j = scale sum_i dS_ij q_i
 // where the sums over i run over every query head of the KV group.
 //
-// bf16, C = 64, d in {64, 128}:
+// bf16, C = 64, a power-of-two group (any other shape: the general kernel
+// below replaces step 3 with fp32 vector math, same items and reductions):
 //  1. delta:   D_i per (query head, row), fp32;
 //  2. the (row, slot) pairs are bucketed by leaf block with the stable
 //     counting sort of bucket.h (each block's pairs in row order), in work
@@ -45,6 +46,7 @@ constexpr int kBwdBlock = 64;     // C
 constexpr int kBwdThreads = 256;  // 4 waves, one per 16 keys of the block
 constexpr int kBwdCols = 32;      // (pair, head) columns per chunk
 constexpr int kBwdItemCols = 2048;  // (pair, head) columns per work item
+constexpr int kGenItemCols = 256;   // columns per work item of the general kernel
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
@@ -62,16 +64,24 @@ __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// bf16, C = 64, a power-of-two group: the MFMA kernel; every other shape
+// the general one.
+bool mfma_path(const LaunchShape& s) {
+  return s.bf16 && s.block == kBwdBlock && (s.group & (s.group - 1)) == 0;
+}
+
 struct BwdWs {
   size_t counts, offsets, cursors, item_offsets, wgc, pairs, inv, delta, part_dq, part_kv, total;
-  int n_buckets, max_items;
+  int n_buckets, max_items, per_item;
 };
 
 BwdWs bwd_layout(const LaunchShape& s) {
   BwdWs w;
+  const bool mf = mfma_path(s);
   const size_t slots = (size_t)s.batch * s.heads_kv * s.seq_len * s.topk;
   w.n_buckets = s.batch * s.heads_kv * s.lv.size[0];
-  w.max_items = bucket::max_items(slots, w.n_buckets, kBwdItemCols / s.group);
+  w.per_item = (mf ? kBwdItemCols : kGenItemCols) / s.group;
+  w.max_items = bucket::max_items(slots, w.n_buckets, w.per_item);
   size_t off = 0;
   w.counts = off; off = align256(off + sizeof(int) * w.n_buckets);
   w.offsets = off; off = align256(off + sizeof(int) * (w.n_buckets + 1));
@@ -82,36 +92,36 @@ BwdWs bwd_layout(const LaunchShape& s) {
   w.pairs = off; off = align256(off + sizeof(int) * slots);
   w.inv = off; off = align256(off + sizeof(int) * slots);
   w.delta = off; off = align256(off + sizeof(float) * s.batch * s.heads_q * s.seq_len);
-  w.part_dq = off; off = align256(off + sizeof(bf16_t) * slots * s.group * s.head_dim);
-  w.part_kv = off; off = align256(off + sizeof(float) * w.max_items * 2 * kBwdBlock * s.head_dim);
+  w.part_dq = off;
+  off = align256(off + (mf ? sizeof(bf16_t) : sizeof(float)) * slots * s.group * s.head_dim);
+  w.part_kv = off; off = align256(off + sizeof(float) * w.max_items * 2 * s.block * s.head_dim);
   w.total = off;
   return w;
 }
 
 // D_i = dO_i . O_i (fp32) for every (batch, query head, row); 16 lanes per row.
-template <int D>
-__global__ __launch_bounds__(256) void attn_bwd_delta_kernel(const bf16_t* __restrict__ out,
-                                                             const bf16_t* __restrict__ dout,
+template <typename T, int D>
+__global__ __launch_bounds__(256) void attn_bwd_delta_kernel(const T* __restrict__ out,
+                                                             const T* __restrict__ dout,
                                                              float* __restrict__ delta,
                                                              size_t n_rows) {
-  constexpr int EPL = D / 16;
+  constexpr int EPL = D / 16;  // elements per lane
+  constexpr int VEC = Vec16<T>::n;
   const size_t row = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) / 16;
   if (row >= n_rows) return;
   const int sub = threadIdx.x & 15;
   float o[EPL], g[EPL];
-  if (EPL == 8) {
-    load16(out + row * D + sub * 8, o);
-    load16(dout + row * D + sub * 8, g);
-  } else {
-    const uint2 a = *reinterpret_cast<const uint2*>(out + row * D + sub * 4);
-    const uint2 b = *reinterpret_cast<const uint2*>(dout + row * D + sub * 4);
-    const uint32_t wa[2] = {a.x, a.y}, wb[2] = {b.x, b.y};
+  if (EPL % VEC == 0) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      o[2 * i] = __uint_as_float(wa[i] << 16);
-      o[2 * i + 1] = __uint_as_float(wa[i] & 0xffff0000u);
-      g[2 * i] = __uint_as_float(wb[i] << 16);
-      g[2 * i + 1] = __uint_as_float(wb[i] & 0xffff0000u);
+    for (int c = 0; c < EPL; c += VEC) {
+      load16(out + row * D + sub * EPL + c, o + c);
+      load16(dout + row * D + sub * EPL + c, g + c);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      o[e] = to_f32(out[row * D + sub * EPL + e]);
+      g[e] = to_f32(dout[row * D + sub * EPL + e]);
     }
   }
   float acc = 0.f;
@@ -468,11 +478,12 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_kernel(
 // dq of each (query head, row): scale times the sum of its slots' partials in
 // slot order (16 lanes per row, loads of up to 16 slots in flight).  Slots
 // without a position (index < 0 or past the last block) add nothing.
-template <int D>
+// Partials P are bf16 (MFMA kernel) or fp32 (general kernel).
+template <typename P, typename T, int D>
 __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
     const int32_t* __restrict__ idx, const int* __restrict__ pos_of,
-    const bf16_t* __restrict__ part_dq, bf16_t* __restrict__ dq, int heads_q, int heads_kv,
-    int n_tok, int topk, int group, int m1, float scale, size_t n_rows) {
+    const P* __restrict__ part_dq, T* __restrict__ dq, int heads_q, int heads_kv, int n_tok,
+    int topk, int group, int m1, float scale, size_t n_rows) {
   constexpr int EPL = D / 16;
   constexpr int B = 16;
   const size_t row = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) / 16;
@@ -484,22 +495,28 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
   const size_t bh = u / n_tok;
   const int b = (int)(bh / heads_kv), kvh = (int)(bh % heads_kv);
   const int32_t* ir = idx + u * topk;
+  constexpr bool kBf = sizeof(P) == 2;
+  constexpr int WPL = kBf ? EPL / 2 : EPL;  // 32-bit words per lane and slot
   float acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
   for (int j0 = 0; j0 < topk; j0 += B) {
-    uint32_t raw[B][EPL / 2];
+    uint32_t raw[B][WPL];  // unpacked when used
     bool live[B];
 #pragma unroll
     for (int jj = 0; jj < B; ++jj) {
       const int j = min(j0 + jj, topk - 1);
-      const int x = ir[j];
-      live[jj] = j0 + jj < topk && x >= 0 && x < m1;
+      const int xj = ir[j];
+      live[jj] = j0 + jj < topk && xj >= 0 && xj < m1;
       const int p = live[jj] ? pos_of[u * topk + j] : 0;  // position 0 always exists
-      const bf16_t* src = part_dq + ((size_t)p * group + h) * D + sub * EPL;
-      if (EPL == 8) {
-        const u32x4_t v4 = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src));
-        raw[jj][0] = v4.x; raw[jj][1] = v4.y; raw[jj][2] = v4.z; raw[jj][3] = v4.w;
+      const uint32_t* src =
+          reinterpret_cast<const uint32_t*>(part_dq + ((size_t)p * group + h) * D + sub * EPL);
+      if (WPL % 4 == 0) {
+#pragma unroll
+        for (int c = 0; c < WPL; c += 4) {
+          const u32x4_t v4 = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src + c));
+          raw[jj][c] = v4.x; raw[jj][c + 1] = v4.y; raw[jj][c + 2] = v4.z; raw[jj][c + 3] = v4.w;
+        }
       } else {
         const uint2 v2 = *reinterpret_cast<const uint2*>(src);
         raw[jj][0] = v2.x; raw[jj][1] = v2.y;
@@ -509,35 +526,30 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
     for (int jj = 0; jj < B; ++jj) {
       if (!live[jj]) continue;
 #pragma unroll
-      for (int e = 0; e < EPL / 2; ++e) {
-        acc[2 * e] += __uint_as_float(raw[jj][e] << 16);
-        acc[2 * e + 1] += __uint_as_float(raw[jj][e] & 0xffff0000u);
+      for (int w = 0; w < WPL; ++w) {
+        if (kBf) {
+          acc[2 * w] += __uint_as_float(raw[jj][w] << 16);
+          acc[2 * w + 1] += __uint_as_float(raw[jj][w] & 0xffff0000u);
+        } else {
+          acc[w] += __uint_as_float(raw[jj][w]);
+        }
       }
     }
   }
-  bf16_t* dst = dq + (((size_t)b * heads_q + (size_t)kvh * group + h) * n_tok + t) * D + sub * EPL;
-  if (EPL == 8) {
-    bf16x8_t o8;
+  T* dst = dq + (((size_t)b * heads_q + (size_t)kvh * group + h) * n_tok + t) * D + sub * EPL;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o8[e] = (__bf16)(acc[e] * scale);
-    *reinterpret_cast<uint4*>(dst) = __builtin_bit_cast(uint4, o8);
-  } else {
-    bf16x4_t o4;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(acc[e] * scale);
-    *reinterpret_cast<uint2*>(dst) = __builtin_bit_cast(uint2, o4);
-  }
+  for (int e = 0; e < EPL; ++e) store_from_f32(dst + e, acc[e] * scale);
 }
 
 // dK, dV rows of blocks whose bucket is not exactly one work item: the sum of
 // the items' partials in item order (no item: zeros).  One thread per (block,
-// key, 4 dims, K or V).
-template <int D>
+// key, 4 dims, K or V); C keys per block (CF > 0 fixes C at compile time).
+template <typename T, int D, int CF>
 __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
-    const int* __restrict__ item_offsets, const float* __restrict__ part_kv,
-    bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, int n_buckets, int n_tok, int m1) {
-  constexpr int C = kBwdBlock;
+    const int* __restrict__ item_offsets, const float* __restrict__ part_kv, T* __restrict__ dk,
+    T* __restrict__ dv, int n_buckets, int n_tok, int m1, int c_rt) {
   constexpr int Q4 = D / 4;
+  const int C = CF > 0 ? CF : c_rt;
   const size_t id = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (id >= (size_t)n_buckets * C * Q4 * 2) return;
   const int d4 = (int)(id % Q4);
@@ -561,18 +573,139 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
     for (int u = 0; u < U; ++u)
       if (i + u < n_items) acc += x[u];
   }
-  bf16x4_t o4;
+  T* dst = (which ? dv : dk) + ((size_t)bh * n_tok + tok) * D + 4 * d4;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) o4[e] = (__bf16)acc[e];
-  bf16_t* dst = (which ? dv : dk) + ((size_t)bh * n_tok + tok) * D + 4 * d4;
-  *reinterpret_cast<uint2*>(dst) = __builtin_bit_cast(uint2, o4);
+  for (int e = 0; e < 4; ++e) store_from_f32(dst + e, acc[e]);
 }
 
-template <int D>
+// General backward kernel (any dtype, C <= 64, any group), fp32 vector math,
+// the same work items as the MFMA kernel.  One workgroup per item keeps the
+// block's K and V in LDS as fp32 and walks the item's (pair, head) columns one
+// at a time:
+//   s_j, g_j = q . k_j, dO . v_j   4 threads per key, lanes over d
+//   P_j, dS_j                      one thread per key (masked entries 0)
+//   dK, dV += dS_j q, P_j dO       each thread owns C*D/256 (key, dim)
+//                                  entries of the block in registers
+//   dQ column = sum_j dS_j k_j     (fp32 partial, bucket order)
+template <typename T, int D>
+__global__ __launch_bounds__(256) void attn_bwd_generic_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const T* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
+    const int* __restrict__ item_offsets, const int* __restrict__ offsets,
+    const int* __restrict__ pairs, float* __restrict__ part_dq, float* __restrict__ part_kv,
+    T* __restrict__ dk, T* __restrict__ dv, int n_buckets, int heads_q, int heads_kv, int n_tok,
+    int C, int m1, int G, int causal, float scale, float scale_log2) {
+  constexpr int KP = D + 1;      // padded fp32 rows
+  constexpr int NG = 256 / D;    // key groups of the dQ sums
+  constexpr int RMAX = 64 * D / 256;  // (key, dim) entries per thread at C = 64
+  __shared__ float ks[64 * KP], vs[64 * KP];
+  __shared__ float qv[D], gv[D];
+  __shared__ float sp[64], sd[64];
+  __shared__ float red[NG][D];
+  __shared__ int tok_s[kGenItemCols];
+  int bucket, start, len;
+  if (!bucket::locate_item(item_offsets, offsets, n_buckets, blockIdx.x, kGenItemCols / G,
+                           &bucket, &start, &len))
+    return;
+  const int bh = bucket / m1, blk = bucket % m1;
+  const int b = bh / heads_kv, kvh = bh % heads_kv;
+  const int tok0 = blk * C;
+  const int n_keys = min(C, n_tok - tok0);
+  const int tid = threadIdx.x;
+  const int rows = len * G;
+  const size_t head0 = (size_t)b * heads_q + (size_t)kvh * G;
+  const T* kb = k + ((size_t)bh * n_tok + tok0) * D;
+  const T* vb = v + ((size_t)bh * n_tok + tok0) * D;
+  for (int i = tid; i < len; i += 256) tok_s[i] = (pairs[start + i] >> 5) - bh * n_tok;
+  for (int x = tid; x < C * D; x += 256) {
+    const int j = x / D, d = x % D;
+    const size_t src = (size_t)min(j, n_keys - 1) * D + d;
+    ks[j * KP + d] = to_f32(kb[src]);
+    vs[j * KP + d] = to_f32(vb[src]);
+  }
+  float ak[RMAX], av[RMAX];
+#pragma unroll
+  for (int r = 0; r < RMAX; ++r) ak[r] = av[r] = 0.f;
+  const int kj = tid / 4, part = tid % 4;
+  const int dd = tid % D, grp = tid / D;
+  __syncthreads();
+  for (int r = 0; r < rows; ++r) {
+    const int h = r % G;
+    const int t = tok_s[r / G];
+    const size_t qrow = ((head0 + h) * n_tok + t) * D;
+    for (int d = tid; d < D; d += 256) {
+      qv[d] = to_f32(q[qrow + d]);
+      gv[d] = to_f32(dout[qrow + d]);
+    }
+    __syncthreads();
+    float sv = 0.f, gd = 0.f;
+    if (kj < C) {
+#pragma unroll 8
+      for (int i = 0; i < D / 4; ++i) {
+        const int d = part + 4 * i;
+        sv = fmaf(qv[d], ks[kj * KP + d], sv);
+        gd = fmaf(gv[d], vs[kj * KP + d], gd);
+      }
+    }
+    sv += __shfl_xor(sv, 1, kWave);
+    sv += __shfl_xor(sv, 2, kWave);
+    gd += __shfl_xor(gd, 1, kWave);
+    gd += __shfl_xor(gd, 2, kWave);
+    if (part == 0 && kj < C) {
+      int lim = n_keys - 1;
+      if (causal) lim = min(lim, t - tok0);
+      const float* lse_h = lse + (head0 + h) * n_tok;
+      const float p = kj <= lim ? fast_exp2(fmaf(sv, scale_log2, -lse_h[t] * kLog2e)) : 0.f;
+      sp[kj] = p;
+      sd[kj] = p * (gd - delta[(head0 + h) * n_tok + t]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r2 = 0; r2 < RMAX; ++r2) {
+      const int e = tid + 256 * r2;
+      if (e < C * D) {
+        const int j = e / D, d = e % D;
+        ak[r2] = fmaf(sd[j], qv[d], ak[r2]);
+        av[r2] = fmaf(sp[j], gv[d], av[r2]);
+      }
+    }
+    float acc = 0.f;
+    for (int j = grp; j < C; j += NG) acc = fmaf(sd[j], ks[j * KP + dd], acc);
+    red[grp][dd] = acc;
+    __syncthreads();
+    if (tid < D) {
+      float sum = 0.f;
+#pragma unroll
+      for (int g2 = 0; g2 < NG; ++g2) sum += red[g2][tid];
+      part_dq[((size_t)start * G + r) * D + tid] = sum;
+    }
+    __syncthreads();
+  }
+  const int n_items = item_offsets[bucket + 1] - item_offsets[bucket];
+#pragma unroll
+  for (int r2 = 0; r2 < RMAX; ++r2) {
+    const int e = tid + 256 * r2;
+    if (e >= C * D) continue;
+    const int j = e / D, d = e % D;
+    if (n_items == 1) {
+      if (j < n_keys) {
+        store_from_f32(dk + ((size_t)bh * n_tok + tok0 + j) * D + d, ak[r2] * scale);
+        store_from_f32(dv + ((size_t)bh * n_tok + tok0 + j) * D + d, av[r2]);
+      }
+    } else {
+      float* pk = part_kv + ((size_t)blockIdx.x * 2) * C * D;
+      pk[e] = ak[r2] * scale;
+      pk[(size_t)C * D + e] = av[r2];
+    }
+  }
+}
+
+template <typename T, int D>
 hipError_t launch_bwd(const LaunchShape& s, const void* q, const void* k, const void* v,
                       const int32_t* idx, const void* out, const float* lse, const void* dout,
                       void* dq, void* dk, void* dv, void* ws, hipStream_t st) {
   const BwdWs lay = bwd_layout(s);
+  const bool mf = mfma_path(s);
   char* base = static_cast<char*>(ws);
   int* counts = reinterpret_cast<int*>(base + lay.counts);
   int* offsets = reinterpret_cast<int*>(base + lay.offsets);
@@ -582,38 +715,43 @@ hipError_t launch_bwd(const LaunchShape& s, const void* q, const void* k, const 
   int* pairs = reinterpret_cast<int*>(base + lay.pairs);
   int* inv = reinterpret_cast<int*>(base + lay.inv);
   float* delta = reinterpret_cast<float*>(base + lay.delta);
-  bf16_t* part_dq = reinterpret_cast<bf16_t*>(base + lay.part_dq);
+  void* part_dq = base + lay.part_dq;
   float* part_kv = reinterpret_cast<float*>(base + lay.part_kv);
   const int m1 = s.lv.size[0];
   const size_t q_rows = (size_t)s.batch * s.heads_q * s.seq_len;
+  const T* qt = static_cast<const T*>(q);
+  const T* kt = static_cast<const T*>(k);
+  const T* vt = static_cast<const T*>(v);
+  const T* gt = static_cast<const T*>(dout);
+  T* dkt = static_cast<T*>(dk);
+  T* dvt = static_cast<T*>(dv);
   {
     prof::Scope ps("attn_bwd_delta", st);
-    hipLaunchKernelGGL((attn_bwd_delta_kernel<D>), dim3((unsigned)((q_rows * 16 + 255) / 256)),
-                       dim3(256), 0, st, static_cast<const bf16_t*>(out),
-                       static_cast<const bf16_t*>(dout), delta, q_rows);
+    hipLaunchKernelGGL((attn_bwd_delta_kernel<T, D>), dim3((unsigned)((q_rows * 16 + 255) / 256)),
+                       dim3(256), 0, st, static_cast<const T*>(out), gt, delta, q_rows);
   }
   hipError_t e;
   {
     prof::Scope ps("attn_bwd_sort", st);
-    e = bucket::sort_pairs_stable(idx, s.batch * s.heads_kv, s.seq_len, s.topk, m1,
-                                  kBwdItemCols / s.group, counts, offsets, cursors, item_offsets,
-                                  wgc, pairs, inv, st);
+    e = bucket::sort_pairs_stable(idx, s.batch * s.heads_kv, s.seq_len, s.topk, m1, lay.per_item,
+                                  counts, offsets, cursors, item_offsets, wgc, pairs, inv, st);
   }
   if (e != hipSuccess) return e;
-  {
+  const int cz = s.causal ? 1 : 0;
+  const float sl = s.scale * kLog2e;
+  if (mf) {
     prof::Scope ps("attn_bwd_main", st);
-    const bf16_t* qb = static_cast<const bf16_t*>(q);
-    const bf16_t* kb = static_cast<const bf16_t*>(k);
-    const bf16_t* vb = static_cast<const bf16_t*>(v);
-    const bf16_t* gb = static_cast<const bf16_t*>(dout);
-    bf16_t* dkb = static_cast<bf16_t*>(dk);
-    bf16_t* dvb = static_cast<bf16_t*>(dv);
-    const int cz = s.causal ? 1 : 0;
-    const float sl = s.scale * kLog2e;
+    const bf16_t* qb = reinterpret_cast<const bf16_t*>(qt);
+    const bf16_t* kb = reinterpret_cast<const bf16_t*>(kt);
+    const bf16_t* vb = reinterpret_cast<const bf16_t*>(vt);
+    const bf16_t* gb = reinterpret_cast<const bf16_t*>(gt);
+    bf16_t* dkb = reinterpret_cast<bf16_t*>(dkt);
+    bf16_t* dvb = reinterpret_cast<bf16_t*>(dvt);
+    bf16_t* pq = static_cast<bf16_t*>(part_dq);
 #define PISA_BWD(G)                                                                            \
   hipLaunchKernelGGL((attn_bwd_kernel<D, G>), dim3(lay.max_items), dim3(kBwdThreads), 0, st, qb, \
-                     kb, vb, gb, lse, delta, item_offsets, offsets, pairs, part_dq, part_kv, dkb, \
-                     dvb, lay.n_buckets, s.heads_q, s.heads_kv, s.seq_len, m1, cz, s.scale, sl)
+                     kb, vb, gb, lse, delta, item_offsets, offsets, pairs, pq, part_kv, dkb, dvb, \
+                     lay.n_buckets, s.heads_q, s.heads_kv, s.seq_len, m1, cz, s.scale, sl)
     switch (s.group) {
       case 1: PISA_BWD(1); break;
       case 2: PISA_BWD(2); break;
@@ -622,19 +760,35 @@ hipError_t launch_bwd(const LaunchShape& s, const void* q, const void* k, const 
       default: PISA_BWD(16); break;
     }
 #undef PISA_BWD
+  } else {
+    prof::Scope ps("attn_bwd_general", st);
+    hipLaunchKernelGGL((attn_bwd_generic_kernel<T, D>), dim3(lay.max_items), dim3(256), 0, st, qt,
+                       kt, vt, gt, lse, delta, item_offsets, offsets, pairs,
+                       static_cast<float*>(part_dq), part_kv, dkt, dvt, lay.n_buckets, s.heads_q,
+                       s.heads_kv, s.seq_len, s.block, m1, s.group, cz, s.scale, sl);
   }
   {
     prof::Scope ps("attn_bwd_dkv", st);
-    const size_t n = (size_t)lay.n_buckets * kBwdBlock * (D / 4) * 2;
-    hipLaunchKernelGGL((attn_bwd_dkv_kernel<D>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
-                       st, item_offsets, part_kv, static_cast<bf16_t*>(dk),
-                       static_cast<bf16_t*>(dv), lay.n_buckets, s.seq_len, m1);
+    const size_t n = (size_t)lay.n_buckets * s.block * (D / 4) * 2;
+    const dim3 grid((unsigned)((n + 255) / 256));
+    if (s.block == kBwdBlock)
+      hipLaunchKernelGGL((attn_bwd_dkv_kernel<T, D, kBwdBlock>), grid, dim3(256), 0, st,
+                         item_offsets, part_kv, dkt, dvt, lay.n_buckets, s.seq_len, m1, s.block);
+    else
+      hipLaunchKernelGGL((attn_bwd_dkv_kernel<T, D, 0>), grid, dim3(256), 0, st, item_offsets,
+                         part_kv, dkt, dvt, lay.n_buckets, s.seq_len, m1, s.block);
   }
   prof::Scope ps("attn_bwd_dq", st);
   const size_t rows = (size_t)s.batch * s.heads_kv * s.seq_len * s.group;
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<D>), dim3((unsigned)((rows * 16 + 255) / 256)),
-                     dim3(256), 0, st, idx, inv, part_dq, static_cast<bf16_t*>(dq), s.heads_q,
-                     s.heads_kv, s.seq_len, s.topk, s.group, m1, s.scale, rows);
+  const dim3 grid((unsigned)((rows * 16 + 255) / 256));
+  if (mf)
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<bf16_t, T, D>), grid, dim3(256), 0, st, idx, inv,
+                       static_cast<const bf16_t*>(part_dq), static_cast<T*>(dq), s.heads_q,
+                       s.heads_kv, s.seq_len, s.topk, s.group, m1, s.scale, rows);
+  else
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<float, T, D>), grid, dim3(256), 0, st, idx, inv,
+                       static_cast<const float*>(part_dq), static_cast<T*>(dq), s.heads_q,
+                       s.heads_kv, s.seq_len, s.topk, s.group, m1, s.scale, rows);
   return hipGetLastError();
 }
 
@@ -642,8 +796,8 @@ hipError_t launch_bwd(const LaunchShape& s, const void* q, const void* k, const 
 
 bool attn_bwd_supported(const LaunchShape& s) {
   const int64_t rows = (int64_t)s.batch * s.heads_kv * s.seq_len;
-  return s.bf16 && s.block == kBwdBlock && (s.head_dim == 64 || s.head_dim == 128) &&
-         (s.group & (s.group - 1)) == 0 && s.group <= kMaxGroup && rows < (int64_t(1) << 26) &&
+  return (s.head_dim == 64 || s.head_dim == 128) && s.block <= kBwdBlock &&
+         s.group <= kMaxGroup && rows < (int64_t(1) << 26) &&
          s.lv.size[0] <= bucket::kMaxLocalBuckets;
 }
 
@@ -655,9 +809,13 @@ hipError_t launch_attn_bwd(const LaunchShape& s, const void* q, const void* k, c
                            const int32_t* idx, const void* out, const float* lse,
                            const void* dout, void* dq, void* dk, void* dv, void* ws,
                            hipStream_t st) {
+  if (s.bf16)
+    return s.head_dim == 128
+               ? launch_bwd<bf16_t, 128>(s, q, k, v, idx, out, lse, dout, dq, dk, dv, ws, st)
+               : launch_bwd<bf16_t, 64>(s, q, k, v, idx, out, lse, dout, dq, dk, dv, ws, st);
   return s.head_dim == 128
-             ? launch_bwd<128>(s, q, k, v, idx, out, lse, dout, dq, dk, dv, ws, st)
-             : launch_bwd<64>(s, q, k, v, idx, out, lse, dout, dq, dk, dv, ws, st);
+             ? launch_bwd<float, 128>(s, q, k, v, idx, out, lse, dout, dq, dk, dv, ws, st)
+             : launch_bwd<float, 64>(s, q, k, v, idx, out, lse, dout, dq, dk, dv, ws, st);
 }
 
 }  // namespace pisa

@@ -211,9 +211,11 @@ int pisa_block_sparse_attn(const pisa_problem* problem, const void* q, const voi
  *   dq:        [B, Hq, N, d] dtype, out (every row written)
  *   dk, dv:    [B, Hkv, N, d] dtype, out (every row written)
  *   ws/ws_bytes: pisa_workspace_bytes(PISA_OP_ATTN_BWD) bytes
- * Supported: bf16, C = 64, d in {64, 128}, Hq / Hkv a power of two <= 16,
- * ceil(N / C) <= 8192 (PISA_ERR_UNSUPPORTED otherwise).  Deterministic: each
- * block's rows are visited in row order and every sum has a fixed order. */
+ * Supported: every shape pisa_block_sparse_attn supports with ceil(N / C) <=
+ * 8192 (PISA_ERR_UNSUPPORTED otherwise); bf16 with C = 64 and a power-of-two
+ * Hq / Hkv runs on the matrix cores, the rest on fp32 vector arithmetic.
+ * Deterministic: each block's rows are visited in row order and every sum has
+ * a fixed order. */
 int pisa_block_sparse_attn_backward(const pisa_problem* problem, const void* q, const void* k,
                                     const void* v, const int32_t* block_idx, const void* out,
                                     const float* row_lse, const void* dout, void* dq, void* dk,

@@ -175,37 +175,49 @@ def test_score_variants_need_the_per_query_selector():
 
 
 def test_backward_arguments():
-    """The backward refuses shapes outside its kernels (fp32, C != 64, a group
-    that is not a power of two, more than 8192 leaf blocks), a missing row_lse
-    or output, and a short
-    workspace; its workspace is the sort's maps, D, the bf16 dq partials and
-    the fp32 per-item dk/dv partials."""
+    """The backward runs every shape the forward runs (bf16 C=64 power-of-two
+    groups on MFMA, the rest on the general kernel) up to 8192 leaf blocks; it
+    refuses more blocks, a missing row_lse or output, and a short workspace.
+    Its workspace: the stable sort's maps, D, the dQ rows (bf16 on MFMA, fp32
+    otherwise) and the fp32 per-item dk/dv partials."""
     L = lib()
     dummy = ctypes.create_string_buffer(64)
     ptr = ctypes.cast(dummy, ctypes.c_void_p)
     bwd = L.pisa_block_sparse_attn_backward
-    for kw in (dict(dtype=_lib.PISA_F32), dict(block=32), dict(heads_q=6, heads_kv=2),
-               dict(seq_len=64 * 8192 + 1)):
-        p = problem(**kw)
-        assert bwd(ctypes.byref(p), ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, 1 << 40,
-                   None) == _lib.PISA_ERR_UNSUPPORTED, kw
-        sz = ctypes.c_size_t()
-        assert L.pisa_workspace_bytes(ctypes.byref(p), _lib.PISA_OP_ATTN_BWD,
-                                      ctypes.byref(sz)) == _lib.PISA_ERR_UNSUPPORTED
-    p = problem(heads_q=8, heads_kv=2, seq_len=3000, topk=8)
-    pp = ctypes.byref(p)
     sz = ctypes.c_size_t()
-    assert L.pisa_workspace_bytes(pp, _lib.PISA_OP_ATTN_BWD, ctypes.byref(sz)) == 0
+    for kw in (dict(dtype=_lib.PISA_F32), dict(block=32), dict(block=16, heads_q=6, heads_kv=2)):
+        p = problem(**kw)
+        assert L.pisa_workspace_bytes(ctypes.byref(p), _lib.PISA_OP_ATTN_BWD,
+                                      ctypes.byref(sz)) == 0, kw
+        assert sz.value > 0
+    p = problem(seq_len=64 * 8192 + 1)
+    assert bwd(ctypes.byref(p), ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, 1 << 40,
+               None) == _lib.PISA_ERR_UNSUPPORTED
+    assert L.pisa_workspace_bytes(ctypes.byref(p), _lib.PISA_OP_ATTN_BWD,
+                                  ctypes.byref(sz)) == _lib.PISA_ERR_UNSUPPORTED
 
     def a256(x):
         return (x + 255) // 256 * 256
-    g, slots, m1 = 4, 1 * 2 * 3000 * 8, 2 * 47
-    items = (slots + 512 - 1) // 512 + m1  # 2048 columns per item = 512 pairs at G = 4
-    chunks = -(-3000 // 128)  # row chunks of the stable sort
-    want = (a256(4 * m1) + a256(4 * (m1 + 1)) + a256(4 * m1) + a256(4 * (m1 + 1))
-            + a256(4 * 2 * chunks * 47) + a256(4 * slots) + a256(4 * slots) + a256(4 * 8 * 3000) + a256(2 * slots * g * 128)
-            + a256(4 * items * 2 * 64 * 128))
-    assert sz.value == want
+
+    def want(g, hkv, n, k, c, d, per_item, dq_bytes):
+        slots, m1 = hkv * n * k, hkv * -(-n // c)
+        items = -(-slots // per_item) + m1
+        chunks = -(-n // 128)  # row chunks of the stable sort
+        return (a256(4 * m1) + a256(4 * (m1 + 1)) + a256(4 * m1) + a256(4 * (m1 + 1))
+                + a256(4 * m1 * chunks) + a256(4 * slots) + a256(4 * slots)
+                + a256(4 * g * hkv * n) + a256(dq_bytes * slots * g * d)
+                + a256(4 * items * 2 * c * d))
+
+    p = problem(heads_q=8, heads_kv=2, seq_len=3000, topk=8)
+    pp = ctypes.byref(p)
+    assert L.pisa_workspace_bytes(pp, _lib.PISA_OP_ATTN_BWD, ctypes.byref(sz)) == 0
+    # MFMA path: 2048 columns per item = 512 pairs at G = 4, bf16 dQ rows
+    assert sz.value == want(4, 2, 3000, 8, 64, 128, 512, 2)
+    gp = problem(heads_q=6, heads_kv=2, seq_len=1000, topk=5, block=32, dtype=_lib.PISA_F32)
+    assert L.pisa_workspace_bytes(ctypes.byref(gp), _lib.PISA_OP_ATTN_BWD, ctypes.byref(sz)) == 0
+    # general path: 256 columns per item = 85 pairs at G = 3, fp32 dQ rows
+    assert sz.value == want(3, 2, 1000, 5, 32, 128, 85, 4)
+    assert L.pisa_workspace_bytes(pp, _lib.PISA_OP_ATTN_BWD, ctypes.byref(sz)) == 0
     args = [ptr] * 10
     for i in range(10):
         a = list(args)

@@ -34,17 +34,19 @@ from test_gpu_parity import DEV, announce, arbitrary_block_lists
 pytestmark = pytest.mark.gpu
 
 MAX_REL, NORM_REL = 2e-2, 1e-2
+# fp32 inputs (general kernel, fp32 throughout): the forward's fp32 bound
+MAX_REL_F32, NORM_REL_F32 = 1e-3, 1e-4
 
 
-def close(name, got, ref, floor=0.0):
+def close(name, got, ref, floor=0.0, max_rel=MAX_REL, norm_rel=NORM_REL):
     """Max and normwise error relative to the reference; ``floor`` stands in
     for max|ref| when the exact gradient vanishes (fp32 rounding of the
     dP - D difference then decides the result)."""
     err = np.abs(got - ref)
     scale = max(float(np.abs(ref).max()), floor, 1e-30)
-    assert err.max() <= MAX_REL * scale, f"{name}: max err {err.max():.3e} vs {scale:.3e}"
+    assert err.max() <= max_rel * scale, f"{name}: max err {err.max():.3e} vs {scale:.3e}"
     nr = max(float(np.linalg.norm(ref)), floor * math.sqrt(ref.size), 1e-30)
-    assert np.linalg.norm(err) <= NORM_REL * nr, f"{name}: normwise {np.linalg.norm(err) / nr:.3e}"
+    assert np.linalg.norm(err) <= norm_rel * nr, f"{name}: normwise {np.linalg.norm(err) / nr:.3e}"
 
 
 def rounding_floor(q, k, v, dout, scale):
@@ -63,51 +65,60 @@ def run_gpu(prob, inp, idx, dout):
 
 
 CASES = [
-    # (N, d, K, Hq, Hkv, causal, lists)
-    (3000, 128, 8, 2, 1, True, "selector"),     # ragged last block (56 keys), G = 2
-    (4160, 64, 16, 4, 4, True, "selector"),     # G = 1, d = 64, block 0 in 3 work items
-    (4160, 128, 16, 16, 1, True, "selector"),   # G = 16: 128 pairs per item, 33 items on block 0
-    (1500, 64, 8, 8, 2, False, "selector"),     # non-causal, G = 4, unselected blocks
-    (2100, 128, 12, 4, 2, True, "arbitrary"),   # unsorted rows, junk, future and empty rows
-    (700, 64, 5, 2, 2, False, "arbitrary"),
-    (64, 128, 3, 8, 1, True, "selector"),       # one block
-    (1, 64, 3, 2, 1, True, "selector"),         # one token
+    # (N, d, K, Hq, Hkv, causal, lists, dtype, C); bf16 with C = 64 and a
+    # power-of-two group runs the MFMA kernel, everything else the general one
+    (3000, 128, 8, 2, 1, True, "selector", "bf16", 64),     # ragged last block (56 keys), G = 2
+    (4160, 64, 16, 4, 4, True, "selector", "bf16", 64),     # G = 1, d = 64, block 0 in 3 items
+    (4160, 128, 16, 16, 1, True, "selector", "bf16", 64),   # G = 16: 128 pairs per item
+    (1500, 64, 8, 8, 2, False, "selector", "bf16", 64),     # non-causal, G = 4, unselected blocks
+    (2100, 128, 12, 4, 2, True, "arbitrary", "bf16", 64),   # unsorted, junk, future, empty rows
+    (700, 64, 5, 2, 2, False, "arbitrary", "bf16", 64),
+    (64, 128, 3, 8, 1, True, "selector", "bf16", 64),       # one block
+    (1, 64, 3, 2, 1, True, "selector", "bf16", 64),         # one token
+    # general kernel
+    (2048, 64, 4, 2, 2, True, "selector", "fp32", 64),      # the fp32 workload shape; block 0 in 8 items
+    (1000, 128, 5, 6, 2, False, "selector", "fp32", 16),    # C = 16, G = 3, non-causal, ragged
+    (3000, 64, 8, 1, 1, True, "selector", "bf16", 32),      # bf16, C = 32
+    (2500, 128, 16, 3, 1, True, "selector", "bf16", 64),    # bf16, C = 64, G = 3
+    (1300, 64, 6, 4, 4, True, "arbitrary", "fp32", 64),     # caller-style lists on the general kernel
 ]
 
 
 @pytest.mark.parametrize("case", CASES, ids=[f"N{c[0]}_d{c[1]}_K{c[2]}_G{c[3] // c[4]}_"
-                                             f"{'causal' if c[5] else 'full'}_{c[6]}"
+                                             f"{'causal' if c[5] else 'full'}_{c[6]}_{c[7]}_C{c[8]}"
                                              for c in CASES])
 def test_backward_small(case):
-    n, d, k, hq, hkv, causal, kind = case
+    n, d, k, hq, hkv, causal, kind, dt, c = case
     announce(f"backward {case}")
-    prob = Problem(1, hq, hkv, n, d, block=64, topk=k, dtype=torch.bfloat16, causal=causal,
+    dtype = torch.float32 if dt == "fp32" else torch.bfloat16
+    prob = Problem(1, hq, hkv, n, d, block=c, topk=k, dtype=dtype, causal=causal,
                    force_first_prev=causal and k >= 3)
-    inp = prefill_inputs(1, hq, hkv, n, d, torch.bfloat16, seed=900 + n, recipe="unit",
-                         device=DEV)
-    dout = seeded_normal((1, hq, n, d), 905 + n, 1.0, torch.bfloat16, DEV)
+    inp = prefill_inputs(1, hq, hkv, n, d, dtype, seed=900 + n, recipe="unit", device=DEV)
+    dout = seeded_normal((1, hq, n, d), 905 + n, 1.0, dtype, DEV)
     if kind == "selector":
-        idx = block_lists(1, hkv, n, 64, k, seed=n, causal=causal, device=DEV)
+        idx = block_lists(1, hkv, n, c, k, seed=n, causal=causal, device=DEV)
     else:
         idx = torch.from_numpy(arbitrary_block_lists(n, hkv, k, causal, seed=n + 1)).to(DEV)
     dq, dk, dv = run_gpu(prob, inp, idx, dout)
     g = hq // hkv
     idx_np = idx.cpu().numpy()
-    m1 = -(-n // 64)
+    m1 = -(-n // c)
     fl = rounding_floor(inp.q, inp.k, inp.v, dout, prob.logit_scale)
+    tol = (dict(max_rel=MAX_REL_F32, norm_rel=NORM_REL_F32) if dtype == torch.float32
+           else dict(max_rel=MAX_REL, norm_rel=NORM_REL))
     for h in range(hkv):
         lists = np.where(idx_np[0, h] >= m1, -1, idx_np[0, h])
         rq, rk, rv = oracle.attention_backward(
             parity.to_np(inp.q[0, h * g:(h + 1) * g]), parity.to_np(inp.k[0, h]),
-            parity.to_np(inp.v[0, h]), lists, parity.to_np(dout[0, h * g:(h + 1) * g]), 64,
+            parity.to_np(inp.v[0, h]), lists, parity.to_np(dout[0, h * g:(h + 1) * g]), c,
             causal, prob.logit_scale)
-        close(f"dq h{h}", parity.to_np(dq[0, h * g:(h + 1) * g]), rq, fl)
-        close(f"dk h{h}", parity.to_np(dk[0, h]), rk, fl)
-        close(f"dv h{h}", parity.to_np(dv[0, h]), rv)
+        close(f"dq h{h}", parity.to_np(dq[0, h * g:(h + 1) * g]), rq, fl, **tol)
+        close(f"dk h{h}", parity.to_np(dk[0, h]), rk, fl, **tol)
+        close(f"dv h{h}", parity.to_np(dv[0, h]), rv, **tol)
         # keys that no row attends get exact zeros
         seen = np.zeros(n, bool)
         for t in range(n):
-            seen[oracle.attended_tokens(lists[t], t, 64, n, causal)] = True
+            seen[oracle.attended_tokens(lists[t], t, c, n, causal)] = True
         assert np.all(parity.to_np(dk[0, h])[~seen] == 0) and np.all(parity.to_np(dv[0, h])[~seen] == 0)
 
 

@@ -13,7 +13,7 @@ Beside it (not part of the step): the backward of the block-sparse attention
 with the step's block lists held fixed, and the GQA decode step.
 
 Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--no-sweep] [--no-cpu] [--no-decode]
-                       [--no-backward] [--cpu-seconds 15] [--calibrate-copy-mb 0]
+                       [--no-backward] [--no-cold] [--cpu-seconds 15] [--calibrate-copy-mb 0]
 """
 from __future__ import annotations
 
@@ -219,6 +219,26 @@ def run(args):
     pisa.pisa_profile_enable(False)
     kernels = {k: tot / cnt for k, (tot, cnt) in pisa.pisa_profile_report().items()}
     ms_per_step = start.elapsed_time(stop) / args.steps
+    per_step = np.array([e[0].elapsed_time(e[3]) for e in ev])
+    # Cold-cache steps: before each, 1 GiB of writes evicts L2 and the 256 MB
+    # Infinity Cache; the step itself is bracketed by events on the stream.
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    cold = []
+    for i in range(0 if args.no_cold else 5):
+        flush.fill_(float(i))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1))
+    del flush
+    step_stats = {"warm_p10": float(np.percentile(per_step, 10)),
+                  "warm_p50": float(np.percentile(per_step, 50)),
+                  "warm_p90": float(np.percentile(per_step, 90)),
+                  "cold_p50": float(np.median(cold)) if cold else None,
+                  "cold_max": float(np.max(cold)) if cold else None,
+                  "note": "per-step events; value uses the mean over the timed steps (warm)"}
     stage = {name: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in ev]))
              for i, name in enumerate(("pyramid", "select", "attn"))}
 
@@ -271,6 +291,7 @@ def run(args):
                                "bf16 N(0,1/d), forced first/prev/current blocks",
                    "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)"},
         "stages_ms": stage,
+        "step_ms": step_stats,
         "kernels_ms": kernels,
         "wall_ms_per_step": wall_ms,
         "algorithmic": {"select_gflop": sel_flops / 1e9, "attn_gflop": attn_flops / 1e9,
@@ -548,6 +569,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache steps (counter runs)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--cpu-worker", default=None, help=argparse.SUPPRESS)
     ap.add_argument("--cpu-block", type=int, default=64, help=argparse.SUPPRESS)

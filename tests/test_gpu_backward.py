@@ -122,6 +122,43 @@ def test_backward_small(case):
         assert np.all(parity.to_np(dk[0, h])[~seen] == 0) and np.all(parity.to_np(dv[0, h])[~seen] == 0)
 
 
+BATCH_CASES = [
+    # (B, N, d, K, Hq, Hkv, dtype, C)
+    (2, 1700, 128, 8, 4, 2, "bf16", 64),   # MFMA kernel, batch index in every address
+    (3, 900, 64, 6, 2, 2, "fp32", 32),     # general kernel
+    (2, 2000, 64, 32, 16, 1, "bf16", 64),  # K = 32 (5 slot bits), G = 16
+]
+
+
+@pytest.mark.parametrize("case", BATCH_CASES, ids=[f"B{c[0]}_N{c[1]}_d{c[2]}_K{c[3]}_"
+                                                   f"G{c[4] // c[5]}_{c[6]}_C{c[7]}"
+                                                   for c in BATCH_CASES])
+def test_backward_batches(case):
+    """Several sequences at once: each (batch, KV head) against the oracle."""
+    bsz, n, d, k, hq, hkv, dt, c = case
+    announce(f"backward batch {case}")
+    dtype = torch.float32 if dt == "fp32" else torch.bfloat16
+    prob = Problem(bsz, hq, hkv, n, d, block=c, topk=k, dtype=dtype)
+    inp = prefill_inputs(bsz, hq, hkv, n, d, dtype, seed=700 + n, recipe="unit", device=DEV)
+    dout = seeded_normal((bsz, hq, n, d), 705 + n, 1.0, dtype, DEV)
+    idx = block_lists(bsz, hkv, n, c, k, seed=n + 3, device=DEV)
+    dq, dk, dv = run_gpu(prob, inp, idx, dout)
+    g = hq // hkv
+    idx_np = idx.cpu().numpy()
+    fl = rounding_floor(inp.q, inp.k, inp.v, dout, prob.logit_scale)
+    tol = (dict(max_rel=MAX_REL_F32, norm_rel=NORM_REL_F32) if dtype == torch.float32
+           else dict(max_rel=MAX_REL, norm_rel=NORM_REL))
+    for b in range(bsz):
+        for h in range(hkv):
+            rq, rk, rv = oracle.attention_backward(
+                parity.to_np(inp.q[b, h * g:(h + 1) * g]), parity.to_np(inp.k[b, h]),
+                parity.to_np(inp.v[b, h]), idx_np[b, h], parity.to_np(dout[b, h * g:(h + 1) * g]),
+                c, True, prob.logit_scale)
+            close(f"dq b{b} h{h}", parity.to_np(dq[b, h * g:(h + 1) * g]), rq, fl, **tol)
+            close(f"dk b{b} h{h}", parity.to_np(dk[b, h]), rk, fl, **tol)
+            close(f"dv b{b} h{h}", parity.to_np(dv[b, h]), rv, **tol)
+
+
 def test_backward_is_deterministic():
     """Same inputs twice: bitwise identical gradients (no floating-point atomics)."""
     n, d, k, hq, hkv = 4160, 128, 16, 8, 2

@@ -28,9 +28,9 @@
 //       dQ^T  = K^T dS^T for the wave's quarter of d (dS passes through LDS;
 //               computed one chunk later, so each chunk needs two barriers)
 //     Each column's dQ over this block goes (bf16) through an LDS tile and
-//     leaves as whole rows, in bucket order.  At
-//     the end the block's dK, dV go straight to the outputs when its bucket is
-//     one work item, else to a per-item fp32 partial;
+//     leaves as whole rows, in bucket order.  At the end the block's dK, dV
+//     go straight to the outputs when its bucket is one work item, else to a
+//     per-item fp32 partial;
 //  4. dq combine: the row's K partials summed in slot order, times scale;
 //  5. dkv reduce: blocks of several work items sum their partials in item
 //     order; blocks that no row selected get zeros.

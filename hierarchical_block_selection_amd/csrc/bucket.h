@@ -56,6 +56,12 @@ __global__ __launch_bounds__(256) void count_kernel(const int* __restrict__ node
     if (hist[i]) atomicAdd(&counts[(size_t)bh * m + i], hist[i]);
 }
 
+// Up to kScanLds buckets the counts pass through LDS, so that every global
+// load and store of the scan is coalesced; beyond that each thread reads and
+// writes its own contiguous range.
+constexpr int kScanLds = 8192;
+constexpr int kScanPer = kScanLds / 1024;  // buckets per thread when staged
+
 __global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ counts,
                                                     int* __restrict__ offsets,
                                                     int* __restrict__ cursors,
@@ -63,14 +69,23 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ coun
                                                     int per_item) {
   __shared__ int part_pairs[1024];
   __shared__ int part_items[1024];
+  extern __shared__ int c_s[];  // [n_buckets] when n_buckets <= kScanLds
+  const bool staged = n_buckets <= kScanLds;
   const int tid = threadIdx.x;
+  if (staged) {
+    for (int i = tid; i < n_buckets; i += 1024) c_s[i] = counts[i];
+    __syncthreads();
+  }
   const int per = (n_buckets + 1023) / 1024;
   const int lo = min(tid * per, n_buckets), hi = min(lo + per, n_buckets);
   int sp = 0, si = 0;
   for (int i0 = lo; i0 < hi; i0 += 8) {  // 8 loads in flight
     int c8[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) c8[k] = counts[min(i0 + k, hi - 1)];
+    for (int k = 0; k < 8; ++k) {
+      const int i = min(i0 + k, hi - 1);
+      c8[k] = staged ? c_s[i] : counts[i];
+    }
 #pragma unroll
     for (int k = 0; k < 8; ++k)
       if (i0 + k < hi) {
@@ -91,18 +106,51 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ coun
   }
   int pos = tid ? part_pairs[tid - 1] : 0;
   int ipos = tid ? part_items[tid - 1] : 0;
-  for (int i = lo; i < hi; ++i) {
-    const int c = counts[i];
-    offsets[i] = pos;
-    cursors[i] = pos;
-    item_offsets[i] = ipos;
-    pos += c;
-    ipos += (c + per_item - 1) / per_item;
-  }
   if (tid == 1023) {
     offsets[n_buckets] = part_pairs[1023];
     item_offsets[n_buckets] = part_items[1023];
   }
+  if (!staged) {
+    for (int i = lo; i < hi; ++i) {
+      const int c = counts[i];
+      offsets[i] = pos;
+      cursors[i] = pos;
+      item_offsets[i] = ipos;
+      pos += c;
+      ipos += (c + per_item - 1) / per_item;
+    }
+    return;
+  }
+  // Staged: this thread's counts to registers, then its range of c_s becomes
+  // the pair offsets (written out coalesced), then the item offsets.
+  int cr[kScanPer];
+#pragma unroll
+  for (int k = 0; k < kScanPer; ++k) cr[k] = lo + k < hi ? c_s[lo + k] : 0;
+#pragma unroll
+  for (int k = 0; k < kScanPer; ++k)
+    if (lo + k < hi) {
+      c_s[lo + k] = pos;
+      pos += cr[k];
+    }
+  __syncthreads();
+  for (int i = tid; i < n_buckets; i += 1024) {
+    const int o = c_s[i];
+    offsets[i] = o;
+    cursors[i] = o;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kScanPer; ++k)
+    if (lo + k < hi) {
+      c_s[lo + k] = ipos;
+      ipos += (cr[k] + per_item - 1) / per_item;
+    }
+  __syncthreads();
+  for (int i = tid; i < n_buckets; i += 1024) item_offsets[i] = c_s[i];
+}
+
+inline size_t scan_lds_bytes(int n_buckets) {
+  return n_buckets <= kScanLds ? sizeof(int) * (size_t)n_buckets : 0;
 }
 
 __global__ __launch_bounds__(256) void scatter_kernel(const int* __restrict__ node,
@@ -378,8 +426,8 @@ inline hipError_t sort_pairs(const int* node, int batch_heads, int n_tok, int to
       hipLaunchKernelGGL(count_global_kernel, dim3(grid_for(n_slots)), dim3(256), 0, st, node,
                          counts, n_tok, topk, m, n_slots);
   }
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, counts, offsets, cursors,
-                     item_offsets, n_buckets, per_item);
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), scan_lds_bytes(n_buckets), st, counts,
+                     offsets, cursors, item_offsets, n_buckets, per_item);
   if (local)
     hipLaunchKernelGGL(scatter_kernel, grid, dim3(256), 2 * sizeof(int) * m, st, node, cursors,
                        pairs, inv, n_tok, topk, m);
@@ -407,8 +455,8 @@ inline hipError_t sort_pairs_stable(const int* node, int batch_heads, int n_tok,
                      m);
   hipLaunchKernelGGL(wg_prefix_kernel, dim3((n_buckets + kPrefixBuckets - 1) / kPrefixBuckets),
                      dim3(256), 0, st, wgc, counts, (int)grid.x, m, n_buckets);
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, counts, offsets, cursors,
-                     item_offsets, n_buckets, per_item);
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), scan_lds_bytes(n_buckets), st, counts,
+                     offsets, cursors, item_offsets, n_buckets, per_item);
   hipLaunchKernelGGL(scatter_stable_kernel, grid, dim3(64), sizeof(int) * (m + (m + 3) / 4), st,
                      node, offsets, wgc, pairs, inv, n_tok, topk, m);
   return hipGetLastError();

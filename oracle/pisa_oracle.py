@@ -29,7 +29,7 @@ equation.  Where the page is silent the reading taken is stated at the spot.
 * Its backward with the block lists held fixed (§5.3): the softmax chain rule
   written out per row.
 
-Readings taken where the page leaves a step open (each also listed in the design doc):
+Readings taken where the page leaves a step open:
 
 R1  Ragged tails: eq. (4) is applied literally (mean of the children that
     exist); the leaf LSE runs over the keys that exist.

@@ -48,6 +48,8 @@ R10 Decode: the new query sits at t = cache_len - 1; its own key is already in
     the cache and in the pyramid.
 R11 Var(z) in eq. (9) is the population variance (1/m), as the cumulant
     expansion of eq. (8) implies.
+R12 (eq. (15) of §5.1 lost its right-hand side) bears on the kernel design
+    only; nothing here uses it.
 R13 Backward (§5.3): the leaf lists are inputs, not functions of Q and K; the
     gradients are those of eq. (2) over the fixed token set, so nothing reaches
     the pyramid or the scores.  dK and dV of a key sum over every query head

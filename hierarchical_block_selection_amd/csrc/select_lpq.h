@@ -473,12 +473,18 @@ __global__ __launch_bounds__(kWaves * kWave) void final_kernel(
   int nk3 = 0;
 #pragma unroll
   for (int i = 0; i < kMaxK; ++i) nk3 += n3[i] >= 0 ? 1 : 0;
-  // Level-2 scores of both children of every slot (slot indices are clamped
-  // so that unused entries never read past this query's K slots).
+  // Every slot's four leaf LSEs and two level-2 scores, loaded in one pass
+  // (slot indices are clamped so that unused entries never read past this
+  // query's K slots).  Reading the leaf LSEs only after the level-2 decision
+  // fetched the query's score lines from memory a second time.
+  float4 lv[kMaxK];
   float2 l2[kMaxK];
 #pragma unroll
-  for (int i = 0; i < kMaxK; ++i)
-    l2[i] = *reinterpret_cast<const float2*>(sc + min(i, topk - 1) * STRIDE + 4);
+  for (int i = 0; i < kMaxK; ++i) {
+    const float* p = sc + min(i, topk - 1) * STRIDE;
+    lv[i] = *reinterpret_cast<const float4*>(p);
+    l2[i] = *reinterpret_cast<const float2*>(p + 4);
+  }
 
   // Level 2: candidate j = child (j & 1) of level-3 node n3[j >> 1].
   int lim = cz ? (cur >> 1) : m2 - 1;
@@ -507,14 +513,22 @@ __global__ __launch_bounds__(kWaves * kWave) void final_kernel(
   for (int i = 0; i < kMaxK; ++i) k2[i] = lrow[i];
   wave_lds_sync();
   // Level 1: candidate j = leaf (j & 1) of the kept level-2 node k2[j >> 1]
-  // (node k2 >> 5); its exact LSE sits in the stage-2 slot (j2 >> 1), entry
-  // 2 * (j2 & 1) + (j & 1), where j2 = k2 & 31.
-  float2 l1[kMaxK];
+  // (node k2 >> 5).  The leaf pairs of the kept level-2 candidates are
+  // compacted through LDS in the same order as k2: the first leaf's LSE as
+  // bits through the int column, the second's through the float column.
 #pragma unroll
-  for (int i = 0; i < kMaxK; ++i) {
-    const int j2 = k2[i] & 31;
-    l1[i] = *reinterpret_cast<const float2*>(sc + min(j2 >> 1, topk - 1) * STRIDE + 2 * (j2 & 1));
+  for (int j = 0; j < kSlots; ++j) {
+    const bool k = (km2 >> j) & 1u;
+    const int pos = k ? min(__popc(km2 & ((1u << j) - 1u)), kMaxK) : kMaxK;
+    const float4 v = lv[j >> 1];
+    lrow[pos] = __float_as_int((j & 1) ? v.z : v.x);
+    frow[pos] = (j & 1) ? v.w : v.y;
   }
+  wave_lds_sync();
+  float2 l1[kMaxK];  // entries past nk2 are stale and never ranked
+#pragma unroll
+  for (int i = 0; i < kMaxK; ++i) l1[i] = make_float2(__int_as_float(lrow[i]), frow[i]);
+  wave_lds_sync();
   lim = cz ? cur : m1 - 1;
   x_max = min(m1 - 1, lim);
   nv = 0;

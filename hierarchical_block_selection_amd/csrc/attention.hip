@@ -309,7 +309,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_partial_kernel(
 // LSEs, then up to 16 partials (16-byte loads), are all requested before any
 // is used.  Slots that are -1 or out of range have no position (rows need
 // not be sorted, so slot 0 may be one of them): they read position 0, which
-// is always inside the partial buffers, with weight 0.
+// is always inside the partial buffers, with weight 0 and their loaded values
+// replaced by zeros.
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(
     const int32_t* __restrict__ idx, const int* __restrict__ pos_of, const bf16_t* __restrict__ part_o,
@@ -368,7 +369,12 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
     }
 #pragma unroll
     for (int jj = 0; jj < B; ++jj) {
-      const float w = lj[jj] != neg_inf() ? fast_exp2(lj[jj] - M) : 0.f;
+      const bool live = lj[jj] != neg_inf();
+      const float w = live ? fast_exp2(lj[jj] - M) : 0.f;
+      // a slot without a partial read position 0, which need not hold one
+      // (no pair at all, or not yet written): take zeros, never 0 * garbage
+#pragma unroll
+      for (int e = 0; e < EPL / 2; ++e) raw[jj][e] = live ? raw[jj][e] : 0u;
       W += w;
 #pragma unroll
       for (int e = 0; e < EPL / 2; ++e) {

@@ -18,7 +18,8 @@ import oracle
 import parity
 from hierarchical_block_selection_amd import (Problem, pisa_block_sparse_attn, pisa_bsa_select,
                                               pisa_build_pyramid, pisa_decode_step,
-                                              pisa_pyramid_layout, pisa_select)
+                                              pisa_pyramid_layout, pisa_select,
+                                              pisa_workspace_bytes)
 from hierarchical_block_selection_amd.inputs import (WORKLOADS, decode_inputs, prefill_inputs,
                                                      sample_rows)
 
@@ -425,6 +426,28 @@ def test_attention_arbitrary_block_lists(case):
         parity.compare_attention(o, ls, qg, keys, vals, sub, full, 64, causal,
                                  prob.logit_scale, fp32=False)
         assert len(empty) > 0 and len(full) > len(rows) // 2
+
+
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+def test_attention_nothing_attendable(causal):
+    """Lists that name no block at all (-1, negative junk and indices past the
+    last block) leave the block path with no (row, block) pair and so no
+    partial anywhere: every row must come out as zeros with row_lse = -inf,
+    here from a workspace whose bytes are all 0xff (NaN in bf16 and fp32), so
+    that a merge which multiplied an unwritten partial by a zero weight would
+    show up as NaN."""
+    n, d, k, hq, hkv = 300, 128, 4, 4, 2
+    prob = Problem(1, hq, hkv, n, d, block=64, topk=k, dtype=torch.bfloat16, causal=causal,
+                   force_first_prev=False)
+    announce(f"nothing attendable causal={causal}")
+    inp = prefill_inputs(1, hq, hkv, n, d, torch.bfloat16, seed=530, recipe="unit", device=DEV)
+    m1 = -(-n // 64)
+    idx = torch.tensor([-1, m1, -5, m1 + 3], dtype=torch.int32).repeat(1, hkv, n, 1).to(DEV)
+    ws = torch.full((pisa_workspace_bytes(prob, "attn"),), 255, dtype=torch.uint8, device=DEV)
+    out, lse = pisa_block_sparse_attn(prob, inp.q, inp.k, inp.v, idx, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0).item()
+    assert torch.all(torch.isneginf(lse)).item()
 
 
 SCORE_CASES = [

@@ -41,8 +41,8 @@ namespace {
 constexpr int kSplitLevel = 3;   // stage 1 decides levels L..3
 constexpr int kS1Waves = 4;
 constexpr int kS2Threads = 256;
-constexpr int kS2Rows = 256;    // (pair, head) rows per stage-2 batch
-constexpr int kS2Batches = 4;   // batches per stage-2 work item
+constexpr int kS2Rows = 128;    // (pair, head) rows per stage-2 batch
+constexpr int kS2Batches = 8;   // batches per stage-2 work item
 constexpr int kS2Cols = 32;      // MFMA 32x32x16: 32 (query, head) columns
 constexpr int kScoreStride = 8;  // floats per pair: 4 leaf LSE, 2 level-2, 2 pad
 
@@ -305,8 +305,11 @@ __device__ __forceinline__ void stage2_fetch(u32x4_t (&stage)[PER_THREAD], int& 
 // kS2Batches batches of kS2Rows / G of its (query, slot) pairs; wavefront w
 // owns leaf 4n + w and keeps its 64 raw keys as MFMA A operands in registers
 // for the whole item.  Per batch:
-//   1. the batch's query rows of every (pair, head), loaded into registers
-//      while the previous batch computed, go to LDS;
+//   1. the batch's query rows of every (pair, head) are loaded and staged in
+//      LDS (no register prefetch: batches of 128 rows keep the LDS tile at
+//      35 KB and the kernel under 168 VGPRs, so three workgroups share a CU
+//      and hide each other's loads, which measured faster than two
+//      workgroups prefetching the next batch);
 //   2. each wave walks the staged rows 32 columns at a time: S = K_leaf . Q^T
 //      on bf16 MFMA 32x32x16 (a lane holds 32 keys of one column), then the
 //      exact leaf LSE (eq. (7) at level 1: max, sum of exp2) and the mean
@@ -315,7 +318,7 @@ __device__ __forceinline__ void stage2_fetch(u32x4_t (&stage)[PER_THREAD], int& 
 //      the two level-2 scores LSE(mean_2c, mean_2c+1), each summed over the
 //      group's heads (eq. (11)), in nats.
 template <int D, int G>
-__global__ __launch_bounds__(kS2Threads, 2) void stage2_kernel(
+__global__ __launch_bounds__(kS2Threads, 3) void stage2_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const int* __restrict__ item_offsets, const int* __restrict__ offsets,
     const int* __restrict__ pairs, float* __restrict__ scores, int n_buckets, int heads_q,
@@ -345,7 +348,6 @@ __global__ __launch_bounds__(kS2Threads, 2) void stage2_kernel(
   // rows past the item repeat its last pair) -> registers.
   u32x4_t stage[PER_THREAD];
   int pid_reg = 0;
-  stage2_fetch<D, G, PER_THREAD>(stage, pid_reg, pairs, start, len, 0, qh, bh, n_tok, topk);
   const int leaf_tok0 = (4 * node + wave) * LEAF;
   const int n_keys = max(0, min(LEAF, n_tok - leaf_tok0));  // keys of this wave's leaf
   // A operands: key rows leaf_tok0 + 32 rb + col (rows past the sequence end
@@ -369,6 +371,7 @@ __global__ __launch_bounds__(kS2Threads, 2) void stage2_kernel(
     constexpr bool kFull = decltype(full_tag)::value;
     for (int bt = 0; bt < n_batches; ++bt) {
       const int blen = min(PAIRS, len - bt * PAIRS);  // pairs in this batch
+      stage2_fetch<D, G, PER_THREAD>(stage, pid_reg, pairs, start, len, bt, qh, bh, n_tok, topk);
       __syncthreads();  // the previous batch's readers of qs, xs and pid_s are done
       if (tid < PAIRS) pid_s[tid] = pid_reg;
 #pragma unroll
@@ -377,9 +380,6 @@ __global__ __launch_bounds__(kS2Threads, 2) void stage2_kernel(
         *reinterpret_cast<u32x4_t*>(&qs[(x / V16) * QROW + 8 * (x % V16)]) = stage[i];
       }
       __syncthreads();
-      // next batch in flight while this one computes (the last batch fetches itself again)
-      stage2_fetch<D, G, PER_THREAD>(stage, pid_reg, pairs, start, len,
-                                     min(bt + 1, n_batches - 1), qh, bh, n_tok, topk);
 
       const int n_chunks = (blen * G + 31) / 32;
       for (int ch = 0; ch < n_chunks; ++ch) {

@@ -3,12 +3,12 @@
 //
 // bf16, C = 64 (block path): a (query row, selected block) pair moves only the
 // query (d bf16) and a partial result instead of the block's 2*C*d key/value
-// bytes.  Pairs are bucketed by block; one workgroup per (block, <= 256 pairs)
-// keeps K_b (row-major) and V_b (transposed) in LDS and, per 32 (query, head)
-// columns, runs S = K_b Q^T and O = P V_b as bf16 MFMA 32x32x16 with fp32
-// accumulation, masks keys after t, and writes the block's normalised output
-// (bf16) and its log2-sum-exp.  A combine pass merges the K partials of each
-// row with the usual max-rescaled weights.  V is stored transposed so that the
+// bytes.  Pairs are bucketed by block; one workgroup per (block, <= 1024
+// (pair, head) rows) keeps K_b (row-major) and V_b (transposed) in LDS and,
+// per 32 (query, head) columns, runs S = K_b Q^T and O = P V_b as bf16 MFMA
+// 32x32x16 with fp32 accumulation, masks keys after t, and writes the
+// block's normalised output (bf16) and its log2-sum-exp.  A combine pass
+// merges the K partials of each row with the usual max-rescaled weights.  V is stored transposed so that the
 // probabilities held in the QK^T accumulators feed the PV product directly:
 // the key order inside the PV reduction is permuted to match the accumulator
 // layout, which leaves the sum unchanged.

@@ -16,8 +16,10 @@
 //             wavefront per (b, kv head, t) (stage1_kernel below).
 //   scan      one workgroup: bucket offsets and the stage-2 work list.
 //   scatter   pairs (row << 5 | slot) into per-node buckets.
-//   stage 2   one workgroup per (node, <= 256 pairs): the node's keys in LDS,
-//             bf16 MFMA 32x32x16 (keys x queries), per-leaf LSE and mean.
+//   stage 2   one workgroup per (node, <= 1024 / G pairs): each wave holds one
+//             leaf's keys in registers, the pairs' query rows pass through LDS
+//             in batches; bf16 MFMA 32x32x16 (keys x queries), per-leaf LSE
+//             and mean.
 //   final     level-2 and leaf decisions from the stage-2 scores, ascending
 //             leaf list out: one lane per query (K <= 16) or one wavefront
 //             per query (final_kernel below).

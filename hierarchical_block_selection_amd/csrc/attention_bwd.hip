@@ -508,7 +508,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
       const int j = min(j0 + jj, topk - 1);
       const int xj = ir[j];
       live[jj] = j0 + jj < topk && xj >= 0 && xj < m1;
-      const int p = live[jj] ? pos_of[u * topk + j] : 0;  // position 0 always exists
+      // requested with the block index, not after it (a dead slot's entry is
+      // never written and never used): position 0 always exists
+      const int pj = pos_of[u * topk + j];
+      const int p = live[jj] ? pj : 0;
       const uint32_t* src =
           reinterpret_cast<const uint32_t*>(part_dq + ((size_t)p * group + h) * D + sub * EPL);
       if (WPL % 4 == 0) {

@@ -64,8 +64,8 @@ namespace {
 
 constexpr int kAttnBlock = 64;
 constexpr int kAttnThreads = 256;
-constexpr int kAttnRows = 256;   // (pair, head) rows per batch
-constexpr int kAttnBatches = 4;  // batches per work item
+constexpr int kAttnRows = 128;   // (pair, head) rows per batch
+constexpr int kAttnBatches = 8;  // batches per work item
 constexpr int kAttnCols = 32;
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
@@ -109,9 +109,10 @@ AttnWs attn_layout(const LaunchShape& s) {
 // One workgroup per work item: leaf block blk of KV head bh and up to
 // kAttnBatches batches of kAttnRows / G of the (query, slot) pairs that
 // selected it.  K_blk (row-major) and V_blk (transposed) sit in LDS for the
-// whole item; in every batch wave w takes the 32-column chunks w and w + 4
-// of the batch's (pair, head) rows, whose query rows it loaded while the
-// previous batch computed.  Per chunk:
+// whole item; in every batch wave w takes the 32-column chunk w of the
+// batch's (pair, head) rows, loading its query rows at the batch's start
+// (no register prefetch: at 168 VGPRs and 53 KB of LDS three workgroups
+// share a CU and cover each other's loads).  Per chunk:
 //   S^T = K_blk Q^T   (MFMA A = keys from LDS, B = queries; a lane holds the
 //                      logits of 32 keys for one column)
 //   P   = exp2(S * scale - m) in fp32, row sum l, then bf16
@@ -142,7 +143,7 @@ __device__ __forceinline__ void attn_fetch(bf16x8_t (&bq)[NCH][KSTEPS], int (&pi
 }
 
 template <int D, int G>
-__global__ __launch_bounds__(kAttnThreads, 2) void attn_partial_kernel(
+__global__ __launch_bounds__(kAttnThreads, 3) void attn_partial_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const int* __restrict__ item_offsets, const int* __restrict__ offsets,
     const int* __restrict__ pairs, bf16_t* __restrict__ part_o, float* __restrict__ part_lse,
@@ -158,7 +159,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_partial_kernel(
   constexpr int NCH = kAttnRows / kAttnCols / NW;  // chunks per wave and batch
   __shared__ __attribute__((aligned(16))) bf16_t ks[C * KROW];
   __shared__ __attribute__((aligned(16))) bf16_t vt[D * VROW];
-  constexpr int OROW = D + 8;  // padded output tile row (bf16)
+  constexpr int OROW = D / 2 + 8;  // padded output tile row (bf16): half of d per pass
   __shared__ __attribute__((aligned(16))) bf16_t os[NW][kAttnCols * OROW];
   int bucket, start, len;
   if (!bucket::locate_item(item_offsets, offsets, n_buckets, blockIdx.x, PAIRS * kAttnBatches,
@@ -199,10 +200,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_partial_kernel(
   const int rows = len * G;
   const int n_batches = (len + PAIRS - 1) / PAIRS;
   for (int bt = 0; bt < n_batches; ++bt) {
-    bf16x8_t bn[NCH][KSTEPS];
-    int pid_n[NCH], tq_n[NCH];
-    attn_fetch<D, G, NCH, KSTEPS>(bn, pid_n, tq_n, pairs, start, len, min(bt + 1, n_batches - 1),
-                                  wave, col, kh, qh, bh, n_tok, topk);
+    if (bt > 0)
+      attn_fetch<D, G, NCH, KSTEPS>(bq, pid, tq, pairs, start, len, bt, wave, col, kh, qh, bh,
+                                    n_tok, topk);
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const int r0 = bt * kAttnRows + (wave + NW * c) * kAttnCols;
@@ -264,41 +264,39 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_partial_kernel(
       // o[db][i] = O[column][d = 32 db + (i/4)*8 + 4kh + i%4].  Partials are
       // stored in bucket order (row start * G + r of the sorted pairs): the
       // chunk's 32 rows are one contiguous run, written through an LDS tile
-      // as 16-byte pieces, 1 KB per store instruction.
+      // (half of d per pass) as 16-byte pieces, 1 KB per store instruction.
       const float inv = l > 0.f ? 1.f / l : 0.f;
       bf16_t* tile = &os[wave][0];
-#pragma unroll
-      for (int db = 0; db < DBLK; ++db)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
-          bf16x4_t w;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[db][4 * g4 + e] * inv);
-          *reinterpret_cast<uint2*>(&tile[col * OROW + 32 * db + 8 * g4 + 4 * kh]) =
-              __builtin_bit_cast(uint2, w);
-        }
       if (live && kh == 0) part_lse[(size_t)start * G + r0 + col] = ms + fast_log2(l);
-      wave_lds_sync();
       const int n_live = min(kAttnCols, rows - r0);  // rows of this chunk that exist
       bf16_t* dst = part_o + ((size_t)start * G + r0) * D;
-      constexpr int PIECES = kAttnCols * D / 8;  // 16-byte pieces of the chunk
+      // two passes, each over half of d
 #pragma unroll
-      for (int x = lane; x < PIECES; x += kWave) {
-        const int rr = x / (D / 8), c8 = (x % (D / 8)) * 8;
-        if (rr < n_live)
-          // streamed out: read once, by the combine
-          __builtin_nontemporal_store(*reinterpret_cast<const u32x4_t*>(&tile[rr * OROW + c8]),
-                                      reinterpret_cast<u32x4_t*>(dst + (size_t)rr * D + c8));
+      for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+        for (int dh = 0; dh < DBLK / 2; ++dh)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+            bf16x4_t w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[hf * (DBLK / 2) + dh][4 * g4 + e] * inv);
+            *reinterpret_cast<uint2*>(&tile[col * OROW + 32 * dh + 8 * g4 + 4 * kh]) =
+                __builtin_bit_cast(uint2, w);
+          }
+        wave_lds_sync();
+        constexpr int PIECES = kAttnCols * D / 16;  // 16-byte pieces of the half chunk
+#pragma unroll
+        for (int x = lane; x < PIECES; x += kWave) {
+          const int rr = x / (D / 16), c8 = (x % (D / 16)) * 8;
+          if (rr < n_live)
+            // streamed out: read once, by the combine
+            __builtin_nontemporal_store(
+                *reinterpret_cast<const u32x4_t*>(&tile[rr * OROW + c8]),
+                reinterpret_cast<u32x4_t*>(dst + (size_t)rr * D + hf * (D / 2) + c8));
+        }
+        wave_lds_sync();
       }
-      wave_lds_sync();
-    }
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      pid[c] = pid_n[c];
-      tq[c] = tq_n[c];
-#pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) bq[c][s] = bn[c][s];
     }
   }
 }

@@ -35,6 +35,8 @@
 //  5. dkv reduce: blocks of several work items sum their partials in item
 //     order; blocks that no row selected get zeros.
 // No floating-point atomics: the results are bitwise reproducible.
+#include <algorithm>
+
 #include "bucket.h"
 #include "pisa_common.h"
 #include "pisa_launch.h"
@@ -544,41 +546,79 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
   for (int e = 0; e < EPL; ++e) store_from_f32(dst + e, acc[e] * scale);
 }
 
-// dK, dV rows of blocks whose bucket is not exactly one work item: the sum of
-// the items' partials in item order (no item: zeros).  One thread per (block,
-// key, 4 dims, K or V); C keys per block (CF > 0 fixes C at compile time).
+// The blocks whose dK and dV the reduction below writes: those whose bucket
+// is split over several work items, and those with no pair (zeros), in
+// increasing order.  One workgroup; the list length goes to *n_list.
+__global__ __launch_bounds__(1024) void attn_bwd_dkv_plan_kernel(
+    const int* __restrict__ item_offsets, int* __restrict__ list, int* __restrict__ n_list,
+    int n_buckets) {
+  constexpr int NW = 1024 / kWave;
+  __shared__ int wave_n[NW];
+  __shared__ int base_s;
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  if (threadIdx.x == 0) base_s = 0;
+  __syncthreads();
+  for (int b0 = 0; b0 < n_buckets; b0 += 1024) {
+    const int b = b0 + (int)threadIdx.x;
+    const bool f = b < n_buckets && item_offsets[b + 1] - item_offsets[b] != 1;
+    const uint64_t m = __ballot(f);
+    if (lane == 0) wave_n[wave] = __popcll(m);
+    __syncthreads();
+    int before = base_s;
+    for (int x = 0; x < wave; ++x) before += wave_n[x];
+    if (f) list[before + lanes_below(m)] = b;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int tot = 0;
+      for (int x = 0; x < NW; ++x) tot += wave_n[x];
+      base_s += tot;
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *n_list = base_s;
+}
+
+// dK, dV rows of the listed blocks: the sum of their items' partials in item
+// order (no item: zeros).  A block's C * D / 4 * 2 (key, 4 dims, K or V)
+// units form slices of 256, one thread per unit; the grid walks the list's
+// slices, so a block split over many items still spreads over many
+// workgroups while blocks of one item launch nothing.  C keys per block (CF >
+// 0 fixes C at compile time).
 template <typename T, int D, int CF>
 __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
-    const int* __restrict__ item_offsets, const float* __restrict__ part_kv, T* __restrict__ dk,
-    T* __restrict__ dv, int n_buckets, int n_tok, int m1, int c_rt) {
+    const int* __restrict__ item_offsets, const int* __restrict__ list,
+    const int* __restrict__ n_list, const float* __restrict__ part_kv, T* __restrict__ dk,
+    T* __restrict__ dv, int n_tok, int m1, int c_rt) {
   constexpr int Q4 = D / 4;
   const int C = CF > 0 ? CF : c_rt;
-  const size_t id = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (id >= (size_t)n_buckets * C * Q4 * 2) return;
-  const int d4 = (int)(id % Q4);
-  const int key = (int)((id / Q4) % C);
-  const int which = (int)((id / Q4 / C) % 2);
-  const int bucket = (int)(id / Q4 / C / 2);
-  const int bh = bucket / m1, blk = bucket % m1;
-  const int tok = blk * C + key;
-  if (tok >= n_tok) return;
-  const int i0 = item_offsets[bucket], n_items = item_offsets[bucket + 1] - i0;
-  if (n_items == 1) return;  // written by its work item
-  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const float* src = part_kv + ((size_t)i0 * 2 + which) * C * D + (size_t)key * D + 4 * d4;
-  constexpr int U = 8;
-  for (int i = 0; i < n_items; i += U) {
-    f32x4_t x[U];
+  const int slices = C * Q4 * 2 / 256;  // C >= 16 and D >= 64: a whole number
+  const int n = *n_list * slices;
+  for (int sl = blockIdx.x; sl < n; sl += gridDim.x) {
+    const int bucket = list[sl / slices];
+    const int id = (sl % slices) * 256 + (int)threadIdx.x;
+    const int d4 = id % Q4;
+    const int key = (id / Q4) % C;
+    const int which = id / Q4 / C;
+    const int bh = bucket / m1, blk = bucket % m1;
+    const int tok = blk * C + key;
+    if (tok >= n_tok) continue;
+    const int i0 = item_offsets[bucket], n_items = item_offsets[bucket + 1] - i0;
+    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const float* src = part_kv + ((size_t)i0 * 2 + which) * C * D + (size_t)key * D + 4 * d4;
+    constexpr int U = 8;
+    for (int i = 0; i < n_items; i += U) {
+      f32x4_t x[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      x[u] = *reinterpret_cast<const f32x4_t*>(src + (size_t)min(i + u, n_items - 1) * 2 * C * D);
+      for (int u = 0; u < U; ++u)
+        x[u] = *reinterpret_cast<const f32x4_t*>(src + (size_t)min(i + u, n_items - 1) * 2 * C * D);
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (i + u < n_items) acc += x[u];
+      for (int u = 0; u < U; ++u)
+        if (i + u < n_items) acc += x[u];
+    }
+    T* dst = (which ? dv : dk) + ((size_t)bh * n_tok + tok) * D + 4 * d4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) store_from_f32(dst + e, acc[e]);
   }
-  T* dst = (which ? dv : dk) + ((size_t)bh * n_tok + tok) * D + 4 * d4;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) store_from_f32(dst + e, acc[e]);
 }
 
 // General backward kernel (any dtype, C <= 64, any group), fp32 vector math,
@@ -772,14 +812,19 @@ hipError_t launch_bwd(const LaunchShape& s, const void* q, const void* k, const 
   }
   {
     prof::Scope ps("attn_bwd_dkv", st);
-    const size_t n = (size_t)lay.n_buckets * s.block * (D / 4) * 2;
-    const dim3 grid((unsigned)((n + 255) / 256));
+    // counts and cursors are free once the sort is done: the list of blocks
+    // to reduce goes to cursors, its length to counts[0]
+    hipLaunchKernelGGL(attn_bwd_dkv_plan_kernel, dim3(1), dim3(1024), 0, st, item_offsets,
+                       cursors, counts, lay.n_buckets);
+    const size_t slices = (size_t)lay.n_buckets * s.block * (D / 4) * 2 / 256;
+    const dim3 grid((unsigned)std::min<size_t>(slices, 8192));
     if (s.block == kBwdBlock)
       hipLaunchKernelGGL((attn_bwd_dkv_kernel<T, D, kBwdBlock>), grid, dim3(256), 0, st,
-                         item_offsets, part_kv, dkt, dvt, lay.n_buckets, s.seq_len, m1, s.block);
+                         item_offsets, cursors, counts, part_kv, dkt, dvt, s.seq_len, m1,
+                         s.block);
     else
       hipLaunchKernelGGL((attn_bwd_dkv_kernel<T, D, 0>), grid, dim3(256), 0, st, item_offsets,
-                         part_kv, dkt, dvt, lay.n_buckets, s.seq_len, m1, s.block);
+                         cursors, counts, part_kv, dkt, dvt, s.seq_len, m1, s.block);
   }
   prof::Scope ps("attn_bwd_dq", st);
   const size_t rows = (size_t)s.batch * s.heads_kv * s.seq_len * s.group;

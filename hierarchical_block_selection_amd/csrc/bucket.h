@@ -22,7 +22,8 @@
 namespace pisa {
 namespace bucket {
 
-constexpr int kRowsPerGroup = 512;    // rows of one head per count/scatter workgroup
+constexpr int kRowsPerGroup = 512;    // least rows of one head per count/scatter workgroup
+constexpr int kMaxRowsPerGroup = 2048;
 constexpr int kMaxLocalBuckets = 8192;  // LDS histogram limit (two int arrays = 64 KB)
 constexpr int kBatch = 16;  // slots per thread whose loads are issued together
 constexpr int kStableRows = 128;  // rows per chunk of the stable sort (one wave scatters a chunk)
@@ -35,12 +36,12 @@ __global__ void fill_zero_kernel(int* __restrict__ p, int n) {
 
 __global__ __launch_bounds__(256) void count_kernel(const int* __restrict__ node,
                                                     int* __restrict__ counts, int n_tok, int topk,
-                                                    int m) {
+                                                    int m, int rpg) {
   extern __shared__ int hist[];  // [m]
   for (int i = threadIdx.x; i < m; i += blockDim.x) hist[i] = 0;
   __syncthreads();
   const int bh = blockIdx.y;
-  const int t0 = blockIdx.x * kRowsPerGroup, t1 = min(t0 + kRowsPerGroup, n_tok);
+  const int t0 = blockIdx.x * rpg, t1 = min(t0 + rpg, n_tok);
   const int* src = node + ((size_t)bh * n_tok) * topk;
   const int i1 = t1 * topk;
   for (int ib = t0 * topk + threadIdx.x; ib < i1; ib += kBatch * blockDim.x) {
@@ -157,7 +158,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int* __restrict__ no
                                                       int* __restrict__ cursors,
                                                       int* __restrict__ pairs,
                                                       int* __restrict__ inv, int n_tok, int topk,
-                                                      int m) {
+                                                      int m, int rpg) {
   extern __shared__ int lds[];  // hist/base [m], local cursor [m]
   int* base = lds;
   int* cur = lds + m;
@@ -167,7 +168,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int* __restrict__ no
   }
   __syncthreads();
   const int bh = blockIdx.y;
-  const int t0 = blockIdx.x * kRowsPerGroup, t1 = min(t0 + kRowsPerGroup, n_tok);
+  const int t0 = blockIdx.x * rpg, t1 = min(t0 + rpg, n_tok);
   const size_t row0 = (size_t)bh * n_tok;
   const int* src = node + row0 * topk;
   const int i1 = t1 * topk;
@@ -414,14 +415,21 @@ inline hipError_t sort_pairs(const int* node, int batch_heads, int n_tok, int to
                              hipStream_t st) {
   const int n_buckets = batch_heads * m;
   const size_t n_slots = (size_t)batch_heads * n_tok * topk;
-  const dim3 grid((n_tok + kRowsPerGroup - 1) / kRowsPerGroup, batch_heads);
+  // Rows per count/scatter workgroup: fewer, larger workgroups place their
+  // pairs with fewer global counter updates, as long as the grid still has a
+  // few hundred of them.
+  int rpg = kRowsPerGroup;
+  while (rpg < kMaxRowsPerGroup &&
+         (size_t)((n_tok + 2 * rpg - 1) / (2 * rpg)) * batch_heads >= 256)
+    rpg *= 2;
+  const dim3 grid((n_tok + rpg - 1) / rpg, batch_heads);
   const bool local = m <= kMaxLocalBuckets;
   if (!counts_ready) {
     hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for(n_buckets)), dim3(256), 0, st, counts,
                        n_buckets);
     if (local)
       hipLaunchKernelGGL(count_kernel, grid, dim3(256), sizeof(int) * m, st, node, counts, n_tok,
-                         topk, m);
+                         topk, m, rpg);
     else
       hipLaunchKernelGGL(count_global_kernel, dim3(grid_for(n_slots)), dim3(256), 0, st, node,
                          counts, n_tok, topk, m, n_slots);
@@ -430,7 +438,7 @@ inline hipError_t sort_pairs(const int* node, int batch_heads, int n_tok, int to
                      offsets, cursors, item_offsets, n_buckets, per_item);
   if (local)
     hipLaunchKernelGGL(scatter_kernel, grid, dim3(256), 2 * sizeof(int) * m, st, node, cursors,
-                       pairs, inv, n_tok, topk, m);
+                       pairs, inv, n_tok, topk, m, rpg);
   else
     hipLaunchKernelGGL(scatter_global_kernel, dim3(grid_for(n_slots)), dim3(256), 0, st, node,
                        cursors, pairs, inv, n_tok, topk, m, n_slots);

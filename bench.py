@@ -277,11 +277,16 @@ def run(args):
     bound, work, peak, unit = roof_table.get(dominant, ("hbm", 0.0, HBM_PEAK_GBS, "GB/s"))
     scale = 1e9 if unit == "GB/s" else 1e12
     achieved = work / (kernels[dominant] * 1e-3) / scale
+    traffic = stored_traffic(dominant)
     roof = {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
-            "frac": achieved / peak, "traffic": stored_traffic(dominant),
+            "frac": achieved / peak, "traffic": traffic,
             "kernel": dominant, "avg_kernel_ms": kernels[dominant],
             "algorithmic_work": work,
             "work_unit": "bytes" if unit == "GB/s" else "flop"}
+    if traffic is not None:
+        # the counters' HBM bytes over the same launch time, against the HBM peak
+        roof["traffic_gbs"] = traffic / (kernels[dominant] * 1e-3) / 1e9
+        roof["traffic_frac_of_hbm_peak"] = roof["traffic_gbs"] / HBM_PEAK_GBS
 
     result = {
         "metric": METRIC,
@@ -361,15 +366,19 @@ def backward_bench(prob, inp, idx, dev):
     main_flop = cols * 5 * 2.0 * C * d  # S, dP, dV, dK, dQ products over the block
     main_ms = kernels.get("attn_bwd_main", float("nan"))
     achieved = main_bytes / (main_ms * 1e-3) / 1e9
+    traffic = stored_traffic("bwd_main")
+    roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+            "algorithmic_bytes": main_bytes,
+            "mfma_tflops": main_flop / (main_ms * 1e-3) / 1e12}
+    if traffic is not None:
+        roof["traffic_gbs"] = traffic / (main_ms * 1e-3) / 1e9
+        roof["traffic_frac_of_hbm_peak"] = roof["traffic_gbs"] / HBM_PEAK_GBS
     return {
         "ms": ms,
         "kernels_ms": kernels,
         "columns": cols,
-        "roofline_main": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                          "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                          "traffic": stored_traffic("bwd_main"),
-                          "algorithmic_bytes": main_bytes,
-                          "mfma_tflops": main_flop / (main_ms * 1e-3) / 1e12},
+        "roofline_main": roof,
         "tokens_per_s": B * N / (ms * 1e-3),
     }
 

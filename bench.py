@@ -320,10 +320,11 @@ def run(args):
         result["decode"] = decode_bench(args)
     if not args.no_sweep:
         result["selection_sweep"] = selection_sweep(args)
-        # the pages' own latency shape: 16 query heads per KV head, d=64, K=8
-        result["selection_sweep_g16"] = selection_sweep(
-            args, heads_q=16, heads_kv=1, head_dim=64, topk=8,
-            sizes=(16384, 65536, 131072, 262144), seed=4100)
+        if not args.no_sweep_g16:
+            # the pages' own latency shape: 16 query heads per KV head, d=64, K=8
+            result["selection_sweep_g16"] = selection_sweep(
+                args, heads_q=16, heads_kv=1, head_dim=64, topk=8,
+                sizes=(16384, 65536, 131072, 262144), seed=4100)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(args, inp, prob)
     return result
@@ -447,8 +448,11 @@ def selection_sweep(args, heads_q=4, heads_kv=4, head_dim=128, topk=16,
     from hierarchical_block_selection_amd.inputs import prefill_inputs
 
     dev = torch.device("cuda:0")
+    only = ({int(x) for x in args.sweep_sizes.split(",")} if args.sweep_sizes else None)
     pts = []
     for i, n in enumerate(sizes):
+        if only is not None and n not in only:
+            continue  # a subset keeps each size's own seed
         prob = pisa.Problem(1, heads_q, heads_kv, n, head_dim, block=64, topk=topk,
                             dtype=torch.bfloat16)
         inp = prefill_inputs(1, heads_q, heads_kv, n, head_dim, torch.bfloat16,
@@ -584,6 +588,10 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--sweep-sizes", default=None,
+                    help="comma-separated subset of the selection sweeps' N (default: all)")
+    ap.add_argument("--no-sweep-g16", action="store_true",
+                    help="skip the 16-heads-per-KV-head selection sweep")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")

@@ -609,7 +609,7 @@ def main():
         cpu_worker(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the (batch, KV head) units would shard across GPUs without communication)",
               file=sys.stderr)
         sys.exit(2)

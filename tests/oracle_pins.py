@@ -593,11 +593,102 @@ def pin_attention_grad_invariants(O):
         assert np.allclose(bv, dv[blk * c:(blk + 1) * c], atol=1e-12)
 
 
+# ------------------------------------------- selection-quality diagnostics
+def dense_block_masses(q_heads, keys, block, scale):
+    """Leaf-block attention masses by a route independent of the oracle: each
+    head's full causal softmax matrix (torch, float64), its columns summed per
+    leaf block, then averaged over the heads.  q_heads [G, n, d], keys [n, d];
+    returns [n, n_leaves] (row t is zero past t's leaf)."""
+    q = torch.tensor(np.asarray(q_heads, dtype=np.float64))
+    k = torch.tensor(np.asarray(keys, dtype=np.float64))
+    n = k.shape[0]
+    s = scale * torch.matmul(q, k.T)
+    s = s.masked_fill(~torch.ones(n, n, dtype=torch.bool).tril(), float("-inf"))
+    p = torch.softmax(s, dim=-1)
+    nb = -(-n // block)
+    p = torch.nn.functional.pad(p, (0, nb * block - n))
+    return p.reshape(p.shape[0], n, nb, block).sum(dim=-1).mean(dim=0).numpy()
+
+
+def _quality_problem(seed=41, n=200, block=16, d=8, g=3):
+    r = rng(seed)
+    # heads of different norms, so that summing instead of averaging, or
+    # weighting heads unevenly, changes the numbers
+    q = r.standard_normal((g, n, d)) * np.array([0.5, 1.0, 2.0][:g])[:, None, None]
+    keys = r.standard_normal((n, d))
+    return q, keys, block, 1.0 / math.sqrt(d)
+
+
+def pin_block_masses_dense(M):
+    """§7.2's retained attention mass is a share of each head's full causal
+    attention; for a GQA group the reference averages the heads (§4.4).
+    block_masses must equal the dense route's row, and sum to one."""
+    q, keys, block, scale = _quality_problem()
+    dense = dense_block_masses(q, keys, block, scale)
+    for t in (0, 15, 16, 77, 150, 199):
+        c = t // block
+        got = M.block_masses(q[:, t], keys, t, block, scale)
+        assert got.shape == (c + 1,), (t, got.shape)
+        assert np.max(np.abs(got - dense[t, :c + 1])) <= 1e-12, t
+        assert abs(got.sum() - 1.0) <= 1e-12, t
+
+
+def pin_selection_quality_hand_sets(M):
+    """Recall@K counts the forced blocks (§7.2, Table 7 note), net recall drops
+    them from both sets, retained mass is the selected blocks' share of the
+    full causal mass (not renormalised over the selection) and the mass ratio
+    divides by the reference set's share.  Hand-built sets with known counts."""
+    q, keys, block, scale = _quality_problem()
+    dense = dense_block_masses(q, keys, block, scale)
+    t = 9 * block + 5                      # leaf c = 9: forced {0, 8, 9}
+    sel = [0, 2, 4, 5, 8, 9, -1]
+    ref = [0, 2, 3, 7, 8, 9]
+    res = M.selection_quality(sel, ref, q[:, t], keys, t, block, 6, True, scale)
+    assert res["recall"] == 4 / 6, res     # 0, 2, 8, 9 shared
+    assert res["net_recall"] == 1 / 3, res  # only 2 of the 3 free slots
+    kept = dense[t, [0, 2, 4, 5, 8, 9]].sum()
+    kept_ref = dense[t, ref].sum()
+    assert abs(res["retained_mass"] - kept) <= 1e-12, res
+    assert abs(res["mass_ratio"] - kept / kept_ref) <= 1e-12, res
+    # every eligible block selected: all of the mass, full recall
+    everything = list(range(10))
+    res = M.selection_quality(everything, everything, q[:, t], keys, t, block, 10, True, scale)
+    assert abs(res["retained_mass"] - 1.0) <= 1e-12 and res["recall"] == 1.0, res
+    assert res["net_recall"] == 1.0 and abs(res["mass_ratio"] - 1.0) <= 1e-12, res
+
+
+def pin_exhaustive_mean_mass(O):
+    """The mean-mass reference of §4.4 for a GQA group: forced blocks plus the
+    best K - #F others by head-averaged block mass (dense route, lexsort with
+    ties to the lower index).  With one head it ranks as the summed exact leaf
+    LSE does (the mass is a monotone function of the leaf LSE)."""
+    q, keys, block, scale = _quality_problem(seed=43)
+    dense = dense_block_masses(q, keys, block, scale)
+    k = 5
+    for t in range(40, 200, 3):
+        c = t // block
+        forced = {0, c - 1, c}
+        rank = [i for i in range(c + 1) if i not in forced]
+        m = dense[t, rank]
+        order = np.lexsort((np.asarray(rank), -m))
+        want = sorted(forced | {rank[j] for j in order[:k - len(forced)]})
+        got = O.select_exhaustive_row(q[:, t], keys, t, block, k, True, True, scale,
+                                      rule="mean_mass").leaves
+        assert got == want, (t, got, want)
+        one = O.select_exhaustive_row(q[2:, t], keys, t, block, k, True, True, scale,
+                                      rule="mean_mass").leaves
+        lse = O.select_exhaustive_row(q[2:, t], keys, t, block, k, True, True, scale).leaves
+        assert one == lse, (t, one, lse)
+
+
 ALL_PINS = [
     pin_tower_tables, pin_eq6_bounds, pin_pyramid_closed_form, pin_leaf_lse_is_logsumexp,
     pin_jensen_sandwich, pin_taylor_expansion, pin_no_pruning_equals_exhaustive,
     pin_dense_attention_recovered, pin_brute_force_tiny, pin_bsa_is_gemm_topk,
     pin_gqa_duplication, pin_causality_and_decode, pin_worked_causal_example, pin_tie_rule,
     pin_attention_grad_finite_differences, pin_attention_grad_autograd,
-    pin_attention_grad_invariants,
+    pin_attention_grad_invariants, pin_exhaustive_mean_mass,
 ]
+
+# Pins of the selection-quality diagnostics; they take the metrics module.
+METRIC_PINS = [pin_block_masses_dense, pin_selection_quality_hand_sets]

@@ -11,6 +11,7 @@ import oracle_pins
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "pisa_oracle.py")
+METRICS_SRC = os.path.join(ROOT, "oracle", "metrics.py")
 
 # (name, text to find, replacement) -- each must occur exactly once.
 MUTATIONS = [
@@ -51,15 +52,32 @@ MUTATIONS = [
      "if (not causal) or j < t]\n\n\ndef attend_row_grad"),
     ("grad_block_rows_dropped", "rows = np.nonzero((np.asarray(idx_rows) == blk).any(axis=1))[0]",
      "rows = np.nonzero((np.asarray(idx_rows) == blk).any(axis=1))[0][1:]"),
+    ("mean_mass_of_log_masses", "np.mean([math.exp(leaf_lse(q, i) - tot)",
+     "np.mean([(leaf_lse(q, i) - tot)"),
+    ("mean_mass_noncausal_total", "totals = [logsumexp(scale * (keys[:last + 1] @ q)) for q in q_heads]",
+     "totals = [logsumexp(scale * (keys @ q)) for q in q_heads]"),
+]
+
+# Planted mistakes in the selection-quality diagnostics (oracle/metrics.py).
+METRICS_MUTATIONS = [
+    ("masses_heads_summed", "return out / len(q_heads)", "return out"),
+    ("masses_total_over_block_only", "total = logsumexp(z)", "total = logsumexp(z[t // block * block:])"),
+    ("retained_renormalised_over_selection", '"retained_mass": kept,',
+     '"retained_mass": kept / sum(mass[i] for i in sel),'),
+    ("net_recall_keeps_forced", "len((sel - forced) & (ref - forced)) / free",
+     "len(sel & ref) / free"),
+    ("recall_drops_forced", '"recall": len(sel & ref) / topk', '"recall": len((sel - forced) & (ref - forced)) / topk'),
+    ("mass_ratio_inverted", '"mass_ratio": kept / kept_ref', '"mass_ratio": kept_ref / kept'),
 ]
 
 
-def load_mutant(name, find, repl):
-    text = open(SRC).read()
+def load_mutant(name, find, repl, src=SRC):
+    text = open(src).read()
     assert text.count(find) == 1, f"mutation {name}: pattern occurs {text.count(find)} times"
     mutated = text.replace(find, repl)
     mod = types.ModuleType(f"oracle_mutant_{name}")
-    mod.__file__ = SRC
+    mod.__file__ = src
+    mod.__package__ = "oracle"  # metrics.py imports from the real oracle package
     sys.modules[mod.__name__] = mod  # dataclasses look the module up by name
     try:
         exec(compile(mutated, f"<mutant {name}>", "exec"), mod.__dict__)
@@ -76,6 +94,19 @@ def test_mutation_is_caught(name, find, repl):
         try:
             pin(mutant)
         except Exception as exc:  # AssertionError or a crash both count as caught
+            caught.append(f"{pin.__name__}: {type(exc).__name__}")
+            break
+    assert caught, f"no pin caught the planted mistake {name}"
+
+
+@pytest.mark.parametrize("name,find,repl", METRICS_MUTATIONS, ids=[m[0] for m in METRICS_MUTATIONS])
+def test_metrics_mutation_is_caught(name, find, repl):
+    mutant = load_mutant(name, find, repl, METRICS_SRC)
+    caught = []
+    for pin in oracle_pins.METRIC_PINS:
+        try:
+            pin(mutant)
+        except Exception as exc:
             caught.append(f"{pin.__name__}: {type(exc).__name__}")
             break
     assert caught, f"no pin caught the planted mistake {name}"

@@ -76,13 +76,6 @@ typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-// Order-preserving key of a score, low 5 bits = 31 - slot (lower slot, i.e.
-// lower node, first among scores equal to within 2^-18 relative).
-__device__ __forceinline__ uint32_t dec_key(float s, int slot) {
-  const uint32_t b = __float_as_uint(s);
-  return ((b ^ (uint32_t(int32_t(b) >> 31) | 0x80000000u)) & ~31u) | uint32_t(31 - slot);
-}
-
 // One Top-K decision over the candidates held by lanes 0..31 (lane j = slot
 // j, ascending nodes): keep all when at most K are valid, else the forced
 // ones plus the best K - #F rankable ones.  Returns the kept-slot mask.
@@ -94,7 +87,11 @@ __device__ __forceinline__ uint32_t decide32(bool valid, bool forced, float scor
   const uint32_t fm = uint32_t(__ballot(fz));
   const int keep_n = topk - __popc(fm);
   const bool rankable = valid & !forced & (lane < 32);
-  uint32_t key = rankable ? dec_key(score, lane) : 0u;
+  // best rankable score of the decision (xor shuffles stay inside 32-lane halves)
+  float smax = rankable ? score : neg_inf();
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) smax = fmaxf(smax, __shfl_xor(smax, o, kWave));
+  uint32_t key = rankable ? rank_key_rel(score, smax, lane) : 0u;
   // bitonic sort, descending, inside each 32-lane half
 #pragma unroll
   for (int k = 2; k <= 32; k <<= 1)

@@ -113,4 +113,20 @@ __device__ __forceinline__ bool ranks_before(float s1, int i1, float s2, int i2)
   return (s1 > s2) | ((s1 == s2) & (i1 < i2));
 }
 
+// Packed 32-bit rank key of a candidate in slot `slot` (0..31) whose score is
+// s, given the best score smax among the candidates being ranked.  The upper
+// 27 bits hold the distance below smax in fixed point (quantum 2^-12 of the
+// score's unit, saturating 2^15 units below smax); the low 5 bits hold
+// 31 - slot.  A larger key ranks first, so candidates whose scores differ by
+// more than 2^-11 units (plus the fp32 rounding of smax - s) are ordered by
+// score whatever their magnitude, and equal scores go to the lower slot, i.e.
+// the lower node index.  Keys of ranked candidates are >= 32, so 0 can mark an
+// unranked slot.
+__device__ __forceinline__ uint32_t rank_key_rel(float s, float smax, int slot) {
+  constexpr uint32_t kTop = (1u << 27) - 1u;
+  const float dq = (smax - s) * 4096.f;  // >= 0; NaN when both are -inf
+  const uint32_t qv = dq < float(kTop - 1u) ? uint32_t(dq) : kTop - 1u;
+  return ((kTop - qv) << 5) | uint32_t(31 - slot);
+}
+
 }  // namespace pisa

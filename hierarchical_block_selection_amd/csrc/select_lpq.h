@@ -6,12 +6,12 @@
 // one level up, at most 2K <= 32 of them, ascending) and ranks the rankable
 // ones with a sorting network over packed 32-bit keys in registers.
 //
-// Rank keys.  A candidate in slot j (slots follow node order) is keyed by the
-// order-preserving integer image of its score with the low 5 bits replaced by
-// 31 - j.  A larger key ranks first; scores that agree to within 2^-18
-// relative are therefore ordered by node index, which is the tie rule of the
-// selection (equal scores -> lower index first).  Scores are fp32 sums of
-// fp32 log-sum-exps, already uncertain at that level.
+// Rank keys.  A candidate in slot j (slots follow node order) is keyed by its
+// score's distance below the best rankable score of the decision, in fixed
+// point (rank_key_rel: quantum 2^-12 of the score unit), with 31 - j in the
+// low 5 bits.  A larger key ranks first: scores more than 2^-11 units apart
+// are ordered by score at any magnitude, equal scores by node index, which is
+// the tie rule of the selection (equal scores -> lower index first).
 //
 // Forced slots.  In causal mode the forced nodes of a level (current path,
 // and with forcing the first and previous leaf's ancestors) are always
@@ -56,16 +56,6 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
-
-// Order-preserving image of a float (larger float -> larger unsigned).
-__device__ __forceinline__ uint32_t ordered_bits(float s) {
-  const uint32_t b = __float_as_uint(s);
-  return b ^ (uint32_t(int32_t(b) >> 31) | 0x80000000u);
-}
-
-__device__ __forceinline__ uint32_t rank_key(float s, int slot) {
-  return (ordered_bits(s) & ~31u) | uint32_t(31 - slot);
-}
 
 // Batcher's odd-even merge sort network on 32 elements (191 comparators),
 // generated at compile time.
@@ -119,9 +109,12 @@ __device__ __forceinline__ uint32_t top_slots(int n_valid, int topk, uint32_t fm
                                               const float (&s)[kSlots]) {
   const uint32_t rm = prefix_mask(n_valid) & ~fm;
   const int keep_n = topk - __popc(fm);
+  float smax = neg_inf();
+#pragma unroll
+  for (int j = 0; j < kSlots; ++j) smax = ((rm >> j) & 1u) ? fmaxf(smax, s[j]) : smax;
   uint32_t key[kSlots];
 #pragma unroll
-  for (int j = 0; j < kSlots; ++j) key[j] = ((rm >> j) & 1u) ? rank_key(s[j], j) : 0u;
+  for (int j = 0; j < kSlots; ++j) key[j] = ((rm >> j) & 1u) ? rank_key_rel(s[j], smax, j) : 0u;
   sort32_desc(key);
   uint32_t km = fm;
 #pragma unroll

@@ -9,7 +9,9 @@ decode: q [B, Hq, d], caches [B, Hkv, capacity, d], cache_len [B].
 
 Value recipes:
   * "inv_sqrt_d": i.i.d. N(0, 1/d) entries (random long-context prefill);
-  * "unit":       i.i.d. N(0, 1) entries (larger logit spread, fewer near-ties).
+  * "unit":       i.i.d. N(0, 1) entries (larger logit spread, fewer near-ties);
+  * "wide_q":     queries N(0, 64), keys and values N(0, 1): logits of standard
+                  deviation 8, peaked attention and large group-summed scores.
 Planted needles (per KV head): ``n_needles`` distinct leaf blocks b drawn from
 [1, M_1 - 3]; for each a target row r from [(b + 2) C, N); the block's keys are
 replaced by alpha * q_r / |q_r| + fresh noise of the recipe's scale, where q_r
@@ -27,11 +29,17 @@ import torch
 
 
 def _sigma(recipe: str, head_dim: int) -> float:
+    """Standard deviation of the keys and values (and of the queries unless
+    _sigma_q says otherwise)."""
     if recipe == "inv_sqrt_d":
         return 1.0 / math.sqrt(head_dim)
-    if recipe == "unit":
+    if recipe in ("unit", "wide_q"):
         return 1.0
     raise ValueError(f"unknown value recipe {recipe!r}")
+
+
+def _sigma_q(recipe: str, head_dim: int) -> float:
+    return 8.0 if recipe == "wide_q" else _sigma(recipe, head_dim)
 
 
 def seeded_normal(shape, seed: int, sigma: float, dtype: torch.dtype, device) -> torch.Tensor:
@@ -67,7 +75,8 @@ def prefill_inputs(batch, heads_q, heads_kv, seq_len, head_dim, dtype=torch.bflo
                    seed=0, recipe="inv_sqrt_d", n_needles=0, alpha=4.0, block=64,
                    device="cpu") -> PrefillInputs:
     sigma = _sigma(recipe, head_dim)
-    q = seeded_normal((batch, heads_q, seq_len, head_dim), seed + 0, sigma, dtype, device)
+    q = seeded_normal((batch, heads_q, seq_len, head_dim), seed + 0, _sigma_q(recipe, head_dim),
+                      dtype, device)
     k = seeded_normal((batch, heads_kv, seq_len, head_dim), seed + 1, sigma, dtype, device)
     v = seeded_normal((batch, heads_kv, seq_len, head_dim), seed + 2, sigma, dtype, device)
     needles = []
@@ -109,7 +118,8 @@ def decode_inputs(batch, heads_q, heads_kv, capacity, head_dim, dtype=torch.bflo
     ``cache_len``: None (every sequence full), an int, or a list of B ints.
     """
     sigma = _sigma(recipe, head_dim)
-    q = seeded_normal((batch, heads_q, head_dim), seed + 0, sigma, dtype, device)
+    q = seeded_normal((batch, heads_q, head_dim), seed + 0, _sigma_q(recipe, head_dim), dtype,
+                      device)
     kc = seeded_normal((batch, heads_kv, capacity, head_dim), seed + 1, sigma, dtype, device)
     vc = seeded_normal((batch, heads_kv, capacity, head_dim), seed + 2, sigma, dtype, device)
     if cache_len is None:

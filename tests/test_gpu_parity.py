@@ -238,7 +238,7 @@ def test_selection_and_attention_deterministic():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-def decode_compare(prob, inp, pyr, pairs, fp32=False, min_compared=None):
+def decode_compare(prob, inp, pyr, pairs, fp32=False, min_compared=None, min_count=None):
     idx, score, out, lse = pisa_decode_step(prob, inp.cache_len, inp.q, inp.k_cache, inp.v_cache,
                                             pyr)
     torch.cuda.synchronize()
@@ -272,6 +272,8 @@ def decode_compare(prob, inp, pyr, pairs, fp32=False, min_compared=None):
     print(f"  decode: compared {tally.compared}/{tally.rows}", flush=True)
     if min_compared is not None:
         assert tally.frac() >= min_compared
+    if min_count is not None:
+        assert tally.compared >= min_count, (tally.compared, tally.rows)
     return idx, out
 
 
@@ -283,6 +285,85 @@ def test_decode_c5_sampled():
                         device=DEV)
     pyr = pisa_build_pyramid(prob, inp.k_cache)
     decode_compare(prob, inp, pyr, [(0, h) for h in range(8)] + [(17, h) for h in range(8)])
+
+
+def test_decode_c5_unit_variance():
+    """The decode workload at its full shape (32 sequences, 131072-token caches,
+    32 query heads over 8 KV heads, d = 128, K = 16, 12 pyramid levels) with
+    N(0,1) entries, so that the selection can be compared: 96 (sequence, KV
+    head) units, bit-exact on every unit whose decision margins all exceed
+    1e-3 (about a quarter of them at this length), at least 8 such units."""
+    cfg = WORKLOADS["c5"]
+    prob = problem_of(cfg)
+    announce("decode c5 B=32 cache=131072 GQA 32/8 unit")
+    inp = decode_inputs(32, 32, 8, cfg["seq_len"], 128, torch.bfloat16, seed=cfg["seed"],
+                        recipe="unit", device=DEV)
+    pyr = pisa_build_pyramid(prob, inp.k_cache)
+    seqs = (0, 2, 5, 7, 10, 13, 16, 19, 22, 25, 28, 31)
+    decode_compare(prob, inp, pyr, [(b, h) for b in seqs for h in range(8)], min_count=8)
+
+
+def test_prefill_level2_beyond_dense_rows():
+    """A prefill of 262272 tokens (4098 leaves; level 2 holds 2049 rows, more
+    than the first selection stage scores as one dense tile, so its level-3
+    decision gathers each query's candidates), 2 query heads over one KV head,
+    N(0,1) entries, 200 sampled rows: selections bit-exact past the margin
+    (at least 20 rows), attention within the bf16 bounds."""
+    n = 262144 + 128
+    prob = Problem(1, 2, 1, n, 128, block=64, topk=16, dtype=torch.bfloat16)
+    announce(f"prefill N={n} G=2 unit (level 2 beyond the dense tile)")
+    inp = prefill_inputs(1, 2, 1, n, 128, torch.bfloat16, seed=7100, recipe="unit", device=DEV)
+    pyr = pisa_build_pyramid(prob, inp.k)
+    idx, score = pisa_select(prob, inp.q, inp.k, pyr)
+    out, lse = pisa_block_sparse_attn(prob, inp.q, inp.k, inp.v, idx)
+    torch.cuda.synchronize()
+    check_pyramid(pyr, inp.k, prob, [(0, 0)])
+    rows = sample_rows(n, 64, 16, 200, 7100)
+    keys, vals = parity.to_np(inp.k[0, 0]), parity.to_np(inp.v[0, 0])
+    qg = parity.to_np(inp.q[0, 0:2])
+    levels = oracle.build_pyramid(keys, 64)
+    tl = parity.compare_selection("pisa", idx[0, 0].cpu().numpy(), score[0, 0].cpu().numpy(), qg,
+                                  keys, levels, rows, 64, 16, True, True, prob.logit_scale,
+                                  parity.Tally())
+    print(f"  pisa: compared {tl.compared}/{tl.rows} rows, mismatches {len(tl.mismatches)}",
+          flush=True)
+    assert not tl.mismatches, tl.mismatches[:3]
+    assert tl.compared >= 20, (tl.compared, tl.rows)
+    parity.compare_attention(parity.to_np(out[0, 0:2]), lse[0, 0:2].cpu().numpy(), qg, keys, vals,
+                             idx[0, 0].cpu().numpy(), rows, 64, True, prob.logit_scale, False)
+
+
+def test_large_group_scores():
+    """Peaked attention and large group-summed scores (queries N(0,64), keys
+    N(0,1): group sums of several hundred nats over 16 query heads): the
+    ranking must follow the scores, not the magnitude's rounding.  Prefill at
+    16 query heads per KV head, d = 64, K = 8, every 13th row; decode at 8
+    query heads per KV head, K = 16."""
+    n = 16384
+    prob = Problem(1, 16, 1, n, 64, block=64, topk=8, dtype=torch.bfloat16)
+    announce(f"prefill N={n} G=16 d=64 K=8 wide_q")
+    inp = prefill_inputs(1, 16, 1, n, 64, torch.bfloat16, seed=8100, recipe="wide_q", device=DEV)
+    pyr = pisa_build_pyramid(prob, inp.k)
+    idx, score = pisa_select(prob, inp.q, inp.k, pyr)
+    torch.cuda.synchronize()
+    keys = parity.to_np(inp.k[0, 0])
+    qg = parity.to_np(inp.q[0])
+    levels = oracle.build_pyramid(keys, 64)
+    rows = list(range(0, n, 13)) + [n - 1]
+    tl = parity.compare_selection("pisa", idx[0, 0].cpu().numpy(), score[0, 0].cpu().numpy(), qg,
+                                  keys, levels, rows, 64, 8, True, True, prob.logit_scale,
+                                  parity.Tally())
+    print(f"  pisa: compared {tl.compared}/{tl.rows} rows, mismatches {len(tl.mismatches)}",
+          flush=True)
+    assert not tl.mismatches, tl.mismatches[:3]
+    assert tl.frac() > 0.9, tl.frac()
+    dprob = Problem(4, 16, 2, n, 128, block=64, topk=16, dtype=torch.bfloat16)
+    announce("decode G=8 wide_q")
+    dinp = decode_inputs(4, 16, 2, n, 128, torch.bfloat16, seed=8200, recipe="wide_q",
+                         cache_len=[n, 12345, 9000, 4097], device=DEV)
+    dpyr = pisa_build_pyramid(dprob, dinp.k_cache)
+    decode_compare(dprob, dinp, dpyr, [(b, h) for b in range(4) for h in range(2)],
+                   min_compared=0.75)
 
 
 def test_decode_unit_variant_ragged_lengths():

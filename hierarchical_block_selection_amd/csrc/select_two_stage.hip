@@ -43,8 +43,8 @@ namespace {
 constexpr int kSplitLevel = 3;   // stage 1 decides levels L..3
 constexpr int kS1Waves = 4;
 constexpr int kS2Threads = 256;
-constexpr int kS2Rows = 128;    // (pair, head) rows per stage-2 batch
-constexpr int kS2Batches = 8;   // batches per stage-2 work item
+constexpr int kS2Rows = 64;       // (pair, head) rows per stage-2 batch
+constexpr int kS2ItemRows = 1024; // (pair, head) rows per stage-2 work item
 constexpr int kS2Cols = 32;      // MFMA 32x32x16: 32 (query, head) columns
 constexpr int kScoreStride = 8;  // floats per pair: 4 leaf LSE, 2 level-2, 2 pad
 
@@ -77,7 +77,7 @@ WsLayout ws_layout(const LaunchShape& s) {
   const size_t units = (size_t)s.batch * s.heads_kv * s.seq_len;
   const int m3 = s.lv.n >= kSplitLevel ? s.lv.size[kSplitLevel - 1] : 1;
   w.n_buckets = s.batch * s.heads_kv * m3;
-  w.max_items = bucket::max_items(units * s.topk, w.n_buckets, kS2Rows / s.group * kS2Batches);
+  w.max_items = bucket::max_items(units * s.topk, w.n_buckets, kS2ItemRows / s.group);
   size_t off = 0;
   w.counts = off; off = align256(off + sizeof(int) * w.n_buckets);
   w.offsets = off; off = align256(off + sizeof(int) * (w.n_buckets + 1));
@@ -279,63 +279,86 @@ __global__ __launch_bounds__(kS1Waves * kWave) void stage1_kernel(
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-// Stage 2 batch bt of an item: pair ids (threads < kS2Rows / G) and the query
-// rows of every (pair, head), 16 bytes per load, into registers.  Rows past
-// the item repeat its last pair.
-template <int D, int G, int PER_THREAD>
-__device__ __forceinline__ void stage2_fetch(u32x4_t (&stage)[PER_THREAD], int& pid_reg,
-                                             const int* __restrict__ pairs, int start, int len,
-                                             int bt, const bf16_t* __restrict__ qh, int bh,
-                                             int n_tok, int topk) {
-  constexpr int PAIRS = kS2Rows / G;
-  constexpr int V16 = D / 8;
-  const int tid = threadIdx.x;
-  const int base = bt * PAIRS;
-  const int last = len - 1;
-  if (tid < PAIRS) pid_reg = pairs[start + min(base + tid, last)];
+// Stage-2 batches of ROWS (pair, head) rows: row r of a batch's LDS tile holds
+// the query row of pair r / G, head r % G (D bf16, rows padded to D + 8 so
+// that the MFMA operand reads of 32 consecutive rows spread over the banks).
+// Rows past the item repeat its last pair.  Thread x of the workgroup loads
+// pieces x + i * kS2Threads (i < LOADS) of the tile into registers one batch
+// ahead and writes them to LDS when the batch starts.
+template <int D, int G, int ROWS>
+struct S2Tile {
+  static constexpr int PIECES = D / 8;                      // 16-byte pieces per row
+  static constexpr int LOADS = ROWS * PIECES / kS2Threads;  // pieces per thread
+  static constexpr int PAIRS = ROWS / G;
+  static constexpr int QROW = D + 8;  // padded row (bf16): 32 rows' 16-byte reads spread over banks
+  static_assert(LOADS >= 1 && ROWS % 32 == 0 && PAIRS >= 1, "stage-2 tile shape");
+
+  // Pair ids of the rows this thread's pieces of batch bt belong to.
+  __device__ __forceinline__ static void pair_ids(int (&pid)[LOADS], const int* __restrict__ pairs,
+                                                  int start, int len, int bt) {
 #pragma unroll
-  for (int i = 0; i < PER_THREAD; ++i) {
-    const int x = tid + i * kS2Threads;
-    const int r = x / V16, c = x % V16;
-    const int pid = pairs[start + min(base + r / G, last)];
-    const int t = (pid >> 5) - bh * n_tok;  // pair = (row << 5) | slot
-    stage[i] = *reinterpret_cast<const u32x4_t*>(qh + ((size_t)(r % G) * n_tok + t) * D + 8 * c);
+    for (int i = 0; i < LOADS; ++i) {
+      const int r = (threadIdx.x + i * kS2Threads) / PIECES;
+      pid[i] = pairs[start + min(bt * PAIRS + r / G, len - 1)];
+    }
   }
-}
+
+  __device__ __forceinline__ static void load(u32x4_t (&v)[LOADS], const int (&pid)[LOADS],
+                                              const bf16_t* __restrict__ qh, int bh, int n_tok) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int x = threadIdx.x + i * kS2Threads;
+      const int r = x / PIECES, p = x % PIECES;
+      const int t = (pid[i] >> 5) - bh * n_tok;  // pair = (row << 5) | slot
+      v[i] = *reinterpret_cast<const u32x4_t*>(qh + ((size_t)(r % G) * n_tok + t) * D + 8 * p);
+    }
+  }
+
+  __device__ __forceinline__ static void store(bf16_t* tile, const u32x4_t (&v)[LOADS]) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int x = threadIdx.x + i * kS2Threads;
+      const int r = x / PIECES, p = x % PIECES;
+      *reinterpret_cast<u32x4_t*>(tile + r * QROW + 8 * p) = v[i];
+    }
+  }
+
+  // Piece p of row r (an MFMA operand).
+  __device__ __forceinline__ static bf16x8_t read(const bf16_t* tile, int r, int p) {
+    return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(tile + r * QROW + 8 * p));
+  }
+};
 
 // One workgroup per work item: level-3 node n of KV head bh and up to
-// kS2Batches batches of kS2Rows / G of its (query, slot) pairs; wavefront w
-// owns leaf 4n + w and keeps its 64 raw keys as MFMA A operands in registers
-// for the whole item.  Per batch:
-//   1. the batch's query rows of every (pair, head) are loaded and staged in
-//      LDS (no register prefetch: batches of 128 rows keep the LDS tile at
-//      35 KB and the kernel under 168 VGPRs, so three workgroups share a CU
-//      and hide each other's loads, which measured faster than two
-//      workgroups prefetching the next batch);
-//   2. each wave walks the staged rows 32 columns at a time: S = K_leaf . Q^T
+// kS2ItemRows / G of its (query, slot) pairs; wavefront w owns leaf 4n + w and
+// keeps its 64 raw keys as MFMA A operands in registers for the whole item.
+// The item's pairs run in batches of ROWS / G.  Batch bt's query rows were
+// loaded into registers during batch bt - 1; per batch:
+//   1. they go to one of two LDS tiles and the loads of batch bt + 1 start;
+//      an LDS-only barrier (no wait for the loads or for earlier score
+//      stores: only the registers' uses wait for their loads);
+//   2. each wave walks the batch's rows 32 columns at a time: S = K_leaf . Q^T
 //      on bf16 MFMA 32x32x16 (a lane holds 32 keys of one column), then the
 //      exact leaf LSE (eq. (7) at level 1: max, sum of exp2) and the mean
 //      logit, which equals q . kbar_leaf (eq. (4) is a mean), go to LDS;
-//   3. after a barrier every thread finishes one pair: the four leaf LSEs and
-//      the two level-2 scores LSE(mean_2c, mean_2c+1), each summed over the
-//      group's heads (eq. (11)), in nats.
-template <int D, int G>
-__global__ __launch_bounds__(kS2Threads, 3) void stage2_kernel(
+//   3. after an LDS-only barrier every thread finishes one pair: the four
+//      leaf LSEs and the two level-2 scores LSE(mean_2c, mean_2c+1), each
+//      summed over the group's heads (eq. (11)), in nats.
+template <int D, int G, int ROWS>
+__global__ __launch_bounds__(kS2Threads, (G == 1 || D == 64) ? 3 : 2) void stage2_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const int* __restrict__ item_offsets, const int* __restrict__ offsets,
     const int* __restrict__ pairs, float* __restrict__ scores, int n_buckets, int heads_q,
     int heads_kv, int n_tok, int topk, int m3, float scale_log2) {
+  using Tile = S2Tile<D, G, ROWS>;
   constexpr int KSTEPS = D / 16;
-  constexpr int PAIRS = kS2Rows / G;  // pairs per batch
-  constexpr int QROW = D + 8;         // padded LDS row (bf16): 16-byte reads spread over banks
-  constexpr int LEAF = 64;            // keys per leaf (C = 64)
-  constexpr int V16 = D / 8;          // 16-byte pieces per row
-  constexpr int PER_THREAD = kS2Rows * V16 / kS2Threads;
-  __shared__ __attribute__((aligned(16))) bf16_t qs[kS2Rows * QROW];
-  __shared__ float xs[4][2][kS2Rows];  // [leaf][lse, mean][row], log2 units
-  __shared__ int pid_s[PAIRS];
+  constexpr int PAIRS = Tile::PAIRS;
+  constexpr int LEAF = 64;  // keys per leaf (C = 64)
+  __shared__ __attribute__((aligned(16))) bf16_t tile_a[ROWS * Tile::QROW];
+  __shared__ __attribute__((aligned(16))) bf16_t tile_b[ROWS * Tile::QROW];
+  __shared__ float xs[4][2][ROWS];  // [leaf][lse, mean][row], log2 units
   int bucket, start, len;
-  if (!bucket::locate_item(item_offsets, offsets, n_buckets, blockIdx.x, PAIRS * kS2Batches,
+  if (!bucket::locate_item(item_offsets, offsets, n_buckets, blockIdx.x, kS2ItemRows / G,
                            &bucket, &start, &len))
     return;
   const int bh = bucket / m3, node = bucket % m3;
@@ -345,11 +368,17 @@ __global__ __launch_bounds__(kS2Threads, 3) void stage2_kernel(
   const int wave = tid / kWave;
   const int col = lane & 31, kh = lane >> 5;
   const bf16_t* qh = q + ((size_t)b * heads_q + (size_t)kvh * G) * n_tok * D;
+  const int n_batches = (len + PAIRS - 1) / PAIRS;
 
-  // Batch bt's pair ids and query rows (row r = pair r / G, head r % G;
-  // rows past the item repeat its last pair) -> registers.
-  u32x4_t stage[PER_THREAD];
-  int pid_reg = 0;
+  // Batch 0's rows, and the pair ids of batch 1 (rows and the pair each
+  // finishing thread owns).
+  int pid[Tile::LOADS];
+  u32x4_t stage[Tile::LOADS];
+  Tile::pair_ids(pid, pairs, start, len, 0);
+  Tile::load(stage, pid, qh, bh, n_tok);
+  int fin_pid = pairs[start + min(tid, len - 1)];
+  Tile::pair_ids(pid, pairs, start, len, 1);
+
   const int leaf_tok0 = (4 * node + wave) * LEAF;
   const int n_keys = max(0, min(LEAF, n_tok - leaf_tok0));  // keys of this wave's leaf
   // A operands: key rows leaf_tok0 + 32 rb + col (rows past the sequence end
@@ -364,103 +393,112 @@ __global__ __launch_bounds__(kS2Threads, 3) void stage2_kernel(
     for (int s = 0; s < KSTEPS; ++s) ka[rb][s] = as_bf16x8(*reinterpret_cast<const uint4*>(kr + 16 * s));
   }
   const float inv_keys = n_keys > 0 ? 1.f / float(n_keys) : 0.f;
-  const int n_batches = (len + PAIRS - 1) / PAIRS;
+  // The keys and batch 0 are in before the loop: inside it, only the staged
+  // registers' uses wait for the loads of the next batch.
+  wait_vmcnt<0>();
 
-  // The batch loop, compiled twice: for a leaf with all C keys (no masking)
-  // and for the sequence's last, partial leaf.  Waves of one workgroup may
-  // run different copies; both pass the same barriers in the same order.
-  auto run = [&](auto full_tag) __attribute__((always_inline)) {
+  // One batch, compiled for a leaf with all C keys (no masking) and for the
+  // sequence's last, partial leaf.  Waves of one workgroup may run different
+  // copies; both pass the same barriers in the same order.
+  auto batch = [&](auto full_tag, int bt, bf16_t* cur) __attribute__((always_inline)) {
     constexpr bool kFull = decltype(full_tag)::value;
-    for (int bt = 0; bt < n_batches; ++bt) {
-      const int blen = min(PAIRS, len - bt * PAIRS);  // pairs in this batch
-      stage2_fetch<D, G, PER_THREAD>(stage, pid_reg, pairs, start, len, bt, qh, bh, n_tok, topk);
-      __syncthreads();  // the previous batch's readers of qs, xs and pid_s are done
-      if (tid < PAIRS) pid_s[tid] = pid_reg;
-#pragma unroll
-      for (int i = 0; i < PER_THREAD; ++i) {
-        const int x = tid + i * kS2Threads;
-        *reinterpret_cast<u32x4_t*>(&qs[(x / V16) * QROW + 8 * (x % V16)]) = stage[i];
-      }
-      __syncthreads();
+    const int blen = min(PAIRS, len - bt * PAIRS);  // pairs in this batch
+    // cur was last read two batches ago (both barriers of batch bt - 1 lie
+    // between); xs was last read by batch bt - 1's finishing step, which
+    // every thread completes before the barrier below.
+    Tile::store(cur, stage);
+    const int my_pid = fin_pid;
+    // The next batch's loads are issued unconditionally (past the item's end
+    // the clamped rows repeat its last pair, one cache line), so that every
+    // batch issues the same memory operations and the waits for the staged
+    // rows never have to cover the score stores that follow them.
+    Tile::load(stage, pid, qh, bh, n_tok);
+    fin_pid = pairs[start + min((bt + 1) * PAIRS + tid, len - 1)];
+    Tile::pair_ids(pid, pairs, start, len, bt + 2);
+    lds_barrier();
 
-      const int n_chunks = (blen * G + 31) / 32;
-      for (int ch = 0; ch < n_chunks; ++ch) {
-        const bf16_t* qr = &qs[(32 * ch + col) * QROW + 8 * kh];
-        f32x16_t acc0 = {}, acc1 = {};
+    const int n_chunks = (blen * G + 31) / 32;
+    for (int ch = 0; ch < n_chunks; ++ch) {
+      const int r = 32 * ch + col;
+      f32x16_t acc0 = {}, acc1 = {};
 #pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) {
-          const bf16x8_t bq = as_bf16x8(*reinterpret_cast<const uint4*>(qr + 16 * s));
-          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0][s], bq, acc0, 0, 0, 0);
-          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[1][s], bq, acc1, 0, 0, 0);
+      for (int s = 0; s < KSTEPS; ++s) {
+        const bf16x8_t bq = Tile::read(cur, r, 2 * s + kh);
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0][s], bq, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[1][s], bq, acc1, 0, 0, 0);
+      }
+      // Lane holds the logits of keys (i/4)*8 + 4kh + i%4 (acc0) and 32 + that (acc1).
+      float sraw = 0.f, se = 0.f;
+      if constexpr (!kFull) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kr = (i / 4) * 8 + 4 * kh + (i % 4);
+          sraw += (kr < n_keys ? acc0[i] : 0.f) + (kr + 32 < n_keys ? acc1[i] : 0.f);
+          acc0[i] = kr < n_keys ? acc0[i] : neg_inf();
+          acc1[i] = kr + 32 < n_keys ? acc1[i] : neg_inf();
         }
-        // Lane holds the logits of keys (i/4)*8 + 4kh + i%4 (acc0) and 32 + that (acc1).
-        float sraw = 0.f, se = 0.f;
-        if constexpr (!kFull) {
+      } else {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int r = (i / 4) * 8 + 4 * kh + (i % 4);
-            sraw += (r < n_keys ? acc0[i] : 0.f) + (r + 32 < n_keys ? acc1[i] : 0.f);
-            acc0[i] = r < n_keys ? acc0[i] : neg_inf();
-            acc1[i] = r + 32 < n_keys ? acc1[i] : neg_inf();
-          }
-        } else {
+        for (int i = 0; i < 16; ++i) sraw += acc0[i] + acc1[i];
+      }
+      // The exps are taken relative to the mean logit, which the level-2
+      // scores need anyway: the sum is >= 1 (some logit is >= the mean) and
+      // only overflows when a logit exceeds the mean by ~128 (log2 units);
+      // then the wave redoes the column relative to its maximum.
+      sraw += __shfl_xor(sraw, 32, kWave);
+      const float mean = sraw * inv_keys * scale_log2;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) sraw += acc0[i] + acc1[i];
-        }
-        // The exps are taken relative to the mean logit, which the level-2
-        // scores need anyway: the sum is >= 1 (some logit is >= the mean) and
-        // only overflows when a logit exceeds the mean by ~128 (log2 units);
-        // then the wave redoes the column relative to its maximum.
-        sraw += __shfl_xor(sraw, 32, kWave);
-        const float mean = sraw * inv_keys * scale_log2;
+      for (int i = 0; i < 16; ++i)
+        se += fast_exp2(fmaf(acc0[i], scale_log2, -mean)) + fast_exp2(fmaf(acc1[i], scale_log2, -mean));
+      se += __shfl_xor(se, 32, kWave);
+      float ref = mean;
+      if (__ballot(!(se <= FLT_MAX)) != 0) {
+        float m = fmaxf(fmaxf(acc0[0], acc0[1]), fmaxf(acc1[0], acc1[1]));
+#pragma unroll
+        for (int i = 2; i < 16; i += 2)
+          m = fmaxf(m, fmaxf(fmaxf(acc0[i], acc0[i + 1]), fmaxf(acc1[i], acc1[i + 1])));
+        m = fmaxf(m, __shfl_xor(m, 32, kWave));
+        ref = (kFull || n_keys > 0) ? m * scale_log2 : 0.f;
+        se = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          se += fast_exp2(fmaf(acc0[i], scale_log2, -mean)) + fast_exp2(fmaf(acc1[i], scale_log2, -mean));
+          se += fast_exp2(fmaf(acc0[i], scale_log2, -ref)) + fast_exp2(fmaf(acc1[i], scale_log2, -ref));
         se += __shfl_xor(se, 32, kWave);
-        float ref = mean;
-        if (__ballot(!(se <= FLT_MAX)) != 0) {
-          float m = fmaxf(fmaxf(acc0[0], acc0[1]), fmaxf(acc1[0], acc1[1]));
-#pragma unroll
-          for (int i = 2; i < 16; i += 2)
-            m = fmaxf(m, fmaxf(fmaxf(acc0[i], acc0[i + 1]), fmaxf(acc1[i], acc1[i + 1])));
-          m = fmaxf(m, __shfl_xor(m, 32, kWave));
-          ref = (kFull || n_keys > 0) ? m * scale_log2 : 0.f;
-          se = 0.f;
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            se += fast_exp2(fmaf(acc0[i], scale_log2, -ref)) + fast_exp2(fmaf(acc1[i], scale_log2, -ref));
-          se += __shfl_xor(se, 32, kWave);
-        }
-        if (kh == 0) {
-          const bool has = kFull || n_keys > 0;
-          xs[wave][0][32 * ch + col] = has ? ref + fast_log2(se) : neg_inf();
-          xs[wave][1][32 * ch + col] = has ? mean : neg_inf();
-        }
       }
-      __syncthreads();
+      if (kh == 0) {
+        const bool has = kFull || n_keys > 0;
+        xs[wave][0][r] = has ? ref + fast_log2(se) : neg_inf();
+        xs[wave][1][r] = has ? mean : neg_inf();
+      }
+    }
+    lds_barrier();  // xs complete
 
-      // One pair per thread.
-      if (tid < blen) {
-        float o[6] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    // One pair per thread.
+    if (tid < blen) {
+      float o[6] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+      for (int hh = 0; hh < G; ++hh) {
+        const int r = tid * G + hh;
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-          const int r = tid * G + hh;
+        for (int f = 0; f < 4; ++f) o[f] += xs[f][0][r];
 #pragma unroll
-          for (int f = 0; f < 4; ++f) o[f] += xs[f][0][r];
-#pragma unroll
-          for (int c2 = 0; c2 < 2; ++c2) {
-            const float a = xs[2 * c2][1][r], bb = xs[2 * c2 + 1][1][r];
-            const float mx = fmaxf(a, bb), mn = fminf(a, bb);
-            // a missing leaf has mean -inf and drops out
-            o[4 + c2] += mn == neg_inf() ? mx : mx + fast_log2(1.f + fast_exp2(mn - mx));
-          }
+        for (int c2 = 0; c2 < 2; ++c2) {
+          const float a = xs[2 * c2][1][r], bb = xs[2 * c2 + 1][1][r];
+          const float mx = fmaxf(a, bb), mn = fminf(a, bb);
+          // a missing leaf has mean -inf and drops out
+          o[4 + c2] += mn == neg_inf() ? mx : mx + fast_log2(1.f + fast_exp2(mn - mx));
         }
-        const int pid = pid_s[tid];  // (row << 5) | slot
-        float* dst = scores + ((size_t)(pid >> 5) * topk + (pid & 31)) * kScoreStride;
-        *reinterpret_cast<float4*>(dst) =
-            make_float4(o[0] * kLn2, o[1] * kLn2, o[2] * kLn2, o[3] * kLn2);
-        *reinterpret_cast<float4*>(dst + 4) = make_float4(o[4] * kLn2, o[5] * kLn2, 0.f, 0.f);
       }
+      float* dst = scores + ((size_t)(my_pid >> 5) * topk + (my_pid & 31)) * kScoreStride;
+      *reinterpret_cast<float4*>(dst) =
+          make_float4(o[0] * kLn2, o[1] * kLn2, o[2] * kLn2, o[3] * kLn2);
+      *reinterpret_cast<float4*>(dst + 4) = make_float4(o[4] * kLn2, o[5] * kLn2, 0.f, 0.f);
+    }
+  };
+  auto run = [&](auto full_tag) __attribute__((always_inline)) {
+    for (int bt = 0; bt < n_batches; bt += 2) {
+      batch(full_tag, bt, tile_a);
+      if (bt + 1 < n_batches) batch(full_tag, bt + 1, tile_b);
     }
   };
   if (n_keys == LEAF)
@@ -639,7 +677,7 @@ hipError_t launch_select_two_stage(const LaunchShape& s, const void* q, const vo
   {
     prof::Scope ps("select_sort", st);
     e = bucket::sort_pairs(w.s1_nodes, s.batch * s.heads_kv, s.seq_len, s.topk, m3,
-                           kS2Rows / s.group * kS2Batches,
+                           kS2ItemRows / s.group,
                            w.counts, w.offsets, w.cursors, w.item_offsets, w.pairs, nullptr,
                            false, st);
   }
@@ -650,7 +688,7 @@ hipError_t launch_select_two_stage(const LaunchShape& s, const void* q, const vo
     const bf16_t* kb = static_cast<const bf16_t*>(k);
     const float sl = s.scale * kLog2e;
 #define PISA_S2(D, G)                                                                         \
-  hipLaunchKernelGGL((stage2_kernel<D, G>), dim3(lay.max_items), dim3(kS2Threads), 0, st, qb, kb, \
+  hipLaunchKernelGGL((stage2_kernel<D, G, kS2Rows>), dim3(lay.max_items), dim3(kS2Threads), 0, st, qb, kb, \
                      w.item_offsets, w.offsets, w.pairs, w.scores, lay.n_buckets, s.heads_q,   \
                      s.heads_kv, s.seq_len, s.topk, m3, sl)
     switch (s.group * 1000 + s.head_dim) {

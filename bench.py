@@ -477,7 +477,33 @@ def selection_sweep(args, heads_q=4, heads_kv=4, head_dim=128, topk=16,
         reps = 5 if n <= 65536 else 3
         p_ms = timed_call(pisa_sel, reps, 1)
         b_ms = timed_call(bsa_sel, reps, 1)
-        pts.append({"N": n, "pisa_ms": p_ms, "bsa_ms": b_ms, "speedup_vs_bsa": b_ms / p_ms})
+        # one more call of each with the library's per-kernel events
+        kern = {}
+        for name, fn in (("pisa", pisa_sel), ("bsa", bsa_sel)):
+            pisa.pisa_profile_enable(True)
+            fn()
+            torch.cuda.synchronize()
+            rep = pisa.pisa_profile_report()
+            pisa.pisa_profile_enable(False)
+            kern[name] = {k: round(v[0] / v[1], 4) for k, v in rep.items()}
+        # BSA's score matrix: row t holds its c + 1 eligible leaves (c = t // C),
+        # padded to a multiple of 4, fp32; written by bsa_scores, read by bsa_topk
+        c = 64
+        m1 = -(-n // c)
+        s_bytes = heads_kv * c * sum(4 * ((i + 1 + 3) // 4) * 4 for i in range(m1))
+        q_bytes = heads_q * n * head_dim * 2
+        idx_bytes = heads_kv * n * topk * 4
+        bsa_frac = {}
+        if "bsa_scores" in kern["bsa"]:
+            bsa_frac["bsa_scores"] = (s_bytes + q_bytes) / (kern["bsa"]["bsa_scores"] * 1e-3) \
+                / 1e9 / HBM_PEAK_GBS
+        if "bsa_topk" in kern["bsa"]:
+            bsa_frac["bsa_topk"] = (s_bytes + idx_bytes) / (kern["bsa"]["bsa_topk"] * 1e-3) \
+                / 1e9 / HBM_PEAK_GBS
+        pts.append({"N": n, "pisa_ms": p_ms, "bsa_ms": b_ms, "speedup_vs_bsa": b_ms / p_ms,
+                    "pisa_kernels_ms": kern["pisa"], "bsa_kernels_ms": kern["bsa"],
+                    "bsa_score_matrix_mb": s_bytes / 1e6,
+                    "bsa_hbm_frac": {k: round(v, 3) for k, v in bsa_frac.items()}})
         del wbsa, inp
         torch.cuda.empty_cache()
     cross = None
@@ -493,7 +519,9 @@ def selection_sweep(args, heads_q=4, heads_kv=4, head_dim=128, topk=16,
     return {"points": pts, "crossover_N": cross,
             "note": f"timings include pyramid construction (all levels) for both selectors; "
                     f"attention excluded; Hq={heads_q} Hkv={heads_kv}, d={head_dim}, C=64, "
-                    f"K={topk}, bf16"}
+                    f"K={topk}, bf16; bsa_hbm_frac: algorithmic bytes of each BSA kernel "
+                    f"(score matrix written / read, queries, leaf ids) over its launch time, "
+                    f"as a fraction of {HBM_PEAK_GBS:.0f} GB/s"}
 
 
 def cpu_baseline(args, inp, prob):

@@ -115,10 +115,14 @@ __global__ void bsa_split_kernel(const float* __restrict__ pyr, bf16_t* __restri
   }
 }
 
+// The row of query t holds eq. (1) scores of its rankable leaves; its forced
+// leaves (§5.3: current, and with forcing the first and the previous) and the
+// entries from its causal bound up to the next multiple of 4 hold -inf, so
+// that the Top-K pass reads whole 16-byte groups without masks.
 template <int D, int G>
 __global__ __launch_bounds__(256, 2) void bsa_scores_mfma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ planes, float* __restrict__ S,
-    int heads_q, int heads_kv, int n_tok, int block, int m1, int causal, float scale,
+    int heads_q, int heads_kv, int n_tok, int block, int m1, int causal, int force, float scale,
     size_t plane_stride) {
   constexpr int KSTEPS = D / 16;
   constexpr int ROW = D + 8;                 // padded LDS row (bf16)
@@ -213,8 +217,9 @@ __global__ __launch_bounds__(256, 2) void bsa_scores_mfma_kernel(
     for (int i = 0; i < 16; ++i) {
       const int t = tq0 + (i / 4) * 8 + 4 * kh + (i % 4);
       const int lim = causal ? t / block : m1 - 1;
-      if (t < n_tok && leaf <= lim && leaf < m1)
-        S[((size_t)bh * n_tok + t) * m1 + leaf] = acc[i] * scale;
+      const bool forced = causal && ((leaf == lim) | (force && ((leaf == 0) | (leaf == lim - 1))));
+      if (t < n_tok && leaf < m1 && leaf < ((lim + 4) & ~3))
+        S[((size_t)bh * n_tok + t) * m1 + leaf] = (leaf <= lim && !forced) ? acc[i] * scale : neg_inf();
     }
     if (lt + 1 < n_tiles) {
       put(buf ^ 1);  // the other buffer was last read one tile ago
@@ -384,6 +389,197 @@ __global__ __launch_bounds__(256) void bsa_topk_kernel(const float* __restrict__
   }
 }
 
+// Top-K over rows written by bsa_scores_mfma_kernel (forced leaves and the
+// padding to a multiple of 4 already hold -inf; M1 % 4 == 0), LPR lanes per
+// query row (32: two rows per wavefront; 64: one), VPL scores per lane:
+//   1. the row in registers (16-byte loads up to the causal bound);
+//   2. the (K-#F)-th largest lane maximum, by a bitonic sort across the row's
+//      lanes, bounds the answer from below;
+//   3. each lane marks its scores at or above that bound in a bitmask; the
+//      marked entries (rarely more than a few per lane) are gathered through
+//      LDS as 64-bit (score, ~index) keys and sorted exactly: higher score
+//      first, lower index first on ties;
+//   4. the kept leaves plus the forced ones are put in ascending order by one
+//      more sort and written.
+// A row whose marked entries exceed LPR falls back to extracting the best
+// entries one at a time.
+__device__ __forceinline__ uint32_t xlane_u32(uint32_t v, int j) {
+  return uint32_t(__shfl_xor(int(v), j, kWave));
+}
+template <int LPR>
+__device__ __forceinline__ float row_sort_desc(float x, int hl) {
+#pragma unroll
+  for (int k = 2; k <= LPR; k <<= 1)
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const float y = __shfl_xor(x, j, kWave);
+      const bool desc = (hl & k) == 0 || k == LPR;
+      const bool lower = (hl & j) == 0;
+      x = (desc == lower) ? fmaxf(x, y) : fminf(x, y);
+    }
+  return x;
+}
+template <int LPR>
+__device__ __forceinline__ uint64_t row_sort_desc64(uint64_t x, int hl) {
+#pragma unroll
+  for (int k = 2; k <= LPR; k <<= 1)
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const uint64_t y = (uint64_t(xlane_u32(uint32_t(x >> 32), j)) << 32) | xlane_u32(uint32_t(x), j);
+      const bool desc = (hl & k) == 0 || k == LPR;
+      const bool lower = (hl & j) == 0;
+      x = (desc == lower) ? (x > y ? x : y) : (x < y ? x : y);
+    }
+  return x;
+}
+template <int LPR>
+__device__ __forceinline__ uint32_t row_sort_desc32(uint32_t x, int hl) {
+#pragma unroll
+  for (int k = 2; k <= LPR; k <<= 1)
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const uint32_t y = xlane_u32(x, j);
+      const bool desc = (hl & k) == 0 || k == LPR;
+      const bool lower = (hl & j) == 0;
+      x = (desc == lower) ? max(x, y) : min(x, y);
+    }
+  return x;
+}
+
+template <int LPR, int VPL>  // lanes per row (32 or 64), scores per lane (% 4 == 0)
+__global__ __launch_bounds__(256) void bsa_topk_rows_kernel(const float* __restrict__ S,
+                                                            int32_t* __restrict__ idx,
+                                                            float* __restrict__ score, int n_tok,
+                                                            int block, int m1, int topk,
+                                                            int causal, int force) {
+  constexpr int ROWS = 256 / LPR;  // rows per workgroup
+  constexpr int NM = (VPL + 31) / 32;  // 32-bit candidate masks per lane
+  __shared__ uint64_t cand[ROWS][LPR + 1];  // entry LPR takes non-candidates
+  const int lane = lane_id();
+  const int hl = lane & (LPR - 1);
+  const int slot = threadIdx.x / LPR;
+  const int t = blockIdx.x * ROWS + slot;
+  const bool live = t < n_tok;
+  const int bh = blockIdx.y;
+  const size_t row = (size_t)bh * n_tok + (live ? t : n_tok - 1);
+  const float* srow = S + row * m1;
+  const int cur = (live ? t : n_tok - 1) / block;
+  const bool cz = causal != 0, fz = force != 0;
+  const int n_el = cz ? cur + 1 : m1;
+  const bool keep_all = n_el <= topk;
+  const int n_forced = cz ? 1 + (fz ? (cur >= 2 ? 2 : 1) : 0) : 0;
+  const int keep_n = keep_all ? 0 : topk - n_forced;
+  // 1. The row: element i = 4 LPR g + 4 hl + e (g < VPL / 4, e < 4).
+  float x[VPL];
+  float lmax = neg_inf();
+#pragma unroll
+  for (int g = 0; g < VPL / 4; ++g) {
+    const int i0 = 4 * LPR * g + 4 * hl;
+    float4 v = make_float4(neg_inf(), neg_inf(), neg_inf(), neg_inf());
+    if (!keep_all && i0 < n_el) v = *reinterpret_cast<const float4*>(srow + i0);
+    x[4 * g] = v.x; x[4 * g + 1] = v.y; x[4 * g + 2] = v.z; x[4 * g + 3] = v.w;
+    lmax = fmaxf(lmax, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
+  }
+  // 2. Lower bound: the keep_n-th largest lane maximum of the row.
+  const float srt = row_sort_desc<LPR>(lmax, hl);
+  const int kk = max(keep_n, 1) - 1;
+  const float thr = __shfl(srt, (lane & ~(LPR - 1)) + kk, kWave);
+  // 3. Marked entries (>= thr and rankable, i.e. > -inf).
+  uint32_t m[NM];
+#pragma unroll
+  for (int w = 0; w < NM; ++w) m[w] = 0u;
+#pragma unroll
+  for (int r = 0; r < VPL; ++r)
+    m[r / 32] |= (x[r] >= thr && x[r] > neg_inf()) ? (1u << (r % 32)) : 0u;
+  int cnt = 0;
+#pragma unroll
+  for (int w = 0; w < NM; ++w) cnt += __popc(m[w]);
+  int incl = cnt;
+#pragma unroll
+  for (int o = 1; o < LPR; o <<= 1) {
+    const int y = __shfl_up(incl, o, LPR);
+    if (hl >= o) incl += y;
+  }
+  const int total = __shfl(incl, (lane & ~(LPR - 1)) + LPR - 1, kWave);
+  bool chosen = false;
+  uint64_t mine = 0;
+  if (keep_n > 0 && total <= LPR) {
+    int off = incl - cnt;
+    bool more = cnt > 0;
+    // marked entries, one per lane per round (their scores are re-read: L2)
+    while (__ballot(more) != 0) {
+      if (more) {
+        int w = 0;
+#pragma unroll
+        for (int ww = NM - 1; ww >= 0; --ww) w = m[ww] != 0u ? ww : w;
+        uint32_t mw = m[0];
+#pragma unroll
+        for (int ww = 1; ww < NM; ++ww) mw = w == ww ? m[ww] : mw;
+        const int r = 32 * w + __builtin_ctz(mw);
+        const int i = 4 * LPR * (r / 4) + 4 * hl + (r % 4);
+        cand[slot][off] = (uint64_t(ord32(srow[i])) << 32) | uint32_t(0xffffffffu - uint32_t(i));
+        ++off;
+        mw &= mw - 1u;
+#pragma unroll
+        for (int ww = 0; ww < NM; ++ww) m[ww] = w == ww ? mw : m[ww];
+        more = false;
+#pragma unroll
+        for (int ww = 0; ww < NM; ++ww) more |= m[ww] != 0u;
+      }
+    }
+    wave_lds_sync();
+    const uint64_t ck = hl < total ? cand[slot][hl] : 0ull;
+    wave_lds_sync();
+    const uint64_t s64 = row_sort_desc64<LPR>(ck, hl);
+    chosen = hl < keep_n;
+    mine = s64;
+  } else if (keep_n > 0) {
+    // Rare: many entries at the bound.  The keep_n best, one at a time
+    // (largest score, then the lowest index holding it).
+    uint32_t key[VPL];
+#pragma unroll
+    for (int r = 0; r < VPL; ++r) key[r] = x[r] > neg_inf() ? ord32(x[r]) | 1u : 0u;
+    for (int q = 0; q < keep_n; ++q) {
+      uint32_t best = 0;
+#pragma unroll
+      for (int r = 0; r < VPL; ++r) best = max(best, key[r]);
+#pragma unroll
+      for (int o = LPR / 2; o >= 1; o >>= 1) best = max(best, xlane_u32(best, o));
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int r = 0; r < VPL; ++r)
+        bi = key[r] == best ? min(bi, 4 * LPR * (r / 4) + 4 * hl + (r % 4)) : bi;
+#pragma unroll
+      for (int o = LPR / 2; o >= 1; o >>= 1) bi = min(bi, __shfl_xor(bi, o, kWave));
+#pragma unroll
+      for (int r = 0; r < VPL; ++r)
+        key[r] = 4 * LPR * (r / 4) + 4 * hl + (r % 4) == bi ? 0u : key[r];
+      if (hl == q) {
+        chosen = true;
+        mine = (uint64_t(ord32(srow[bi])) << 32) | uint32_t(0xffffffffu - uint32_t(bi));
+      }
+    }
+  }
+  // 4. Kept leaves (lanes < keep_n), forced leaves appended, ascending.
+  int node = chosen ? int(0xffffffffu - uint32_t(mine)) : -1;
+  if (keep_all) {
+    node = hl < n_el ? hl : -1;
+  } else if (cz) {
+    if (hl == keep_n) node = cur;
+    if (fz && hl == keep_n + 1 && cur >= 1) node = 0;
+    if (fz && hl == keep_n + 2 && cur >= 2) node = cur - 1;
+  }
+  const uint32_t o_sorted = row_sort_desc32<LPR>(node >= 0 ? 0xffffffffu - uint32_t(node) : 0u, hl);
+  const int out = o_sorted ? int(0xffffffffu - o_sorted) : -1;
+  if (live && hl < topk) {
+    idx[row * topk + hl] = out;
+    if (score) {
+      const bool unranked = keep_all || (cz & ((out == cur) | (fz & ((out == 0) | (out == cur - 1)))));
+      score[row * topk + hl] = out < 0 ? neg_inf() : (unranked ? pos_inf() : srow[out]);
+    }
+  }
+}
+
 // Score matrix plus 16 bytes of slack for the Top-K pass's 16-byte row reads.
 static size_t scores_bytes(const LaunchShape& s) {
   return ((size_t)s.batch * s.heads_kv * s.seq_len * s.lv.size[0] * sizeof(float) + 16 + 255) &
@@ -420,6 +616,17 @@ static hipError_t launch_bsa_topk_t(const LaunchShape& s, const float* S, int32_
   return hipGetLastError();
 }
 
+template <int LPR, int VPL>
+static hipError_t launch_bsa_topk_rows_t(const LaunchShape& s, const float* S, int32_t* idx,
+                                         float* score, hipStream_t st) {
+  constexpr int ROWS = 256 / LPR;
+  dim3 grid((s.seq_len + ROWS - 1) / ROWS, s.batch * s.heads_kv);
+  prof::Scope ps("bsa_topk", st);
+  hipLaunchKernelGGL((bsa_topk_rows_kernel<LPR, VPL>), grid, dim3(256), 0, st, S, idx, score,
+                     s.seq_len, s.block, s.lv.size[0], s.topk, s.causal ? 1 : 0, s.force ? 1 : 0);
+  return hipGetLastError();
+}
+
 template <int D, int G>
 static hipError_t launch_bsa_mfma_t(const LaunchShape& s, const void* q, const float* pyr,
                                     float* S, bf16_t* planes, hipStream_t st) {
@@ -434,7 +641,7 @@ static hipError_t launch_bsa_mfma_t(const LaunchShape& s, const void* q, const f
   prof::Scope ps("bsa_scores", st);
   hipLaunchKernelGGL((bsa_scores_mfma_kernel<D, G>), grid, dim3(256), 0, st,
                      static_cast<const bf16_t*>(q), planes, S, s.heads_q, s.heads_kv, s.seq_len,
-                     s.block, m1, s.causal ? 1 : 0, s.scale, n);
+                     s.block, m1, s.causal ? 1 : 0, s.force ? 1 : 0, s.scale, n);
   return hipGetLastError();
 }
 
@@ -454,11 +661,20 @@ hipError_t launch_bsa(const LaunchShape& s, const void* q, const float* pyr, int
                       float* score, void* ws, hipStream_t st) {
   float* S = static_cast<float*>(ws);
   hipError_t e;
+  const int m1 = s.lv.size[0];
   // MFMA scores for bf16 with a power-of-two group; else fp32 FMA tiles.
   if (s.bf16 && (s.group & (s.group - 1)) == 0) {
     bf16_t* planes = reinterpret_cast<bf16_t*>(static_cast<char*>(ws) + scores_bytes(s));
     e = s.head_dim == 128 ? launch_bsa_mfma_d<128>(s, q, pyr, S, planes, st)
                           : launch_bsa_mfma_d<64>(s, q, pyr, S, planes, st);
+    if (e != hipSuccess) return e;
+    // Rows written by the MFMA kernel (forced leaves and padding at -inf).
+    if (m1 % 4 == 0) {
+      if (m1 <= 32 * 16) return launch_bsa_topk_rows_t<32, 16>(s, S, idx, score, st);
+      if (m1 <= 32 * 32) return launch_bsa_topk_rows_t<32, 32>(s, S, idx, score, st);
+      if (m1 <= 32 * 64) return launch_bsa_topk_rows_t<32, 64>(s, S, idx, score, st);
+      return launch_bsa_topk_rows_t<64, kBsaMaxLeaves / kWave>(s, S, idx, score, st);
+    }
   } else if (s.bf16) {
     e = s.head_dim == 128 ? launch_bsa_scores_t<bf16_t, 128>(s, q, pyr, S, st)
                           : launch_bsa_scores_t<bf16_t, 64>(s, q, pyr, S, st);
@@ -467,7 +683,6 @@ hipError_t launch_bsa(const LaunchShape& s, const void* q, const float* pyr, int
                           : launch_bsa_scores_t<float, 64>(s, q, pyr, S, st);
   }
   if (e != hipSuccess) return e;
-  const int m1 = s.lv.size[0];
   if (m1 <= 4 * kWave) return launch_bsa_topk_t<4>(s, S, idx, score, st);
   if (m1 <= 16 * kWave) return launch_bsa_topk_t<16>(s, S, idx, score, st);
   if (m1 <= 32 * kWave) return launch_bsa_topk_t<32>(s, S, idx, score, st);

@@ -4,21 +4,21 @@
 // the mean of the existing level-l rows {2i, 2i+1}.  HBM-bound: K is read once
 // (N*d*sizeof(T) bytes per KV head) and R*d*4 bytes of summaries are written.
 //
-// Pass 1 (chunk kernel): one workgroup of 16 waves per (KV head, aligned
-// chunk of 2^j = 32 leaves).  Each wave streams whole leaf blocks with 16-byte
-// loads (a row is spread over d*sizeof(T)/16 lanes, several rows per load),
-// reduces the rows across lanes, then the workgroup builds levels 2..j+1 of its
-// chunk in LDS.  Pass 2 (top kernel): one workgroup per KV head builds levels
-// j+2..L from level j+1 (M_1/32 rows), keeping every level after the first in
-// LDS when it fits.
+// Pass 1 (chunk kernel): one workgroup of 8 waves per (KV head, aligned
+// chunk of 2^j = 16 leaves), two workgroups per CU.  Each wave streams whole
+// leaf blocks with 16-byte loads (a row is spread over d*sizeof(T)/16 lanes,
+// several rows per load), reduces the rows across lanes, then the workgroup
+// builds levels 2..j+1 of its chunk in LDS.  Pass 2 (top kernel): one
+// workgroup of 1024 threads per KV head builds levels j+2..L from level j+1
+// (M_1/16 rows), keeping every level after the first in LDS when it fits.
 #include "pisa_common.h"
 #include "pisa_launch.h"
 
 namespace pisa {
 
-constexpr int kPyrThreads = 1024;
-constexpr int kPyrLeavesLog2 = 5;  // 32 leaf blocks per chunk workgroup
-constexpr int kTopThreads = 256;
+constexpr int kPyrThreads = 512;
+constexpr int kPyrLeavesLog2 = 4;  // 16 leaf blocks per chunk workgroup
+constexpr int kTopThreads = 1024;
 constexpr size_t kTopLds = 64 * 1024;
 
 template <typename T, int D>

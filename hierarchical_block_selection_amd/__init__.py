@@ -6,9 +6,9 @@ runs in the library's HIP kernels.  PyTorch provides device memory and streams.
 There is no CPU fallback: without the built library every call raises.
 
 Entry points (see include/pisa.h for layouts and semantics):
-  pisa_build_pyramid, pisa_select, pisa_bsa_select, pisa_block_sparse_attn,
-  pisa_block_sparse_attn_backward, pisa_pyramid_append, pisa_decode_step, plus
-  pisa_pyramid_layout and pisa_workspace_bytes.
+  pisa_build_pyramid, pisa_select, pisa_select_noalloc, pisa_bsa_select,
+  pisa_block_sparse_attn, pisa_block_sparse_attn_backward, pisa_pyramid_append,
+  pisa_decode_step, plus pisa_pyramid_layout and pisa_workspace_bytes.
 """
 from __future__ import annotations
 
@@ -23,7 +23,7 @@ from ._lib import PisaError  # noqa: F401
 
 __all__ = [
     "Problem", "PisaError", "pisa_pyramid_layout", "pisa_workspace_bytes", "pisa_build_pyramid",
-    "pisa_select", "pisa_bsa_select", "pisa_block_sparse_attn",
+    "pisa_select", "pisa_select_noalloc", "pisa_bsa_select", "pisa_block_sparse_attn",
     "pisa_block_sparse_attn_backward", "pisa_pyramid_append", "pisa_decode_step",
     "pisa_profile_enable", "pisa_profile_report",
 ]
@@ -166,6 +166,30 @@ def pisa_select(problem: Problem, q, k, pyramid, block_idx=None, block_score=Non
     _lib.check("pisa_select", _lib.load().pisa_select(
         ctypes.byref(c), _ptr(q), _ptr(k), _ptr(pyramid), _ptr(block_idx), _ptr(block_score),
         _STRATEGIES[strategy], _ptr(ws), ws_bytes, _stream(stream)))
+    return block_idx, block_score
+
+
+def pisa_select_noalloc(problem: Problem, q, k, pyramid, block_idx=None, block_score=None,
+                        strategy: str = "auto", stream=None, want_score=True):
+    """pisa_select without a workspace: the library's fixed device scratch
+    (PISA_NOALLOC_SCRATCH_BYTES) serves the two-stage selector.  Outputs are
+    allocated here when not given; the library call itself allocates nothing."""
+    p = problem
+    _need(q, "q", (p.batch, p.heads_q, p.seq_len, p.head_dim), p.dtype)
+    _need(k, "k", (p.batch, p.heads_kv, p.seq_len, p.head_dim), p.dtype)
+    _need(pyramid, "pyramid", (p.batch, p.heads_kv, pyramid_rows(p), p.head_dim), torch.float32)
+    shape = (p.batch, p.heads_kv, p.seq_len, p.topk)
+    if block_idx is None:
+        block_idx = torch.empty(shape, dtype=torch.int32, device=q.device)
+    _need(block_idx, "block_idx", shape, torch.int32)
+    if block_score is None and want_score:
+        block_score = torch.empty(shape, dtype=torch.float32, device=q.device)
+    if block_score is not None:
+        _need(block_score, "block_score", shape, torch.float32)
+    c = p.to_c()
+    _lib.check("pisa_select_noalloc", _lib.load().pisa_select_noalloc(
+        ctypes.byref(c), _ptr(q), _ptr(k), _ptr(pyramid), _ptr(block_idx), _ptr(block_score),
+        _STRATEGIES[strategy], _stream(stream)))
     return block_idx, block_score
 
 

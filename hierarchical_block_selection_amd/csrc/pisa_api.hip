@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "pisa.h"
@@ -178,6 +179,81 @@ int pisa_select(const pisa_problem* problem, const void* q, const void* k, const
     e = pisa::launch_select_fused(s, q, k, pyramid, block_idx, block_score, st);
   }
   return e == hipSuccess ? PISA_OK : fail_hip(e, "pisa_select");
+}
+
+// ---------------------------------------------------------------------------
+// Selection that allocates nothing: the two-stage selector's workspace lives
+// in one fixed device array of the library.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kScratchBytes = size_t(PISA_NOALLOC_SCRATCH_BYTES);
+constexpr int kMaxDevices = 64;
+
+// Each device holds its own copy for the life of the process.  In host code
+// the name only identifies the symbol; the device address of a device's copy
+// comes from hipGetSymbolAddress with that device current.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch (looked up once per device).
+int scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail_hip(e, "pisa_select_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(PISA_ERR_UNSUPPORTED, "pisa_select_noalloc: device index beyond 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return fail_hip(e, "pisa_select_noalloc: hipGetSymbolAddress");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PISA_OK;
+}
+
+}  // namespace
+
+int pisa_select_noalloc(const pisa_problem* problem, const void* q, const void* k,
+                        const float* pyramid, int32_t* block_idx, float* block_score,
+                        int32_t strategy, void* stream) {
+  pisa::LaunchShape s;
+  int rc = check_problem(problem, PISA_OP_SELECT, &s);
+  if (rc != PISA_OK) return rc;
+  if (!q || !k || !pyramid || !block_idx) return fail(PISA_ERR_INVALID, "null tensor pointer");
+  if (strategy < PISA_SELECT_AUTO || strategy > PISA_SELECT_TWO_STAGE)
+    return fail(PISA_ERR_INVALID, "bad strategy");
+  bool two_stage = false;
+  if (strategy == PISA_SELECT_TWO_STAGE) {
+    if (!pisa::select_two_stage_supported(s))
+      return fail(PISA_ERR_UNSUPPORTED, "two-stage selection does not support this problem");
+    two_stage = true;
+  } else if (strategy == PISA_SELECT_AUTO) {
+    two_stage = pisa::select_two_stage_supported(s);
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (two_stage) {
+    const size_t need = pisa::select_two_stage_ws_bytes(s);
+    if (need > kScratchBytes) {
+      char msg[200];
+      std::snprintf(msg, sizeof msg,
+                    "pisa_select_noalloc: the problem needs %zu bytes of scratch, more than the "
+                    "fixed %zu (use pisa_select with a workspace)",
+                    need, kScratchBytes);
+      return fail(PISA_ERR_WORKSPACE, msg);
+    }
+    void* ws = nullptr;
+    if ((rc = scratch_address(&ws)) != PISA_OK) return rc;
+    e = pisa::launch_select_two_stage(s, q, k, pyramid, block_idx, block_score, ws, st);
+  } else {
+    e = pisa::launch_select_fused(s, q, k, pyramid, block_idx, block_score, st);
+  }
+  return e == hipSuccess ? PISA_OK : fail_hip(e, "pisa_select_noalloc");
 }
 
 int pisa_bsa_select(const pisa_problem* problem, const void* q, const float* pyramid,

@@ -15,7 +15,9 @@
  * - All functions are extern "C", never throw, and return a pisa_status.
  * - Every tensor argument is a DEVICE pointer to contiguous row-major memory,
  *   16-byte aligned, owned by the caller.  The library allocates no device or
- *   host memory and keeps no state between calls; calls are re-entrant.
+ *   host memory and keeps no state between calls; calls are re-entrant.  The
+ *   one exception is pisa_select_noalloc, which uses a fixed device array of
+ *   the library's (see there).
  * - Layouts (B batch, Hq query heads, Hkv KV heads, N tokens, d head dim,
  *   K budget, R pyramid rows):
  *     Q, O        [B, Hq,  N, d]   dtype = problem.dtype
@@ -167,6 +169,26 @@ int pisa_pyramid_append(const pisa_problem* problem, const int32_t* cache_len,
 int pisa_select(const pisa_problem* problem, const void* q, const void* k, const float* pyramid,
                 int32_t* block_idx, float* block_score, int32_t strategy, void* ws,
                 size_t ws_bytes, void* stream);
+
+/* pisa_select for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same selection, bit for bit, with the two-stage selector's workspace taken
+ * from a fixed array of PISA_NOALLOC_SCRATCH_BYTES that the library keeps on
+ * each device it runs on until the process ends.  No allocation, no memset.
+ *   arguments:  as pisa_select, without ws / ws_bytes
+ *   limits:     a problem whose two-stage workspace
+ *               (pisa_workspace_bytes(PISA_OP_SELECT)) exceeds the scratch is
+ *               rejected with PISA_ERR_WORKSPACE before anything is enqueued
+ *               (PISA_SELECT_FUSED needs no scratch and has no such limit)
+ *   stream:     must belong to the current device (the scratch used is the
+ *               current device's)
+ *   concurrency: every call on one device shares that device's scratch and
+ *               leaves the last call's contents in it; calls that overlap on
+ *               one device (different streams or threads) race. */
+#define PISA_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+int pisa_select_noalloc(const pisa_problem* problem, const void* q, const void* k,
+                        const float* pyramid, int32_t* block_idx, float* block_score,
+                        int32_t strategy, void* stream);
 
 /* BSA flat selection (§02 eq. (1)): s_{t,i} = sum over the group's heads of
  * scale * q . kbar_i over every eligible leaf summary (level 1 of `pyramid`),

@@ -225,3 +225,24 @@ def test_backward_arguments():
         assert bwd(pp, *a, ptr, sz.value, None) == _lib.PISA_ERR_INVALID, i
     assert bwd(pp, *args, ptr, sz.value - 1, None) == _lib.PISA_ERR_WORKSPACE
     assert bwd(pp, *args, None, sz.value, None) == _lib.PISA_ERR_WORKSPACE
+
+
+def test_noalloc_select_rejects_before_any_device_work():
+    """pisa_select_noalloc validates on the host: null tensors, a bad strategy and
+    a problem whose two-stage workspace exceeds the fixed scratch are rejected
+    with no device call (this runs without a GPU)."""
+    L = lib()
+    big = problem(heads_q=8, heads_kv=8, seq_len=131072)
+    need = ctypes.c_size_t()
+    assert L.pisa_workspace_bytes(ctypes.byref(big), _lib.PISA_OP_SELECT, ctypes.byref(need)) == 0
+    assert need.value > _lib.PISA_NOALLOC_SCRATCH_BYTES
+    fake = ctypes.c_void_p(256)  # never dereferenced: validation fails first
+    rc = L.pisa_select_noalloc(ctypes.byref(big), fake, fake, fake, fake, None,
+                               _lib.PISA_SELECT_AUTO, None)
+    assert rc == _lib.PISA_ERR_WORKSPACE
+    assert b"scratch" in L.pisa_last_error()
+    small = problem(seq_len=4096)
+    assert L.pisa_select_noalloc(ctypes.byref(small), None, fake, fake, fake, None,
+                                 _lib.PISA_SELECT_AUTO, None) == _lib.PISA_ERR_INVALID
+    assert L.pisa_select_noalloc(ctypes.byref(small), fake, fake, fake, fake, None, 7,
+                                 None) == _lib.PISA_ERR_INVALID

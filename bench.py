@@ -31,7 +31,9 @@ if ROOT not in sys.path:
 METRIC = "prefill tokens/s (select+attn) at 128K d=128; selection ms vs BSA"
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
-FP32_VALU_PEAK_TFLOPS = 157.3
+# Packed fp32 instructions are disabled in this build, so vector fp32 FMA
+# peaks at 256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz.
+FP32_UNPACKED_PEAK_TFLOPS = 78.6
 
 
 # ----------------------------------------------------------------------------
@@ -121,6 +123,29 @@ def stored_traffic(kernel):
         return None
     try:
         return float(rec["fetch_bytes"]) + float(rec["write_bytes"])
+    except (KeyError, ValueError):
+        return None
+
+
+def stored_counters(kernel):
+    """Per-launch counter figures of `kernel` from the committed rocprofv3
+    summary profiles/mfma_<kernel>.txt (MFMA busy fraction, executed MFMA
+    flops, VALU busy fraction), if it was taken on the current kernel
+    sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"mfma_{kernel}.txt")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            key, val = line.split("=", 1)
+            rec[key.strip()] = val.strip()
+    if rec.get("source_hash") != source_hash():
+        return None
+    try:
+        return {"mfma_busy_frac": float(rec["mfma_busy_frac"]),
+                "mfma_flops": float(rec["mfma_flops"]),
+                "valu_busy_frac": float(rec["valu_busy_frac"])}
     except (KeyError, ValueError):
         return None
 
@@ -263,18 +288,43 @@ def run(args):
     elt = 2 if prob.dtype == torch.bfloat16 else 4
     pyr_bytes = B * H * (N * d * elt + rows * d * 4)
     attn_bytes = B * H * N * d * elt * 4  # Q, K, V read once, O written once
+    # Stage 1 scores every child row below a wave's causal bound on the
+    # matrix cores (bf16 hi/lo planes of the summaries), far more than the
+    # method's dots: with counters on the current sources its roofline is
+    # the executed MFMA flops against the bf16 MFMA peak, else the method's
+    # dots against the unpacked fp32 ceiling of this build.
+    s1c = stored_counters("select_stage1")
+    s1_roof = (("mfma", s1c["mfma_flops"], BF16_MFMA_PEAK_TFLOPS, "TFLOP/s",
+                "executed dense MFMA flops (counters)") if s1c else
+               ("alu", 2.0 * d * dots_l3 * H * B, FP32_UNPACKED_PEAK_TFLOPS, "TFLOP/s",
+                "method's intermediate-level dots vs unpacked fp32 FMA"))
     roof_table = {
-        "pyramid_chunk": ("hbm", pyr_bytes, HBM_PEAK_GBS, "GB/s"),
-        "select_stage1": ("alu", 2.0 * d * dots_l3 * H * B, FP32_VALU_PEAK_TFLOPS, "TFLOP/s"),
+        "pyramid_chunk": ("hbm", pyr_bytes, HBM_PEAK_GBS, "GB/s", "K read + pyramid written"),
+        "select_stage1": s1_roof,
         "select_stage2": ("mfma", 2.0 * d * (dots_l2 + dots_l1) * H * B, BF16_MFMA_PEAK_TFLOPS,
-                          "TFLOP/s"),
-        "select_fused": ("alu", sel_flops, FP32_VALU_PEAK_TFLOPS, "TFLOP/s"),
-        "attn_partial": ("mfma", attn_flops, BF16_MFMA_PEAK_TFLOPS, "TFLOP/s"),
-        "attn_query": ("alu", attn_flops, FP32_VALU_PEAK_TFLOPS, "TFLOP/s"),
-        "attn_combine": ("hbm", B * H * N * d * elt, HBM_PEAK_GBS, "GB/s"),
+                          "TFLOP/s", "method's leaf and level-2 dots"),
+        "select_fused": ("alu", sel_flops, FP32_UNPACKED_PEAK_TFLOPS, "TFLOP/s",
+                         "method's dots vs unpacked fp32 FMA"),
+        "attn_partial": ("mfma", attn_flops, BF16_MFMA_PEAK_TFLOPS, "TFLOP/s",
+                         "4 C d flops per (query head, attended block)"),
+        "attn_query": ("alu", attn_flops, FP32_UNPACKED_PEAK_TFLOPS, "TFLOP/s",
+                       "eq. (2) flops vs unpacked fp32 FMA"),
+        "attn_combine": ("hbm", B * H * N * d * elt, HBM_PEAK_GBS, "GB/s", "O written"),
     }
+    kernels_roofline = {}
+    for kname, (kb, kw, kp, ku, basis) in roof_table.items():
+        if kname in kernels and kernels[kname] > 0:
+            ks = 1e9 if ku == "GB/s" else 1e12
+            ka = kw / (kernels[kname] * 1e-3) / ks
+            kernels_roofline[kname] = {"bound": kb, "achieved": round(ka, 1), "peak": kp,
+                                       "unit": ku, "frac": round(ka / kp, 4), "basis": basis}
+            kc = stored_counters(kname)
+            if kc:
+                kernels_roofline[kname]["mfma_busy_frac"] = kc["mfma_busy_frac"]
+                kernels_roofline[kname]["valu_busy_frac"] = kc["valu_busy_frac"]
     dominant = max(kernels, key=kernels.get)
-    bound, work, peak, unit = roof_table.get(dominant, ("hbm", 0.0, HBM_PEAK_GBS, "GB/s"))
+    bound, work, peak, unit, _basis = roof_table.get(dominant,
+                                                     ("hbm", 0.0, HBM_PEAK_GBS, "GB/s", ""))
     scale = 1e9 if unit == "GB/s" else 1e12
     achieved = work / (kernels[dominant] * 1e-3) / scale
     traffic = stored_traffic(dominant)
@@ -287,6 +337,13 @@ def run(args):
         # the counters' HBM bytes over the same launch time, against the HBM peak
         roof["traffic_gbs"] = traffic / (kernels[dominant] * 1e-3) / 1e9
         roof["traffic_frac_of_hbm_peak"] = roof["traffic_gbs"] / HBM_PEAK_GBS
+    counters = stored_counters(dominant)
+    if counters is not None:
+        # SQ_VALU_MFMA_BUSY_CYCLES over (GRBM_GUI_ACTIVE per XCD x 1024 SIMDs), and
+        # the MFMA flops the kernel executed (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512)
+        roof["mfma_busy_frac"] = counters["mfma_busy_frac"]
+        roof["mfma_executed_tflops"] = counters["mfma_flops"] / (kernels[dominant] * 1e-3) / 1e12
+        roof["valu_busy_frac"] = counters["valu_busy_frac"]
 
     result = {
         "metric": METRIC,
@@ -312,6 +369,7 @@ def run(args):
                         "pyramid_mb": pyr_bytes / 1e6, "attn_compulsory_mb": attn_bytes / 1e6,
                         "source_hash": source_hash()},
         "roofline": roof,
+        "kernels_roofline": kernels_roofline,
     }
 
     if not args.no_backward:

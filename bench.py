@@ -582,6 +582,77 @@ def selection_sweep(args, heads_q=4, heads_kv=4, head_dim=128, topk=16,
                     f"as a fraction of {HBM_PEAK_GBS:.0f} GB/s"}
 
 
+def q_tile_study(args):
+    """Stage-2 work decomposition against the Q_tile trade-off of the PISA
+    reading page (§5.1, eqs. (12)-(15); Table 4's Q1/Q2/Q4 axis).  In this
+    implementation a level-3 node's keys (4 leaves, 4C raw keys) are loaded
+    once per work item and reused for up to `item_rows` (pair, head) columns
+    (the pages' Q_tile, in query heads); the queries pass through LDS in
+    batches of `batch_rows` columns and through MFMA 32x32x16 tiles of 32
+    columns.  Sweeps both (PISA_S2_ITEM_ROWS, PISA_S2_BATCH_ROWS) for three
+    group sizes, and times the single-stage (fused) selector beside the
+    two-stage one."""
+    import torch
+
+    import hierarchical_block_selection_amd as pisa
+    from hierarchical_block_selection_amd.inputs import prefill_inputs
+
+    dev = torch.device("cuda:0")
+    shapes = [("G1_d128_K16", 4, 4, 128, 16), ("G4_d128_K16", 16, 4, 128, 16),
+              ("G16_d64_K8", 16, 1, 64, 8)]
+    n = args.q_tile_n
+    out = {"study": "stage-2 item and batch sizes", "N": n, "points": [], "fused_vs_two_stage": []}
+    saved = {k: os.environ.get(k) for k in ("PISA_S2_ITEM_ROWS", "PISA_S2_BATCH_ROWS")}
+    try:
+        for name, hq, hkv, d, k in shapes:
+            g = hq // hkv
+            prob = pisa.Problem(1, hq, hkv, n, d, block=64, topk=k, dtype=torch.bfloat16)
+            inp = prefill_inputs(1, hq, hkv, n, d, torch.bfloat16, seed=4100, device=dev)
+            pyr = pisa.pisa_build_pyramid(prob, inp.k)
+            for item in (64, 128, 256, 512, 1024, 2048, 4096):
+                for rows in (32, 64, 128):
+                    os.environ["PISA_S2_ITEM_ROWS"] = str(item)
+                    os.environ["PISA_S2_BATCH_ROWS"] = str(rows)
+                    ws = torch.empty(pisa.pisa_workspace_bytes(prob, "select"), dtype=torch.uint8,
+                                     device=dev)
+                    run = lambda: pisa.pisa_select(prob, inp.q, inp.k, pyr, workspace=ws,
+                                                   want_score=False)
+                    sel_ms = timed_call(run, 5, 2)
+                    pisa.pisa_profile_enable(True)
+                    run()
+                    torch.cuda.synchronize()
+                    rep = pisa.pisa_profile_report()
+                    pisa.pisa_profile_enable(False)
+                    s2 = rep.get("select_stage2", (float("nan"), 1))
+                    out["points"].append({
+                        "shape": name, "group": g, "item_rows": item, "batch_rows": rows,
+                        "pairs_per_key_load": item // g, "select_ms": round(sel_ms, 4),
+                        "stage2_ms": round(s2[0] / s2[1], 4)})
+                    del ws
+            for k_env in ("PISA_S2_ITEM_ROWS", "PISA_S2_BATCH_ROWS"):
+                os.environ.pop(k_env, None)
+            for nn in (4096, 16384):
+                p2 = pisa.Problem(1, hq, hkv, nn, d, block=64, topk=k, dtype=torch.bfloat16)
+                i2 = prefill_inputs(1, hq, hkv, nn, d, torch.bfloat16, seed=4101, device=dev)
+                y2 = pisa.pisa_build_pyramid(p2, i2.k)
+                f_ms = timed_call(lambda: pisa.pisa_select(p2, i2.q, i2.k, y2, strategy="fused",
+                                                           want_score=False), 3, 1)
+                t_ms = timed_call(lambda: pisa.pisa_select(p2, i2.q, i2.k, y2,
+                                                           strategy="two_stage",
+                                                           want_score=False), 5, 2)
+                out["fused_vs_two_stage"].append({"shape": name, "N": nn, "fused_ms": round(f_ms, 4),
+                                                  "two_stage_ms": round(t_ms, 4)})
+            del inp, pyr
+            torch.cuda.empty_cache()
+    finally:
+        for k_env, v in saved.items():
+            if v is None:
+                os.environ.pop(k_env, None)
+            else:
+                os.environ[k_env] = v
+    return out
+
+
 def cpu_baseline(args, inp, prob):
     """The CPU oracle on a bounded sample of the same workload: the full pyramid
     of KV head 0 plus selection + attention for random rows, on the host's
@@ -687,6 +758,9 @@ def main():
     ap.add_argument("--cpu-worker", default=None, help=argparse.SUPPRESS)
     ap.add_argument("--cpu-block", type=int, default=64, help=argparse.SUPPRESS)
     ap.add_argument("--cpu-topk", type=int, default=16, help=argparse.SUPPRESS)
+    ap.add_argument("--q-tile-study", action="store_true",
+                    help="run only the stage-2 item/batch size study and print its JSON")
+    ap.add_argument("--q-tile-n", type=int, default=65536)
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="launch one elementwise copy of this many MiB before the steps "
                          "(HBM counter calibration)")
@@ -699,6 +773,9 @@ def main():
               "(the (batch, KV head) units would shard across GPUs without communication)",
               file=sys.stderr)
         sys.exit(2)
+    if args.q_tile_study:
+        print(json.dumps(q_tile_study(args)), flush=True)
+        return
     res = run(args)
     print(json.dumps(res), flush=True)
 

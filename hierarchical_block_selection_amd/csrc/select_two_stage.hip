@@ -27,6 +27,7 @@
 // computed by the same instruction sequence whatever its position, so the
 // outputs are bitwise reproducible.
 #include <algorithm>
+#include <cstdlib>
 #include <cfloat>
 #include <type_traits>
 
@@ -43,8 +44,33 @@ namespace {
 constexpr int kSplitLevel = 3;   // stage 1 decides levels L..3
 constexpr int kS1Waves = 4;
 constexpr int kS2Threads = 256;
-constexpr int kS2Rows = 64;       // (pair, head) rows per stage-2 batch
-constexpr int kS2ItemRows = 1024; // (pair, head) rows per stage-2 work item
+constexpr int kS2Rows = 64;       // (pair, head) rows per stage-2 batch (default, G = 1)
+constexpr int kS2RowsGrouped = 128;  // default for G > 1 (measured: 9-13% faster there)
+constexpr int kS2ItemRows = 1024; // (pair, head) rows per stage-2 work item (default)
+
+// Tuning overrides of the stage-2 work decomposition (read per call):
+//   PISA_S2_ITEM_ROWS   (pair, head) rows served by one load of a level-3
+//                       node's keys: a power of two in [64, 4096];
+//   PISA_S2_BATCH_ROWS  rows staged in LDS per batch: 32, 64 or 128
+//                       (default 64 for one head per KV head, else 128).
+// Other values fall back to the defaults.  The workspace size follows the
+// item size, so set them before pisa_workspace_bytes.
+int env_int(const char* name, int dflt) {
+  const char* v = std::getenv(name);
+  if (!v || !*v) return dflt;
+  char* end = nullptr;
+  const long x = std::strtol(v, &end, 10);
+  return (end && *end == 0 && x > 0 && x < (1 << 20)) ? int(x) : dflt;
+}
+int s2_item_rows() {
+  const int x = env_int("PISA_S2_ITEM_ROWS", kS2ItemRows);
+  return (x >= 64 && x <= 4096 && (x & (x - 1)) == 0) ? x : kS2ItemRows;
+}
+int s2_batch_rows(int group) {
+  const int dflt = group == 1 ? kS2Rows : kS2RowsGrouped;
+  const int x = env_int("PISA_S2_BATCH_ROWS", dflt);
+  return (x == 32 || x == 64 || x == 128) ? x : dflt;
+}
 constexpr int kS2Cols = 32;      // MFMA 32x32x16: 32 (query, head) columns
 constexpr int kScoreStride = 8;  // floats per pair: 4 leaf LSE, 2 level-2, 2 pad
 
@@ -77,7 +103,7 @@ WsLayout ws_layout(const LaunchShape& s) {
   const size_t units = (size_t)s.batch * s.heads_kv * s.seq_len;
   const int m3 = s.lv.n >= kSplitLevel ? s.lv.size[kSplitLevel - 1] : 1;
   w.n_buckets = s.batch * s.heads_kv * m3;
-  w.max_items = bucket::max_items(units * s.topk, w.n_buckets, kS2ItemRows / s.group);
+  w.max_items = bucket::max_items(units * s.topk, w.n_buckets, s2_item_rows() / s.group);
   size_t off = 0;
   w.counts = off; off = align256(off + sizeof(int) * w.n_buckets);
   w.offsets = off; off = align256(off + sizeof(int) * (w.n_buckets + 1));
@@ -330,7 +356,7 @@ struct S2Tile {
 };
 
 // One workgroup per work item: level-3 node n of KV head bh and up to
-// kS2ItemRows / G of its (query, slot) pairs; wavefront w owns leaf 4n + w and
+// item_pairs of its (query, slot) pairs; wavefront w owns leaf 4n + w and
 // keeps its 64 raw keys as MFMA A operands in registers for the whole item.
 // The item's pairs run in batches of ROWS / G.  Batch bt's query rows were
 // loaded into registers during batch bt - 1; per batch:
@@ -349,7 +375,7 @@ __global__ __launch_bounds__(kS2Threads, (G == 1 || D == 64) ? 3 : 2) void stage
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const int* __restrict__ item_offsets, const int* __restrict__ offsets,
     const int* __restrict__ pairs, float* __restrict__ scores, int n_buckets, int heads_q,
-    int heads_kv, int n_tok, int topk, int m3, float scale_log2) {
+    int heads_kv, int n_tok, int topk, int m3, float scale_log2, int item_pairs) {
   using Tile = S2Tile<D, G, ROWS>;
   constexpr int KSTEPS = D / 16;
   constexpr int PAIRS = Tile::PAIRS;
@@ -358,8 +384,8 @@ __global__ __launch_bounds__(kS2Threads, (G == 1 || D == 64) ? 3 : 2) void stage
   __shared__ __attribute__((aligned(16))) bf16_t tile_b[ROWS * Tile::QROW];
   __shared__ float xs[4][2][ROWS];  // [leaf][lse, mean][row], log2 units
   int bucket, start, len;
-  if (!bucket::locate_item(item_offsets, offsets, n_buckets, blockIdx.x, kS2ItemRows / G,
-                           &bucket, &start, &len))
+  if (!bucket::locate_item(item_offsets, offsets, n_buckets, blockIdx.x, item_pairs, &bucket,
+                           &start, &len))
     return;
   const int bh = bucket / m3, node = bucket % m3;
   const int b = bh / heads_kv, kvh = bh % heads_kv;
@@ -677,7 +703,7 @@ hipError_t launch_select_two_stage(const LaunchShape& s, const void* q, const vo
   {
     prof::Scope ps("select_sort", st);
     e = bucket::sort_pairs(w.s1_nodes, s.batch * s.heads_kv, s.seq_len, s.topk, m3,
-                           kS2ItemRows / s.group,
+                           s2_item_rows() / s.group,
                            w.counts, w.offsets, w.cursors, w.item_offsets, w.pairs, nullptr,
                            false, st);
   }
@@ -687,10 +713,20 @@ hipError_t launch_select_two_stage(const LaunchShape& s, const void* q, const vo
     const bf16_t* qb = static_cast<const bf16_t*>(q);
     const bf16_t* kb = static_cast<const bf16_t*>(k);
     const float sl = s.scale * kLog2e;
-#define PISA_S2(D, G)                                                                         \
-  hipLaunchKernelGGL((stage2_kernel<D, G, kS2Rows>), dim3(lay.max_items), dim3(kS2Threads), 0, st, qb, kb, \
-                     w.item_offsets, w.offsets, w.pairs, w.scores, lay.n_buckets, s.heads_q,   \
-                     s.heads_kv, s.seq_len, s.topk, m3, sl)
+    const int item_pairs = s2_item_rows() / s.group;
+    const int rows = s2_batch_rows(s.group);
+#define PISA_S2_ROWS(D, G, ROWS)                                                              \
+  hipLaunchKernelGGL((stage2_kernel<D, G, ROWS>), dim3(lay.max_items), dim3(kS2Threads), 0, st, \
+                     qb, kb, w.item_offsets, w.offsets, w.pairs, w.scores, lay.n_buckets,     \
+                     s.heads_q, s.heads_kv, s.seq_len, s.topk, m3, sl, item_pairs)
+#define PISA_S2(D, G)          \
+  if (rows == 32) {            \
+    PISA_S2_ROWS(D, G, 32);    \
+  } else if (rows == 128) {    \
+    PISA_S2_ROWS(D, G, 128);   \
+  } else {                     \
+    PISA_S2_ROWS(D, G, 64);    \
+  }
     switch (s.group * 1000 + s.head_dim) {
       case 1128: PISA_S2(128, 1); break;
       case 1064: PISA_S2(64, 1); break;
@@ -704,6 +740,7 @@ hipError_t launch_select_two_stage(const LaunchShape& s, const void* q, const vo
       default: PISA_S2(64, 16); break;
     }
 #undef PISA_S2
+#undef PISA_S2_ROWS
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   prof::Scope ps3("select_final", st);

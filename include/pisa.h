@@ -165,7 +165,12 @@ int pisa_pyramid_append(const pisa_problem* problem, const int32_t* cache_len,
  *   block_idx:   [B, Hkv, N, K] int32, out
  *   block_score: [B, Hkv, N, K] float32, out, may be NULL
  *   strategy:    PISA_SELECT_*
- *   ws/ws_bytes: workspace of pisa_workspace_bytes(PISA_OP_SELECT) bytes */
+ *   ws/ws_bytes: workspace of pisa_workspace_bytes(PISA_OP_SELECT) bytes
+ * Tuning (two-stage path; environment, read per call): PISA_S2_ITEM_ROWS, the
+ * (query, head) columns served by one load of a level-3 node's keys (power of
+ * two in [64, 4096], default 1024; the workspace size follows it), and
+ * PISA_S2_BATCH_ROWS, the columns staged per batch (32, 64 or 128; default 64
+ * with one query head per KV head, else 128).  Results do not depend on them. */
 int pisa_select(const pisa_problem* problem, const void* q, const void* k, const float* pyramid,
                 int32_t* block_idx, float* block_score, int32_t strategy, void* ws,
                 size_t ws_bytes, void* stream);

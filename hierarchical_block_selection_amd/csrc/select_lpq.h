@@ -54,6 +54,7 @@ constexpr int kMaskWords = kDenseRows / 4 / 32;  // parent bitmask words per que
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) unsigned int piece_t;  // 16 bytes
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
@@ -128,17 +129,28 @@ struct Column {
   E* p;
   int stride;
   __device__ __forceinline__ E& operator[](int i) const { return p[i * stride]; }
+  __device__ __forceinline__ void set(int i, E v) const { p[i * stride] = v; }
+};
+
+// An int column stored as bit patterns in a float array, so that one LDS
+// array holds a query's slot scores and, once the decision has read them into
+// registers, its kept-node list.
+struct IntInFloatColumn {
+  float* p;
+  int stride;
+  __device__ __forceinline__ int get(int i) const { return __float_as_int(p[i * stride]); }
+  __device__ __forceinline__ void set(int i, int v) const { p[i * stride] = __int_as_float(v); }
 };
 
 // Kept slots -> ascending node list through LDS (kMaxK + 1 entries; entry
 // kMaxK takes the stores of slots that are not kept).
-template <typename NodeOf>
-__device__ __forceinline__ void compact_kept(uint32_t km, Column<int> row, NodeOf node_of) {
+template <typename Col, typename NodeOf>
+__device__ __forceinline__ void compact_kept(uint32_t km, Col row, NodeOf node_of) {
 #pragma unroll
   for (int j = 0; j < kSlots; ++j) {
     const bool k = (km >> j) & 1u;
     const int pos = __popc(km & ((1u << j) - 1u));
-    row[k ? min(pos, kMaxK) : kMaxK] = node_of(j);
+    row.set(k ? min(pos, kMaxK) : kMaxK, node_of(j));
   }
 }
 
@@ -168,9 +180,18 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void stage1_kernel(
     int split_level) {
   constexpr int T = kWave / G;  // queries per wave
   constexpr int KSTEPS = D / 16;
+  // Summary chunk shared by the workgroup's waves: 32 rows of the hi plane,
+  // then the same 32 rows of the lo plane, each row padded by 16 bytes.
+  constexpr int CROW = D + 8;
+  constexpr int CPIECES = 2 * 32 * D / 8;  // 16-byte pieces of a chunk
+  constexpr int CLOADS = CPIECES / (kWaves * kWave);
+  static_assert(CPIECES % (kWaves * kWave) == 0, "chunk pieces per thread");
+  // score_s holds a query's slot scores and, after its decision has read
+  // them, its kept-node list (int bit patterns in rows 0..kMaxK).
   __shared__ float score_s[kWaves][kSlots + 1][T];
   __shared__ uint32_t mask_s[kWaves][kMaskWords][T];
-  __shared__ int list_s[kWaves][kMaxK + 1][T];
+  __shared__ __align__(16) bf16_t chunk_s[2 * 32 * CROW];
+  __shared__ uint32_t chunks_s[2][kWaves][2];
 
   const int wave = threadIdx.x / kWave;
   const int lane = lane_id();
@@ -180,8 +201,9 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void stage1_kernel(
   const int bh = (int)(lin % gridDim.y);
   const int bx = (int)(gridDim.x - 1 - lin / gridDim.y);
   const int b = bh / heads_kv, kvh = bh % heads_kv;
+  // Waves past the sequence end take part in the workgroup's chunk loads and
+  // barriers with no live query.
   const int t0 = (bx * kWaves + wave) * T;
-  if (t0 >= n_tok) return;
   const bool cz = causal != 0, fzon = force != 0;
   const size_t head_rows = (size_t)bh * lv.rows;
 
@@ -204,15 +226,13 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void stage1_kernel(
   const int t = t0 + lane;
   const bool dlane = lane < T && t < n_tok;
   const int cur = dlane ? t / block : 0;
-  const int t_last = min(t0 + T, n_tok) - 1;
-  const int cur_last = t_last / block;
   int kp[kMaxK];  // kept nodes one level up, ascending
   int nk = 1;
 #pragma unroll
   for (int i = 0; i < kMaxK; ++i) kp[i] = 0;
   const int ql = lane < T ? lane : 0;
   const Column<float> srow{&score_s[wave][0][ql], T};
-  const Column<int> lrow{&list_s[wave][0][ql], T};
+  const IntInFloatColumn lrow{&score_s[wave][0][ql], T};
   const Column<uint32_t> mrow{&mask_s[wave][0][ql], T};
 
   for (int l = lv.n; l >= split_level; --l) {
@@ -230,48 +250,88 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void stage1_kernel(
     }
     if (!dlane) n_valid = 0;
     const bool need = n_valid > topk;
+    const int m_child = lv.size[l - 2];
+    const size_t child0 = head_rows + lv.off[l - 2];
 
-    if (__ballot(need) != 0) {
-      const int m_child = lv.size[l - 2];
-      const size_t child0 = head_rows + lv.off[l - 2];
-      if (m_child <= kDenseRows) {
-        // Parent masks were written after the previous level's decision.
-        const int lim_last = cz ? (cur_last >> sh) : size_l - 1;
-        const int rows_needed = min(m_child, 2 * lim_last + 2);
+    if (m_child <= kDenseRows) {
+      // Chunk c holds child rows 32c..32c+31, whose parents 8c..8c+7 are byte
+      // c of the parent masks (written after the previous level's decision).
+      // The workgroup scores every chunk that holds a kept parent of one of
+      // its ranking queries, all waves together.
+      uint32_t cw[2] = {0u, 0u};
+      if (need) {
+#pragma unroll
+        for (int w = 0; w < kMaskWords; ++w) {
+          const uint32_t word = mrow[w];
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            cw[w >> 3] |= ((word >> (8 * j)) & 0xffu) ? (1u << ((4 * w + j) & 31)) : 0u;
+        }
+      }
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        cw[0] |= __shfl_xor(cw[0], o, kWave);
+        cw[1] |= __shfl_xor(cw[1], o, kWave);
+      }
+      if (lane == 0) {
+        chunks_s[l & 1][wave][0] = cw[0];
+        chunks_s[l & 1][wave][1] = cw[1];
+      }
+      lds_barrier();
+      uint32_t todo[2] = {0u, 0u};
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        todo[0] |= chunks_s[l & 1][w][0];
+        todo[1] |= chunks_s[l & 1][w][1];
+      }
+      todo[0] = __builtin_amdgcn_readfirstlane(todo[0]);
+      todo[1] = __builtin_amdgcn_readfirstlane(todo[1]);
+
+      if ((todo[0] | todo[1]) != 0u) {
+        // Pop the lowest pending chunk (the masks are nonzero).
+        auto pop = [&]() __attribute__((always_inline)) {
+          int c;
+          if (todo[0] != 0u) {
+            c = __builtin_ctz(todo[0]);
+            todo[0] &= todo[0] - 1u;
+          } else {
+            c = 32 + __builtin_ctz(todo[1]);
+            todo[1] &= todo[1] - 1u;
+          }
+          return c;
+        };
+        // This thread's pieces of a chunk: piece p = tid + 256 i is plane
+        // p / (32 D / 8), row (p / (D / 8)) % 32, 16-byte column p % (D / 8).
+        // Rows past the level end repeat its last row (see the ragged-chunk
+        // masking of the pickup).
+        piece_t stage[CLOADS];
+        auto fetch = [&](int r0) __attribute__((always_inline)) {
+#pragma unroll
+          for (int i = 0; i < CLOADS; ++i) {
+            const int p = threadIdx.x + i * kWaves * kWave;
+            const int plane = p / (32 * D / 8), row = (p / (D / 8)) % 32, c8 = p % (D / 8);
+            const bf16_t* src = plane ? plo : phi;
+            stage[i] = *reinterpret_cast<const piece_t*>(
+                src + (child0 + min(r0 + row, m_child - 1)) * D + 8 * c8);
+          }
+        };
+        auto put = [&]() __attribute__((always_inline)) {
+#pragma unroll
+          for (int i = 0; i < CLOADS; ++i) {
+            const int p = threadIdx.x + i * kWaves * kWave;
+            const int plane = p / (32 * D / 8), row = (p / (D / 8)) % 32, c8 = p % (D / 8);
+            *reinterpret_cast<piece_t*>(chunk_s + (plane * 32 + row) * CROW + 8 * c8) = stage[i];
+          }
+        };
         int base[2] = {0, 0};
         const Column<uint32_t> mcol[2] = {{&mask_s[wave][0][(32 * 0 + col) / G], T},
                                           {&mask_s[wave][0][(32 * 1 + col) / G], T}};
         const Column<float> scol[2] = {{&score_s[wave][0][(32 * 0 + col) / G], T},
                                        {&score_s[wave][0][(32 * 1 + col) / G], T}};
         const bool writer = (col % G) == 0;
-        // The next chunk at or after row r whose parents some query of the
-        // wave keeps (rows_needed when there is none).
-        auto next_chunk = [&](int r) __attribute__((always_inline)) {
-          for (; r < rows_needed; r += 32) {
-            const int p = r >> 2;
-            uint32_t any = 0;
-#pragma unroll
-            for (int cb = 0; cb < 2; ++cb) any |= (mcol[cb][p >> 5] >> (p & 31)) & 0xffu;
-            if (__ballot(any != 0u) != 0) break;
-          }
-          return r;
-        };
-        // Summary rows r0 + col of a chunk (rows past the level end repeat its
-        // last row; their logits are never used: see the ragged-chunk masking).
-        uint4 hv[KSTEPS], lv4[KSTEPS];
-        auto fetch = [&](int r0) __attribute__((always_inline)) {
-          const int r = min(r0 + col, m_child - 1);
-          const bf16_t* hrow = phi + (child0 + r) * D + 8 * kh;
-          const bf16_t* lrow2 = plo + (child0 + r) * D + 8 * kh;
-#pragma unroll
-          for (int s = 0; s < KSTEPS; ++s) {
-            hv[s] = *reinterpret_cast<const uint4*>(hrow + 16 * s);
-            lv4[s] = *reinterpret_cast<const uint4*>(lrow2 + 16 * s);
-          }
-        };
-        // One chunk: S = summaries x queries on MFMA (hv, lv4 hold its rows),
-        // then the candidates' LSEs picked up into the slot arrays.
-        auto chunk = [&](int r0, auto&& between) __attribute__((always_inline)) {
+        // One chunk: S = summaries x queries on MFMA from the LDS chunk, then
+        // the candidates' LSEs picked up into the slot arrays.
+        auto chunk = [&](int r0) __attribute__((always_inline)) {
           // Rows of this chunk: r0 + 8g + 4kh + i%4 (acc element 4g + i%4);
           // level-l candidates n = r0/2 + 4g + 2kh + m own rows 2n, 2n+1;
           // their parents p = r0/4 + 2g + kh (bits p0..p0+7 of the masks).
@@ -279,18 +339,20 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void stage1_kernel(
           uint32_t byte[2];
 #pragma unroll
           for (int cb = 0; cb < 2; ++cb) byte[cb] = (mcol[cb][p0 >> 5] >> (p0 & 31)) & 0xffu;
+          const bf16_t* arow = chunk_s + col * CROW + 8 * kh;
           f32x16_t acc[2] = {};
 #pragma unroll
           for (int s = 0; s < KSTEPS; ++s) {
+            const uint4 hv = *reinterpret_cast<const uint4*>(arow + 16 * s);
+            const uint4 lo = *reinterpret_cast<const uint4*>(arow + 32 * CROW + 16 * s);
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb) {
-              acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lv4[s]), bq[cb][s],
+              acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lo), bq[cb][s],
                                                                 acc[cb], 0, 0, 0);
-              acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(hv[s]), bq[cb][s],
+              acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(hv), bq[cb][s],
                                                                 acc[cb], 0, 0, 0);
             }
           }
-          between();
           auto pickup = [&](auto full_tag) {
             constexpr bool kFull = decltype(full_tag)::value;  // every row of the chunk exists
 #pragma unroll
@@ -320,64 +382,70 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void stage1_kernel(
                   scol[cb][w ? 2 * pslot + m : kSlots] = v;
                 }
               }
-              base[cb] += __popc(byte[cb]);
             }
           };
           if (r0 + 32 <= m_child)
             pickup(std::true_type{});
           else
             pickup(std::false_type{});
+          // Parents in chunks skipped by the workgroup are no kept parents of
+          // a ranking query, so the slot bases of those queries stay exact.
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb) base[cb] += __popc(byte[cb]);
         };
-        if constexpr (G == 1) {
-          // the next chunk's rows are in flight while this one is picked up
-          int r0 = next_chunk(0);
-          if (r0 < rows_needed) fetch(r0);
-          while (r0 < rows_needed) {
-            const int rn = next_chunk(r0 + 32);
-            chunk(r0, [&] { if (rn < rows_needed) fetch(rn); });
-            r0 = rn;
-          }
-        } else {  // larger groups need the registers: fetch, then compute
-          for (int r0 = next_chunk(0); r0 < rows_needed; r0 = next_chunk(r0 + 32)) {
-            fetch(r0);
-            chunk(r0, [] {});
-          }
+        // The next chunk's pieces are in flight while this one is scored.
+        int c = pop();
+        fetch(32 * c);
+        for (;;) {
+          const bool more = (todo[0] | todo[1]) != 0u;
+          const int cn = more ? pop() : c;
+          wait_vmcnt<0>();
+          lds_barrier();  // every wave has read the previous chunk
+          put();
+          if (more) fetch(32 * cn);
+          lds_barrier();  // this chunk is in LDS
+          chunk(32 * c);
+          if (!more) break;
+          c = cn;
         }
-      } else {
-        // Gather: one query at a time; lane L scores child row L of the
-        // query's candidate list (candidate L >> 1, child L & 1).
-        for (int qi = 0; qi < T; ++qi) {
-          if (!__builtin_amdgcn_readlane(need ? 1 : 0, qi)) continue;
-          const int j = lane >> 1;
-          const int nkq = __builtin_amdgcn_readlane(nk, qi);
-          const int nvq = __builtin_amdgcn_readlane(n_valid, qi);
-          const int par = list_s[wave][j >> 1][qi];
-          const int cnode = 2 * par + (j & 1);
-          const int row = 2 * cnode + (lane & 1);
-          const bool live = ((j >> 1) < nkq) & (j < nvq) & (row < m_child);
-          const float* xr = pyr + (child0 + (live ? row : 0)) * D;
-          float tot = 0.f;
+      }
+      wave_lds_sync();
+    } else if (__ballot(need) != 0) {
+      // Gather: one query at a time; lane L scores child row L of the
+      // query's candidate list (candidate L >> 1, child L & 1).  The list
+      // entries of query qi are read before its score column is written.
+      for (int qi = 0; qi < T; ++qi) {
+        if (!__builtin_amdgcn_readlane(need ? 1 : 0, qi)) continue;
+        const int j = lane >> 1;
+        const int nkq = __builtin_amdgcn_readlane(nk, qi);
+        const int nvq = __builtin_amdgcn_readlane(n_valid, qi);
+        const int par = __float_as_int(score_s[wave][j >> 1][qi]);
+        const int cnode = 2 * par + (j & 1);
+        const int row = 2 * cnode + (lane & 1);
+        const bool live = ((j >> 1) < nkq) & (j < nvq) & (row < m_child);
+        const float* xr = pyr + (child0 + (live ? row : 0)) * D;
+        float tot = 0.f;
 #pragma unroll
-          for (int h = 0; h < G; ++h) {
-            const bf16_t* qr =
-                q + (((size_t)b * heads_q + (size_t)kvh * G + h) * n_tok + (t0 + qi)) * D;
-            float a = 0.f;
+        for (int h = 0; h < G; ++h) {
+          const bf16_t* qr =
+              q + (((size_t)b * heads_q + (size_t)kvh * G + h) * n_tok + (t0 + qi)) * D;
+          float a = 0.f;
 #pragma unroll
-            for (int c8 = 0; c8 < D; c8 += 8) {
-              float qv[8];
-              load16(qr + c8, qv);
-              const float4 x0 = *reinterpret_cast<const float4*>(xr + c8);
-              const float4 x1 = *reinterpret_cast<const float4*>(xr + c8 + 4);
-              a += qv[0] * x0.x + qv[1] * x0.y + qv[2] * x0.z + qv[3] * x0.w + qv[4] * x1.x +
-                   qv[5] * x1.y + qv[6] * x1.z + qv[7] * x1.w;
-            }
-            const float z = live ? a * scale_log2 : neg_inf();
-            const float zo = __shfl_xor(z, 1, kWave);
-            const float mx = fmaxf(z, zo), mn = fminf(z, zo);
-            tot += mx + fast_log2(1.f + fast_exp2(mn - mx));
+          for (int c8 = 0; c8 < D; c8 += 8) {
+            float qv[8];
+            load16(qr + c8, qv);
+            const float4 x0 = *reinterpret_cast<const float4*>(xr + c8);
+            const float4 x1 = *reinterpret_cast<const float4*>(xr + c8 + 4);
+            a += qv[0] * x0.x + qv[1] * x0.y + qv[2] * x0.z + qv[3] * x0.w + qv[4] * x1.x +
+                 qv[5] * x1.y + qv[6] * x1.z + qv[7] * x1.w;
           }
-          if ((lane & 1) == 0) score_s[wave][live ? j : kSlots][qi] = tot;
+          const float z = live ? a * scale_log2 : neg_inf();
+          const float zo = __shfl_xor(z, 1, kWave);
+          const float mx = fmaxf(z, zo), mn = fminf(z, zo);
+          tot += mx + fast_log2(1.f + fast_exp2(mn - mx));
         }
+        wave_lds_sync();
+        if ((lane & 1) == 0) score_s[wave][live ? j : kSlots][qi] = tot;
       }
       wave_lds_sync();
     }
@@ -391,11 +459,12 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void stage1_kernel(
       const bool prev_distinct = cur >= 1 && ((cur - 1) >> sh) != lim;
       km = top_slots(n_valid, topk, forced_slots(n_valid, cz, fzon, prev_distinct), sc);
     }
+    wave_lds_sync();
     compact_kept(km, lrow, [&](int j) { return 2 * kp[j >> 1] + (j & 1); });
     wave_lds_sync();
     nk = __popc(km);
 #pragma unroll
-    for (int i = 0; i < kMaxK; ++i) kp[i] = lrow[i];
+    for (int i = 0; i < kMaxK; ++i) kp[i] = lrow.get(i);
     if (l == split_level) break;
     // Parent bitmask for the next level's dense pass (kept nodes of level l).
     const int nl = l - 1;

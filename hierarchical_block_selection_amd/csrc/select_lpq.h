@@ -21,11 +21,13 @@
 // is lim or lim - 1 (then the slot before), and node 0 is slot 0.
 //
 // Stage 1 (levels L..3).  One wavefront owns 64 (query, head) columns.  For a
-// level whose children fit in kDenseRows rows, the wave computes the logits
-// of every child row needed by any of its columns on the matrix cores
-// (32 rows x 64 columns per step; bf16 hi/lo planes of the fp32 summaries,
-// so each product is exact and accumulation is fp32), and while the logits
-// are still in the MFMA register layout it forms the log-sum-exp of every
+// level whose children fit in kDenseRows rows, the workgroup's waves walk
+// together over the 32-row chunks of child rows needed by any of their
+// columns: each chunk is loaded once, coalesced, into LDS (the next one is in
+// flight in registers meanwhile), and every wave computes its logits on the
+// matrix cores (32 rows x 64 columns per step; bf16 hi/lo planes of the fp32
+// summaries, so each product is exact and accumulation is fp32).  While the
+// logits are still in the MFMA register layout it forms the log-sum-exp of every
 // sibling pair (eq. (7)), sums the group's heads (eq. (11)) and scatters the
 // scores of the pairs that are candidates of the column's query into that
 // query's slot array.  Candidacy and slot come from a bitmask of the query's

@@ -182,6 +182,11 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void stage1_kernel(
     int split_level) {
   constexpr int T = kWave / G;  // queries per wave
   constexpr int KSTEPS = D / 16;
+  // With 8 or more queries per wave the waves of a workgroup need nearly the
+  // same chunks, and sharing their loads pays; with 4 (G = 16) each wave
+  // needs under half of the workgroup's chunks, and independent waves are
+  // faster.
+  constexpr bool kShared = T >= 8;
   // Summary chunk shared by the workgroup's waves: 32 rows of the hi plane,
   // then the same 32 rows of the lo plane, each row padded by 16 bytes.
   constexpr int CROW = D + 8;
@@ -192,7 +197,7 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void stage1_kernel(
   // them, its kept-node list (int bit patterns in rows 0..kMaxK).
   __shared__ float score_s[kWaves][kSlots + 1][T];
   __shared__ uint32_t mask_s[kWaves][kMaskWords][T];
-  __shared__ __align__(16) bf16_t chunk_s[2 * 32 * CROW];
+  __shared__ __align__(16) bf16_t chunk_s[kShared ? 2 * 32 * CROW : 8];
   __shared__ uint32_t chunks_s[2][kWaves][2];
 
   const int wave = threadIdx.x / kWave;
@@ -228,6 +233,8 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void stage1_kernel(
   const int t = t0 + lane;
   const bool dlane = lane < T && t < n_tok;
   const int cur = dlane ? t / block : 0;
+  const int t_last = min(t0 + T, n_tok) - 1;
+  const int cur_last = t_last / block;
   int kp[kMaxK];  // kept nodes one level up, ascending
   int nk = 1;
 #pragma unroll
@@ -255,7 +262,7 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void stage1_kernel(
     const int m_child = lv.size[l - 2];
     const size_t child0 = head_rows + lv.off[l - 2];
 
-    if (m_child <= kDenseRows) {
+    if (kShared && m_child <= kDenseRows) {
       // Chunk c holds child rows 32c..32c+31, whose parents 8c..8c+7 are byte
       // c of the parent masks (written after the previous level's decision).
       // The workgroup scores every chunk that holds a kept parent of one of
@@ -332,15 +339,12 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void stage1_kernel(
                                        {&score_s[wave][0][(32 * 1 + col) / G], T}};
         const bool writer = (col % G) == 0;
         // One chunk: S = summaries x queries on MFMA from the LDS chunk, then
-        // the candidates' LSEs picked up into the slot arrays.
-        auto chunk = [&](int r0) __attribute__((always_inline)) {
+        // the candidates' LSEs picked up into the slot arrays.  byte[cb]: the
+        // column's kept parents among the chunk's 8.
+        auto chunk = [&](int r0, const uint32_t (&byte)[2]) __attribute__((always_inline)) {
           // Rows of this chunk: r0 + 8g + 4kh + i%4 (acc element 4g + i%4);
           // level-l candidates n = r0/2 + 4g + 2kh + m own rows 2n, 2n+1;
           // their parents p = r0/4 + 2g + kh (bits p0..p0+7 of the masks).
-          const int p0 = r0 >> 2;  // multiple of 8
-          uint32_t byte[2];
-#pragma unroll
-          for (int cb = 0; cb < 2; ++cb) byte[cb] = (mcol[cb][p0 >> 5] >> (p0 & 31)) & 0xffu;
           const bf16_t* arow = chunk_s + col * CROW + 8 * kh;
           f32x16_t acc[2] = {};
 #pragma unroll
@@ -390,10 +394,6 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void stage1_kernel(
             pickup(std::true_type{});
           else
             pickup(std::false_type{});
-          // Parents in chunks skipped by the workgroup are no kept parents of
-          // a ranking query, so the slot bases of those queries stay exact.
-#pragma unroll
-          for (int cb = 0; cb < 2; ++cb) base[cb] += __popc(byte[cb]);
         };
         // The next chunk's pieces are in flight while this one is scored.
         int c = pop();
@@ -406,9 +406,134 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void stage1_kernel(
           put();
           if (more) fetch(32 * cn);
           lds_barrier();  // this chunk is in LDS
-          chunk(32 * c);
+          // A wave none of whose columns keeps a parent here (large groups:
+          // few queries per wave) takes part in the loads only.  Parents in
+          // chunks skipped by the workgroup are no kept parents of a ranking
+          // query, so the slot bases of those queries stay exact.
+          const int p0 = 8 * c;
+          uint32_t byte[2];
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb) byte[cb] = (mcol[cb][p0 >> 5] >> (p0 & 31)) & 0xffu;
+          if (__ballot((byte[0] | byte[1]) != 0u) != 0) chunk(32 * c, byte);
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb) base[cb] += __popc(byte[cb]);
           if (!more) break;
           c = cn;
+        }
+      }
+      wave_lds_sync();
+    } else if (m_child <= kDenseRows) {
+      // Large groups (few queries per wave): each wave walks the chunks its
+      // own columns need, fetching the summary rows straight into MFMA
+      // operand registers, with no workgroup barriers.
+      if (__ballot(need) != 0) {
+        // Parent masks were written after the previous level's decision.
+        const int lim_last = cz ? (cur_last >> sh) : size_l - 1;
+        const int rows_needed = min(m_child, 2 * lim_last + 2);
+        int base[2] = {0, 0};
+        const Column<uint32_t> mcol[2] = {{&mask_s[wave][0][(32 * 0 + col) / G], T},
+                                          {&mask_s[wave][0][(32 * 1 + col) / G], T}};
+        const Column<float> scol[2] = {{&score_s[wave][0][(32 * 0 + col) / G], T},
+                                       {&score_s[wave][0][(32 * 1 + col) / G], T}};
+        const bool writer = (col % G) == 0;
+        // The next chunk at or after row r whose parents some query of the
+        // wave keeps (rows_needed when there is none).
+        auto next_chunk = [&](int r) __attribute__((always_inline)) {
+          for (; r < rows_needed; r += 32) {
+            const int p = r >> 2;
+            uint32_t any = 0;
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) any |= (mcol[cb][p >> 5] >> (p & 31)) & 0xffu;
+            if (__ballot(any != 0u) != 0) break;
+          }
+          return r;
+        };
+        // Summary rows r0 + col of a chunk (rows past the level end repeat its
+        // last row; their logits are never used: see the ragged-chunk masking).
+        uint4 hv[KSTEPS], lv4[KSTEPS];
+        auto fetch = [&](int r0) __attribute__((always_inline)) {
+          const int r = min(r0 + col, m_child - 1);
+          const bf16_t* hrow = phi + (child0 + r) * D + 8 * kh;
+          const bf16_t* lrow2 = plo + (child0 + r) * D + 8 * kh;
+#pragma unroll
+          for (int s = 0; s < KSTEPS; ++s) {
+            hv[s] = *reinterpret_cast<const uint4*>(hrow + 16 * s);
+            lv4[s] = *reinterpret_cast<const uint4*>(lrow2 + 16 * s);
+          }
+        };
+        // One chunk: S = summaries x queries on MFMA (hv, lv4 hold its rows),
+        // then the candidates' LSEs picked up into the slot arrays.
+        auto chunk = [&](int r0, auto&& between) __attribute__((always_inline)) {
+          // Rows of this chunk: r0 + 8g + 4kh + i%4 (acc element 4g + i%4);
+          // level-l candidates n = r0/2 + 4g + 2kh + m own rows 2n, 2n+1;
+          // their parents p = r0/4 + 2g + kh (bits p0..p0+7 of the masks).
+          const int p0 = r0 >> 2;  // multiple of 8
+          uint32_t byte[2];
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb) byte[cb] = (mcol[cb][p0 >> 5] >> (p0 & 31)) & 0xffu;
+          f32x16_t acc[2] = {};
+#pragma unroll
+          for (int s = 0; s < KSTEPS; ++s) {
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) {
+              acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lv4[s]), bq[cb][s],
+                                                                acc[cb], 0, 0, 0);
+              acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(hv[s]), bq[cb][s],
+                                                                acc[cb], 0, 0, 0);
+            }
+          }
+          between();
+          auto pickup = [&](auto full_tag) {
+            constexpr bool kFull = decltype(full_tag)::value;  // every row of the chunk exists
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) {
+#pragma unroll
+              for (int g = 0; g < 4; ++g) {
+                const int pb = 2 * g + kh;
+                const bool has = writer & ((byte[cb] >> pb) & 1u);
+                const int pslot = base[cb] + __popc(byte[cb] & ((1u << pb) - 1u));
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                  const int n = (r0 >> 1) + 4 * g + 2 * kh + m;
+                  const float z0 = acc[cb][4 * g + 2 * m];
+                  float z1 = acc[cb][4 * g + 2 * m + 1];
+                  bool w = has;
+                  if (!kFull) {
+                    z1 = 2 * n + 1 < m_child ? z1 : neg_inf();
+                    w &= 2 * n < m_child;
+                  }
+                  const float mx = fmaxf(z0, z1), mn = fminf(z0, z1);
+                  float v =
+                      fmaf(mx, scale_log2, fast_log2(1.f + fast_exp2((mn - mx) * scale_log2)));
+                  if (G >= 2) v += __shfl_xor(v, 1, kWave);
+                  if (G >= 4) v += __shfl_xor(v, 2, kWave);
+                  if (G >= 8) v += __shfl_xor(v, 4, kWave);
+                  if (G >= 16) v += __shfl_xor(v, 8, kWave);
+                  scol[cb][w ? 2 * pslot + m : kSlots] = v;
+                }
+              }
+              base[cb] += __popc(byte[cb]);
+            }
+          };
+          if (r0 + 32 <= m_child)
+            pickup(std::true_type{});
+          else
+            pickup(std::false_type{});
+        };
+        if constexpr (G == 1) {
+          // the next chunk's rows are in flight while this one is picked up
+          int r0 = next_chunk(0);
+          if (r0 < rows_needed) fetch(r0);
+          while (r0 < rows_needed) {
+            const int rn = next_chunk(r0 + 32);
+            chunk(r0, [&] { if (rn < rows_needed) fetch(rn); });
+            r0 = rn;
+          }
+        } else {  // larger groups need the registers: fetch, then compute
+          for (int r0 = next_chunk(0); r0 < rows_needed; r0 = next_chunk(r0 + 32)) {
+            fetch(r0);
+            chunk(r0, [] {});
+          }
         }
       }
       wave_lds_sync();

@@ -23,7 +23,8 @@
 // Stage 1 (levels L..3).  One wavefront owns 64 (query, head) columns.  For a
 // level whose children fit in kDenseRows rows, the workgroup's waves walk
 // together over the 32-row chunks of child rows needed by any of their
-// columns: each chunk is loaded once, coalesced, into LDS (the next one is in
+// columns (with 16 heads per group, 4 queries per wave, each wave walks the
+// chunks of its own columns instead): each chunk is loaded once, coalesced, into LDS (the next one is in
 // flight in registers meanwhile), and every wave computes its logits on the
 // matrix cores (32 rows x 64 columns per step; bf16 hi/lo planes of the fp32
 // summaries, so each product is exact and accumulation is fp32).  While the

@@ -22,6 +22,7 @@
 namespace pisa {
 namespace bucket {
 
+constexpr int kSortThreads = 1024;    // threads per count/scatter workgroup
 constexpr int kRowsPerGroup = 512;    // least rows of one head per count/scatter workgroup
 constexpr int kMaxRowsPerGroup = 2048;
 constexpr int kMaxLocalBuckets = 8192;  // LDS histogram limit (two int arrays = 64 KB)
@@ -34,7 +35,7 @@ __global__ void fill_zero_kernel(int* __restrict__ p, int n) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
 }
 
-__global__ __launch_bounds__(256) void count_kernel(const int* __restrict__ node,
+__global__ __launch_bounds__(kSortThreads) void count_kernel(const int* __restrict__ node,
                                                     int* __restrict__ counts, int n_tok, int topk,
                                                     int m, int rpg) {
   extern __shared__ int hist[];  // [m]
@@ -154,7 +155,7 @@ inline size_t scan_lds_bytes(int n_buckets) {
   return n_buckets <= kScanLds ? sizeof(int) * (size_t)n_buckets : 0;
 }
 
-__global__ __launch_bounds__(256) void scatter_kernel(const int* __restrict__ node,
+__global__ __launch_bounds__(kSortThreads) void scatter_kernel(const int* __restrict__ node,
                                                       int* __restrict__ cursors,
                                                       int* __restrict__ pairs,
                                                       int* __restrict__ inv, int n_tok, int topk,
@@ -428,7 +429,7 @@ inline hipError_t sort_pairs(const int* node, int batch_heads, int n_tok, int to
     hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for(n_buckets)), dim3(256), 0, st, counts,
                        n_buckets);
     if (local)
-      hipLaunchKernelGGL(count_kernel, grid, dim3(256), sizeof(int) * m, st, node, counts, n_tok,
+      hipLaunchKernelGGL(count_kernel, grid, dim3(kSortThreads), sizeof(int) * m, st, node, counts, n_tok,
                          topk, m, rpg);
     else
       hipLaunchKernelGGL(count_global_kernel, dim3(grid_for(n_slots)), dim3(256), 0, st, node,
@@ -437,7 +438,7 @@ inline hipError_t sort_pairs(const int* node, int batch_heads, int n_tok, int to
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), scan_lds_bytes(n_buckets), st, counts,
                      offsets, cursors, item_offsets, n_buckets, per_item);
   if (local)
-    hipLaunchKernelGGL(scatter_kernel, grid, dim3(256), 2 * sizeof(int) * m, st, node, cursors,
+    hipLaunchKernelGGL(scatter_kernel, grid, dim3(kSortThreads), 2 * sizeof(int) * m, st, node, cursors,
                        pairs, inv, n_tok, topk, m, rpg);
   else
     hipLaunchKernelGGL(scatter_global_kernel, dim3(grid_for(n_slots)), dim3(256), 0, st, node,

@@ -12,9 +12,12 @@ the group's heads, with the same forcing), on sampled rows:
 * retained attention mass and its ratio to the reference set's mass;
 * needle hit rate: how often the needle block is selected at its target row.
 
-The test asserts sanity only (values in range, the reference and BSA finding
-the needles); the measured numbers are printed, and written as JSON to the
-path in the PISA_QUALITY_OUT environment variable when it is set.
+The test asserts the metrics' ranges, the reference and BSA finding the
+needles, and guards the measured quality with margins: PISA's recall, mass
+ratio and needle hits at the N(0,1/d) scale, and with N(0,1) entries the
+ordering of Table 7 (PISA above PISA-1, PISA-2 not below it).  The measured
+numbers are printed, and written as JSON to the path in the PISA_QUALITY_OUT
+environment variable when it is set.
 """
 import json
 import math
@@ -107,16 +110,26 @@ def _check(res, needles_clear=True):
         assert res[name]["recall"] > 0.0
 
 
+def _guard_small_scale(res, min_recall):
+    # measured: recall 0.77 (c2) / 0.59 (c3), mass ratio 0.9998 / 0.9996,
+    # every needle found; the margins leave room for ties broken otherwise
+    assert res["pisa"]["recall"] >= min_recall, res["pisa"]
+    assert res["pisa"]["mass_ratio"] >= 0.999, res["pisa"]
+    assert res["pisa"]["needle_hit_rate"] >= 0.9, res["pisa"]
+
+
 def test_quality_needles_c2():
     res = _quality("c2", heads=range(0, 16, 2), rows_per_head=24)
     _report(res)
     _check(res)
+    _guard_small_scale(res, 0.65)
 
 
 def test_quality_needles_c3():
     res = _quality("c3", heads=range(0, 8, 2), rows_per_head=16, seed_rows=1)
     _report(res)
     _check(res)
+    _guard_small_scale(res, 0.5)
 
 
 def test_quality_needles_c2_unit_variance():
@@ -126,5 +139,11 @@ def test_quality_needles_c2_unit_variance():
     res = _quality("c2", heads=range(0, 16, 4), rows_per_head=24, seed_rows=2, recipe="unit")
     _report(res)
     # with N(0,1) noise the planted blocks no longer stand out from the
-    # strongest random blocks, so only the metrics' ranges are checked
+    # strongest random blocks, so the needles are not required
     _check(res, needles_clear=False)
+    # Table 7's ordering (measured recall 0.653 / 0.639 / 0.570, mass ratio
+    # 0.966 / 0.962 / 0.946 for PISA / PISA-2 / PISA-1)
+    assert res["pisa"]["recall"] >= res["pisa1"]["recall"] + 0.03, res
+    assert res["pisa2"]["recall"] >= res["pisa1"]["recall"], res
+    assert res["pisa"]["mass_ratio"] >= res["pisa1"]["mass_ratio"], res
+    assert res["pisa"]["mass_ratio"] >= 0.95, res["pisa"]

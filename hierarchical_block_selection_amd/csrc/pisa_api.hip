@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 #include <mutex>
 #include <string>
 
@@ -107,10 +108,21 @@ size_t ws_bytes_for(const pisa::LaunchShape& s, int op) {
   }
 }
 
+// The kernels read and write these tensors (and the workspace) with 16-byte
+// vector accesses: a pointer off that alignment is refused before any launch.
+bool misaligned(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (reinterpret_cast<uintptr_t>(p) & 15u) return true;
+  return false;
+}
+
+int fail_align() { return fail(PISA_ERR_INVALID, "tensor pointer not 16-byte aligned"); }
+
 int check_ws(const pisa::LaunchShape& s, int op, const void* ws, size_t ws_bytes) {
   const size_t need = ws_bytes_for(s, op);
   if (need > 0 && (ws == nullptr || ws_bytes < need))
     return fail(PISA_ERR_WORKSPACE, "workspace missing or too small");
+  if (need > 0 && misaligned({ws})) return fail(PISA_ERR_INVALID, "workspace not 16-byte aligned");
   return PISA_OK;
 }
 
@@ -148,6 +160,7 @@ int pisa_build_pyramid(const pisa_problem* problem, const void* k, float* pyrami
   int rc = check_problem(problem, PISA_OP_PYRAMID, &s);
   if (rc != PISA_OK) return rc;
   if (!k || !pyramid) return fail(PISA_ERR_INVALID, "null tensor pointer");
+  if (misaligned({k, pyramid})) return fail_align();
   const hipError_t e = pisa::launch_pyramid(s, k, pyramid, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PISA_OK : fail_hip(e, "pisa_build_pyramid");
 }
@@ -159,6 +172,7 @@ int pisa_select(const pisa_problem* problem, const void* q, const void* k, const
   int rc = check_problem(problem, PISA_OP_SELECT, &s);
   if (rc != PISA_OK) return rc;
   if (!q || !k || !pyramid || !block_idx) return fail(PISA_ERR_INVALID, "null tensor pointer");
+  if (misaligned({q, k, pyramid})) return fail_align();
   if (strategy < PISA_SELECT_AUTO || strategy > PISA_SELECT_TWO_STAGE)
     return fail(PISA_ERR_INVALID, "bad strategy");
   bool two_stage = false;
@@ -225,6 +239,7 @@ int pisa_select_noalloc(const pisa_problem* problem, const void* q, const void* 
   int rc = check_problem(problem, PISA_OP_SELECT, &s);
   if (rc != PISA_OK) return rc;
   if (!q || !k || !pyramid || !block_idx) return fail(PISA_ERR_INVALID, "null tensor pointer");
+  if (misaligned({q, k, pyramid})) return fail_align();
   if (strategy < PISA_SELECT_AUTO || strategy > PISA_SELECT_TWO_STAGE)
     return fail(PISA_ERR_INVALID, "bad strategy");
   bool two_stage = false;
@@ -263,6 +278,7 @@ int pisa_bsa_select(const pisa_problem* problem, const void* q, const float* pyr
   int rc = check_problem(problem, PISA_OP_BSA, &s);
   if (rc != PISA_OK) return rc;
   if (!q || !pyramid || !block_idx) return fail(PISA_ERR_INVALID, "null tensor pointer");
+  if (misaligned({q, pyramid})) return fail_align();
   if ((rc = check_ws(s, PISA_OP_BSA, ws, ws_bytes)) != PISA_OK) return rc;
   const hipError_t e = pisa::launch_bsa(s, q, pyramid, block_idx, block_score, ws,
                                         static_cast<hipStream_t>(stream));
@@ -276,6 +292,7 @@ int pisa_block_sparse_attn(const pisa_problem* problem, const void* q, const voi
   int rc = check_problem(problem, PISA_OP_ATTN, &s);
   if (rc != PISA_OK) return rc;
   if (!q || !k || !v || !block_idx || !out) return fail(PISA_ERR_INVALID, "null tensor pointer");
+  if (misaligned({q, k, v, out})) return fail_align();
   if ((rc = check_ws(s, PISA_OP_ATTN, ws, ws_bytes)) != PISA_OK) return rc;
   const hipError_t e = pisa::launch_attn(s, q, k, v, block_idx, out, row_lse, ws,
                                          static_cast<hipStream_t>(stream));
@@ -291,6 +308,7 @@ int pisa_block_sparse_attn_backward(const pisa_problem* problem, const void* q, 
   if (rc != PISA_OK) return rc;
   if (!q || !k || !v || !block_idx || !out || !row_lse || !dout || !dq || !dk || !dv)
     return fail(PISA_ERR_INVALID, "null tensor pointer");
+  if (misaligned({q, k, v, out, dout, dq, dk, dv})) return fail_align();
   if ((rc = check_ws(s, PISA_OP_ATTN_BWD, ws, ws_bytes)) != PISA_OK) return rc;
   const hipError_t e = pisa::launch_attn_bwd(s, q, k, v, block_idx, out, row_lse, dout, dq, dk, dv,
                                              ws, static_cast<hipStream_t>(stream));
@@ -303,6 +321,7 @@ int pisa_pyramid_append(const pisa_problem* problem, const int32_t* cache_len,
   const int rc = check_problem(problem, PISA_OP_PYRAMID, &s);
   if (rc != PISA_OK) return rc;
   if (!cache_len || !k_cache || !pyramid) return fail(PISA_ERR_INVALID, "null tensor pointer");
+  if (misaligned({k_cache, pyramid})) return fail_align();
   const hipError_t e =
       pisa::launch_pyramid_append(s, cache_len, k_cache, pyramid, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PISA_OK : fail_hip(e, "pisa_pyramid_append");
@@ -317,6 +336,7 @@ int pisa_decode_step(const pisa_problem* problem, const int32_t* cache_len, cons
   if (rc != PISA_OK) return rc;
   if (!cache_len || !q || !k_cache || !v_cache || !pyramid || !block_idx || !out)
     return fail(PISA_ERR_INVALID, "null tensor pointer");
+  if (misaligned({q, k_cache, v_cache, pyramid, out})) return fail_align();
   if ((rc = check_ws(s, PISA_OP_DECODE, ws, ws_bytes)) != PISA_OK) return rc;
   const hipError_t e = pisa::launch_decode(s, cache_len, q, k_cache, v_cache, pyramid, block_idx,
                                            block_score, out, row_lse, ws,

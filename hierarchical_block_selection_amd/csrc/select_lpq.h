@@ -159,15 +159,31 @@ __device__ __forceinline__ void compact_kept(uint32_t km, Col row, NodeOf node_o
 
 // Split fp32 pyramid values into bf16 hi/lo planes: x = hi + lo + r with
 // |r| <= 2^-16 |x|, so that a bf16 MFMA over both planes reproduces an fp32
-// dot product to that accuracy.
+// dot product to that accuracy.  Stage 1 reads child rows of levels 2 and up
+// only, so each head's level 1 (its first skip_rows rows of row_len values)
+// is left out; 8 values per thread and step.
 __global__ void split_planes_kernel(const float* __restrict__ pyr, bf16_t* __restrict__ hi,
-                                    bf16_t* __restrict__ lo, size_t n) {
+                                    bf16_t* __restrict__ lo, int heads, size_t head_len,
+                                    size_t skip) {
+  const size_t per_head = (head_len - skip) / 8;  // 8-value groups split per head
+  const size_t n = per_head * heads;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (size_t)gridDim.x * blockDim.x) {
-    const float x = pyr[i];
-    const uint16_t h = f32_to_bf16(x);
-    hi[i] = h;
-    lo[i] = f32_to_bf16(x - bf16_to_f32(h));
+    const size_t e = (i / per_head) * head_len + skip + 8 * (i % per_head);
+    const float4 x0 = *reinterpret_cast<const float4*>(pyr + e);
+    const float4 x1 = *reinterpret_cast<const float4*>(pyr + e + 4);
+    const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    uint32_t h2[4], l2[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint16_t ha = f32_to_bf16(x[2 * j]), hb = f32_to_bf16(x[2 * j + 1]);
+      const uint16_t la = f32_to_bf16(x[2 * j] - bf16_to_f32(ha));
+      const uint16_t lb = f32_to_bf16(x[2 * j + 1] - bf16_to_f32(hb));
+      h2[j] = uint32_t(ha) | (uint32_t(hb) << 16);
+      l2[j] = uint32_t(la) | (uint32_t(lb) << 16);
+    }
+    *reinterpret_cast<uint4*>(hi + e) = make_uint4(h2[0], h2[1], h2[2], h2[3]);
+    *reinterpret_cast<uint4*>(lo + e) = make_uint4(l2[0], l2[1], l2[2], l2[3]);
   }
 }
 

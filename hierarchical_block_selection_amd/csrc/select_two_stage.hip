@@ -642,11 +642,14 @@ hipError_t stage1_lpq_launch(const LaunchShape& s, const void* q, const float* p
                              hipStream_t st) {
   constexpr int T = kWave / G;  // queries per wave
   dim3 grid((s.seq_len + T * lpq::kWaves - 1) / (T * lpq::kWaves), s.batch * s.heads_kv);
-  const size_t n = (size_t)s.batch * s.heads_kv * s.lv.rows * D;
   {
     prof::Scope ps("select_split_planes", st);
-    hipLaunchKernelGGL(lpq::split_planes_kernel, dim3(bucket::grid_for(n)), dim3(256), 0, st,
-                       pyr, w.plane_hi, w.plane_lo, n);
+    const int heads = s.batch * s.heads_kv;
+    const size_t head_len = (size_t)s.lv.rows * D, skip = (size_t)s.lv.size[0] * D;
+    const size_t groups = (head_len - skip) / 8 * heads;
+    if (groups > 0)
+      hipLaunchKernelGGL(lpq::split_planes_kernel, dim3(bucket::grid_for(groups)), dim3(256), 0, st,
+                         pyr, w.plane_hi, w.plane_lo, heads, head_len, skip);
   }
   prof::Scope ps("select_stage1", st);
   hipLaunchKernelGGL((lpq::stage1_kernel<D, G>), grid, dim3(lpq::kWaves * kWave), 0, st,

@@ -14,7 +14,12 @@
  * ----------------------------------------
  * - All functions are extern "C", never throw, and return a pisa_status.
  * - Every tensor argument is a DEVICE pointer to contiguous row-major memory,
- *   16-byte aligned, owned by the caller.  The library allocates no device or
+ *   16-byte aligned, owned by the caller.  The alignment is checked for the
+ *   tensors the kernels access with 16-byte vector loads and stores (Q, K, V,
+ *   O, the pyramid, the caches, the gradients and the workspace): an address
+ *   off it returns PISA_ERR_INVALID before any launch; block_idx,
+ *   block_score, row_lse and cache_len need only their elements' alignment.
+ *   The library allocates no device or
  *   host memory and keeps no state between calls; calls are re-entrant.  The
  *   one exception is pisa_select_noalloc, which uses a fixed device array of
  *   the library's (see there).

@@ -118,8 +118,7 @@ def test_null_pointers_and_workspace_rejected():
     L = lib()
     p = problem()
     pp = ctypes.byref(p)
-    dummy = ctypes.create_string_buffer(64)
-    ptr = ctypes.cast(dummy, ctypes.c_void_p)
+    ptr = ctypes.c_void_p(4096)  # never dereferenced: validation fails first
     assert L.pisa_build_pyramid(None, ptr, ptr, None) == _lib.PISA_ERR_INVALID
     assert L.pisa_build_pyramid(pp, None, ptr, None) == _lib.PISA_ERR_INVALID
     assert L.pisa_pyramid_append(pp, None, ptr, ptr, None) == _lib.PISA_ERR_INVALID
@@ -146,6 +145,44 @@ def test_null_pointers_and_workspace_rejected():
                              None) == _lib.PISA_ERR_UNSUPPORTED
     assert L.pisa_workspace_bytes(pp, 99, ctypes.byref(sz)) == _lib.PISA_ERR_INVALID
     assert L.pisa_status_string(_lib.PISA_ERR_WORKSPACE) == b"workspace missing or too small"
+
+
+def test_misaligned_pointers_rejected():
+    """Tensors the kernels access with 16-byte vector loads and stores (Q, K, V,
+    O, the pyramid, the caches, the gradients, the workspace) must be 16-byte
+    aligned: every entry point refuses an address off that alignment before any
+    device call (this runs without a GPU)."""
+    L = lib()
+    p = problem()
+    pp = ctypes.byref(p)
+    ok = ctypes.c_void_p(4096)  # never dereferenced: validation fails first
+    bad = ctypes.c_void_p(4096 + 8)
+    inv = _lib.PISA_ERR_INVALID
+
+    def refused(rc):
+        return rc == inv and b"aligned" in L.pisa_last_error()
+
+    assert refused(L.pisa_build_pyramid(pp, bad, ok, None))
+    assert refused(L.pisa_build_pyramid(pp, ok, bad, None))
+    assert refused(L.pisa_select(pp, bad, ok, ok, ok, None, 0, None, 0, None))
+    assert refused(L.pisa_select(pp, ok, ok, bad, ok, None, 0, None, 0, None))
+    assert refused(L.pisa_select_noalloc(pp, ok, bad, ok, ok, None, 0, None))
+    assert refused(L.pisa_bsa_select(pp, bad, ok, ok, None, ok, 1 << 40, None))
+    assert refused(L.pisa_block_sparse_attn(pp, ok, ok, bad, ok, ok, None, ok, 1 << 40, None))
+    assert refused(L.pisa_block_sparse_attn(pp, ok, ok, ok, ok, bad, None, ok, 1 << 40, None))
+    assert refused(L.pisa_block_sparse_attn_backward(pp, ok, ok, ok, ok, ok, ok, ok, ok, bad, ok,
+                                                     ok, 1 << 40, None))
+    assert refused(L.pisa_pyramid_append(pp, ok, bad, ok, None))
+    assert refused(L.pisa_decode_step(pp, ok, ok, ok, ok, bad, ok, None, ok, None, ok, 1 << 40,
+                                      None))
+    # the workspace too
+    sz = ctypes.c_size_t()
+    assert L.pisa_workspace_bytes(pp, _lib.PISA_OP_ATTN, ctypes.byref(sz)) == 0
+    assert sz.value > 0
+    assert refused(L.pisa_block_sparse_attn(pp, ok, ok, ok, ok, ok, None, bad, sz.value, None))
+    # index and score arrays need only their elements' alignment
+    assert L.pisa_bsa_select(pp, ok, ok, ctypes.c_void_p(4096 + 4), None, ok, 1,
+                             None) == _lib.PISA_ERR_WORKSPACE
 
 
 def test_binding_fails_loudly_without_library(tmp_path):

@@ -69,8 +69,8 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ coun
                                                     int* __restrict__ cursors,
                                                     int* __restrict__ item_offsets, int n_buckets,
                                                     int per_item) {
-  __shared__ int part_pairs[1024];
-  __shared__ int part_items[1024];
+  __shared__ int part_pairs[1024 / kWave];  // per-wave totals
+  __shared__ int part_items[1024 / kWave];
   extern __shared__ int c_s[];  // [n_buckets] when n_buckets <= kScanLds
   const bool staged = n_buckets <= kScanLds;
   const int tid = threadIdx.x;
@@ -95,22 +95,36 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ coun
         si += (c8[k] + per_item - 1) / per_item;
       }
   }
-  part_pairs[tid] = sp;
-  part_items[tid] = si;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    const int a = tid >= o ? part_pairs[tid - o] : 0;
-    const int c = tid >= o ? part_items[tid - o] : 0;
-    __syncthreads();
-    part_pairs[tid] += a;
-    part_items[tid] += c;
-    __syncthreads();
+  // Exclusive prefix over the 1024 threads: inclusive scans inside each wave
+  // (shuffles), then the 16 wave totals through LDS (one barrier).
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  int ip = sp, ii = si;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int a = __shfl_up(ip, o, kWave), c = __shfl_up(ii, o, kWave);
+    if (lane >= o) {
+      ip += a;
+      ii += c;
+    }
   }
-  int pos = tid ? part_pairs[tid - 1] : 0;
-  int ipos = tid ? part_items[tid - 1] : 0;
+  if (lane == kWave - 1) {
+    part_pairs[wave] = ip;
+    part_items[wave] = ii;
+  }
+  __syncthreads();
+  int pos = ip - sp, ipos = ii - si;
+  int tot_p = 0, tot_i = 0;
+#pragma unroll
+  for (int w = 0; w < 1024 / kWave; ++w) {
+    const int a = part_pairs[w], c = part_items[w];
+    pos += w < wave ? a : 0;
+    ipos += w < wave ? c : 0;
+    tot_p += a;
+    tot_i += c;
+  }
   if (tid == 1023) {
-    offsets[n_buckets] = part_pairs[1023];
-    item_offsets[n_buckets] = part_items[1023];
+    offsets[n_buckets] = tot_p;
+    item_offsets[n_buckets] = tot_i;
   }
   if (!staged) {
     for (int i = lo; i < hi; ++i) {

@@ -126,6 +126,66 @@ __device__ __forceinline__ uint32_t top_slots(int n_valid, int topk, uint32_t fm
   return km;
 }
 
+// Kept slots of a ranked level, decided by the G lanes of one query's group
+// (G >= 2: lane sub holds slots sub * S .. sub * S + S - 1, S = 32 / G, scores
+// s[i]).  The rank keys are those of top_slots; a bitonic sort of the 32 keys
+// runs across the group (compare-exchanges between lanes through xor
+// shuffles, inside a lane in registers), leaving rank e at lane e / S,
+// element e % S; the kept slots' bits are OR-ed over the group.  The keys are
+// distinct, so the kept set equals top_slots'.  Every lane of the group
+// returns the same mask.
+template <int G>
+__device__ __forceinline__ uint32_t top_slots_group(int n_valid, int topk, uint32_t fm,
+                                                    const float (&s)[kSlots / G], int sub) {
+  constexpr int S = kSlots / G;
+  const uint32_t rm = prefix_mask(n_valid) & ~fm;
+  const int keep_n = topk - __popc(fm);
+  float smax = neg_inf();
+#pragma unroll
+  for (int i = 0; i < S; ++i) smax = ((rm >> (sub * S + i)) & 1u) ? fmaxf(smax, s[i]) : smax;
+#pragma unroll
+  for (int o = 1; o < G; o <<= 1) smax = fmaxf(smax, __shfl_xor(smax, o, kWave));
+  uint32_t key[S];
+#pragma unroll
+  for (int i = 0; i < S; ++i) {
+    const int j = sub * S + i;
+    key[i] = ((rm >> j) & 1u) ? rank_key_rel(s[i], smax, j) : 0u;
+  }
+  // Descending bitonic sort over element e = sub * S + i.
+#pragma unroll
+  for (int k = 2; k <= kSlots; k <<= 1) {
+#pragma unroll
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      if (jj < S) {
+#pragma unroll
+        for (int i = 0; i < S; ++i) {
+          if (i & jj) continue;
+          const int e = sub * S + i;
+          const bool desc = (e & k) == 0;
+          const uint32_t a = key[i], b = key[i | jj];
+          key[i] = desc ? max(a, b) : min(a, b);
+          key[i | jj] = desc ? min(a, b) : max(a, b);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < S; ++i) {
+          const int e = sub * S + i;
+          const uint32_t other = (uint32_t)__shfl_xor((int)key[i], jj / S, kWave);
+          const bool keep_max = ((e & jj) == 0) == ((e & k) == 0);
+          key[i] = keep_max ? max(key[i], other) : min(key[i], other);
+        }
+      }
+    }
+  }
+  uint32_t km = fm;
+#pragma unroll
+  for (int i = 0; i < S; ++i)
+    km |= (sub * S + i < keep_n) ? (1u << (31 - (key[i] & 31u))) : 0u;
+#pragma unroll
+  for (int o = 1; o < G; o <<= 1) km |= (uint32_t)__shfl_xor((int)km, o, kWave);
+  return km;
+}
+
 // A query's column of a slot-major LDS array.
 template <typename E>
 struct Column {
@@ -596,12 +656,31 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void stage1_kernel(
 
     // Decision for this lane's query.
     uint32_t km = prefix_mask(n_valid);
-    if (need) {
-      float sc[kSlots];
+    if constexpr (G == 1) {
+      if (need) {
+        float sc[kSlots];
 #pragma unroll
-      for (int j = 0; j < kSlots; ++j) sc[j] = srow[j];
+        for (int j = 0; j < kSlots; ++j) sc[j] = srow[j];
+        const bool prev_distinct = cur >= 1 && ((cur - 1) >> sh) != lim;
+        km = top_slots(n_valid, topk, forced_slots(n_valid, cz, fzon, prev_distinct), sc);
+      }
+    } else {
+      // T = 64 / G queries per wave: query qd is decided by lanes qd G ..
+      // qd G + G - 1 together instead of by lane qd alone.
       const bool prev_distinct = cur >= 1 && ((cur - 1) >> sh) != lim;
-      km = top_slots(n_valid, topk, forced_slots(n_valid, cz, fzon, prev_distinct), sc);
+      const uint32_t fm = need ? forced_slots(n_valid, cz, fzon, prev_distinct) : 0u;
+      const int qd = lane / G, sub = lane % G;
+      const int nv_g = __shfl(n_valid, qd, kWave);
+      const uint32_t fm_g = (uint32_t)__shfl((int)fm, qd, kWave);
+      uint32_t km_g = 0u;
+      if (__ballot(nv_g > topk) != 0) {
+        float s_loc[kSlots / G];
+#pragma unroll
+        for (int i = 0; i < kSlots / G; ++i) s_loc[i] = score_s[wave][sub * (kSlots / G) + i][qd];
+        km_g = top_slots_group<G>(nv_g, topk, fm_g, s_loc, sub);
+      }
+      const uint32_t kq = (uint32_t)__shfl((int)km_g, lane < T ? lane * G : 0, kWave);
+      if (need) km = kq;
     }
     wave_lds_sync();
     compact_kept(km, lrow, [&](int j) { return 2 * kp[j >> 1] + (j & 1); });

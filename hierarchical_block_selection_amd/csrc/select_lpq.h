@@ -23,8 +23,7 @@
 // Stage 1 (levels L..3).  One wavefront owns 64 (query, head) columns.  For a
 // level whose children fit in kDenseRows rows, the workgroup's waves walk
 // together over the 32-row chunks of child rows needed by any of their
-// columns (with 16 heads per group, 4 queries per wave, each wave walks the
-// chunks of its own columns instead): each chunk is loaded once, coalesced, into LDS (the next one is in
+// columns: each chunk is loaded once, coalesced, into LDS (the next one is in
 // flight in registers meanwhile), and every wave computes its logits on the
 // matrix cores (32 rows x 64 columns per step; bf16 hi/lo planes of the fp32
 // summaries, so each product is exact and accumulation is fp32).  While the
@@ -32,8 +31,11 @@
 // sibling pair (eq. (7)), sums the group's heads (eq. (11)) and scatters the
 // scores of the pairs that are candidates of the column's query into that
 // query's slot array.  Candidacy and slot come from a bitmask of the query's
-// kept parents: slot = 2 * (#kept parents before) + child.  Larger levels
-// gather the candidates' children from the fp32 pyramid, one query at a time.
+// kept parents: slot = 2 * (#kept parents before) + child.  With 16 heads per
+// group (4 queries per wave) each wave instead packs the union of its
+// queries' kept parents, 8 to a 32-row tile, so that its work per level is
+// bounded by 4 K parents.  Larger levels gather the candidates' children from
+// the fp32 pyramid, one query at a time.
 //
 // Final (levels 2 and 1).  One lane per query reads its K kept level-3 nodes
 // and the stage-2 scores of their children, decides level 2 and then the
@@ -276,6 +278,8 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void stage1_kernel(
   __shared__ uint32_t mask_s[kWaves][kMaskWords][T];
   __shared__ __align__(16) bf16_t chunk_s[kShared ? 2 * 32 * CROW : 8];
   __shared__ uint32_t chunks_s[2][kWaves][2];
+  // The union of a wave's kept parents (few queries per wave only).
+  __shared__ int ulist_s[kWaves][kShared ? 1 : kWave];
 
   const int wave = threadIdx.x / kWave;
   const int lane = lane_id();
@@ -310,8 +314,6 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void stage1_kernel(
   const int t = t0 + lane;
   const bool dlane = lane < T && t < n_tok;
   const int cur = dlane ? t / block : 0;
-  const int t_last = min(t0 + T, n_tok) - 1;
-  const int cur_last = t_last / block;
   int kp[kMaxK];  // kept nodes one level up, ascending
   int nk = 1;
 #pragma unroll
@@ -500,116 +502,137 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void stage1_kernel(
       }
       wave_lds_sync();
     } else if (m_child <= kDenseRows) {
-      // Large groups (few queries per wave): each wave walks the chunks its
-      // own columns need, fetching the summary rows straight into MFMA
-      // operand registers, with no workgroup barriers.
-      if (__ballot(need) != 0) {
-        // Parent masks were written after the previous level's decision.
-        const int lim_last = cz ? (cur_last >> sh) : size_l - 1;
-        const int rows_needed = min(m_child, 2 * lim_last + 2);
-        int base[2] = {0, 0};
-        const Column<uint32_t> mcol[2] = {{&mask_s[wave][0][(32 * 0 + col) / G], T},
-                                          {&mask_s[wave][0][(32 * 1 + col) / G], T}};
-        const Column<float> scol[2] = {{&score_s[wave][0][(32 * 0 + col) / G], T},
-                                       {&score_s[wave][0][(32 * 1 + col) / G], T}};
-        const bool writer = (col % G) == 0;
-        // The next chunk at or after row r whose parents some query of the
-        // wave keeps (rows_needed when there is none).
-        auto next_chunk = [&](int r) __attribute__((always_inline)) {
-          for (; r < rows_needed; r += 32) {
-            const int p = r >> 2;
-            uint32_t any = 0;
+      if constexpr (!kShared) {
+        // Few queries per wave (T = 64 / G <= 4): the wave scores only the
+        // union of its ranking queries' kept parents, 8 parents to a 32-row
+        // MFMA tile (a parent's 4 grandchild rows are its two candidates'
+        // children), so a level costs it at most T K / 8 tiles whatever the
+        // level's size.  The parents are tiled in ascending order, so a
+        // query's slot base advances over its own kept parents in the same
+        // order as over the level's rows.
+        static_assert(T * kMaxK <= kWave && kMaskWords * 4 == kWave, "union of kept parents");
+        const uint32_t needers = (uint32_t)__ballot(need);  // query qi is lane qi
+        if (needers != 0u) {
+          // Union of the ranking queries' parent masks (written after the
+          // previous level's decision): lane x holds parents 8x .. 8x + 7.
+          uint32_t ub = 0u;
 #pragma unroll
-            for (int cb = 0; cb < 2; ++cb) any |= (mcol[cb][p >> 5] >> (p & 31)) & 0xffu;
-            if (__ballot(any != 0u) != 0) break;
+          for (int qi = 0; qi < T; ++qi)
+            ub |= ((needers >> qi) & 1u) ? (mask_s[wave][lane >> 2][qi] >> (8 * (lane & 3))) & 0xffu
+                                         : 0u;
+          // Union rank of lane x's first parent (exclusive prefix of the
+          // popcounts); the ascending union list.
+          const int cnt = __popc(ub);
+          int incl = cnt;
+#pragma unroll
+          for (int o = 1; o < kWave; o <<= 1) {
+            const int y = __shfl_up(incl, o, kWave);
+            incl += lane >= o ? y : 0;
           }
-          return r;
-        };
-        // Summary rows r0 + col of a chunk (rows past the level end repeat its
-        // last row; their logits are never used: see the ragged-chunk masking).
-        uint4 hv[KSTEPS], lv4[KSTEPS];
-        auto fetch = [&](int r0) __attribute__((always_inline)) {
-          const int r = min(r0 + col, m_child - 1);
-          const bf16_t* hrow = phi + (child0 + r) * D + 8 * kh;
-          const bf16_t* lrow2 = plo + (child0 + r) * D + 8 * kh;
+          const int rbase = incl - cnt;
+          const int n_union = __builtin_amdgcn_readlane(incl, kWave - 1);
 #pragma unroll
-          for (int s = 0; s < KSTEPS; ++s) {
-            hv[s] = *reinterpret_cast<const uint4*>(hrow + 16 * s);
-            lv4[s] = *reinterpret_cast<const uint4*>(lrow2 + 16 * s);
+          for (int j = 0; j < 8; ++j)
+            if ((ub >> j) & 1u) ulist_s[wave][rbase + __popc(ub & ((1u << j) - 1u))] = 8 * lane + j;
+          // A ranking query's kept parents as bits of their union ranks (its
+          // decision lane; at most 64 ranks).
+          uint32_t ur_lo = 0u, ur_hi = 0u;
+#pragma unroll
+          for (int i = 0; i < kMaxK; ++i) {
+            const int p = kp[i] & (8 * kWave - 1);
+            const int rb = __shfl(rbase, p >> 3, kWave);
+            const uint32_t bb = (uint32_t)__shfl((int)ub, p >> 3, kWave);
+            const int r = rb + __popc(bb & ((1u << (p & 7)) - 1u));
+            const uint32_t bit = (need && i < nk) ? 1u << (r & 31) : 0u;
+            ur_lo |= r < 32 ? bit : 0u;
+            ur_hi |= r < 32 ? 0u : bit;
           }
-        };
-        // One chunk: S = summaries x queries on MFMA (hv, lv4 hold its rows),
-        // then the candidates' LSEs picked up into the slot arrays.
-        auto chunk = [&](int r0, auto&& between) __attribute__((always_inline)) {
-          // Rows of this chunk: r0 + 8g + 4kh + i%4 (acc element 4g + i%4);
-          // level-l candidates n = r0/2 + 4g + 2kh + m own rows 2n, 2n+1;
-          // their parents p = r0/4 + 2g + kh (bits p0..p0+7 of the masks).
-          const int p0 = r0 >> 2;  // multiple of 8
-          uint32_t byte[2];
+          wave_lds_sync();  // the union list is complete
+          // Column c = 32 cb + col belongs to query c / G.
+          uint32_t ur[2][2];
 #pragma unroll
-          for (int cb = 0; cb < 2; ++cb) byte[cb] = (mcol[cb][p0 >> 5] >> (p0 & 31)) & 0xffu;
-          f32x16_t acc[2] = {};
+          for (int cb = 0; cb < 2; ++cb) {
+            const int qc = (32 * cb + col) / G;
+            ur[cb][0] = (uint32_t)__shfl((int)ur_lo, qc, kWave);
+            ur[cb][1] = (uint32_t)__shfl((int)ur_hi, qc, kWave);
+          }
+          const Column<float> scol[2] = {{&score_s[wave][0][(32 * 0 + col) / G], T},
+                                         {&score_s[wave][0][(32 * 1 + col) / G], T}};
+          const bool writer = (col % G) == 0;
+          int base[2] = {0, 0};
+          const int n_tiles = (n_union + 7) >> 3;
+          for (int tt = 0; tt < n_tiles; ++tt) {
+            // Tile row col: union parent 8 tt + col / 4 (past the union's end
+            // its last parent, which no column keeps here), child row
+            // 4 p + col % 4 (rows past the level end repeat its last row;
+            // their logits are masked below).
+            const int pr = ulist_s[wave][min(8 * tt + (col >> 2), n_union - 1)];
+            const int r = min(4 * pr + (col & 3), m_child - 1);
+            const bf16_t* hrow = phi + (child0 + r) * D + 8 * kh;
+            const bf16_t* lrow2 = plo + (child0 + r) * D + 8 * kh;
+            uint4 hv[KSTEPS], lv4[KSTEPS];
 #pragma unroll
-          for (int s = 0; s < KSTEPS; ++s) {
-#pragma unroll
-            for (int cb = 0; cb < 2; ++cb) {
-              acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lv4[s]), bq[cb][s],
-                                                                acc[cb], 0, 0, 0);
-              acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(hv[s]), bq[cb][s],
-                                                                acc[cb], 0, 0, 0);
+            for (int s = 0; s < KSTEPS; ++s) {
+              hv[s] = *reinterpret_cast<const uint4*>(hrow + 16 * s);
+              lv4[s] = *reinterpret_cast<const uint4*>(lrow2 + 16 * s);
             }
-          }
-          between();
-          auto pickup = [&](auto full_tag) {
-            constexpr bool kFull = decltype(full_tag)::value;  // every row of the chunk exists
+            // The tile's last parent is its largest.
+            const int pmax = ulist_s[wave][min(8 * tt + 7, n_union - 1)];
+            uint32_t byte[2];
 #pragma unroll
-            for (int cb = 0; cb < 2; ++cb) {
+            for (int cb = 0; cb < 2; ++cb)
+              byte[cb] = (((tt >> 2) ? ur[cb][1] : ur[cb][0]) >> (8 * (tt & 3))) & 0xffu;
+            f32x16_t acc[2] = {};
 #pragma unroll
-              for (int g = 0; g < 4; ++g) {
-                const int pb = 2 * g + kh;
-                const bool has = writer & ((byte[cb] >> pb) & 1u);
-                const int pslot = base[cb] + __popc(byte[cb] & ((1u << pb) - 1u));
+            for (int s = 0; s < KSTEPS; ++s) {
 #pragma unroll
-                for (int m = 0; m < 2; ++m) {
-                  const int n = (r0 >> 1) + 4 * g + 2 * kh + m;
-                  const float z0 = acc[cb][4 * g + 2 * m];
-                  float z1 = acc[cb][4 * g + 2 * m + 1];
-                  bool w = has;
-                  if (!kFull) {
-                    z1 = 2 * n + 1 < m_child ? z1 : neg_inf();
-                    w &= 2 * n < m_child;
-                  }
-                  const float mx = fmaxf(z0, z1), mn = fminf(z0, z1);
-                  float v =
-                      fmaf(mx, scale_log2, fast_log2(1.f + fast_exp2((mn - mx) * scale_log2)));
-                  if (G >= 2) v += __shfl_xor(v, 1, kWave);
-                  if (G >= 4) v += __shfl_xor(v, 2, kWave);
-                  if (G >= 8) v += __shfl_xor(v, 4, kWave);
-                  if (G >= 16) v += __shfl_xor(v, 8, kWave);
-                  scol[cb][w ? 2 * pslot + m : kSlots] = v;
-                }
+              for (int cb = 0; cb < 2; ++cb) {
+                acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lv4[s]), bq[cb][s],
+                                                                  acc[cb], 0, 0, 0);
+                acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(hv[s]), bq[cb][s],
+                                                                  acc[cb], 0, 0, 0);
               }
-              base[cb] += __popc(byte[cb]);
             }
-          };
-          if (r0 + 32 <= m_child)
-            pickup(std::true_type{});
-          else
-            pickup(std::false_type{});
-        };
-        if constexpr (G == 1) {
-          // the next chunk's rows are in flight while this one is picked up
-          int r0 = next_chunk(0);
-          if (r0 < rows_needed) fetch(r0);
-          while (r0 < rows_needed) {
-            const int rn = next_chunk(r0 + 32);
-            chunk(r0, [&] { if (rn < rows_needed) fetch(rn); });
-            r0 = rn;
-          }
-        } else {  // larger groups need the registers: fetch, then compute
-          for (int r0 = next_chunk(0); r0 < rows_needed; r0 = next_chunk(r0 + 32)) {
-            fetch(r0);
-            chunk(r0, [] {});
+            // Lane rows 8g + 4kh + i%4 (acc element 4g + i%4) belong to tile
+            // parent pb = 2g + kh, fetched by lane 4 pb; candidate m = 0, 1
+            // of that parent owns its rows 2m, 2m + 1.
+            auto pickup = [&](auto full_tag) {
+              constexpr bool kFull = decltype(full_tag)::value;  // every row of the tile exists
+#pragma unroll
+              for (int cb = 0; cb < 2; ++cb) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                  const int pb = 2 * g + kh;
+                  const bool has = writer & ((byte[cb] >> pb) & 1u);
+                  const int pslot = base[cb] + __popc(byte[cb] & ((1u << pb) - 1u));
+                  const int pp = kFull ? 0 : __shfl(pr, 4 * pb, kWave);
+#pragma unroll
+                  for (int m = 0; m < 2; ++m) {
+                    const int n = 2 * pp + m;
+                    const float z0 = acc[cb][4 * g + 2 * m];
+                    float z1 = acc[cb][4 * g + 2 * m + 1];
+                    bool w = has;
+                    if (!kFull) {
+                      z1 = 2 * n + 1 < m_child ? z1 : neg_inf();
+                      w &= 2 * n < m_child;
+                    }
+                    const float mx = fmaxf(z0, z1), mn = fminf(z0, z1);
+                    float v =
+                        fmaf(mx, scale_log2, fast_log2(1.f + fast_exp2((mn - mx) * scale_log2)));
+                    if (G >= 2) v += __shfl_xor(v, 1, kWave);
+                    if (G >= 4) v += __shfl_xor(v, 2, kWave);
+                    if (G >= 8) v += __shfl_xor(v, 4, kWave);
+                    if (G >= 16) v += __shfl_xor(v, 8, kWave);
+                    scol[cb][w ? 2 * pslot + m : kSlots] = v;
+                  }
+                }
+                base[cb] += __popc(byte[cb]);
+              }
+            };
+            if (4 * pmax + 4 <= m_child)
+              pickup(std::true_type{});
+            else
+              pickup(std::false_type{});
           }
         }
       }

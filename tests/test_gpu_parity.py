@@ -334,6 +334,17 @@ def test_prefill_level2_beyond_dense_rows():
                              idx[0, 0].cpu().numpy(), rows, 64, True, prob.logit_scale, False)
 
 
+@pytest.mark.parametrize("n,d,k", [(65536, 64, 8), (131072, 64, 8), (32768, 128, 16)])
+def test_pages_latency_shape_g16(n, d, k):
+    """16 query heads per KV head (the pages' latency shape: d = 64, K = 8)
+    at lengths where each wave of the two-stage selector scores only the
+    union of its 4 queries' kept parents: unit entries, sampled rows bit-exact
+    past the margin, at least 60 rows compared."""
+    cfg = dict(batch=1, heads_q=16, heads_kv=1, seq_len=n, head_dim=d, block=64, topk=k,
+               dtype=torch.bfloat16, n_needles=0, seed=9100 + d + k)
+    run_and_compare(cfg, "unit", [(0, 0)], n_random=160, min_rows=60)
+
+
 def test_large_group_scores():
     """Peaked attention and large group-summed scores (queries N(0,64), keys
     N(0,1): group sums of several hundred nats over 16 query heads): the

@@ -20,22 +20,22 @@
 // current-path node lim is the last valid slot, the previous leaf's ancestor
 // is lim or lim - 1 (then the slot before), and node 0 is slot 0.
 //
-// Stage 1 (levels L..3).  One wavefront owns 64 (query, head) columns.  For a
-// level whose children fit in kDenseRows rows, the workgroup's waves walk
-// together over the 32-row chunks of child rows needed by any of their
-// columns: each chunk is loaded once, coalesced, into LDS (the next one is in
-// flight in registers meanwhile), and every wave computes its logits on the
-// matrix cores (32 rows x 64 columns per step; bf16 hi/lo planes of the fp32
-// summaries, so each product is exact and accumulation is fp32).  While the
-// logits are still in the MFMA register layout it forms the log-sum-exp of every
-// sibling pair (eq. (7)), sums the group's heads (eq. (11)) and scatters the
+// Stage 1 (levels L..3).  One wavefront owns 64 (query, head) columns.  A
+// level's child rows are taken in windows of kDenseRows rows.  In a window
+// the workgroup's waves walk together over the 32-row chunks of child rows
+// needed by any of their columns: each chunk is loaded once, coalesced, into
+// LDS (the next one is in flight in registers meanwhile), and every wave
+// computes its logits on the matrix cores (32 rows x 64 columns per step;
+// bf16 hi/lo planes of the fp32 summaries, so each product is exact and
+// accumulation is fp32).  While the logits are still in the MFMA register
+// layout it forms the log-sum-exp of every sibling pair (eq. (7)), sums the
+// group's heads (eq. (11)) and scatters the
 // scores of the pairs that are candidates of the column's query into that
 // query's slot array.  Candidacy and slot come from a bitmask of the query's
-// kept parents: slot = 2 * (#kept parents before) + child.  With 16 heads per
-// group (4 queries per wave) each wave instead packs the union of its
-// queries' kept parents, 8 to a 32-row tile, so that its work per level is
-// bounded by 4 K parents.  Larger levels gather the candidates' children from
-// the fp32 pyramid, one query at a time.
+// kept parents in the window: slot = 2 * (#kept parents before) + child, the
+// count running on across windows.  With 16 heads per group (4 queries per
+// wave) each wave instead packs the union of its queries' kept parents, 8 to
+// a 32-row tile, so that its work per window is bounded by 4 K parents.
 //
 // Final (levels 2 and 1).  One lane per query reads its K kept level-3 nodes
 // and the stage-2 scores of their children, decides level 2 and then the
@@ -52,7 +52,7 @@ namespace lpq {
 constexpr int kSlots = 32;       // 2K candidates, K <= 16
 constexpr int kMaxK = 16;
 constexpr int kWaves = 4;        // independent wavefronts per workgroup
-constexpr int kDenseRows = 2048; // child rows scored densely
+constexpr int kDenseRows = 2048; // child rows per window of stage 1
 constexpr int kMaskWords = kDenseRows / 4 / 32;  // parent bitmask words per query
 // Per-query LDS arrays are stored slot-major ([slot][query]) so that lanes of
 // different queries always touch different banks.
@@ -253,10 +253,13 @@ __global__ void split_planes_kernel(const float* __restrict__ pyr, bf16_t* __res
 // Stage 1
 // ---------------------------------------------------------------------------
 
+// Two workgroups per CU; three when a query spans several lanes at d = 64,
+// where the kernel then fits 168 VGPRs (at d = 128 the spills cost more than
+// the third workgroup gains).
 template <int D, int G>
-__global__ __launch_bounds__(kWaves * kWave, 2) void stage1_kernel(
-    const bf16_t* __restrict__ q, const float* __restrict__ pyr, const bf16_t* __restrict__ phi,
-    const bf16_t* __restrict__ plo, int* __restrict__ s1_nodes, int heads_q, int heads_kv,
+__global__ __launch_bounds__(kWaves * kWave, (G >= 2 && D == 64) ? 3 : 2) void stage1_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ phi, const bf16_t* __restrict__ plo,
+    int* __restrict__ s1_nodes, int heads_q, int heads_kv,
     int n_tok, int block, int topk, int causal, int force, float scale_log2, LevelTable lv,
     int split_level) {
   constexpr int T = kWave / G;  // queries per wave
@@ -275,11 +278,15 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void stage1_kernel(
   // score_s holds a query's slot scores and, after its decision has read
   // them, its kept-node list (int bit patterns in rows 0..kMaxK).
   __shared__ float score_s[kWaves][kSlots + 1][T];
-  __shared__ uint32_t mask_s[kWaves][kMaskWords][T];
+  __shared__ uint32_t mask_s[kWaves][kShared ? kMaskWords : 1][T];
   __shared__ __align__(16) bf16_t chunk_s[kShared ? 2 * 32 * CROW : 8];
   __shared__ uint32_t chunks_s[2][kWaves][2];
-  // The union of a wave's kept parents (few queries per wave only).
+  // The union of a wave's kept parents, as a bitmap and as an ascending list
+  // (few queries per wave only).
+  __shared__ uint32_t umask_s[kWaves][kShared ? 1 : kMaskWords];
   __shared__ int ulist_s[kWaves][kShared ? 1 : kWave];
+  // Kept-node lists when a query spans several lanes.
+  __shared__ int kp_s[kWaves][kMaxK][G == 1 ? 1 : T];
 
   const int wave = threadIdx.x / kWave;
   const int lane = lane_id();
@@ -314,15 +321,32 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void stage1_kernel(
   const int t = t0 + lane;
   const bool dlane = lane < T && t < n_tok;
   const int cur = dlane ? t / block : 0;
-  int kp[kMaxK];  // kept nodes one level up, ascending
+  const int ql = lane < T ? lane : 0;
+  // The query's kept nodes one level up, ascending: in registers when every
+  // lane holds a query (G = 1), else in the query's LDS column (lanes >= T
+  // read query 0's and write nothing).
+  int kp_r[G == 1 ? kMaxK : 1];
+  auto kp = [&](int i) __attribute__((always_inline)) -> int {
+    if constexpr (G == 1)
+      return kp_r[i];
+    else
+      return kp_s[wave][i][ql];
+  };
+  auto kp_put = [&](int i, int v) __attribute__((always_inline)) {
+    if constexpr (G == 1)
+      kp_r[i] = v;
+    else if (lane < T)
+      kp_s[wave][i][ql] = v;
+  };
   int nk = 1;
 #pragma unroll
-  for (int i = 0; i < kMaxK; ++i) kp[i] = 0;
-  const int ql = lane < T ? lane : 0;
+  for (int i = 0; i < kMaxK; ++i) kp_put(i, 0);
+  wave_lds_sync();
   const Column<float> srow{&score_s[wave][0][ql], T};
   const IntInFloatColumn lrow{&score_s[wave][0][ql], T};
   const Column<uint32_t> mrow{&mask_s[wave][0][ql], T};
 
+  int phase = 0;  // windows so far (parity selects the chunk-bits buffer)
   for (int l = lv.n; l >= split_level; --l) {
     const int sh = l - 1;
     const int size_l = lv.size[l - 1];
@@ -333,7 +357,7 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void stage1_kernel(
     int n_valid = 0;
 #pragma unroll
     for (int i = 0; i < kMaxK; ++i) {
-      const int c = 2 * kp[i];
+      const int c = 2 * kp(i);
       n_valid += (i < nk) ? int(c <= x_max) + int(c + 1 <= x_max) : 0;
     }
     if (!dlane) n_valid = 0;
@@ -341,168 +365,183 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void stage1_kernel(
     const int m_child = lv.size[l - 2];
     const size_t child0 = head_rows + lv.off[l - 2];
 
-    if (kShared && m_child <= kDenseRows) {
-      // Chunk c holds child rows 32c..32c+31, whose parents 8c..8c+7 are byte
-      // c of the parent masks (written after the previous level's decision).
-      // The workgroup scores every chunk that holds a kept parent of one of
-      // its ranking queries, all waves together.
-      uint32_t cw[2] = {0u, 0u};
-      if (need) {
+    // The candidates' children are scored in windows of kDenseRows child
+    // rows w0 .. w0 + kDenseRows - 1 (parents pw = w0 / 4 onwards), in
+    // ascending order, so that a query's slot base runs on from one window to
+    // the next and its slots come out as from one pass over the level.
+    int base[2] = {0, 0};
+    auto window = [&](const int w0) __attribute__((always_inline)) {
+      const int pw = w0 >> 2;
+      if constexpr (kShared) {
+        // The window's parent bitmask: the query's kept nodes one level up.
 #pragma unroll
-        for (int w = 0; w < kMaskWords; ++w) {
-          const uint32_t word = mrow[w];
+        for (int w = 0; w < kMaskWords; ++w) mrow[w] = 0u;
+        wave_lds_sync();
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            cw[w >> 3] |= ((word >> (8 * j)) & 0xffu) ? (1u << ((4 * w + j) & 31)) : 0u;
+        for (int i = 0; i < kMaxK; ++i) {
+          const int p = kp(i) - pw;
+          if (dlane & (i < nk) & (p >= 0) & (p < 32 * kMaskWords))
+            atomicOr(&mrow[p >> 5], 1u << (p & 31));
         }
-      }
+        wave_lds_sync();
+        // Chunk c holds child rows w0 + 32c .. w0 + 32c + 31, whose parents
+        // pw + 8c .. pw + 8c + 7 are byte c of the parent masks.  The workgroup
+        // scores every chunk that holds a kept parent of one of its ranking
+        // queries, all waves together.
+        uint32_t cw[2] = {0u, 0u};
+        if (need) {
 #pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        cw[0] |= __shfl_xor(cw[0], o, kWave);
-        cw[1] |= __shfl_xor(cw[1], o, kWave);
-      }
-      if (lane == 0) {
-        chunks_s[l & 1][wave][0] = cw[0];
-        chunks_s[l & 1][wave][1] = cw[1];
-      }
-      lds_barrier();
-      uint32_t todo[2] = {0u, 0u};
+          for (int w = 0; w < kMaskWords; ++w) {
+            const uint32_t word = mrow[w];
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        todo[0] |= chunks_s[l & 1][w][0];
-        todo[1] |= chunks_s[l & 1][w][1];
-      }
-      todo[0] = __builtin_amdgcn_readfirstlane(todo[0]);
-      todo[1] = __builtin_amdgcn_readfirstlane(todo[1]);
+            for (int j = 0; j < 4; ++j)
+              cw[w >> 3] |= ((word >> (8 * j)) & 0xffu) ? (1u << ((4 * w + j) & 31)) : 0u;
+          }
+        }
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+          cw[0] |= __shfl_xor(cw[0], o, kWave);
+          cw[1] |= __shfl_xor(cw[1], o, kWave);
+        }
+        if (lane == 0) {
+          chunks_s[phase & 1][wave][0] = cw[0];
+          chunks_s[phase & 1][wave][1] = cw[1];
+        }
+        lds_barrier();
+        uint32_t todo[2] = {0u, 0u};
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          todo[0] |= chunks_s[phase & 1][w][0];
+          todo[1] |= chunks_s[phase & 1][w][1];
+        }
+        todo[0] = __builtin_amdgcn_readfirstlane(todo[0]);
+        todo[1] = __builtin_amdgcn_readfirstlane(todo[1]);
 
-      if ((todo[0] | todo[1]) != 0u) {
-        // Pop the lowest pending chunk (the masks are nonzero).
-        auto pop = [&]() __attribute__((always_inline)) {
-          int c;
-          if (todo[0] != 0u) {
-            c = __builtin_ctz(todo[0]);
-            todo[0] &= todo[0] - 1u;
-          } else {
-            c = 32 + __builtin_ctz(todo[1]);
-            todo[1] &= todo[1] - 1u;
-          }
-          return c;
-        };
-        // This thread's pieces of a chunk: piece p = tid + 256 i is plane
-        // p / (32 D / 8), row (p / (D / 8)) % 32, 16-byte column p % (D / 8).
-        // Rows past the level end repeat its last row (see the ragged-chunk
-        // masking of the pickup).
-        piece_t stage[CLOADS];
-        auto fetch = [&](int r0) __attribute__((always_inline)) {
-#pragma unroll
-          for (int i = 0; i < CLOADS; ++i) {
-            const int p = threadIdx.x + i * kWaves * kWave;
-            const int plane = p / (32 * D / 8), row = (p / (D / 8)) % 32, c8 = p % (D / 8);
-            const bf16_t* src = plane ? plo : phi;
-            stage[i] = *reinterpret_cast<const piece_t*>(
-                src + (child0 + min(r0 + row, m_child - 1)) * D + 8 * c8);
-          }
-        };
-        auto put = [&]() __attribute__((always_inline)) {
-#pragma unroll
-          for (int i = 0; i < CLOADS; ++i) {
-            const int p = threadIdx.x + i * kWaves * kWave;
-            const int plane = p / (32 * D / 8), row = (p / (D / 8)) % 32, c8 = p % (D / 8);
-            *reinterpret_cast<piece_t*>(chunk_s + (plane * 32 + row) * CROW + 8 * c8) = stage[i];
-          }
-        };
-        int base[2] = {0, 0};
-        const Column<uint32_t> mcol[2] = {{&mask_s[wave][0][(32 * 0 + col) / G], T},
-                                          {&mask_s[wave][0][(32 * 1 + col) / G], T}};
-        const Column<float> scol[2] = {{&score_s[wave][0][(32 * 0 + col) / G], T},
-                                       {&score_s[wave][0][(32 * 1 + col) / G], T}};
-        const bool writer = (col % G) == 0;
-        // One chunk: S = summaries x queries on MFMA from the LDS chunk, then
-        // the candidates' LSEs picked up into the slot arrays.  byte[cb]: the
-        // column's kept parents among the chunk's 8.
-        auto chunk = [&](int r0, const uint32_t (&byte)[2]) __attribute__((always_inline)) {
-          // Rows of this chunk: r0 + 8g + 4kh + i%4 (acc element 4g + i%4);
-          // level-l candidates n = r0/2 + 4g + 2kh + m own rows 2n, 2n+1;
-          // their parents p = r0/4 + 2g + kh (bits p0..p0+7 of the masks).
-          const bf16_t* arow = chunk_s + col * CROW + 8 * kh;
-          f32x16_t acc[2] = {};
-#pragma unroll
-          for (int s = 0; s < KSTEPS; ++s) {
-            const uint4 hv = *reinterpret_cast<const uint4*>(arow + 16 * s);
-            const uint4 lo = *reinterpret_cast<const uint4*>(arow + 32 * CROW + 16 * s);
-#pragma unroll
-            for (int cb = 0; cb < 2; ++cb) {
-              acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lo), bq[cb][s],
-                                                                acc[cb], 0, 0, 0);
-              acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(hv), bq[cb][s],
-                                                                acc[cb], 0, 0, 0);
+        if ((todo[0] | todo[1]) != 0u) {
+          // Pop the lowest pending chunk (the masks are nonzero).
+          auto pop = [&]() __attribute__((always_inline)) {
+            int c;
+            if (todo[0] != 0u) {
+              c = __builtin_ctz(todo[0]);
+              todo[0] &= todo[0] - 1u;
+            } else {
+              c = 32 + __builtin_ctz(todo[1]);
+              todo[1] &= todo[1] - 1u;
             }
-          }
-          auto pickup = [&](auto full_tag) {
-            constexpr bool kFull = decltype(full_tag)::value;  // every row of the chunk exists
+            return c;
+          };
+          // This thread's pieces of a chunk: piece p = tid + 256 i is plane
+          // p / (32 D / 8), row (p / (D / 8)) % 32, 16-byte column p % (D / 8).
+          // Rows past the level end repeat its last row (see the ragged-chunk
+          // masking of the pickup).
+          piece_t stage[CLOADS];
+          auto fetch = [&](int r0) __attribute__((always_inline)) {
 #pragma unroll
-            for (int cb = 0; cb < 2; ++cb) {
-#pragma unroll
-              for (int g = 0; g < 4; ++g) {
-                const int pb = 2 * g + kh;
-                const bool has = writer & ((byte[cb] >> pb) & 1u);
-                const int pslot = base[cb] + __popc(byte[cb] & ((1u << pb) - 1u));
-#pragma unroll
-                for (int m = 0; m < 2; ++m) {
-                  const int n = (r0 >> 1) + 4 * g + 2 * kh + m;
-                  const float z0 = acc[cb][4 * g + 2 * m];
-                  float z1 = acc[cb][4 * g + 2 * m + 1];
-                  bool w = has;
-                  if (!kFull) {
-                    z1 = 2 * n + 1 < m_child ? z1 : neg_inf();
-                    w &= 2 * n < m_child;
-                  }
-                  const float mx = fmaxf(z0, z1), mn = fminf(z0, z1);
-                  float v =
-                      fmaf(mx, scale_log2, fast_log2(1.f + fast_exp2((mn - mx) * scale_log2)));
-                  if (G >= 2) v += __shfl_xor(v, 1, kWave);
-                  if (G >= 4) v += __shfl_xor(v, 2, kWave);
-                  if (G >= 8) v += __shfl_xor(v, 4, kWave);
-                  if (G >= 16) v += __shfl_xor(v, 8, kWave);
-                  scol[cb][w ? 2 * pslot + m : kSlots] = v;
-                }
-              }
+            for (int i = 0; i < CLOADS; ++i) {
+              const int p = threadIdx.x + i * kWaves * kWave;
+              const int plane = p / (32 * D / 8), row = (p / (D / 8)) % 32, c8 = p % (D / 8);
+              const bf16_t* src = plane ? plo : phi;
+              stage[i] = *reinterpret_cast<const piece_t*>(
+                  src + (child0 + min(r0 + row, m_child - 1)) * D + 8 * c8);
             }
           };
-          if (r0 + 32 <= m_child)
-            pickup(std::true_type{});
-          else
-            pickup(std::false_type{});
-        };
-        // The next chunk's pieces are in flight while this one is scored.
-        int c = pop();
-        fetch(32 * c);
-        for (;;) {
-          const bool more = (todo[0] | todo[1]) != 0u;
-          const int cn = more ? pop() : c;
-          wait_vmcnt<0>();
-          lds_barrier();  // every wave has read the previous chunk
-          put();
-          if (more) fetch(32 * cn);
-          lds_barrier();  // this chunk is in LDS
-          // A wave none of whose columns keeps a parent here (large groups:
-          // few queries per wave) takes part in the loads only.  Parents in
-          // chunks skipped by the workgroup are no kept parents of a ranking
-          // query, so the slot bases of those queries stay exact.
-          const int p0 = 8 * c;
-          uint32_t byte[2];
+          auto put = [&]() __attribute__((always_inline)) {
 #pragma unroll
-          for (int cb = 0; cb < 2; ++cb) byte[cb] = (mcol[cb][p0 >> 5] >> (p0 & 31)) & 0xffu;
-          if (__ballot((byte[0] | byte[1]) != 0u) != 0) chunk(32 * c, byte);
+            for (int i = 0; i < CLOADS; ++i) {
+              const int p = threadIdx.x + i * kWaves * kWave;
+              const int plane = p / (32 * D / 8), row = (p / (D / 8)) % 32, c8 = p % (D / 8);
+              *reinterpret_cast<piece_t*>(chunk_s + (plane * 32 + row) * CROW + 8 * c8) = stage[i];
+            }
+          };
+          const Column<uint32_t> mcol[2] = {{&mask_s[wave][0][(32 * 0 + col) / G], T},
+                                            {&mask_s[wave][0][(32 * 1 + col) / G], T}};
+          const Column<float> scol[2] = {{&score_s[wave][0][(32 * 0 + col) / G], T},
+                                         {&score_s[wave][0][(32 * 1 + col) / G], T}};
+          const bool writer = (col % G) == 0;
+          // One chunk: S = summaries x queries on MFMA from the LDS chunk, then
+          // the candidates' LSEs picked up into the slot arrays.  byte[cb]: the
+          // column's kept parents among the chunk's 8.
+          auto chunk = [&](int r0, const uint32_t (&byte)[2]) __attribute__((always_inline)) {
+            // Rows of this chunk: r0 + 8g + 4kh + i%4 (acc element 4g + i%4);
+            // level-l candidates n = r0/2 + 4g + 2kh + m own rows 2n, 2n+1;
+            // their parents p = r0/4 + 2g + kh (bits p0..p0+7 of the masks).
+            const bf16_t* arow = chunk_s + col * CROW + 8 * kh;
+            f32x16_t acc[2] = {};
 #pragma unroll
-          for (int cb = 0; cb < 2; ++cb) base[cb] += __popc(byte[cb]);
-          if (!more) break;
-          c = cn;
+            for (int s = 0; s < KSTEPS; ++s) {
+              const uint4 hv = *reinterpret_cast<const uint4*>(arow + 16 * s);
+              const uint4 lo = *reinterpret_cast<const uint4*>(arow + 32 * CROW + 16 * s);
+#pragma unroll
+              for (int cb = 0; cb < 2; ++cb) {
+                acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lo), bq[cb][s],
+                                                                  acc[cb], 0, 0, 0);
+                acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(hv), bq[cb][s],
+                                                                  acc[cb], 0, 0, 0);
+              }
+            }
+            auto pickup = [&](auto full_tag) {
+              constexpr bool kFull = decltype(full_tag)::value;  // every row of the chunk exists
+#pragma unroll
+              for (int cb = 0; cb < 2; ++cb) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                  const int pb = 2 * g + kh;
+                  const bool has = writer & ((byte[cb] >> pb) & 1u);
+                  const int pslot = base[cb] + __popc(byte[cb] & ((1u << pb) - 1u));
+#pragma unroll
+                  for (int m = 0; m < 2; ++m) {
+                    const int n = (r0 >> 1) + 4 * g + 2 * kh + m;
+                    const float z0 = acc[cb][4 * g + 2 * m];
+                    float z1 = acc[cb][4 * g + 2 * m + 1];
+                    bool w = has;
+                    if (!kFull) {
+                      z1 = 2 * n + 1 < m_child ? z1 : neg_inf();
+                      w &= 2 * n < m_child;
+                    }
+                    const float mx = fmaxf(z0, z1), mn = fminf(z0, z1);
+                    float v =
+                        fmaf(mx, scale_log2, fast_log2(1.f + fast_exp2((mn - mx) * scale_log2)));
+                    if (G >= 2) v += __shfl_xor(v, 1, kWave);
+                    if (G >= 4) v += __shfl_xor(v, 2, kWave);
+                    if (G >= 8) v += __shfl_xor(v, 4, kWave);
+                    if (G >= 16) v += __shfl_xor(v, 8, kWave);
+                    scol[cb][w ? 2 * pslot + m : kSlots] = v;
+                  }
+                }
+              }
+            };
+            if (r0 + 32 <= m_child)
+              pickup(std::true_type{});
+            else
+              pickup(std::false_type{});
+          };
+          // The next chunk's pieces are in flight while this one is scored.
+          int c = pop();
+          fetch(w0 + 32 * c);
+          for (;;) {
+            const bool more = (todo[0] | todo[1]) != 0u;
+            const int cn = more ? pop() : c;
+            wait_vmcnt<0>();
+            lds_barrier();  // every wave has read the previous chunk
+            put();
+            if (more) fetch(w0 + 32 * cn);
+            lds_barrier();  // this chunk is in LDS
+            // A wave none of whose columns keeps a parent here (large groups:
+            // few queries per wave) takes part in the loads only.  Parents in
+            // chunks skipped by the workgroup are no kept parents of a ranking
+            // query, so the slot bases of those queries stay exact.
+            const int p0 = 8 * c;
+            uint32_t byte[2];
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) byte[cb] = (mcol[cb][p0 >> 5] >> (p0 & 31)) & 0xffu;
+            if (__ballot((byte[0] | byte[1]) != 0u) != 0) chunk(w0 + 32 * c, byte);
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) base[cb] += __popc(byte[cb]);
+            if (!more) break;
+            c = cn;
+          }
         }
-      }
-      wave_lds_sync();
-    } else if (m_child <= kDenseRows) {
-      if constexpr (!kShared) {
+      } else {
         // Few queries per wave (T = 64 / G <= 4): the wave scores only the
         // union of its ranking queries' kept parents, 8 parents to a 32-row
         // MFMA tile (a parent's 4 grandchild rows are its two candidates'
@@ -513,13 +552,18 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void stage1_kernel(
         static_assert(T * kMaxK <= kWave && kMaskWords * 4 == kWave, "union of kept parents");
         const uint32_t needers = (uint32_t)__ballot(need);  // query qi is lane qi
         if (needers != 0u) {
-          // Union of the ranking queries' parent masks (written after the
-          // previous level's decision): lane x holds parents 8x .. 8x + 7.
-          uint32_t ub = 0u;
+          // Bitmap of the union of the ranking queries' kept parents in the
+          // window: lane x then holds parents pw + 8x .. pw + 8x + 7.
+          if (lane < kMaskWords) umask_s[wave][lane] = 0u;
+          wave_lds_sync();
 #pragma unroll
-          for (int qi = 0; qi < T; ++qi)
-            ub |= ((needers >> qi) & 1u) ? (mask_s[wave][lane >> 2][qi] >> (8 * (lane & 3))) & 0xffu
-                                         : 0u;
+          for (int i = 0; i < kMaxK; ++i) {
+            const int p = kp(i) - pw;
+            if (need & (i < nk) & (p >= 0) & (p < 32 * kMaskWords))
+              atomicOr(&umask_s[wave][p >> 5], 1u << (p & 31));
+          }
+          wave_lds_sync();
+          const uint32_t ub = (umask_s[wave][lane >> 2] >> (8 * (lane & 3))) & 0xffu;
           // Union rank of lane x's first parent (exclusive prefix of the
           // popcounts); the ascending union list.
           const int cnt = __popc(ub);
@@ -533,17 +577,20 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void stage1_kernel(
           const int n_union = __builtin_amdgcn_readlane(incl, kWave - 1);
 #pragma unroll
           for (int j = 0; j < 8; ++j)
-            if ((ub >> j) & 1u) ulist_s[wave][rbase + __popc(ub & ((1u << j) - 1u))] = 8 * lane + j;
+            if ((ub >> j) & 1u)
+              ulist_s[wave][rbase + __popc(ub & ((1u << j) - 1u))] = pw + 8 * lane + j;
           // A ranking query's kept parents as bits of their union ranks (its
           // decision lane; at most 64 ranks).
           uint32_t ur_lo = 0u, ur_hi = 0u;
 #pragma unroll
           for (int i = 0; i < kMaxK; ++i) {
-            const int p = kp[i] & (8 * kWave - 1);
-            const int rb = __shfl(rbase, p >> 3, kWave);
-            const uint32_t bb = (uint32_t)__shfl((int)ub, p >> 3, kWave);
+            const int p = kp(i) - pw;  // in the window: 0 .. 8 kWave - 1
+            const bool in = (p >= 0) & (p < 8 * kWave);
+            const int x = (p >> 3) & (kWave - 1);
+            const int rb = __shfl(rbase, x, kWave);
+            const uint32_t bb = (uint32_t)__shfl((int)ub, x, kWave);
             const int r = rb + __popc(bb & ((1u << (p & 7)) - 1u));
-            const uint32_t bit = (need && i < nk) ? 1u << (r & 31) : 0u;
+            const uint32_t bit = (need && i < nk && in) ? 1u << (r & 31) : 0u;
             ur_lo |= r < 32 ? bit : 0u;
             ur_hi |= r < 32 ? 0u : bit;
           }
@@ -559,7 +606,6 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void stage1_kernel(
           const Column<float> scol[2] = {{&score_s[wave][0][(32 * 0 + col) / G], T},
                                          {&score_s[wave][0][(32 * 1 + col) / G], T}};
           const bool writer = (col % G) == 0;
-          int base[2] = {0, 0};
           const int n_tiles = (n_union + 7) >> 3;
           for (int tt = 0; tt < n_tiles; ++tt) {
             // Tile row col: union parent 8 tt + col / 4 (past the union's end
@@ -637,44 +683,16 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void stage1_kernel(
         }
       }
       wave_lds_sync();
-    } else if (__ballot(need) != 0) {
-      // Gather: one query at a time; lane L scores child row L of the
-      // query's candidate list (candidate L >> 1, child L & 1).  The list
-      // entries of query qi are read before its score column is written.
-      for (int qi = 0; qi < T; ++qi) {
-        if (!__builtin_amdgcn_readlane(need ? 1 : 0, qi)) continue;
-        const int j = lane >> 1;
-        const int nkq = __builtin_amdgcn_readlane(nk, qi);
-        const int nvq = __builtin_amdgcn_readlane(n_valid, qi);
-        const int par = __float_as_int(score_s[wave][j >> 1][qi]);
-        const int cnode = 2 * par + (j & 1);
-        const int row = 2 * cnode + (lane & 1);
-        const bool live = ((j >> 1) < nkq) & (j < nvq) & (row < m_child);
-        const float* xr = pyr + (child0 + (live ? row : 0)) * D;
-        float tot = 0.f;
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const bf16_t* qr =
-              q + (((size_t)b * heads_q + (size_t)kvh * G + h) * n_tok + (t0 + qi)) * D;
-          float a = 0.f;
-#pragma unroll
-          for (int c8 = 0; c8 < D; c8 += 8) {
-            float qv[8];
-            load16(qr + c8, qv);
-            const float4 x0 = *reinterpret_cast<const float4*>(xr + c8);
-            const float4 x1 = *reinterpret_cast<const float4*>(xr + c8 + 4);
-            a += qv[0] * x0.x + qv[1] * x0.y + qv[2] * x0.z + qv[3] * x0.w + qv[4] * x1.x +
-                 qv[5] * x1.y + qv[6] * x1.z + qv[7] * x1.w;
-          }
-          const float z = live ? a * scale_log2 : neg_inf();
-          const float zo = __shfl_xor(z, 1, kWave);
-          const float mx = fmaxf(z, zo), mn = fminf(z, zo);
-          tot += mx + fast_log2(1.f + fast_exp2(mn - mx));
-        }
-        wave_lds_sync();
-        if ((lane & 1) == 0) score_s[wave][live ? j : kSlots][qi] = tot;
+      ++phase;
+    };
+    // A level within one window (every level up to 256K tokens at C = 64)
+    // runs a copy of the window code compiled for w0 = 0.
+    if (size_l > topk) {
+      if (m_child <= kDenseRows) {
+        window(0);
+      } else {
+        for (int w0 = 0; w0 < m_child; w0 += kDenseRows) window(w0);
       }
-      wave_lds_sync();
     }
 
     // Decision for this lane's query.
@@ -706,22 +724,12 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void stage1_kernel(
       if (need) km = kq;
     }
     wave_lds_sync();
-    compact_kept(km, lrow, [&](int j) { return 2 * kp[j >> 1] + (j & 1); });
+    compact_kept(km, lrow, [&](int j) { return 2 * kp(j >> 1) + (j & 1); });
     wave_lds_sync();
     nk = __popc(km);
 #pragma unroll
-    for (int i = 0; i < kMaxK; ++i) kp[i] = lrow.get(i);
+    for (int i = 0; i < kMaxK; ++i) kp_put(i, lrow.get(i));
     if (l == split_level) break;
-    // Parent bitmask for the next level's dense pass (kept nodes of level l).
-    const int nl = l - 1;
-    if (lv.size[nl - 1] > topk && lv.size[nl - 2] <= kDenseRows) {
-#pragma unroll
-      for (int w = 0; w < kMaskWords; ++w) mrow[w] = 0u;
-      wave_lds_sync();
-#pragma unroll
-      for (int i = 0; i < kMaxK; ++i)
-        if (dlane & (i < nk)) atomicOr(&mrow[kp[i] >> 5], 1u << (kp[i] & 31));
-    }
     wave_lds_sync();
   }
   if (dlane) {
@@ -731,12 +739,12 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void stage1_kernel(
       for (int i = 0; i < kMaxK; i += 4)
         if (i < topk)
           *reinterpret_cast<int4*>(out + i) =
-              make_int4(i < nk ? kp[i] : -1, i + 1 < nk ? kp[i + 1] : -1,
-                        i + 2 < nk ? kp[i + 2] : -1, i + 3 < nk ? kp[i + 3] : -1);
+              make_int4(i < nk ? kp(i) : -1, i + 1 < nk ? kp(i + 1) : -1,
+                        i + 2 < nk ? kp(i + 2) : -1, i + 3 < nk ? kp(i + 3) : -1);
     } else {
 #pragma unroll
       for (int i = 0; i < kMaxK; ++i)
-        if (i < topk) out[i] = i < nk ? kp[i] : -1;
+        if (i < topk) out[i] = i < nk ? kp(i) : -1;
     }
   }
 }

@@ -653,7 +653,7 @@ hipError_t stage1_lpq_launch(const LaunchShape& s, const void* q, const float* p
   }
   prof::Scope ps("select_stage1", st);
   hipLaunchKernelGGL((lpq::stage1_kernel<D, G>), grid, dim3(lpq::kWaves * kWave), 0, st,
-                     static_cast<const bf16_t*>(q), pyr, w.plane_hi, w.plane_lo, w.s1_nodes,
+                     static_cast<const bf16_t*>(q), w.plane_hi, w.plane_lo, w.s1_nodes,
                      s.heads_q, s.heads_kv, s.seq_len, s.block, s.topk, s.causal ? 1 : 0,
                      s.force ? 1 : 0, s.scale * kLog2e, s.lv, kSplitLevel);
   return hipGetLastError();

@@ -304,34 +304,39 @@ def test_decode_c5_unit_variance():
     decode_compare(prob, inp, pyr, [(b, h) for b in seqs for h in range(8)], min_count=8)
 
 
-def test_prefill_level2_beyond_dense_rows():
-    """A prefill of 262272 tokens (4098 leaves; level 2 holds 2049 rows, more
-    than the first selection stage scores as one dense tile, so its level-3
-    decision gathers each query's candidates), 2 query heads over one KV head,
-    N(0,1) entries, 200 sampled rows: selections bit-exact past the margin
-    (at least 20 rows), attention within the bf16 bounds."""
-    n = 262144 + 128
-    prob = Problem(1, 2, 1, n, 128, block=64, topk=16, dtype=torch.bfloat16)
-    announce(f"prefill N={n} G=2 unit (level 2 beyond the dense tile)")
-    inp = prefill_inputs(1, 2, 1, n, 128, torch.bfloat16, seed=7100, recipe="unit", device=DEV)
+@pytest.mark.parametrize("n,hq,d,k", [(262144 + 128, 2, 128, 16), (262144 + 128, 1, 128, 16),
+                                      (262144 + 128, 16, 64, 8), (524288, 1, 128, 16)])
+def test_prefill_level2_beyond_dense_rows(n, hq, d, k):
+    """Prefills past 256K tokens, where level 2 holds more rows than one
+    window of the first selection stage (2048), so that its level-3 decision
+    runs over several windows: 262272 tokens (level 2: 2049 rows, the second
+    window one row) at 1, 2 and 16 query heads per KV head, and 524288
+    (level 2: two full windows).  N(0,1) entries, 200 sampled rows:
+    selections bit-exact past the margin (at least 20 rows), attention within
+    the bf16 bounds."""
+    prob = Problem(1, hq, 1, n, d, block=64, topk=k, dtype=torch.bfloat16)
+    announce(f"prefill N={n} G={hq} d={d} K={k} unit (level 2 beyond one window)")
+    inp = prefill_inputs(1, hq, 1, n, d, torch.bfloat16, seed=7100 + hq, recipe="unit",
+                         device=DEV)
     pyr = pisa_build_pyramid(prob, inp.k)
     idx, score = pisa_select(prob, inp.q, inp.k, pyr)
     out, lse = pisa_block_sparse_attn(prob, inp.q, inp.k, inp.v, idx)
     torch.cuda.synchronize()
     check_pyramid(pyr, inp.k, prob, [(0, 0)])
-    rows = sample_rows(n, 64, 16, 200, 7100)
+    rows = sample_rows(n, 64, k, 200, 7100)
     keys, vals = parity.to_np(inp.k[0, 0]), parity.to_np(inp.v[0, 0])
-    qg = parity.to_np(inp.q[0, 0:2])
+    qg = parity.to_np(inp.q[0, 0:hq])
     levels = oracle.build_pyramid(keys, 64)
     tl = parity.compare_selection("pisa", idx[0, 0].cpu().numpy(), score[0, 0].cpu().numpy(), qg,
-                                  keys, levels, rows, 64, 16, True, True, prob.logit_scale,
+                                  keys, levels, rows, 64, k, True, True, prob.logit_scale,
                                   parity.Tally())
     print(f"  pisa: compared {tl.compared}/{tl.rows} rows, mismatches {len(tl.mismatches)}",
           flush=True)
     assert not tl.mismatches, tl.mismatches[:3]
     assert tl.compared >= 20, (tl.compared, tl.rows)
-    parity.compare_attention(parity.to_np(out[0, 0:2]), lse[0, 0:2].cpu().numpy(), qg, keys, vals,
-                             idx[0, 0].cpu().numpy(), rows, 64, True, prob.logit_scale, False)
+    parity.compare_attention(parity.to_np(out[0, 0:hq]), lse[0, 0:hq].cpu().numpy(), qg, keys,
+                             vals, idx[0, 0].cpu().numpy(), rows, 64, True, prob.logit_scale,
+                             False)
 
 
 @pytest.mark.parametrize("n,d,k", [(65536, 64, 8), (131072, 64, 8), (32768, 128, 16)])

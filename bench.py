@@ -382,7 +382,7 @@ def run(args):
             # the pages' own latency shape: 16 query heads per KV head, d=64, K=8
             result["selection_sweep_g16"] = selection_sweep(
                 args, heads_q=16, heads_kv=1, head_dim=64, topk=8,
-                sizes=(16384, 65536, 131072, 262144), seed=4100)
+                sizes=(16384, 65536, 131072, 262144, 524288, 1048576), seed=4100)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(args, inp, prob)
     return result
@@ -497,7 +497,7 @@ def decode_bench(args):
 
 
 def selection_sweep(args, heads_q=4, heads_kv=4, head_dim=128, topk=16,
-                    sizes=(16384, 32768, 65536, 131072, 262144), seed=4000):
+                    sizes=(16384, 32768, 65536, 131072, 262144, 524288), seed=4000):
     """Selection latency (pyramid + selection, attention excluded) of PISA and
     of the GPU BSA baseline for N over `sizes` (default: H=4, d=128, K=16)."""
     import torch
@@ -520,8 +520,11 @@ def selection_sweep(args, heads_q=4, heads_kv=4, head_dim=128, topk=16,
         idx = torch.empty((1, heads_kv, n, topk), dtype=torch.int32, device=dev)
         ws_s = pisa.pisa_workspace_bytes(prob, "select")
         wsel = torch.empty(max(ws_s, 1), dtype=torch.uint8, device=dev)
-        ws_b = pisa.pisa_workspace_bytes(prob, "bsa")
-        wbsa = torch.empty(ws_b, dtype=torch.uint8, device=dev)
+        # BSA's Top-K holds a row of leaf scores in registers (at most 4096
+        # leaf blocks, 256K tokens at C = 64): past that PISA is timed alone.
+        bsa_ok = -(-n // 64) <= 4096
+        ws_b = pisa.pisa_workspace_bytes(prob, "bsa") if bsa_ok else 0
+        wbsa = torch.empty(max(ws_b, 1), dtype=torch.uint8, device=dev)
 
         def pisa_sel():
             pisa.pisa_build_pyramid(prob, inp.k, pyr)
@@ -534,10 +537,12 @@ def selection_sweep(args, heads_q=4, heads_kv=4, head_dim=128, topk=16,
 
         reps = 5 if n <= 65536 else 3
         p_ms = timed_call(pisa_sel, reps, 1)
-        b_ms = timed_call(bsa_sel, reps, 1)
+        b_ms = timed_call(bsa_sel, reps, 1) if bsa_ok else None
         # one more call of each with the library's per-kernel events
-        kern = {}
+        kern = {"bsa": {}}
         for name, fn in (("pisa", pisa_sel), ("bsa", bsa_sel)):
+            if name == "bsa" and not bsa_ok:
+                continue
             pisa.pisa_profile_enable(True)
             fn()
             torch.cuda.synchronize()
@@ -558,28 +563,31 @@ def selection_sweep(args, heads_q=4, heads_kv=4, head_dim=128, topk=16,
         if "bsa_topk" in kern["bsa"]:
             bsa_frac["bsa_topk"] = (s_bytes + idx_bytes) / (kern["bsa"]["bsa_topk"] * 1e-3) \
                 / 1e9 / HBM_PEAK_GBS
-        pts.append({"N": n, "pisa_ms": p_ms, "bsa_ms": b_ms, "speedup_vs_bsa": b_ms / p_ms,
+        pts.append({"N": n, "pisa_ms": p_ms, "bsa_ms": b_ms,
+                    "speedup_vs_bsa": b_ms / p_ms if bsa_ok else None,
                     "pisa_kernels_ms": kern["pisa"], "bsa_kernels_ms": kern["bsa"],
-                    "bsa_score_matrix_mb": s_bytes / 1e6,
+                    "bsa_score_matrix_mb": s_bytes / 1e6 if bsa_ok else None,
                     "bsa_hbm_frac": {k: round(v, 3) for k, v in bsa_frac.items()}})
         del wbsa, inp
         torch.cuda.empty_cache()
     cross = None
-    for a, b in zip(pts, pts[1:]):
+    timed = [p for p in pts if p["bsa_ms"] is not None]
+    for a, b in zip(timed, timed[1:]):
         if a["speedup_vs_bsa"] < 1.0 <= b["speedup_vs_bsa"]:
             la, lb = math.log(a["N"]), math.log(b["N"])
             ra, rb = math.log(a["speedup_vs_bsa"]), math.log(b["speedup_vs_bsa"])
             cross = math.exp(la + (lb - la) * (0 - ra) / (rb - ra))
-    if pts and pts[0]["speedup_vs_bsa"] >= 1.0:
-        cross = f"<= {pts[0]['N']}"
-    if cross is None and pts:
-        cross = f"> {pts[-1]['N']}"
+    if timed and timed[0]["speedup_vs_bsa"] >= 1.0:
+        cross = f"<= {timed[0]['N']}"
+    if cross is None and timed:
+        cross = f"> {timed[-1]['N']}"
     return {"points": pts, "crossover_N": cross,
             "note": f"timings include pyramid construction (all levels) for both selectors; "
                     f"attention excluded; Hq={heads_q} Hkv={heads_kv}, d={head_dim}, C=64, "
                     f"K={topk}, bf16; bsa_hbm_frac: algorithmic bytes of each BSA kernel "
                     f"(score matrix written / read, queries, leaf ids) over its launch time, "
-                    f"as a fraction of {HBM_PEAK_GBS:.0f} GB/s"}
+                    f"as a fraction of {HBM_PEAK_GBS:.0f} GB/s; bsa_ms null: past BSA's "
+                    f"4096 leaf blocks (its Top-K holds a row in registers)"}
 
 
 def q_tile_study(args):

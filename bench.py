@@ -520,9 +520,9 @@ def selection_sweep(args, heads_q=4, heads_kv=4, head_dim=128, topk=16,
         idx = torch.empty((1, heads_kv, n, topk), dtype=torch.int32, device=dev)
         ws_s = pisa.pisa_workspace_bytes(prob, "select")
         wsel = torch.empty(max(ws_s, 1), dtype=torch.uint8, device=dev)
-        # BSA's Top-K holds a row of leaf scores in registers (at most 4096
-        # leaf blocks, 256K tokens at C = 64): past that PISA is timed alone.
-        bsa_ok = -(-n // 64) <= 4096
+        # past 4096 leaf blocks BSA needs a multiple of 4 leaf blocks (its
+        # Top-K then takes rows in segments); else PISA is timed alone
+        bsa_ok = -(-n // 64) <= 4096 or -(-n // 64) % 4 == 0
         ws_b = pisa.pisa_workspace_bytes(prob, "bsa") if bsa_ok else 0
         wbsa = torch.empty(max(ws_b, 1), dtype=torch.uint8, device=dev)
 
@@ -586,8 +586,7 @@ def selection_sweep(args, heads_q=4, heads_kv=4, head_dim=128, topk=16,
                     f"attention excluded; Hq={heads_q} Hkv={heads_kv}, d={head_dim}, C=64, "
                     f"K={topk}, bf16; bsa_hbm_frac: algorithmic bytes of each BSA kernel "
                     f"(score matrix written / read, queries, leaf ids) over its launch time, "
-                    f"as a fraction of {HBM_PEAK_GBS:.0f} GB/s; bsa_ms null: past BSA's "
-                    f"4096 leaf blocks (its Top-K holds a row in registers)"}
+                    f"as a fraction of {HBM_PEAK_GBS:.0f} GB/s"}
 
 
 def q_tile_study(args):

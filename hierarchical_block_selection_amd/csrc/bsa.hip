@@ -29,7 +29,9 @@ namespace pisa {
 
 constexpr int kBsaTile = 64;
 constexpr int kBsaDk = 32;
-constexpr int kBsaMaxLeaves = 4096;  // row length held in registers by the Top-K pass
+// Row length held in registers by the Top-K pass: the longest row of the
+// general pass; rows of the MFMA path are taken in segments of this length.
+constexpr int kBsaMaxLeaves = 4096;
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bsa_scores_kernel(const T* __restrict__ q,
@@ -402,7 +404,9 @@ __global__ __launch_bounds__(256) void bsa_topk_kernel(const float* __restrict__
 //   4. the kept leaves plus the forced ones are put in ascending order by one
 //      more sort and written.
 // A row whose marked entries exceed LPR falls back to extracting the best
-// entries one at a time.
+// entries one at a time.  Rows longer than LPR * VPL scores (past 4096 leaf
+// blocks, one row per wavefront) run steps 1-3 per segment of that length and
+// merge each segment's sorted keys into the running best LPR.
 __device__ __forceinline__ uint32_t xlane_u32(uint32_t v, int j) {
   return uint32_t(__shfl_xor(int(v), j, kWave));
 }
@@ -446,7 +450,8 @@ __device__ __forceinline__ uint32_t row_sort_desc32(uint32_t x, int hl) {
   return x;
 }
 
-template <int LPR, int VPL>  // lanes per row (32 or 64), scores per lane (% 4 == 0)
+// lanes per row (32 or 64), scores per lane (% 4 == 0), rows longer than LPR * VPL
+template <int LPR, int VPL, bool kLong>
 __global__ __launch_bounds__(256) void bsa_topk_rows_kernel(const float* __restrict__ S,
                                                             int32_t* __restrict__ idx,
                                                             float* __restrict__ score, int n_tok,
@@ -469,95 +474,125 @@ __global__ __launch_bounds__(256) void bsa_topk_rows_kernel(const float* __restr
   const bool keep_all = n_el <= topk;
   const int n_forced = cz ? 1 + (fz ? (cur >= 2 ? 2 : 1) : 0) : 0;
   const int keep_n = keep_all ? 0 : topk - n_forced;
-  // 1. The row: element i = 4 LPR g + 4 hl + e (g < VPL / 4, e < 4).
-  float x[VPL];
-  float lmax = neg_inf();
-#pragma unroll
-  for (int g = 0; g < VPL / 4; ++g) {
-    const int i0 = 4 * LPR * g + 4 * hl;
-    float4 v = make_float4(neg_inf(), neg_inf(), neg_inf(), neg_inf());
-    if (!keep_all && i0 < n_el) v = *reinterpret_cast<const float4*>(srow + i0);
-    x[4 * g] = v.x; x[4 * g + 1] = v.y; x[4 * g + 2] = v.z; x[4 * g + 3] = v.w;
-    lmax = fmaxf(lmax, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
-  }
-  // 2. Lower bound: the keep_n-th largest lane maximum of the row.
-  const float srt = row_sort_desc<LPR>(lmax, hl);
-  const int kk = max(keep_n, 1) - 1;
-  const float thr = __shfl(srt, (lane & ~(LPR - 1)) + kk, kWave);
-  // 3. Marked entries (>= thr and rankable, i.e. > -inf).
-  uint32_t m[NM];
-#pragma unroll
-  for (int w = 0; w < NM; ++w) m[w] = 0u;
-#pragma unroll
-  for (int r = 0; r < VPL; ++r)
-    m[r / 32] |= (x[r] >= thr && x[r] > neg_inf()) ? (1u << (r % 32)) : 0u;
-  int cnt = 0;
-#pragma unroll
-  for (int w = 0; w < NM; ++w) cnt += __popc(m[w]);
-  int incl = cnt;
-#pragma unroll
-  for (int o = 1; o < LPR; o <<= 1) {
-    const int y = __shfl_up(incl, o, LPR);
-    if (hl >= o) incl += y;
-  }
-  const int total = __shfl(incl, (lane & ~(LPR - 1)) + LPR - 1, kWave);
+  // A row longer than LPR * VPL scores (one row per wavefront: LPR = 64) is
+  // taken in segments of that length; the sorted keys of each segment are
+  // merged into the running list, lane hl holding the hl-th best so far.
+  constexpr int SEG = LPR * VPL;
   bool chosen = false;
   uint64_t mine = 0;
-  if (keep_n > 0 && total <= LPR) {
-    int off = incl - cnt;
-    bool more = cnt > 0;
-    // marked entries, one per lane per round (their scores are re-read: L2)
-    while (__ballot(more) != 0) {
-      if (more) {
-        int w = 0;
+  static_assert(!kLong || LPR == 64, "segments need one row per wavefront");
+  for (int s0 = 0; s0 == 0 || (kLong && s0 < n_el); s0 += SEG) {
+    // 1. The segment: element i = s0 + 4 LPR g + 4 hl + e (g < VPL / 4, e < 4).
+    float x[VPL];
+    float lmax = neg_inf();
 #pragma unroll
-        for (int ww = NM - 1; ww >= 0; --ww) w = m[ww] != 0u ? ww : w;
-        uint32_t mw = m[0];
+    for (int g = 0; g < VPL / 4; ++g) {
+      const int i0 = s0 + 4 * LPR * g + 4 * hl;
+      float4 v = make_float4(neg_inf(), neg_inf(), neg_inf(), neg_inf());
+      if (!keep_all && i0 < n_el) v = *reinterpret_cast<const float4*>(srow + i0);
+      x[4 * g] = v.x; x[4 * g + 1] = v.y; x[4 * g + 2] = v.z; x[4 * g + 3] = v.w;
+      lmax = fmaxf(lmax, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
+    }
+    // 2. Lower bound: the keep_n-th largest lane maximum of the segment.
+    const float srt = row_sort_desc<LPR>(lmax, hl);
+    const int kk = max(keep_n, 1) - 1;
+    const float thr = __shfl(srt, (lane & ~(LPR - 1)) + kk, kWave);
+    // 3. Marked entries (>= thr and rankable, i.e. > -inf).
+    uint32_t m[NM];
 #pragma unroll
-        for (int ww = 1; ww < NM; ++ww) mw = w == ww ? m[ww] : mw;
-        const int r = 32 * w + __builtin_ctz(mw);
-        const int i = 4 * LPR * (r / 4) + 4 * hl + (r % 4);
-        cand[slot][off] = (uint64_t(ord32(srow[i])) << 32) | uint32_t(0xffffffffu - uint32_t(i));
-        ++off;
-        mw &= mw - 1u;
+    for (int w = 0; w < NM; ++w) m[w] = 0u;
 #pragma unroll
-        for (int ww = 0; ww < NM; ++ww) m[ww] = w == ww ? mw : m[ww];
-        more = false;
+    for (int r = 0; r < VPL; ++r)
+      m[r / 32] |= (x[r] >= thr && x[r] > neg_inf()) ? (1u << (r % 32)) : 0u;
+    int cnt = 0;
 #pragma unroll
-        for (int ww = 0; ww < NM; ++ww) more |= m[ww] != 0u;
+    for (int w = 0; w < NM; ++w) cnt += __popc(m[w]);
+    int incl = cnt;
+#pragma unroll
+    for (int o = 1; o < LPR; o <<= 1) {
+      const int y = __shfl_up(incl, o, LPR);
+      if (hl >= o) incl += y;
+    }
+    const int total = __shfl(incl, (lane & ~(LPR - 1)) + LPR - 1, kWave);
+    bool seg_chosen = false;
+    uint64_t seg_key = 0;
+    if (keep_n > 0 && total <= LPR) {
+      int off = incl - cnt;
+      bool more = cnt > 0;
+      // marked entries, one per lane per round (their scores are re-read: L2)
+      while (__ballot(more) != 0) {
+        if (more) {
+          int w = 0;
+#pragma unroll
+          for (int ww = NM - 1; ww >= 0; --ww) w = m[ww] != 0u ? ww : w;
+          uint32_t mw = m[0];
+#pragma unroll
+          for (int ww = 1; ww < NM; ++ww) mw = w == ww ? m[ww] : mw;
+          const int r = 32 * w + __builtin_ctz(mw);
+          const int i = s0 + 4 * LPR * (r / 4) + 4 * hl + (r % 4);
+          cand[slot][off] = (uint64_t(ord32(srow[i])) << 32) | uint32_t(0xffffffffu - uint32_t(i));
+          ++off;
+          mw &= mw - 1u;
+#pragma unroll
+          for (int ww = 0; ww < NM; ++ww) m[ww] = w == ww ? mw : m[ww];
+          more = false;
+#pragma unroll
+          for (int ww = 0; ww < NM; ++ww) more |= m[ww] != 0u;
+        }
+      }
+      wave_lds_sync();
+      const uint64_t ck = hl < total ? cand[slot][hl] : 0ull;
+      wave_lds_sync();
+      seg_key = row_sort_desc64<LPR>(ck, hl);
+      seg_chosen = hl < keep_n;
+    } else if (keep_n > 0) {
+      // Rare: many entries at the bound.  The keep_n best, one at a time
+      // (largest score, then the lowest index holding it).
+      uint32_t key[VPL];
+#pragma unroll
+      for (int r = 0; r < VPL; ++r) key[r] = x[r] > neg_inf() ? ord32(x[r]) | 1u : 0u;
+      for (int q = 0; q < keep_n; ++q) {
+        uint32_t best = 0;
+#pragma unroll
+        for (int r = 0; r < VPL; ++r) best = max(best, key[r]);
+#pragma unroll
+        for (int o = LPR / 2; o >= 1; o >>= 1) best = max(best, xlane_u32(best, o));
+        int bi = 0x7fffffff;
+#pragma unroll
+        for (int r = 0; r < VPL; ++r)
+          bi = key[r] == best ? min(bi, s0 + 4 * LPR * (r / 4) + 4 * hl + (r % 4)) : bi;
+#pragma unroll
+        for (int o = LPR / 2; o >= 1; o >>= 1) bi = min(bi, __shfl_xor(bi, o, kWave));
+#pragma unroll
+        for (int r = 0; r < VPL; ++r)
+          key[r] = s0 + 4 * LPR * (r / 4) + 4 * hl + (r % 4) == bi ? 0u : key[r];
+        if (hl == q) {
+          seg_chosen = true;
+          seg_key = (uint64_t(ord32(srow[bi])) << 32) | uint32_t(0xffffffffu - uint32_t(bi));
+        }
       }
     }
-    wave_lds_sync();
-    const uint64_t ck = hl < total ? cand[slot][hl] : 0ull;
-    wave_lds_sync();
-    const uint64_t s64 = row_sort_desc64<LPR>(ck, hl);
-    chosen = hl < keep_n;
-    mine = s64;
-  } else if (keep_n > 0) {
-    // Rare: many entries at the bound.  The keep_n best, one at a time
-    // (largest score, then the lowest index holding it).
-    uint32_t key[VPL];
+    if (s0 == 0) {
+      chosen = seg_chosen;
+      mine = seg_key;
+    } else {
+      // Merge: the running list and the segment's, both descending with 0
+      // past their ends and keys distinct.  The larger of run[hl] and
+      // seg[LPR - 1 - hl] is a bitonic sequence holding the best LPR of
+      // both; a bitonic merge sorts it descending.
+      const uint64_t a = chosen ? mine : 0ull;
+      const uint64_t sk = seg_chosen ? seg_key : 0ull;
+      const int src = (lane & ~(LPR - 1)) + LPR - 1 - hl;
+      const uint64_t rv = (uint64_t(uint32_t(__shfl(int(uint32_t(sk >> 32)), src, kWave))) << 32) |
+                          uint32_t(__shfl(int(uint32_t(sk)), src, kWave));
+      uint64_t v = a > rv ? a : rv;
 #pragma unroll
-    for (int r = 0; r < VPL; ++r) key[r] = x[r] > neg_inf() ? ord32(x[r]) | 1u : 0u;
-    for (int q = 0; q < keep_n; ++q) {
-      uint32_t best = 0;
-#pragma unroll
-      for (int r = 0; r < VPL; ++r) best = max(best, key[r]);
-#pragma unroll
-      for (int o = LPR / 2; o >= 1; o >>= 1) best = max(best, xlane_u32(best, o));
-      int bi = 0x7fffffff;
-#pragma unroll
-      for (int r = 0; r < VPL; ++r)
-        bi = key[r] == best ? min(bi, 4 * LPR * (r / 4) + 4 * hl + (r % 4)) : bi;
-#pragma unroll
-      for (int o = LPR / 2; o >= 1; o >>= 1) bi = min(bi, __shfl_xor(bi, o, kWave));
-#pragma unroll
-      for (int r = 0; r < VPL; ++r)
-        key[r] = 4 * LPR * (r / 4) + 4 * hl + (r % 4) == bi ? 0u : key[r];
-      if (hl == q) {
-        chosen = true;
-        mine = (uint64_t(ord32(srow[bi])) << 32) | uint32_t(0xffffffffu - uint32_t(bi));
+      for (int j = LPR / 2; j > 0; j >>= 1) {
+        const uint64_t y = (uint64_t(xlane_u32(uint32_t(v >> 32), j)) << 32) | xlane_u32(uint32_t(v), j);
+        v = ((hl & j) == 0) ? (v > y ? v : y) : (v < y ? v : y);
       }
+      mine = v;
+      chosen = hl < keep_n && v != 0ull;
     }
   }
   // 4. Kept leaves (lanes < keep_n), forced leaves appended, ascending.
@@ -616,13 +651,13 @@ static hipError_t launch_bsa_topk_t(const LaunchShape& s, const float* S, int32_
   return hipGetLastError();
 }
 
-template <int LPR, int VPL>
+template <int LPR, int VPL, bool kLong = false>
 static hipError_t launch_bsa_topk_rows_t(const LaunchShape& s, const float* S, int32_t* idx,
                                          float* score, hipStream_t st) {
   constexpr int ROWS = 256 / LPR;
   dim3 grid((s.seq_len + ROWS - 1) / ROWS, s.batch * s.heads_kv);
   prof::Scope ps("bsa_topk", st);
-  hipLaunchKernelGGL((bsa_topk_rows_kernel<LPR, VPL>), grid, dim3(256), 0, st, S, idx, score,
+  hipLaunchKernelGGL((bsa_topk_rows_kernel<LPR, VPL, kLong>), grid, dim3(256), 0, st, S, idx, score,
                      s.seq_len, s.block, s.lv.size[0], s.topk, s.causal ? 1 : 0, s.force ? 1 : 0);
   return hipGetLastError();
 }
@@ -673,7 +708,9 @@ hipError_t launch_bsa(const LaunchShape& s, const void* q, const float* pyr, int
       if (m1 <= 32 * 16) return launch_bsa_topk_rows_t<32, 16>(s, S, idx, score, st);
       if (m1 <= 32 * 32) return launch_bsa_topk_rows_t<32, 32>(s, S, idx, score, st);
       if (m1 <= 32 * 64) return launch_bsa_topk_rows_t<32, 64>(s, S, idx, score, st);
-      return launch_bsa_topk_rows_t<64, kBsaMaxLeaves / kWave>(s, S, idx, score, st);
+      constexpr int V = kBsaMaxLeaves / kWave;
+      if (m1 <= kBsaMaxLeaves) return launch_bsa_topk_rows_t<64, V>(s, S, idx, score, st);
+      return launch_bsa_topk_rows_t<64, V, true>(s, S, idx, score, st);
     }
   } else if (s.bf16) {
     e = s.head_dim == 128 ? launch_bsa_scores_t<bf16_t, 128>(s, q, pyr, S, st)

@@ -92,8 +92,13 @@ int check_problem(const pisa_problem* p, int op, pisa::LaunchShape* s) {
   if (!layout(p->seq_len, p->block, &s->lv)) return fail(PISA_ERR_INVALID, "pyramid too tall");
   if (op == PISA_OP_ATTN_BWD && !pisa::attn_bwd_supported(*s))
     return fail(PISA_ERR_UNSUPPORTED, "the backward needs bf16, block 64 and a power-of-two group");
-  if (op == PISA_OP_BSA && s->lv.size[0] > 4096)
-    return fail(PISA_ERR_UNSUPPORTED, "BSA supports at most 4096 leaf blocks");
+  // Past 4096 leaf blocks only the MFMA path's Top-K (bf16, power-of-two
+  // group, leaf count a multiple of 4) takes rows in segments.
+  if (op == PISA_OP_BSA && s->lv.size[0] > 4096 &&
+      !(s->bf16 && (s->group & (s->group - 1)) == 0 && s->lv.size[0] % 4 == 0))
+    return fail(PISA_ERR_UNSUPPORTED,
+                "BSA past 4096 leaf blocks needs bf16, a power-of-two group and a multiple of 4 "
+                "leaf blocks");
   return PISA_OK;
 }
 

@@ -35,7 +35,8 @@
 // kept parents in the window: slot = 2 * (#kept parents before) + child, the
 // count running on across windows.  With 16 heads per group (4 queries per
 // wave) each wave instead packs the union of its queries' kept parents, 8 to
-// a 32-row tile, so that its work per window is bounded by 4 K parents.
+// a 32-row tile, so that its work per level is bounded by 4 K parents (its
+// windows are kTileRows long).
 //
 // Final (levels 2 and 1).  One lane per query reads its K kept level-3 nodes
 // and the stage-2 scores of their children, decides level 2 and then the
@@ -54,6 +55,10 @@ constexpr int kMaxK = 16;
 constexpr int kWaves = 4;        // independent wavefronts per workgroup
 constexpr int kDenseRows = 2048; // child rows per window of stage 1
 constexpr int kMaskWords = kDenseRows / 4 / 32;  // parent bitmask words per query
+// Child rows per window with union tiles (few queries per wave: one bitmap per
+// wave, a word per lane).
+constexpr int kTileRows = 4 * kDenseRows;
+constexpr int kTileWords = kTileRows / 4 / 32;
 // Per-query LDS arrays are stored slot-major ([slot][query]) so that lanes of
 // different queries always touch different banks.
 
@@ -283,7 +288,7 @@ __global__ __launch_bounds__(kWaves * kWave, (G >= 2 && D == 64) ? 3 : 2) void s
   __shared__ uint32_t chunks_s[2][kWaves][2];
   // The union of a wave's kept parents, as a bitmap and as an ascending list
   // (few queries per wave only).
-  __shared__ uint32_t umask_s[kWaves][kShared ? 1 : kMaskWords];
+  __shared__ uint32_t umask_s[kWaves][kShared ? 1 : kTileWords];
   __shared__ int ulist_s[kWaves][kShared ? 1 : kWave];
   // Kept-node lists when a query spans several lanes.
   __shared__ int kp_s[kWaves][kMaxK][G == 1 ? 1 : T];
@@ -366,9 +371,9 @@ __global__ __launch_bounds__(kWaves * kWave, (G >= 2 && D == 64) ? 3 : 2) void s
     const size_t child0 = head_rows + lv.off[l - 2];
 
     // The candidates' children are scored in windows of kDenseRows child
-    // rows w0 .. w0 + kDenseRows - 1 (parents pw = w0 / 4 onwards), in
-    // ascending order, so that a query's slot base runs on from one window to
-    // the next and its slots come out as from one pass over the level.
+    // rows (kTileRows with union tiles) w0 .. (parents pw = w0 / 4 onwards),
+    // in ascending order, so that a query's slot base runs on from one window
+    // to the next and its slots come out as from one pass over the level.
     int base[2] = {0, 0};
     auto window = [&](const int w0) __attribute__((always_inline)) {
       const int pw = w0 >> 2;
@@ -549,21 +554,21 @@ __global__ __launch_bounds__(kWaves * kWave, (G >= 2 && D == 64) ? 3 : 2) void s
         // level's size.  The parents are tiled in ascending order, so a
         // query's slot base advances over its own kept parents in the same
         // order as over the level's rows.
-        static_assert(T * kMaxK <= kWave && kMaskWords * 4 == kWave, "union of kept parents");
+        static_assert(T * kMaxK <= kWave && kTileWords == kWave, "union of kept parents");
         const uint32_t needers = (uint32_t)__ballot(need);  // query qi is lane qi
         if (needers != 0u) {
           // Bitmap of the union of the ranking queries' kept parents in the
-          // window: lane x then holds parents pw + 8x .. pw + 8x + 7.
-          if (lane < kMaskWords) umask_s[wave][lane] = 0u;
+          // window: lane x then holds parents pw + 32x .. pw + 32x + 31.
+          umask_s[wave][lane] = 0u;
           wave_lds_sync();
 #pragma unroll
           for (int i = 0; i < kMaxK; ++i) {
             const int p = kp(i) - pw;
-            if (need & (i < nk) & (p >= 0) & (p < 32 * kMaskWords))
+            if (need & (i < nk) & (p >= 0) & (p < 32 * kTileWords))
               atomicOr(&umask_s[wave][p >> 5], 1u << (p & 31));
           }
           wave_lds_sync();
-          const uint32_t ub = (umask_s[wave][lane >> 2] >> (8 * (lane & 3))) & 0xffu;
+          const uint32_t ub = umask_s[wave][lane];
           // Union rank of lane x's first parent (exclusive prefix of the
           // popcounts); the ascending union list.
           const int cnt = __popc(ub);
@@ -575,21 +580,19 @@ __global__ __launch_bounds__(kWaves * kWave, (G >= 2 && D == 64) ? 3 : 2) void s
           }
           const int rbase = incl - cnt;
           const int n_union = __builtin_amdgcn_readlane(incl, kWave - 1);
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            if ((ub >> j) & 1u)
-              ulist_s[wave][rbase + __popc(ub & ((1u << j) - 1u))] = pw + 8 * lane + j;
+          for (uint32_t bits = ub, o = rbase; bits != 0u; bits &= bits - 1u, ++o)
+            ulist_s[wave][o] = pw + 32 * lane + __builtin_ctz(bits);
           // A ranking query's kept parents as bits of their union ranks (its
           // decision lane; at most 64 ranks).
           uint32_t ur_lo = 0u, ur_hi = 0u;
 #pragma unroll
           for (int i = 0; i < kMaxK; ++i) {
-            const int p = kp(i) - pw;  // in the window: 0 .. 8 kWave - 1
-            const bool in = (p >= 0) & (p < 8 * kWave);
-            const int x = (p >> 3) & (kWave - 1);
+            const int p = kp(i) - pw;  // in the window: 0 .. 32 kWave - 1
+            const bool in = (p >= 0) & (p < 32 * kWave);
+            const int x = (p >> 5) & (kWave - 1);
             const int rb = __shfl(rbase, x, kWave);
             const uint32_t bb = (uint32_t)__shfl((int)ub, x, kWave);
-            const int r = rb + __popc(bb & ((1u << (p & 7)) - 1u));
+            const int r = rb + __popc(bb & ((1u << (p & 31)) - 1u));
             const uint32_t bit = (need && i < nk && in) ? 1u << (r & 31) : 0u;
             ur_lo |= r < 32 ? bit : 0u;
             ur_hi |= r < 32 ? 0u : bit;
@@ -688,10 +691,11 @@ __global__ __launch_bounds__(kWaves * kWave, (G >= 2 && D == 64) ? 3 : 2) void s
     // A level within one window (every level up to 256K tokens at C = 64)
     // runs a copy of the window code compiled for w0 = 0.
     if (size_l > topk) {
-      if (m_child <= kDenseRows) {
+      constexpr int kWin = kShared ? kDenseRows : kTileRows;
+      if (m_child <= kWin) {
         window(0);
       } else {
-        for (int w0 = 0; w0 < m_child; w0 += kDenseRows) window(w0);
+        for (int w0 = 0; w0 < m_child; w0 += kWin) window(w0);
       }
     }
 

@@ -205,7 +205,10 @@ int pisa_select_noalloc(const pisa_problem* problem, const void* q, const void* 
  * written in full to the workspace, then the forced blocks plus the best
  * K-#F others (same forcing, causal and tie rules as pisa_select).
  *   q, pyramid, block_idx, block_score: as pisa_select
- *   ws/ws_bytes: pisa_workspace_bytes(PISA_OP_BSA) bytes (holds the scores) */
+ *   ws/ws_bytes: pisa_workspace_bytes(PISA_OP_BSA) bytes (holds the scores:
+ *                B * Hkv * N * M1 fp32, M1 = ceil(N / C), plus the bf16 planes)
+ * Up to 4096 leaf blocks for every supported shape; beyond that only for bf16,
+ * a power-of-two group and M1 a multiple of 4 (else PISA_ERR_UNSUPPORTED). */
 int pisa_bsa_select(const pisa_problem* problem, const void* q, const float* pyramid,
                     int32_t* block_idx, float* block_score, void* ws, size_t ws_bytes,
                     void* stream);

@@ -140,9 +140,17 @@ def test_null_pointers_and_workspace_rejected():
     nc = problem(flags=0)
     assert L.pisa_decode_step(ctypes.byref(nc), ptr, ptr, ptr, ptr, ptr, ptr, None, ptr, None,
                               None, 0, None) == _lib.PISA_ERR_INVALID
+    # BSA past 4096 leaf blocks: the MFMA path only (bf16, power-of-two
+    # group, a multiple of 4 leaf blocks), whose Top-K takes rows in segments
     big = problem(seq_len=64 * 4097)
     assert L.pisa_bsa_select(ctypes.byref(big), ptr, ptr, ptr, None, ptr, 1 << 60,
                              None) == _lib.PISA_ERR_UNSUPPORTED
+    long_ok = problem(seq_len=64 * 4100)
+    assert L.pisa_workspace_bytes(ctypes.byref(long_ok), _lib.PISA_OP_BSA, ctypes.byref(sz)) == 0
+    assert sz.value >= 4 * 64 * 4100 * 4100 * 4
+    long_f32 = problem(seq_len=64 * 4100, dtype=_lib.PISA_F32)
+    assert L.pisa_workspace_bytes(ctypes.byref(long_f32), _lib.PISA_OP_BSA,
+                                  ctypes.byref(sz)) == _lib.PISA_ERR_UNSUPPORTED
     assert L.pisa_workspace_bytes(pp, 99, ctypes.byref(sz)) == _lib.PISA_ERR_INVALID
     assert L.pisa_status_string(_lib.PISA_ERR_WORKSPACE) == b"workspace missing or too small"
 

@@ -311,9 +311,10 @@ def test_prefill_level2_beyond_dense_rows(n, hq, d, k):
     window of the first selection stage (2048), so that its level-3 decision
     runs over several windows: 262272 tokens (level 2: 2049 rows, the second
     window one row) at 1, 2 and 16 query heads per KV head, and 524288
-    (level 2: two full windows).  N(0,1) entries, 200 sampled rows:
-    selections bit-exact past the margin (at least 20 rows), attention within
-    the bf16 bounds."""
+    (level 2: two full windows).  At 524288 BSA as well: 8192 leaf blocks, so
+    its Top-K takes the longer rows in two segments.  N(0,1) entries, 200
+    sampled rows: selections bit-exact past the margin (at least 20 rows),
+    attention within the bf16 bounds."""
     prob = Problem(1, hq, 1, n, d, block=64, topk=k, dtype=torch.bfloat16)
     announce(f"prefill N={n} G={hq} d={d} K={k} unit (level 2 beyond one window)")
     inp = prefill_inputs(1, hq, 1, n, d, torch.bfloat16, seed=7100 + hq, recipe="unit",
@@ -321,6 +322,9 @@ def test_prefill_level2_beyond_dense_rows(n, hq, d, k):
     pyr = pisa_build_pyramid(prob, inp.k)
     idx, score = pisa_select(prob, inp.q, inp.k, pyr)
     out, lse = pisa_block_sparse_attn(prob, inp.q, inp.k, inp.v, idx)
+    with_bsa = -(-n // 64) % 4 == 0
+    if with_bsa:
+        bidx, bscore = pisa_bsa_select(prob, inp.q, pyr)
     torch.cuda.synchronize()
     check_pyramid(pyr, inp.k, prob, [(0, 0)])
     rows = sample_rows(n, 64, k, 200, 7100)
@@ -334,6 +338,15 @@ def test_prefill_level2_beyond_dense_rows(n, hq, d, k):
           flush=True)
     assert not tl.mismatches, tl.mismatches[:3]
     assert tl.compared >= 20, (tl.compared, tl.rows)
+    if with_bsa:
+        tb = parity.compare_selection("bsa", bidx[0, 0].cpu().numpy(), bscore[0, 0].cpu().numpy(),
+                                      qg, keys, levels, rows, 64, k, True, True,
+                                      prob.logit_scale, parity.Tally())
+        long_rows = sum(1 for r in rows if r // 64 >= 4096)
+        print(f"  bsa: compared {tb.compared}/{tb.rows} rows ({long_rows} past 4096 leaves), "
+              f"mismatches {len(tb.mismatches)}", flush=True)
+        assert not tb.mismatches, tb.mismatches[:3]
+        assert tb.compared >= 20 and long_rows >= 50, (tb.compared, long_rows)
     parity.compare_attention(parity.to_np(out[0, 0:hq]), lse[0, 0:hq].cpu().numpy(), qg, keys,
                              vals, idx[0, 0].cpu().numpy(), rows, 64, True, prob.logit_scale,
                              False)

@@ -161,6 +161,28 @@ def attended_keys(n, c, k):
 # GPU timing helpers
 # ----------------------------------------------------------------------------
 
+def copy_bandwidth(dev, mib=1024, reps=5):
+    """GB/s of a plain device-to-device copy of `mib` MiB (bytes read plus
+    bytes written over the copy's time): the HBM bandwidth a streaming kernel
+    can reach on this GPU, beside the 8 TB/s specification."""
+    import torch
+    src = torch.ones(mib << 18, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    gbs = 2 * src.numel() * 4 / (ms * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return gbs
+
+
 def timed_call(fn, reps, warmup):
     import torch
     for _ in range(warmup):
@@ -311,6 +333,7 @@ def run(args):
                        "eq. (2) flops vs unpacked fp32 FMA"),
         "attn_combine": ("hbm", B * H * N * d * elt, HBM_PEAK_GBS, "GB/s", "O written"),
     }
+    copy_gbs = copy_bandwidth(dev)
     kernels_roofline = {}
     for kname, (kb, kw, kp, ku, basis) in roof_table.items():
         if kname in kernels and kernels[kname] > 0:
@@ -318,6 +341,14 @@ def run(args):
             ka = kw / (kernels[kname] * 1e-3) / ks
             kernels_roofline[kname] = {"bound": kb, "achieved": round(ka, 1), "peak": kp,
                                        "unit": ku, "frac": round(ka / kp, 4), "basis": basis}
+            if ku == "GB/s":
+                kernels_roofline[kname]["frac_of_copy"] = round(ka / copy_gbs, 4)
+            kt = stored_traffic(kname)
+            if kt is not None:
+                # HBM bytes the counters saw (on the current sources) per launch
+                tg = kt / (kernels[kname] * 1e-3) / 1e9
+                kernels_roofline[kname]["traffic_gbs"] = round(tg, 1)
+                kernels_roofline[kname]["traffic_frac_of_copy"] = round(tg / copy_gbs, 4)
             kc = stored_counters(kname)
             if kc:
                 kernels_roofline[kname]["mfma_busy_frac"] = kc["mfma_busy_frac"]
@@ -337,6 +368,7 @@ def run(args):
         # the counters' HBM bytes over the same launch time, against the HBM peak
         roof["traffic_gbs"] = traffic / (kernels[dominant] * 1e-3) / 1e9
         roof["traffic_frac_of_hbm_peak"] = roof["traffic_gbs"] / HBM_PEAK_GBS
+        roof["traffic_frac_of_copy"] = roof["traffic_gbs"] / copy_gbs
     counters = stored_counters(dominant)
     if counters is not None:
         # SQ_VALU_MFMA_BUSY_CYCLES over (GRBM_GUI_ACTIVE per XCD x 1024 SIMDs), and
@@ -370,12 +402,14 @@ def run(args):
                         "source_hash": source_hash()},
         "roofline": roof,
         "kernels_roofline": kernels_roofline,
+        "hbm_copy_gbs": copy_gbs,
     }
 
     if not args.no_backward:
         result["backward"] = backward_bench(prob, inp, idx, dev)
     if not args.no_decode:
         result["decode"] = decode_bench(args)
+        result["decode"]["frac_of_copy"] = result["decode"]["achieved_gbs"] / copy_gbs
     if not args.no_sweep:
         result["selection_sweep"] = selection_sweep(args)
         if not args.no_sweep_g16:

@@ -266,7 +266,7 @@ __global__ __launch_bounds__(kWaves * kWave, (G >= 2 && D == 64) ? 3 : 2) void s
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ phi, const bf16_t* __restrict__ plo,
     int* __restrict__ s1_nodes, int heads_q, int heads_kv,
     int n_tok, int block, int topk, int causal, int force, float scale_log2, LevelTable lv,
-    int split_level) {
+    int split_level, int tile_rows) {
   constexpr int T = kWave / G;  // queries per wave
   constexpr int KSTEPS = D / 16;
   // With 8 or more queries per wave the waves of a workgroup need nearly the
@@ -564,7 +564,7 @@ __global__ __launch_bounds__(kWaves * kWave, (G >= 2 && D == 64) ? 3 : 2) void s
 #pragma unroll
           for (int i = 0; i < kMaxK; ++i) {
             const int p = kp(i) - pw;
-            if (need & (i < nk) & (p >= 0) & (p < 32 * kTileWords))
+            if (need & (i < nk) & (p >= 0) & (p < (tile_rows >> 2)))
               atomicOr(&umask_s[wave][p >> 5], 1u << (p & 31));
           }
           wave_lds_sync();
@@ -587,8 +587,8 @@ __global__ __launch_bounds__(kWaves * kWave, (G >= 2 && D == 64) ? 3 : 2) void s
           uint32_t ur_lo = 0u, ur_hi = 0u;
 #pragma unroll
           for (int i = 0; i < kMaxK; ++i) {
-            const int p = kp(i) - pw;  // in the window: 0 .. 32 kWave - 1
-            const bool in = (p >= 0) & (p < 32 * kWave);
+            const int p = kp(i) - pw;  // in the window: 0 .. tile_rows / 4 - 1
+            const bool in = (p >= 0) & (p < (tile_rows >> 2));
             const int x = (p >> 5) & (kWave - 1);
             const int rb = __shfl(rbase, x, kWave);
             const uint32_t bb = (uint32_t)__shfl((int)ub, x, kWave);
@@ -691,11 +691,12 @@ __global__ __launch_bounds__(kWaves * kWave, (G >= 2 && D == 64) ? 3 : 2) void s
     // A level within one window (every level up to 256K tokens at C = 64)
     // runs a copy of the window code compiled for w0 = 0.
     if (size_l > topk) {
-      constexpr int kWin = kShared ? kDenseRows : kTileRows;
-      if (m_child <= kWin) {
+      // tile_rows: a multiple of 64 up to kTileRows (the union bitmap's span)
+      const int win = kShared ? kDenseRows : tile_rows;
+      if (m_child <= win) {
         window(0);
       } else {
-        for (int w0 = 0; w0 < m_child; w0 += kWin) window(w0);
+        for (int w0 = 0; w0 < m_child; w0 += win) window(w0);
       }
     }
 

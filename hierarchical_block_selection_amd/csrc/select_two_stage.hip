@@ -53,6 +53,11 @@ constexpr int kS2ItemRows = 1024; // (pair, head) rows per stage-2 work item (de
 //                       node's keys: a power of two in [64, 4096];
 //   PISA_S2_BATCH_ROWS  rows staged in LDS per batch: 32, 64 or 128
 //                       (default 64 for one head per KV head, else 128).
+// and of stage 1:
+//   PISA_S1_TILE_ROWS   child rows per window of the union tiles (16 heads
+//                       per KV head): a multiple of 64 in [64, 8192], default
+//                       8192; smaller windows only serve tests of the window
+//                       loop at moderate lengths.
 // Other values fall back to the defaults.  The workspace size follows the
 // item size, so set them before pisa_workspace_bytes.
 int env_int(const char* name, int dflt) {
@@ -70,6 +75,10 @@ int s2_batch_rows(int group) {
   const int dflt = group == 1 ? kS2Rows : kS2RowsGrouped;
   const int x = env_int("PISA_S2_BATCH_ROWS", dflt);
   return (x == 32 || x == 64 || x == 128) ? x : dflt;
+}
+int s1_tile_rows() {
+  const int x = env_int("PISA_S1_TILE_ROWS", lpq::kTileRows);
+  return (x >= 64 && x <= lpq::kTileRows && x % 64 == 0) ? x : lpq::kTileRows;
 }
 constexpr int kS2Cols = 32;      // MFMA 32x32x16: 32 (query, head) columns
 constexpr int kScoreStride = 8;  // floats per pair: 4 leaf LSE, 2 level-2, 2 pad
@@ -655,7 +664,7 @@ hipError_t stage1_lpq_launch(const LaunchShape& s, const void* q, const float* p
   hipLaunchKernelGGL((lpq::stage1_kernel<D, G>), grid, dim3(lpq::kWaves * kWave), 0, st,
                      static_cast<const bf16_t*>(q), w.plane_hi, w.plane_lo, w.s1_nodes,
                      s.heads_q, s.heads_kv, s.seq_len, s.block, s.topk, s.causal ? 1 : 0,
-                     s.force ? 1 : 0, s.scale * kLog2e, s.lv, kSplitLevel);
+                     s.force ? 1 : 0, s.scale * kLog2e, s.lv, kSplitLevel, s1_tile_rows());
   return hipGetLastError();
 }
 

@@ -175,7 +175,9 @@ int pisa_pyramid_append(const pisa_problem* problem, const int32_t* cache_len,
  * (query, head) columns served by one load of a level-3 node's keys (power of
  * two in [64, 4096], default 1024; the workspace size follows it), and
  * PISA_S2_BATCH_ROWS, the columns staged per batch (32, 64 or 128; default 64
- * with one query head per KV head, else 128).  Results do not depend on them. */
+ * with one query head per KV head, else 128), and PISA_S1_TILE_ROWS, the child
+ * rows per window of the first stage with 16 query heads per KV head (multiple
+ * of 64 in [64, 8192], default 8192).  Results do not depend on them. */
 int pisa_select(const pisa_problem* problem, const void* q, const void* k, const float* pyramid,
                 int32_t* block_idx, float* block_score, int32_t strategy, void* ws,
                 size_t ws_bytes, void* stream);

@@ -365,6 +365,44 @@ def test_pages_latency_shape_g16(n, d, k):
     run_and_compare(cfg, "unit", [(0, 0)], n_random=160, min_rows=60)
 
 
+def test_union_tile_windows():
+    """The union tiles' window loop (16 query heads per KV head), which the
+    default 8192-row windows reach only past 1M tokens: with 128-row windows
+    (PISA_S1_TILE_ROWS) a 64K prefill scores its level-3 decision over 4
+    windows and its level-4 decision over 2.  The selection must equal the
+    one-window run bit for bit (each candidate's score does not depend on the
+    tile it lands in) and the oracle past the margin."""
+    import os
+    n, d, k = 65536, 64, 8
+    prob = Problem(1, 16, 1, n, d, block=64, topk=k, dtype=torch.bfloat16)
+    announce(f"prefill N={n} G=16 d={d} K={k} unit, 128-row union-tile windows")
+    inp = prefill_inputs(1, 16, 1, n, d, torch.bfloat16, seed=9300, recipe="unit", device=DEV)
+    pyr = pisa_build_pyramid(prob, inp.k)
+    idx1, score1 = pisa_select(prob, inp.q, inp.k, pyr)
+    saved = os.environ.get("PISA_S1_TILE_ROWS")
+    os.environ["PISA_S1_TILE_ROWS"] = "128"
+    try:
+        idx2, score2 = pisa_select(prob, inp.q, inp.k, pyr)
+        torch.cuda.synchronize()
+    finally:
+        if saved is None:
+            del os.environ["PISA_S1_TILE_ROWS"]
+        else:
+            os.environ["PISA_S1_TILE_ROWS"] = saved
+    assert torch.equal(idx1, idx2) and torch.equal(score1, score2)
+    rows = sample_rows(n, 64, k, 120, 9300)
+    keys = parity.to_np(inp.k[0, 0])
+    qg = parity.to_np(inp.q[0])
+    levels = oracle.build_pyramid(keys, 64)
+    tl = parity.compare_selection("pisa", idx2[0, 0].cpu().numpy(), score2[0, 0].cpu().numpy(),
+                                  qg, keys, levels, rows, 64, k, True, True, prob.logit_scale,
+                                  parity.Tally())
+    print(f"  pisa: compared {tl.compared}/{tl.rows} rows, mismatches {len(tl.mismatches)}",
+          flush=True)
+    assert not tl.mismatches, tl.mismatches[:3]
+    assert tl.compared >= 40, (tl.compared, tl.rows)
+
+
 def test_large_group_scores():
     """Peaked attention and large group-summed scores (queries N(0,64), keys
     N(0,1): group sums of several hundred nats over 16 query heads): the

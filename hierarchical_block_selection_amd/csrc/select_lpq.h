@@ -114,6 +114,50 @@ __device__ __forceinline__ uint32_t forced_slots(int n_valid, bool causal, bool 
   return m;
 }
 
+// Lane permutations inside a row of 16 lanes as DPP operand modifiers (no
+// LDS crossbar): swap neighbours, swap pairs, mirror each half row (i <-> 7 - i),
+// mirror the row (i <-> 15 - i).  Applied in this order with a commutative
+// operation they combine all lanes of an aligned group of 2, 4, 8 or 16; the
+// lanes may associate differently, so for floating-point sums only one lane's
+// total should be used.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xf, 0xf, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL,
+                                                             0xf, 0xf, false));
+}
+constexpr int kDppSwap1 = 0xb1;       // quad_perm [1, 0, 3, 2]
+constexpr int kDppSwap2 = 0x4e;       // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141; // row_half_mirror
+constexpr int kDppMirror = 0x140;     // row_mirror
+template <int G>
+__device__ __forceinline__ float group_add(float v) {
+  if (G >= 2) v += dpp_f32<kDppSwap1>(v);
+  if (G >= 4) v += dpp_f32<kDppSwap2>(v);
+  if (G >= 8) v += dpp_f32<kDppHalfMirror>(v);
+  if (G >= 16) v += dpp_f32<kDppMirror>(v);
+  return v;
+}
+template <int G>
+__device__ __forceinline__ float group_max(float v) {
+  if (G >= 2) v = fmaxf(v, dpp_f32<kDppSwap1>(v));
+  if (G >= 4) v = fmaxf(v, dpp_f32<kDppSwap2>(v));
+  if (G >= 8) v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
+  if (G >= 16) v = fmaxf(v, dpp_f32<kDppMirror>(v));
+  return v;
+}
+template <int G>
+__device__ __forceinline__ uint32_t group_or(uint32_t v) {
+  if (G >= 2) v |= dpp_u32<kDppSwap1>(v);
+  if (G >= 4) v |= dpp_u32<kDppSwap2>(v);
+  if (G >= 8) v |= dpp_u32<kDppHalfMirror>(v);
+  if (G >= 16) v |= dpp_u32<kDppMirror>(v);
+  return v;
+}
+
 // Kept slots of a ranked level: the forced ones plus the best K - #F of the
 // other valid ones by score s[j].
 __device__ __forceinline__ uint32_t top_slots(int n_valid, int topk, uint32_t fm,
@@ -150,8 +194,7 @@ __device__ __forceinline__ uint32_t top_slots_group(int n_valid, int topk, uint3
   float smax = neg_inf();
 #pragma unroll
   for (int i = 0; i < S; ++i) smax = ((rm >> (sub * S + i)) & 1u) ? fmaxf(smax, s[i]) : smax;
-#pragma unroll
-  for (int o = 1; o < G; o <<= 1) smax = fmaxf(smax, __shfl_xor(smax, o, kWave));
+  smax = group_max<G>(smax);
   uint32_t key[S];
 #pragma unroll
   for (int i = 0; i < S; ++i) {
@@ -188,8 +231,7 @@ __device__ __forceinline__ uint32_t top_slots_group(int n_valid, int topk, uint3
 #pragma unroll
   for (int i = 0; i < S; ++i)
     km |= (sub * S + i < keep_n) ? (1u << (31 - (key[i] & 31u))) : 0u;
-#pragma unroll
-  for (int o = 1; o < G; o <<= 1) km |= (uint32_t)__shfl_xor((int)km, o, kWave);
+  km = group_or<G>(km);
   return km;
 }
 
@@ -506,10 +548,7 @@ __global__ __launch_bounds__(kWaves * kWave, (G >= 2 && D == 64) ? 3 : 2) void s
                     const float mx = fmaxf(z0, z1), mn = fminf(z0, z1);
                     float v =
                         fmaf(mx, scale_log2, fast_log2(1.f + fast_exp2((mn - mx) * scale_log2)));
-                    if (G >= 2) v += __shfl_xor(v, 1, kWave);
-                    if (G >= 4) v += __shfl_xor(v, 2, kWave);
-                    if (G >= 8) v += __shfl_xor(v, 4, kWave);
-                    if (G >= 16) v += __shfl_xor(v, 8, kWave);
+                    v = group_add<G>(v);  // the writer lane's total is stored
                     scol[cb][w ? 2 * pslot + m : kSlots] = v;
                   }
                 }
@@ -668,10 +707,7 @@ __global__ __launch_bounds__(kWaves * kWave, (G >= 2 && D == 64) ? 3 : 2) void s
                     const float mx = fmaxf(z0, z1), mn = fminf(z0, z1);
                     float v =
                         fmaf(mx, scale_log2, fast_log2(1.f + fast_exp2((mn - mx) * scale_log2)));
-                    if (G >= 2) v += __shfl_xor(v, 1, kWave);
-                    if (G >= 4) v += __shfl_xor(v, 2, kWave);
-                    if (G >= 8) v += __shfl_xor(v, 4, kWave);
-                    if (G >= 16) v += __shfl_xor(v, 8, kWave);
+                    v = group_add<G>(v);  // the writer lane's total is stored
                     scol[cb][w ? 2 * pslot + m : kSlots] = v;
                   }
                 }

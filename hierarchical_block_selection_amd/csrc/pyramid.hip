@@ -10,7 +10,8 @@
 // several rows per load), reduces the rows across lanes, then the workgroup
 // builds levels 2..j+1 of its chunk in LDS.  Pass 2 (top kernel): one
 // workgroup of 1024 threads per KV head builds levels j+2..L from level j+1
-// (M_1/16 rows), keeping every level after the first in LDS when it fits.
+// (M_1/16 rows): the first of them with float4 loads, four outputs' worth
+// requested per thread at once, the rest in LDS when they fit.
 #include "pisa_common.h"
 #include "pisa_launch.h"
 
@@ -53,6 +54,7 @@ __global__ __launch_bounds__(kPyrThreads) void pyramid_chunk_kernel(
 #pragma unroll
       for (int e = 0; e < VEC; ++e) acc[e] += v[e];
     }
+    }
 #pragma unroll
     for (int o = LPR; o < kWave; o <<= 1)
 #pragma unroll
@@ -91,19 +93,56 @@ __global__ __launch_bounds__(kPyrThreads) void pyramid_chunk_kernel(
   }
 }
 
-// Levels first_level..L.  The first of them is read from global memory; the
+// Levels first_level..L.  The first of them is built from global memory
+// with every thread's loads of a batch requested together (src and dst share
+// the pyramid buffer, so a plain loop would wait on each load in turn); the
 // rest ping-pong in LDS (dynamic, two buffers) when use_lds is set.
 template <int D>
 __global__ __launch_bounds__(kTopThreads) void pyramid_top_kernel(float* __restrict__ pyr,
                                                                    LevelTable lv, int first_level,
                                                                    int use_lds) {
   extern __shared__ float top_lds[];
+  constexpr int D4 = D / 4;
+  constexpr int NB = 4;  // float4 outputs per thread per batch
   float* pb = pyr + (size_t)blockIdx.x * lv.rows * D;
   float* bufs[2] = {top_lds, top_lds + (size_t)lv.size[first_level - 1] * D};
-  for (int l = first_level; l <= lv.n; ++l) {
+  {
+    const int l = first_level;
     const int m_prev = lv.size[l - 2], m_cur = lv.size[l - 1];
-    const bool from_lds = use_lds && l > first_level;
-    const float* src = from_lds ? bufs[(l - first_level - 1) & 1] : pb + (size_t)lv.off[l - 2] * D;
+    const float4* src = reinterpret_cast<const float4*>(pb + (size_t)lv.off[l - 2] * D);
+    float4* dst = reinterpret_cast<float4*>(pb + (size_t)lv.off[l - 1] * D);
+    float4* ldst = reinterpret_cast<float4*>(bufs[0]);
+    const int total = m_cur * D4;
+    for (int x0 = threadIdx.x; x0 < total; x0 += NB * kTopThreads) {
+      float4 a[NB], b[NB];
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        const int x = min(x0 + k * kTopThreads, total - 1);
+        const int node = x / D4, c4 = x % D4;
+        a[k] = src[(size_t)(2 * node) * D4 + c4];
+        b[k] = src[(size_t)min(2 * node + 1, m_prev - 1) * D4 + c4];
+      }
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        const int x = x0 + k * kTopThreads;
+        if (x >= total) break;
+        const int node = x / D4;
+        float4 v = a[k];
+        if (2 * node + 1 < m_prev) {
+          v.x = 0.5f * (v.x + b[k].x);
+          v.y = 0.5f * (v.y + b[k].y);
+          v.z = 0.5f * (v.z + b[k].z);
+          v.w = 0.5f * (v.w + b[k].w);
+        }
+        dst[x] = v;
+        if (use_lds) ldst[x] = v;
+      }
+    }
+    __syncthreads();
+  }
+  for (int l = first_level + 1; l <= lv.n; ++l) {
+    const int m_prev = lv.size[l - 2], m_cur = lv.size[l - 1];
+    const float* src = use_lds ? bufs[(l - first_level - 1) & 1] : pb + (size_t)lv.off[l - 2] * D;
     float* ldst = bufs[(l - first_level) & 1];
     float* dst = pb + (size_t)lv.off[l - 1] * D;
     for (int x = threadIdx.x; x < m_cur * D; x += kTopThreads) {

@@ -6,13 +6,16 @@ key pyramid -> PISA Top-K block selection -> block-sparse attention, on the
 N(0, 1/d) entries).  Inputs are resident in HBM before timing starts.
 
 Prints ONE JSON line: tokens/s of the whole step, per-stage times, the
-selection-latency comparison with the GPU BSA baseline across N (crossover),
+selection-latency comparison with the GPU BSA baseline across N (crossover;
+three sweeps: 4 heads at d = 128 with K = 16 and with K = 8, and the pages'
+latency shape of 16 query heads per KV head at d = 64, K = 8),
 the roofline of the dominant kernel (HIP events on the launch stream) and the
 CPU oracle timed on a bounded sample of the same workload (cpu_baseline).
 Beside it (not part of the step): the backward of the block-sparse attention
 with the step's block lists held fixed, and the GQA decode step.
 
-Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--no-sweep] [--no-cpu] [--no-decode]
+Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--no-sweep] [--no-sweep-g16]
+                       [--no-sweep-k8] [--no-cpu] [--no-decode]
                        [--no-backward] [--no-cold] [--cpu-seconds 15] [--calibrate-copy-mb 0]
 """
 from __future__ import annotations
@@ -417,6 +420,11 @@ def run(args):
             result["selection_sweep_g16"] = selection_sweep(
                 args, heads_q=16, heads_kv=1, head_dim=64, topk=8,
                 sizes=(16384, 65536, 131072, 262144, 524288, 1048576), seed=4100)
+        if not args.no_sweep_k8:
+            # one query head per KV head as the default sweep, at the pages' K = 8
+            result["selection_sweep_k8"] = selection_sweep(
+                args, heads_q=4, heads_kv=4, head_dim=128, topk=8,
+                sizes=(16384, 32768, 65536, 131072, 262144), seed=4200)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(args, inp, prob)
     return result
@@ -616,6 +624,10 @@ def selection_sweep(args, heads_q=4, heads_kv=4, head_dim=128, topk=16,
     if cross is None and timed:
         cross = f"> {timed[-1]['N']}"
     return {"points": pts, "crossover_N": cross,
+            # the PISA reading page's order-of-magnitude estimate of the
+            # crossover (section 5.2): N/C summaries per query for BSA against
+            # g*K*C raw leaf keys for PISA, equal at N = g*K*C^2
+            "estimate_N": 2 * topk * 64 * 64,
             "note": f"timings include pyramid construction (all levels) for both selectors; "
                     f"attention excluded; Hq={heads_q} Hkv={heads_kv}, d={head_dim}, C=64, "
                     f"K={topk}, bf16; bsa_hbm_frac: algorithmic bytes of each BSA kernel "
@@ -790,6 +802,8 @@ def main():
                     help="comma-separated subset of the selection sweeps' N (default: all)")
     ap.add_argument("--no-sweep-g16", action="store_true",
                     help="skip the 16-heads-per-KV-head selection sweep")
+    ap.add_argument("--no-sweep-k8", action="store_true",
+                    help="skip the K = 8 selection sweep (4 heads, d = 128)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")

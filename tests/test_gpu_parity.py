@@ -146,6 +146,14 @@ def test_workload_parity_unit_variant(name):
     run_and_compare(WORKLOADS[name], "unit", HEADS[name], n_random=n_random, min_rows=100)
 
 
+def test_mha_k8_sweep_shape():
+    """The shape of the benchmark's K = 8 selection sweep (4 heads, one per KV
+    head, d = 128) at 64K tokens, with N(0,1) entries: at least 100 rows per
+    selector compared bit for bit past the margin."""
+    cfg = dict(WORKLOADS["c4a"], seq_len=65536, topk=8, seed=4220)
+    run_and_compare(cfg, "unit", [(0, 0), (0, 3)], n_random=192, min_rows=100)
+
+
 @pytest.mark.parametrize("name", ["c2", "c3", "c4a", "c4b", "c4c"])
 def test_workload_parity_as_configured(name):
     """Workload as configured (N(0,1/d), needles where stated): near-ties dominate,

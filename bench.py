@@ -578,8 +578,8 @@ def selection_sweep(args, heads_q=4, heads_kv=4, head_dim=128, topk=16,
             pisa.pisa_bsa_select(prob, inp.q, pyr, idx, None, workspace=wbsa, want_score=False)
 
         reps = 5 if n <= 65536 else 3
-        p_ms = timed_call(pisa_sel, reps, 1)
-        b_ms = timed_call(bsa_sel, reps, 1) if bsa_ok else None
+        p_ms = timed_call(pisa_sel, reps, 3)
+        b_ms = timed_call(bsa_sel, reps, 3) if bsa_ok else None
         # one more call of each with the library's per-kernel events
         kern = {"bsa": {}}
         for name, fn in (("pisa", pisa_sel), ("bsa", bsa_sel)):
@@ -626,8 +626,11 @@ def selection_sweep(args, heads_q=4, heads_kv=4, head_dim=128, topk=16,
     return {"points": pts, "crossover_N": cross,
             # the PISA reading page's order-of-magnitude estimate of the
             # crossover (section 5.2): N/C summaries per query for BSA against
-            # g*K*C raw leaf keys for PISA, equal at N = g*K*C^2
-            "estimate_N": 2 * topk * 64 * 64,
+            # g*K*C raw leaf keys for PISA, equal at N = g*K*C^2 for one head;
+            # with G query heads per KV head PISA pays it per head (eq. (11)
+            # sums per-head LSEs) while this BSA scores one group-summed query
+            # (eq. (1) is linear in q), so the balance moves to g*K*C^2*G
+            "estimate_N": 2 * topk * 64 * 64 * (heads_q // heads_kv),
             "note": f"timings include pyramid construction (all levels) for both selectors; "
                     f"attention excluded; Hq={heads_q} Hkv={heads_kv}, d={head_dim}, C=64, "
                     f"K={topk}, bf16; bsa_hbm_frac: algorithmic bytes of each BSA kernel "

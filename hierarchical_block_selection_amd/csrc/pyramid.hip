@@ -54,7 +54,6 @@ __global__ __launch_bounds__(kPyrThreads) void pyramid_chunk_kernel(
 #pragma unroll
       for (int e = 0; e < VEC; ++e) acc[e] += v[e];
     }
-    }
 #pragma unroll
     for (int o = LPR; o < kWave; o <<= 1)
 #pragma unroll

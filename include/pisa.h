@@ -42,6 +42,12 @@
  *   returns < 0 and has written nothing.  A failed launch returns PISA_ERR_HIP;
  *   pisa_last_error() then describes it (thread-local text).
  * - Outputs are bitwise reproducible run to run (no floating-point atomics).
+ * - No call clears memory with hipMemsetAsync (workspaces are initialised by
+ *   the library's own kernels) or waits on the host, so the launches an entry
+ *   point enqueues can be captured into a HIP graph and replayed.  Exceptions:
+ *   the per-kernel events of pisa_profile_enable, and pisa_select_noalloc's
+ *   first call on a device, which looks its scratch up (make one call before
+ *   capturing).
  *
  * Supported now: d in {64, 128}; C in {16, 32, 64}; g = 2; 1 <= K <= 32;
  * K >= 3 with PISA_FORCE_FIRST_PREV (K >= 1 otherwise); Hq % Hkv == 0 with

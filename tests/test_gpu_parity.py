@@ -220,6 +220,52 @@ def test_edge_shapes_every_row(case):
                                  fp32=dtype == torch.float32)
 
 
+BATCHED = [
+    # (B, N, C, d, K, Hq, Hkv, dtype): several sequences per call on the paths
+    # the workloads take (two-stage selection, block-centric attention, MFMA
+    # BSA for bf16 at C = 64) and on the general ones
+    (3, 6000, 64, 128, 16, 8, 2, torch.bfloat16),
+    (2, 4096, 64, 64, 8, 2, 2, torch.bfloat16),
+    (2, 2500, 32, 64, 6, 4, 4, torch.float32),
+]
+
+
+@pytest.mark.parametrize("case", BATCHED, ids=[f"B{c[0]}_N{c[1]}_C{c[2]}_d{c[3]}_K{c[4]}_"
+                                               f"G{c[5] // c[6]}_"
+                                               f"{'bf16' if c[7] == torch.bfloat16 else 'f32'}"
+                                               for c in BATCHED])
+def test_prefill_batches(case):
+    """Prefill with several sequences per call: every (sequence, KV head)
+    against the oracle on every eleventh row and the last (N(0,1) entries)."""
+    bsz, n, c, d, k, hq, hkv, dtype = case
+    prob = Problem(bsz, hq, hkv, n, d, block=c, topk=k, dtype=dtype)
+    announce(f"prefill batch {case}")
+    inp = prefill_inputs(bsz, hq, hkv, n, d, dtype, seed=9100 + n, recipe="unit", device=DEV)
+    pyr = pisa_build_pyramid(prob, inp.k)
+    idx, score = pisa_select(prob, inp.q, inp.k, pyr)
+    bidx, bscore = pisa_bsa_select(prob, inp.q, pyr)
+    out, lse = pisa_block_sparse_attn(prob, inp.q, inp.k, inp.v, idx)
+    torch.cuda.synchronize()
+    check_pyramid(pyr, inp.k, prob, [(b, h) for b in range(bsz) for h in range(hkv)])
+    g = hq // hkv
+    rows = list(range(0, n, 11)) + [n - 1]
+    for b in range(bsz):
+        for h in range(hkv):
+            keys, vals = parity.to_np(inp.k[b, h]), parity.to_np(inp.v[b, h])
+            qg = parity.to_np(inp.q[b, h * g:(h + 1) * g])
+            levels = oracle.build_pyramid(keys, c)
+            for kind, ii, ss in (("pisa", idx, score), ("bsa", bidx, bscore)):
+                tl = parity.compare_selection(kind, ii[b, h].cpu().numpy(), ss[b, h].cpu().numpy(),
+                                              qg, keys, levels, rows, c, k, True, True,
+                                              prob.logit_scale, parity.Tally())
+                assert not tl.mismatches, (kind, b, h, tl.mismatches[:3])
+                assert tl.frac() > 0.5, (kind, b, h, tl.frac())
+            parity.compare_attention(parity.to_np(out[b, h * g:(h + 1) * g]),
+                                     lse[b, h * g:(h + 1) * g].cpu().numpy(), qg, keys, vals,
+                                     idx[b, h].cpu().numpy(), rows, c, True, prob.logit_scale,
+                                     fp32=dtype == torch.float32)
+
+
 @pytest.mark.parametrize("name", ["c2", "c4a"])
 def test_workload_parity_fused_strategy(name):
     """The per-query fused selector on the workload shape (the default picks the

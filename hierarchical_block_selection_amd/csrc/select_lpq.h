@@ -545,9 +545,11 @@ __global__ __launch_bounds__(kWaves * kWave, (G >= 2 && D == 64) ? 3 : 2) void s
                       z1 = 2 * n + 1 < m_child ? z1 : neg_inf();
                       w &= 2 * n < m_child;
                     }
-                    const float mx = fmaxf(z0, z1), mn = fminf(z0, z1);
-                    float v =
-                        fmaf(mx, scale_log2, fast_log2(1.f + fast_exp2((mn - mx) * scale_log2)));
+                    // min - max is -|z0 - z1| bit for bit; the sign and the
+                    // absolute value fold into the multiply's input modifiers
+                    const float mx = fmaxf(z0, z1);
+                    float v = fmaf(mx, scale_log2,
+                                   fast_log2(1.f + fast_exp2(-fabsf(z0 - z1) * scale_log2)));
                     v = group_add<G>(v);  // the writer lane's total is stored
                     scol[cb][w ? 2 * pslot + m : kSlots] = v;
                   }
@@ -704,9 +706,11 @@ __global__ __launch_bounds__(kWaves * kWave, (G >= 2 && D == 64) ? 3 : 2) void s
                       z1 = 2 * n + 1 < m_child ? z1 : neg_inf();
                       w &= 2 * n < m_child;
                     }
-                    const float mx = fmaxf(z0, z1), mn = fminf(z0, z1);
-                    float v =
-                        fmaf(mx, scale_log2, fast_log2(1.f + fast_exp2((mn - mx) * scale_log2)));
+                    // min - max is -|z0 - z1| bit for bit; the sign and the
+                    // absolute value fold into the multiply's input modifiers
+                    const float mx = fmaxf(z0, z1);
+                    float v = fmaf(mx, scale_log2,
+                                   fast_log2(1.f + fast_exp2(-fabsf(z0 - z1) * scale_log2)));
                     v = group_add<G>(v);  // the writer lane's total is stored
                     scol[cb][w ? 2 * pslot + m : kSlots] = v;
                   }

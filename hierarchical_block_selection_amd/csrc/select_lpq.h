@@ -323,8 +323,9 @@ __global__ __launch_bounds__(kWaves * kWave, (G >= 2 && D == 64) ? 3 : 2) void s
   constexpr int CLOADS = CPIECES / (kWaves * kWave);
   static_assert(CPIECES % (kWaves * kWave) == 0, "chunk pieces per thread");
   // score_s holds a query's slot scores and, after its decision has read
-  // them, its kept-node list (int bit patterns in rows 0..kMaxK).
-  __shared__ float score_s[kWaves][kSlots + 1][T];
+  // them, its kept-node list (int bit patterns in rows 0..kMaxK).  Rows
+  // kSlots and kSlots + 1 take the stores of positions that are no candidate.
+  __shared__ float score_s[kWaves][kSlots + 2][T];
   __shared__ uint32_t mask_s[kWaves][kShared ? kMaskWords : 1][T];
   __shared__ __align__(16) bf16_t chunk_s[kShared ? 2 * 32 * CROW : 8];
   __shared__ uint32_t chunks_s[2][kWaves][2];
@@ -551,7 +552,10 @@ __global__ __launch_bounds__(kWaves * kWave, (G >= 2 && D == 64) ? 3 : 2) void s
                     float v = fmaf(mx, scale_log2,
                                    fast_log2(1.f + fast_exp2(-fabsf(z0 - z1) * scale_log2)));
                     v = group_add<G>(v);  // the writer lane's total is stored
-                    scol[cb][w ? 2 * pslot + m : kSlots] = v;
+                    if constexpr (kFull)  // both children exist: one row select per pair
+                      scol[cb][(has ? 2 * pslot : kSlots) + m] = v;
+                    else
+                      scol[cb][w ? 2 * pslot + m : kSlots] = v;
                   }
                 }
               }
@@ -712,7 +716,10 @@ __global__ __launch_bounds__(kWaves * kWave, (G >= 2 && D == 64) ? 3 : 2) void s
                     float v = fmaf(mx, scale_log2,
                                    fast_log2(1.f + fast_exp2(-fabsf(z0 - z1) * scale_log2)));
                     v = group_add<G>(v);  // the writer lane's total is stored
-                    scol[cb][w ? 2 * pslot + m : kSlots] = v;
+                    if constexpr (kFull)  // both children exist: one row select per pair
+                      scol[cb][(has ? 2 * pslot : kSlots) + m] = v;
+                    else
+                      scol[cb][w ? 2 * pslot + m : kSlots] = v;
                   }
                 }
                 base[cb] += __popc(byte[cb]);

@@ -26,8 +26,8 @@
 // needed by any of their columns: each chunk is loaded once, coalesced, into
 // LDS (the next one is in flight in registers meanwhile), and every wave
 // computes its logits on the matrix cores (32 rows x 64 columns per step;
-// bf16 hi/lo planes of the fp32 summaries, so each product is exact and
-// accumulation is fp32).  While the logits are still in the MFMA register
+// bf16 hi/lo planes of the fp32 summaries times the logit scale in log2
+// units, so each product is exact and accumulation is fp32).  While the logits are still in the MFMA register
 // layout it forms the log-sum-exp of every sibling pair (eq. (7)), sums the
 // group's heads (eq. (11)) and scatters the
 // scores of the pairs that are candidates of the column's query into that
@@ -266,14 +266,15 @@ __device__ __forceinline__ void compact_kept(uint32_t km, Col row, NodeOf node_o
   }
 }
 
-// Split fp32 pyramid values into bf16 hi/lo planes: x = hi + lo + r with
-// |r| <= 2^-16 |x|, so that a bf16 MFMA over both planes reproduces an fp32
-// dot product to that accuracy.  Stage 1 reads child rows of levels 2 and up
-// only, so each head's level 1 (its first skip_rows rows of row_len values)
-// is left out; 8 values per thread and step.
+// Split fp32 pyramid values, times mul (the logit scale in log2 units, so
+// that stage 1's products come out as log2-unit logits), into bf16 hi/lo
+// planes: mul x = hi + lo + r with |r| <= 2^-16 |mul x|, so that a bf16 MFMA
+// over both planes reproduces an fp32 dot product to that accuracy.  Stage 1
+// reads child rows of levels 2 and up only, so each head's level 1 (its first
+// skip_rows rows of row_len values) is left out; 8 values per thread and step.
 __global__ void split_planes_kernel(const float* __restrict__ pyr, bf16_t* __restrict__ hi,
                                     bf16_t* __restrict__ lo, int heads, size_t head_len,
-                                    size_t skip) {
+                                    size_t skip, float mul) {
   const size_t per_head = (head_len - skip) / 8;  // 8-value groups split per head
   const size_t n = per_head * heads;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
@@ -281,7 +282,8 @@ __global__ void split_planes_kernel(const float* __restrict__ pyr, bf16_t* __res
     const size_t e = (i / per_head) * head_len + skip + 8 * (i % per_head);
     const float4 x0 = *reinterpret_cast<const float4*>(pyr + e);
     const float4 x1 = *reinterpret_cast<const float4*>(pyr + e + 4);
-    const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    const float x[8] = {x0.x * mul, x0.y * mul, x0.z * mul, x0.w * mul,
+                        x1.x * mul, x1.y * mul, x1.z * mul, x1.w * mul};
     uint32_t h2[4], l2[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -307,8 +309,8 @@ template <int D, int G>
 __global__ __launch_bounds__(kWaves * kWave, (G >= 2 && D == 64) ? 3 : 2) void stage1_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ phi, const bf16_t* __restrict__ plo,
     int* __restrict__ s1_nodes, int heads_q, int heads_kv,
-    int n_tok, int block, int topk, int causal, int force, float scale_log2, LevelTable lv,
-    int split_level, int tile_rows) {
+    int n_tok, int block, int topk, int causal, int force, LevelTable lv, int split_level,
+    int tile_rows) {
   constexpr int T = kWave / G;  // queries per wave
   constexpr int KSTEPS = D / 16;
   // With 8 or more queries per wave the waves of a workgroup need nearly the
@@ -546,11 +548,11 @@ __global__ __launch_bounds__(kWaves * kWave, (G >= 2 && D == 64) ? 3 : 2) void s
                       z1 = 2 * n + 1 < m_child ? z1 : neg_inf();
                       w &= 2 * n < m_child;
                     }
-                    // min - max is -|z0 - z1| bit for bit; the sign and the
-                    // absolute value fold into the multiply's input modifiers
+                    // the planes carry scale * log2(e) already: logits in
+                    // log2 units; -|z0 - z1| folds into the exp's input
+                    // modifiers
                     const float mx = fmaxf(z0, z1);
-                    float v = fmaf(mx, scale_log2,
-                                   fast_log2(1.f + fast_exp2(-fabsf(z0 - z1) * scale_log2)));
+                    float v = mx + fast_log2(1.f + fast_exp2(-fabsf(z0 - z1)));
                     v = group_add<G>(v);  // the writer lane's total is stored
                     if constexpr (kFull)  // both children exist: one row select per pair
                       scol[cb][(has ? 2 * pslot : kSlots) + m] = v;
@@ -710,11 +712,11 @@ __global__ __launch_bounds__(kWaves * kWave, (G >= 2 && D == 64) ? 3 : 2) void s
                       z1 = 2 * n + 1 < m_child ? z1 : neg_inf();
                       w &= 2 * n < m_child;
                     }
-                    // min - max is -|z0 - z1| bit for bit; the sign and the
-                    // absolute value fold into the multiply's input modifiers
+                    // the planes carry scale * log2(e) already: logits in
+                    // log2 units; -|z0 - z1| folds into the exp's input
+                    // modifiers
                     const float mx = fmaxf(z0, z1);
-                    float v = fmaf(mx, scale_log2,
-                                   fast_log2(1.f + fast_exp2(-fabsf(z0 - z1) * scale_log2)));
+                    float v = mx + fast_log2(1.f + fast_exp2(-fabsf(z0 - z1)));
                     v = group_add<G>(v);  // the writer lane's total is stored
                     if constexpr (kFull)  // both children exist: one row select per pair
                       scol[cb][(has ? 2 * pslot : kSlots) + m] = v;

@@ -658,13 +658,13 @@ hipError_t stage1_lpq_launch(const LaunchShape& s, const void* q, const float* p
     const size_t groups = (head_len - skip) / 8 * heads;
     if (groups > 0)
       hipLaunchKernelGGL(lpq::split_planes_kernel, dim3(bucket::grid_for(groups)), dim3(256), 0, st,
-                         pyr, w.plane_hi, w.plane_lo, heads, head_len, skip);
+                         pyr, w.plane_hi, w.plane_lo, heads, head_len, skip, s.scale * kLog2e);
   }
   prof::Scope ps("select_stage1", st);
   hipLaunchKernelGGL((lpq::stage1_kernel<D, G>), grid, dim3(lpq::kWaves * kWave), 0, st,
                      static_cast<const bf16_t*>(q), w.plane_hi, w.plane_lo, w.s1_nodes,
                      s.heads_q, s.heads_kv, s.seq_len, s.block, s.topk, s.causal ? 1 : 0,
-                     s.force ? 1 : 0, s.scale * kLog2e, s.lv, kSplitLevel, s1_tile_rows());
+                     s.force ? 1 : 0, s.lv, kSplitLevel, s1_tile_rows());
   return hipGetLastError();
 }
 

@@ -221,7 +221,9 @@ __global__ __launch_bounds__(256, 2) void bsa_scores_mfma_kernel(
       const int lim = causal ? t / block : m1 - 1;
       const bool forced = causal && ((leaf == lim) | (force && ((leaf == 0) | (leaf == lim - 1))));
       if (t < n_tok && leaf < m1 && leaf < ((lim + 4) & ~3))
-        S[((size_t)bh * n_tok + t) * m1 + leaf] = (leaf <= lim && !forced) ? acc[i] * scale : neg_inf();
+        // streamed out: read once, by the Top-K pass
+        __builtin_nontemporal_store((leaf <= lim && !forced) ? acc[i] * scale : neg_inf(),
+                                    &S[((size_t)bh * n_tok + t) * m1 + leaf]);
     }
     if (lt + 1 < n_tiles) {
       put(buf ^ 1);  // the other buffer was last read one tile ago

@@ -196,6 +196,10 @@ __global__ __launch_bounds__(256, 2) void bsa_scores_mfma_kernel(
         *reinterpret_cast<u32x4_t*>(&bs[buf][p][(rem / V16) * ROW + 8 * (rem % V16)]) = stage[i];
     }
   };
+  // The tile loop decides its stores and masks without branches: the
+  // causal bound of row t is t >> log2(C) (C is a power of two).
+  const bool cz = causal != 0, fz = force != 0;
+  const int cshift = 31 - __builtin_clz(block);
   fetch(0);
   put(0);
   __syncthreads();
@@ -215,15 +219,17 @@ __global__ __launch_bounds__(256, 2) void bsa_scores_mfma_kernel(
       }
     // acc[i] = S[query tq0 + (i/4)*8 + 4kh + i%4][leaf lt*32 + col]
     const int leaf = lt * kMfmaL + col;
+    const bool leaf_ok = leaf < m1;
+    float* const srow0 = S + ((size_t)bh * n_tok + tq0 + 4 * kh) * m1 + leaf;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int t = tq0 + (i / 4) * 8 + 4 * kh + (i % 4);
-      const int lim = causal ? t / block : m1 - 1;
-      const bool forced = causal && ((leaf == lim) | (force && ((leaf == 0) | (leaf == lim - 1))));
-      if (t < n_tok && leaf < m1 && leaf < ((lim + 4) & ~3))
-        // streamed out: read once, by the Top-K pass
-        __builtin_nontemporal_store((leaf <= lim && !forced) ? acc[i] * scale : neg_inf(),
-                                    &S[((size_t)bh * n_tok + t) * m1 + leaf]);
+      const int lim = cz ? t >> cshift : m1 - 1;
+      const bool forced = cz & ((leaf == lim) | (fz & ((leaf == 0) | (leaf == lim - 1))));
+      const bool keep = (t < n_tok) & leaf_ok & (leaf < ((lim + 4) & ~3));
+      const float val = (leaf <= lim) & !forced ? acc[i] * scale : neg_inf();
+      if (keep)  // streamed out: read once, by the Top-K pass
+        __builtin_nontemporal_store(val, srow0 + (size_t)((i / 4) * 8 + (i % 4)) * m1);
     }
     if (lt + 1 < n_tiles) {
       put(buf ^ 1);  // the other buffer was last read one tile ago

@@ -144,7 +144,9 @@ __device__ __forceinline__ bool ranks_before(float s1, int i1, float s2, int i2)
 // unranked slot.
 __device__ __forceinline__ uint32_t rank_key_rel(float s, float smax, int slot) {
   constexpr uint32_t kTop = (1u << 27) - 1u;
-  const float dq = (smax - s) * 4096.f;  // >= 0; NaN when both are -inf
+  // (smax - s) * 4096 as one fma: scaling by a power of two commutes with
+  // the rounding, and smax * 4096 is shared by every slot of a decision
+  const float dq = fmaf(s, -4096.f, smax * 4096.f);  // >= 0; NaN when both are -inf
   const uint32_t qv = dq < float(kTop - 1u) ? uint32_t(dq) : kTop - 1u;
   return ((kTop - qv) << 5) | uint32_t(31 - slot);
 }

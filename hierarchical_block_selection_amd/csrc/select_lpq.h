@@ -164,9 +164,15 @@ __device__ __forceinline__ uint32_t top_slots(int n_valid, int topk, uint32_t fm
                                               const float (&s)[kSlots]) {
   const uint32_t rm = prefix_mask(n_valid) & ~fm;
   const int keep_n = topk - __popc(fm);
-  float smax = neg_inf();
+  // best rankable score by a tree of maxima (independent steps, not a chain)
+  float mv[kSlots];
 #pragma unroll
-  for (int j = 0; j < kSlots; ++j) smax = ((rm >> j) & 1u) ? fmaxf(smax, s[j]) : smax;
+  for (int j = 0; j < kSlots; ++j) mv[j] = ((rm >> j) & 1u) ? s[j] : neg_inf();
+#pragma unroll
+  for (int w = kSlots / 2; w >= 1; w /= 2)
+#pragma unroll
+    for (int j = 0; j < w; ++j) mv[j] = fmaxf(mv[j], mv[j + w]);
+  const float smax = mv[0];
   uint32_t key[kSlots];
 #pragma unroll
   for (int j = 0; j < kSlots; ++j) key[j] = ((rm >> j) & 1u) ? rank_key_rel(s[j], smax, j) : 0u;

@@ -459,11 +459,12 @@ __device__ __forceinline__ uint32_t row_sort_desc32(uint32_t x, int hl) {
 }
 
 // lanes per row (32 or 64), scores per lane (% 4 == 0), rows longer than LPR * VPL.
-// Rows of up to 2048 leaves run four waves per SIMD (128 VGPRs, a few spilled):
-// the pass waits on its row loads, and more waves keep more of them in flight
-// (Top-K at 128K 0.66 -> 0.56-0.62 ms against three waves per SIMD).
+// Rows held as 64 scores per lane (1025 to 4096 leaves) run four waves per
+// SIMD (128 VGPRs, a few spilled): the pass waits on its row loads, and more
+// waves keep more of them in flight (Top-K at 128K 0.66 -> 0.56-0.62 ms
+// against three waves per SIMD; about 3% at 256K).
 template <int LPR, int VPL, bool kLong>
-__global__ __launch_bounds__(256, (LPR == 32 && VPL == 64) ? 4 : 1) void bsa_topk_rows_kernel(
+__global__ __launch_bounds__(256, (VPL == 64 && !kLong) ? 4 : 1) void bsa_topk_rows_kernel(
                                                             const float* __restrict__ S,
                                                             int32_t* __restrict__ idx,
                                                             float* __restrict__ score, int n_tok,

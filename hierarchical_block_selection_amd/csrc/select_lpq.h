@@ -449,9 +449,12 @@ __global__ __launch_bounds__(kWaves * kWave, (G >= 2 && D == 64) ? 3 : 2) void s
 #pragma unroll
           for (int w = 0; w < kMaskWords; ++w) {
             const uint32_t word = mrow[w];
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              cw[w >> 3] |= ((word >> (8 * j)) & 0xffu) ? (1u << ((4 * w + j) & 31)) : 0u;
+            // bit 8j + 7 set iff byte j is nonzero, then the four flags packed
+            // into bits 0..3
+            const uint32_t f = (((word & 0x7f7f7f7fu) + 0x7f7f7f7fu) | word) & 0x80808080u;
+            const uint32_t y = f >> 7;
+            const uint32_t nib = (y | (y >> 7) | (y >> 14) | (y >> 21)) & 0xfu;
+            cw[w >> 3] |= nib << (4 * (w & 7));
           }
         }
 #pragma unroll

@@ -122,7 +122,7 @@ __global__ void bsa_split_kernel(const float* __restrict__ pyr, bf16_t* __restri
 // entries from its causal bound up to the next multiple of 4 hold -inf, so
 // that the Top-K pass reads whole 16-byte groups without masks.
 template <int D, int G>
-__global__ __launch_bounds__(256, 2) void bsa_scores_mfma_kernel(
+__global__ __launch_bounds__(256, D == 64 ? 4 : 3) void bsa_scores_mfma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ planes, float* __restrict__ S,
     int heads_q, int heads_kv, int n_tok, int block, int m1, int causal, int force, float scale,
     size_t plane_stride) {
@@ -139,6 +139,7 @@ __global__ __launch_bounds__(256, 2) void bsa_scores_mfma_kernel(
   const int lim_last = causal ? t_last / block : m1 - 1;
   const int n_tiles = lim_last / kMfmaL + 1;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  __builtin_assume(tid < 256);  // the launch's block size: fetch/put guards fold when 256 | PIECES
   const int col = lane & 31, kh = lane >> 5;
   const int tq0 = t0 + 32 * wave;
   // A operands: this lane's query row (clamped).  Eq. (1) summed over the
@@ -152,27 +153,31 @@ __global__ __launch_bounds__(256, 2) void bsa_scores_mfma_kernel(
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) a[0][s] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qr + 16 * s));
   } else {
+    // One head's row at a time (heads in order), so that the loads of all
+    // G rows are never live together.
+    float sum[KSTEPS][8] = {};
+#pragma unroll 1
+    for (int h = 0; h < G; ++h) {
+      const bf16_t* qr = q + (((size_t)b * heads_q + (size_t)kvh * G + h) * n_tok + tq) * D + 8 * kh;
+      u32x4_t w[KSTEPS];
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-      float sum[8] = {};
+      for (int s = 0; s < KSTEPS; ++s) w[s] = *reinterpret_cast<const u32x4_t*>(qr + 16 * s);
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const bf16_t* qr =
-            q + (((size_t)b * heads_q + (size_t)kvh * G + h) * n_tok + tq) * D + 8 * kh + 16 * s;
-        const u32x4_t w = *reinterpret_cast<const u32x4_t*>(qr);
+      for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          sum[2 * e] += __uint_as_float(w[e] << 16);
-          sum[2 * e + 1] += __uint_as_float(w[e] & 0xffff0000u);
+          sum[s][2 * e] += __uint_as_float(w[s][e] << 16);
+          sum[s][2 * e + 1] += __uint_as_float(w[s][e] & 0xffff0000u);
         }
-      }
+    }
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const __bf16 hi = (__bf16)sum[e];
+        const __bf16 hi = (__bf16)sum[s][e];
         a[0][s][e] = hi;
-        a[1][s][e] = (__bf16)(sum[e] - (float)hi);
+        a[1][s][e] = (__bf16)(sum[s][e] - (float)hi);
       }
-    }
   }
   const bf16_t* pb = planes + (size_t)bh * m1 * D;
   u32x4_t stage[PER_THREAD];

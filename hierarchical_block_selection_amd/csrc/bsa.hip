@@ -121,6 +121,11 @@ __global__ void bsa_split_kernel(const float* __restrict__ pyr, bf16_t* __restri
 // leaves (§5.3: current, and with forcing the first and the previous) and the
 // entries from its causal bound up to the next multiple of 4 hold -inf, so
 // that the Top-K pass reads whole 16-byte groups without masks.
+//
+// The pass waits on its score stores, so occupancy is what moves it: three
+// workgroups per CU at d = 128 (their LDS tiles take 153 KB) and four at
+// d = 64, which caps the registers at 168 and 128 (128K: 0.75-0.80 ->
+// 0.67 ms against two per CU).
 template <int D, int G>
 __global__ __launch_bounds__(256, D == 64 ? 4 : 3) void bsa_scores_mfma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ planes, float* __restrict__ S,
